@@ -1,0 +1,217 @@
+"""Seeded synthetic inputs shared by the oracle checks, the tests and the bench.
+
+This package holds no arithmetic of the eviction method: it only draws
+random numbers and converts them to the storage types (bfloat16 keys and
+values via torch's round-to-nearest-even cast, float32 queries).  Both the
+float64 oracle and the HIP library consume what it returns.
+
+Every tensor of every unit has its own numpy stream,
+``default_rng(SeedSequence([seed, workload_id, kind, index]))``, so any one
+unit can be regenerated on its own (the parity tests check sampled units of
+full-size workloads that way).
+
+Value structure (a stand-in for the reasoning traces the pages measure on;
+see the design notes for the recipe and its reasons):
+
+* keys, values ~ N(0, 1), optionally with a few outlier channels scaled up;
+* a pre-RoPE query at nominal position p is *local* with probability
+  1 - pi_g -- a copy of a key near p plus N(0, 0.3^2) noise -- or *global*
+  with probability pi_g -- 8 times one of the head's cluster centres (unit
+  vectors) plus the same noise;
+* buffer queries take p uniform over [P, L - 16); recent query i takes
+  p = its own position.
+"""
+
+from dataclasses import dataclass, field, replace
+
+import numpy as np
+import torch
+
+KIND_K, KIND_V, KIND_CENTRES, KIND_BUF, KIND_RECENT, KIND_OUTLIER, KIND_NEWQ = range(1, 8)
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    wid: int            # workload id, part of every seed
+    layers: int
+    batch: int
+    h_kv: int
+    group: int          # query heads per KV head
+    d_head: int
+    L: int              # live slots when eviction fires
+    b_kv: int           # slots kept
+    prefix: int
+    theta: float
+    recent_tok: int = 16
+    n_beacon: int = 16
+    n_recent_q: int = 16
+    buf_cap: int = 32
+    pi_global: float = 0.25
+    n_centres: int = 3
+    outlier_channels: int = 0
+    outlier_scale: float = 6.0
+    seed: int = 0
+    l_cap: int = 0      # slot stride; 0 means L
+
+    @property
+    def n_units(self):
+        return self.layers * self.batch * self.h_kv
+
+    @property
+    def n_qheads(self):
+        return self.n_units * self.group
+
+    @property
+    def cap(self):
+        return self.l_cap or self.L
+
+    def layer_of(self, u):
+        return u // (self.batch * self.h_kv)
+
+
+def _tiny():
+    return Workload("tiny", 1, layers=1, batch=1, h_kv=2, group=2, d_head=64,
+                    L=256, b_kv=128, prefix=8, theta=1e4)
+
+
+def _qwen3_4b_layer():
+    return Workload("qwen3-4b-1layer-b1", 2, layers=1, batch=1, h_kv=8, group=4,
+                    d_head=128, L=2176, b_kv=2048, prefix=256, theta=1e6,
+                    pi_global=0.10, n_centres=6, outlier_channels=4)
+
+
+def _qwen3_4b_full(b_kv):
+    return Workload(f"qwen3-4b-36L-b16-B{b_kv}", 3, layers=36, batch=16, h_kv=8,
+                    group=4, d_head=128, L=b_kv + 128, b_kv=b_kv, prefix=8,
+                    theta=1e6)
+
+
+def _r1_qwen_7b():
+    return Workload("r1-distill-qwen-7b-28L-b32-B4096", 4, layers=28, batch=32,
+                    h_kv=4, group=7, d_head=128, L=4224, b_kv=4096, prefix=512,
+                    theta=1e6)
+
+
+WORKLOADS = {
+    "tiny": _tiny(),
+    "qwen3_4b_layer": _qwen3_4b_layer(),
+    "qwen3_4b_full_b128": _qwen3_4b_full(128),
+    "qwen3_4b_full_b512": _qwen3_4b_full(512),
+    "qwen3_4b_full_b1024": _qwen3_4b_full(1024),
+    "qwen3_4b_full_b2048": _qwen3_4b_full(2048),
+    "qwen3_4b_full_b4096": _qwen3_4b_full(4096),
+    "r1_qwen_7b": _r1_qwen_7b(),
+}
+
+
+def shrink(w, **kw):
+    """A copy of a workload with some fields replaced (smaller test cases)."""
+    return replace(w, **kw)
+
+
+def _rng(w, kind, index):
+    return np.random.default_rng(np.random.SeedSequence([w.seed, w.wid, kind, index]))
+
+
+def to_bf16_values(x):
+    """float32 -> bfloat16 (torch's RNE cast) -> float32 holding the bf16 values."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).to(torch.float32).numpy()
+
+
+def outlier_channels(w, layer):
+    if w.outlier_channels == 0:
+        return np.zeros(0, dtype=np.int64)
+    r = _rng(w, KIND_OUTLIER, layer)
+    return np.sort(r.choice(w.d_head, size=w.outlier_channels, replace=False))
+
+
+def unit_keys_values(w, u):
+    """Keys and values of unit u, [L, d] float32 holding bfloat16 values."""
+    k = _rng(w, KIND_K, u).standard_normal((w.L, w.d_head), dtype=np.float32)
+    ch = outlier_channels(w, w.layer_of(u))
+    if ch.size:
+        k[:, ch] *= np.float32(w.outlier_scale)
+    v = _rng(w, KIND_V, u).standard_normal((w.L, w.d_head), dtype=np.float32)
+    return to_bf16_values(k), to_bf16_values(v)
+
+
+def _mixture(w, r, keys, centres, positions):
+    """Pre-RoPE queries at the given nominal positions (float32)."""
+    n = len(positions)
+    q = np.empty((n, w.d_head), dtype=np.float32)
+    is_global = r.random(n) < w.pi_global
+    which = r.integers(0, w.n_centres, size=n)
+    noise = r.standard_normal((n, w.d_head), dtype=np.float32) * np.float32(0.3)
+    for i, p in enumerate(positions):
+        if is_global[i]:
+            q[i] = 8.0 * centres[which[i]]
+        else:
+            lo = max(0, int(p) - 31)
+            j = int(r.integers(lo, int(p) + 1))
+            q[i] = keys[min(j, keys.shape[0] - 1)]
+    return q + noise
+
+
+def head_centres(w, qh):
+    c = _rng(w, KIND_CENTRES, qh).standard_normal((w.n_centres, w.d_head))
+    return (c / np.linalg.norm(c, axis=1, keepdims=True)).astype(np.float32)
+
+
+def unit_queries(w, u, keys):
+    """Buffer rows [g, buf_cap, d] and recent queries [g, n_recent_q, d].
+
+    The buffer is full (buf_cap rows); the last n_recent_q slots hold the
+    most recent tokens, whose positions are their slots.
+    """
+    g, d = w.group, w.d_head
+    buf = np.empty((g, w.buf_cap, d), dtype=np.float32)
+    rec = np.empty((g, w.n_recent_q, d), dtype=np.float32)
+    hi = max(w.prefix + 1, w.L - 16)
+    for h in range(g):
+        qh = u * g + h
+        cen = head_centres(w, qh)
+        rb = _rng(w, KIND_BUF, qh)
+        pos = rb.integers(w.prefix, hi, size=w.buf_cap)
+        buf[h] = _mixture(w, rb, keys, cen, pos)
+        rr = _rng(w, KIND_RECENT, qh)
+        rpos = np.arange(w.L - w.n_recent_q, w.L)
+        rec[h] = _mixture(w, rr, keys, cen, rpos)
+    return buf, rec
+
+
+def new_queries(w, u, keys, n_new=1, step=0):
+    """n_new further pre-RoPE queries per head of unit u, [g, n_new, d]."""
+    g = w.group
+    out = np.empty((g, n_new, w.d_head), dtype=np.float32)
+    for h in range(g):
+        qh = u * g + h
+        r = np.random.default_rng(np.random.SeedSequence(
+            [w.seed, w.wid, KIND_NEWQ, qh, step]))
+        pos = np.full(n_new, w.L - 1)
+        out[h] = _mixture(w, r, keys, head_centres(w, qh), pos)
+    return out
+
+
+def unit_inputs(w, u):
+    """Everything one unit needs for a single eviction event at t = L.
+
+    Returns dict(keys, values [L, d] float32 (bf16 values), kpos [L] int32,
+    buf [g, buf_cap, d] float32, recents [g, n_recent_q, d] float32, t).
+    The beacons are rows 0..n_beacon-1 of ``buf`` after it is compressed.
+    """
+    k, v = unit_keys_values(w, u)
+    buf, rec = unit_queries(w, u, k)
+    return {"keys": k, "values": v, "kpos": np.arange(w.L, dtype=np.int32),
+            "buf": buf, "recents": rec, "t": w.L}
+
+
+def workload_inputs(w, units=None):
+    """Stack unit_inputs over ``units`` (default: all), host arrays."""
+    units = range(w.n_units) if units is None else units
+    parts = [unit_inputs(w, u) for u in units]
+    out = {key: np.stack([p[key] for p in parts]) for key in
+           ("keys", "values", "kpos", "buf", "recents")}
+    out["t"] = w.L
+    return out

@@ -1,0 +1,63 @@
+"""Pins of the Continual-FPS cadence and the cache-size closed form."""
+import os
+from collections import Counter
+
+import numpy as np
+
+from oracle.evict import evict_unit, moved_tokens
+from oracle.stream import UnitStream, kv_cache_bytes
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_cadence_per_eviction_interval():
+    # Derived from the summary's steps (2), (3), (6): after an eviction the
+    # buffer holds 16; 128 - 16 = 112 collected queries trigger 112 / 16 = 7
+    # fill-and-compress events, the beacon fix then finds 16 rows (a no-op),
+    # 16 recents are set aside, and the eviction's merge compresses 32 -> 16.
+    g, d, b_kv, P = 1, 8, 64, 4
+    st = UnitStream(g, d, b_max=b_kv + 128, b_kv=b_kv, prefix=P, theta=1e4)
+    r = np.random.default_rng(0)
+    st.prefill(r.standard_normal((P, d)), r.standard_normal((P, d)),
+               r.standard_normal((g, P, d)))
+    n_steps = 3 * 128 + 120
+    for _ in range(n_steps):
+        st.step(r.standard_normal(d), r.standard_normal(d), r.standard_normal((g, d)))
+    ev = [e for e, _ in st.events]
+    cuts = [i for i, e in enumerate(ev) if e == "evict"]
+    assert len(cuts) == 3
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        c = Counter(ev[a + 1:b + 1])
+        assert c["collect_fps"] == 7
+        assert c["beacon_fix_noop"] == 1 and c["beacon_fix_fps"] == 0
+        assert c["merge_fps"] == 1 and c["evict"] == 1
+    first = (b_kv + 128) - P  # steps until the first eviction
+    assert st.keys.shape[0] == b_kv + (n_steps - first - 2 * 128)
+    since = n_steps - first - 2 * 128  # collected since the last merge
+    assert all(b.shape[0] == 16 + since % 16 for b in st.buf)
+
+
+def test_kv_cache_size_claim():
+    vals = {}
+    with open(os.path.join(GOLDEN, "kv_cache_size.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                k, v = line.split()
+                vals[k] = float(v)
+    gb = kv_cache_bytes(int(vals["layers"]), int(vals["kv_heads"]), int(vals["d_head"]),
+                        int(vals["seq"]), int(vals["batch"]), int(vals["bytes_per_elem"])) / 1e9
+    assert gb > vals["claim_gb_more_than"]
+    assert abs(gb - 77.3) < 0.05
+
+
+def test_evict_unit_invariants_and_merge():
+    r = np.random.default_rng(3)
+    L, d, g, b, P = 160, 16, 2, 96, 8
+    keys, vals = r.standard_normal((L, d)), r.standard_normal((L, d))
+    out = evict_unit(keys, vals, np.arange(L), L, r.standard_normal((g, 16, d)),
+                     r.standard_normal((g, 16, d)), L, b, P, 16, 1e4)
+    kept = out["kept"]
+    assert len(kept) == b and set(range(P)) <= set(kept) and set(range(L - 16, L)) <= set(kept)
+    assert np.array_equal(out["keys"], keys[kept])
+    assert out["buf"].shape == (g, 16, d)
+    assert 0 <= moved_tokens(kept) <= b - P

@@ -1,0 +1,206 @@
+/*
+ * bkv.h -- C ABI of the BeaconKV eviction-step library for MI355X (gfx950).
+ *
+ * The library implements the data-parallel eviction step of BeaconKV
+ * ("BeaconKV: Key-Value Cache Compression Guided by Beacon Queries for
+ * Efficient Large Reasoning Model Inference"; cited below as *paper text*
+ * for the paper's own prose, *summary* for the structured summary page whose
+ * section "方法步骤详情" restates Algorithm 2 as steps (1)-(6), and *review*
+ * for the jaehun.me review page).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensor pointers are DEVICE pointers allocated and owned by the caller.
+ *    The library allocates no device memory in these calls and keeps no
+ *    state between calls; scratch memory comes from the caller's workspace.
+ *  - bfloat16 tensors are passed as uint16_t bit patterns.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Every call only enqueues work on `stream`; none synchronises the host.
+ *  - Return codes: BKV_OK, or a negative error.  Arguments are validated on
+ *    the host BEFORE anything is enqueued; on an error nothing is launched
+ *    and bkv_last_error() describes the problem.  No C++ exception crosses
+ *    this ABI.  A launch or runtime failure returns BKV_EHIP (work enqueued
+ *    earlier in the same call may already be running).
+ *  - Inputs are const.  Outputs must not alias inputs, except where a call
+ *    documents an in-place mode.
+ *  - Layouts (row-major; U = n_units KV groups, g = group, Uq = U*g query
+ *    heads, d = d_head):
+ *        K, V      bf16  [U, l_cap, d]   post-RoPE keys / values per slot
+ *        kpos      int32 [U, l_cap]      absolute position of each slot
+ *        score     fp32  [U, l_cap]      pooled attention score per slot
+ *        kept      int32 [U, b_kv]       kept slots, ascending
+ *        buf       fp32  [Uq, buf_cap, d] pre-RoPE query buffer per head
+ *        count     int32 [Uq]            rows in use in buf
+ *        recents   fp32  [Uq, n_recent_q, d] pre-RoPE recent queries
+ *    Unit u is (layer * batch + b) * h_kv + kv_head; query head j of unit u
+ *    is u * g + j.
+ */
+#ifndef BKV_H
+#define BKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BKV_ABI_VERSION 1
+
+enum {
+    BKV_OK = 0,
+    BKV_EINVAL = -1,  /* bad pointer, shape or parameter */
+    BKV_ENOTSUP = -2, /* valid but unsupported (d_head, group, buffer size) */
+    BKV_ENOSPC = -3,  /* workspace too small */
+    BKV_EHIP = -4     /* HIP launch/runtime error */
+};
+
+/* Shape of the cache being processed. */
+typedef struct bkv_dims {
+    int64_t n_units; /* U: KV groups (layers x batch x KV heads); 0 is a no-op */
+    int32_t group;   /* g: query heads sharing one KV head, 1..8 */
+    int32_t d_head;  /* d: 64 or 128 */
+    int64_t l_cap;   /* slot stride of K, V, kpos and score (>= L) */
+} bkv_dims;
+
+/* Method parameters.  Paper text §5.1 ("Implementation Details"): beacon
+ * budget max 32 / min 16, recent query budget 16; summary step (5): prefix
+ * and recent tokens always kept. */
+typedef struct bkv_policy {
+    int32_t n_beacon;   /* beacon rows per query head used for scoring: 16 */
+    int32_t n_recent_q; /* recent queries per query head: 16 */
+    int32_t buf_cap;    /* rows per head in buf (32; up to 256 for prefill) */
+    int32_t prefix;     /* P: leading slots always kept */
+    int32_t recent_tok; /* R: trailing slots always kept */
+    int32_t flags;      /* reserved, must be 0 */
+    double rope_theta;  /* RoPE base theta (> 0) */
+    float sm_scale;     /* softmax scale; 0 means 1/sqrt(d_head) */
+    int32_t reserved;   /* must be 0 */
+} bkv_policy;
+
+/* ABI version the library was built with (BKV_ABI_VERSION). */
+int bkv_abi_version(void);
+
+/* Message for the last error returned on the calling thread ("" if none).
+ * The pointer stays valid until the next bkv_* call on the same thread. */
+const char* bkv_last_error(void);
+
+/* Workspace bytes.  With b_kv == 0: what bkv_score needs (the RoPE angle
+ * table).  With b_kv > 0: what bkv_evict needs for (L, b_kv), which also
+ * covers the score and kept arrays when the caller passes none.  Returns 0
+ * on invalid arguments (see bkv_last_error). */
+size_t bkv_workspace_bytes(const bkv_dims* dims, const bkv_policy* pol,
+                           int64_t L, int64_t b_kv);
+
+/*
+ * bkv_fps_update -- Continual-FPS fill and compress of the per-head buffers.
+ *
+ * Paper text §4.2 ("Continual FPS") and App. D.1 (Algorithm 1, FPS);
+ * summary steps (2), (3) and (6).  For every query head q in [0, Uq):
+ *   1. append: rows new_q[q, 0..n_new) are copied to buf[q, count[q] + i];
+ *      count[q] += n_new.  A head whose rows would not fit
+ *      (count + n_new > buf_cap) is left completely unchanged and, if
+ *      n_overflow is non-NULL, *n_overflow is atomically incremented.
+ *   2. compress: if count[q] >= trigger, FPS under cosine similarity picks m
+ *      rows (seed: lowest average cosine to the whole buffer; then
+ *      repeatedly the row whose largest cosine to the picked set is lowest;
+ *      ties to the lower slot).  The picked rows are stored in ascending
+ *      original slot order in buf[q, 0..m) and count[q] = m.  If sel_order is
+ *      non-NULL, sel_order[q, i] is the original slot of the i-th pick
+ *      (heads that do not compress get -1 there).
+ * Typical calls: trigger = buf_cap = 32, m = 16 (fill and compress);
+ * trigger = m + 1 (beacon fix: compress only heads holding more than m);
+ * n_new = 16 recents with trigger 32 after an eviction (merge).
+ * Arithmetic is fp32.  Requires 0 <= n_new <= buf_cap, new_q NULL iff
+ * n_new == 0, 1 <= m < trigger <= buf_cap <= 256, every count in
+ * [0, buf_cap] on entry.  buf and count are updated in place; new_q must not
+ * overlap buf.
+ */
+int bkv_fps_update(const bkv_dims* dims, const bkv_policy* pol, float* buf,
+                   int32_t* count, const float* new_q, int32_t n_new,
+                   int32_t trigger, int32_t m, int32_t* sel_order,
+                   int32_t* n_overflow, void* stream);
+
+/*
+ * bkv_score -- observation-set attention score of every live slot.
+ *
+ * Paper text §4.3 ("Query Construction and Alignment", "Importance Scoring
+ * via Max-Aggregation"); summary step (4); review §4.3.  Per unit u, query
+ * head h of its group:
+ *   - beacon rows: buf rows 0..n_beacon-1 of head h (stride buf_cap rows),
+ *     rotated by RoPE to position t;
+ *   - recent rows: recents[h, i] rotated to tau_i = kpos[u, L-n_recent_q+i];
+ *   RoPE pairs coordinate k with k + d/2 at angle pos * theta^(-2k/d),
+ *   computed in fp64 and rounded to fp32 and then to bf16 (both RNE).
+ *   logits s = q . k * sm_scale against K[u, 0..L) (bf16 in, fp32 accumulate);
+ *   recent row i sees slots 0..L-n_recent_q+i, beacon rows see all L slots;
+ *   W = row softmax over the visible slots;
+ *   score[u, j] = max over the g*(n_beacon+n_recent_q) rows of W[row, j].
+ * Writes score[u, 0..L); other slots are untouched.  If qobs_out is non-NULL
+ * it receives the bf16 observation rows, [U, g*(n_beacon+n_recent_q), d],
+ * row = h*(n_beacon+n_recent_q) + (beacons first, then recents).
+ * Requires n_recent_q <= L <= l_cap, t >= 0,
+ * ws_bytes >= bkv_workspace_bytes(dims, pol, L, 0).
+ */
+int bkv_score(const bkv_dims* dims, const bkv_policy* pol, const uint16_t* K,
+              const int32_t* kpos, int64_t L, const float* beacons,
+              const float* recents, int64_t t, float* score,
+              uint16_t* qobs_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * bkv_select -- keep set of every unit.
+ *
+ * Summary step (5); paper text §2.2 (retain the top-scoring pairs) and
+ * App. D.2.  kept[u] = slots [0, P) U [L-R, L) U the b_kv-P-R middle slots
+ * with the highest score (ties: lower slot first), written ascending.
+ * Scores are compared as fp32 values (non-negative, so by their bits).
+ * Requires P + R <= b_kv < L <= l_cap.
+ */
+int bkv_select(const bkv_dims* dims, const bkv_policy* pol,
+               const float* score, int64_t L, int64_t b_kv, int32_t* kept,
+               void* stream);
+
+/*
+ * bkv_compact -- gather the kept slots to the front of the cache.
+ *
+ * Paper text §2.2 (index the sequence dimension with the kept set); summary
+ * step (5) (written back in position order).  For k < b_kv:
+ *   K'[u, k] = K[u, kept[u, k]], V'[u, k] = V[u, kept[u, k]],
+ *   kpos'[u, k] = kpos[u, kept[u, k]].
+ * With K_out, V_out and kpos_out all NULL the update is in place (slots at
+ * and beyond b_kv are left as they were); otherwise all three must be
+ * non-NULL with slot stride out_cap >= b_kv and must not overlap the inputs.
+ * kept must be strictly ascending with values in [0, L) (as bkv_select
+ * writes it); in place relies on that order.  An entry outside [0, L) is
+ * skipped (its destination slot is left as it was) rather than followed.
+ * Requires 0 < b_kv <= L <= l_cap.
+ */
+int bkv_compact(const bkv_dims* dims, uint16_t* K, uint16_t* V, int32_t* kpos,
+                int64_t L, const int32_t* kept, int64_t b_kv, uint16_t* K_out,
+                uint16_t* V_out, int32_t* kpos_out, int64_t out_cap,
+                void* stream);
+
+/*
+ * bkv_evict -- one full eviction event (summary steps (4)-(6)).
+ *
+ * Runs bkv_score, bkv_select and an in-place bkv_compact on K, V, kpos; then,
+ * if buf is non-NULL, the rolling update of summary step (6): the recent
+ * queries are appended to each head's buffer (which must hold exactly the
+ * n_beacon beacons, count == n_beacon) and the buffer is compressed back to
+ * n_beacon rows with FPS.  `beacons` is normally `buf` itself.
+ * score_out / kept_out, if non-NULL, receive the scores and kept slots;
+ * otherwise they live in the workspace.
+ * Requires what the three calls require and
+ * ws_bytes >= bkv_workspace_bytes(dims, pol, L, b_kv).
+ */
+int bkv_evict(const bkv_dims* dims, const bkv_policy* pol, uint16_t* K,
+              uint16_t* V, int32_t* kpos, int64_t L, const float* beacons,
+              const float* recents, int64_t t, int64_t b_kv, float* buf,
+              int32_t* count, float* score_out, int32_t* kept_out, void* ws,
+              size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BKV_H */

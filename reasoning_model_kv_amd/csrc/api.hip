@@ -1,0 +1,305 @@
+// Host side of the C ABI: argument validation, workspace layout, error
+// reporting and the launch sequence of each entry point.  Nothing here
+// allocates device memory; every call enqueues work on the caller's stream.
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <string>
+
+#include "common.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+    char msg[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(msg, sizeof msg, fmt, ap);
+    va_end(ap);
+    g_err = msg;
+    return code;
+}
+
+int ok() {
+    g_err.clear();
+    return BKV_OK;
+}
+
+// Test hook: BKV_FAULT_INJECT=<entry point name> or "all" makes that entry
+// point report a HIP failure after validation, without launching anything.
+bool fault_injected(const char* name) {
+    const char* e = getenv("BKV_FAULT_INJECT");
+    return e && (strcmp(e, "all") == 0 || strcmp(e, name) == 0);
+}
+
+int hip_result(hipError_t e, const char* name) {
+    if (e != hipSuccess)
+        return fail(BKV_EHIP, "%s: HIP error %d (%s)", name, (int)e, hipGetErrorString(e));
+    return ok();
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+    if (a < 0 || b < 0) return false;
+    if (a != 0 && b > INT64_MAX / a) return false;
+    *out = a * b;
+    return true;
+}
+
+// Checks shared by every call that takes dims and (optionally) a policy.
+int check_dims(const char* fn, const bkv_dims* d) {
+    if (!d) return fail(BKV_EINVAL, "%s: dims is NULL", fn);
+    if (d->n_units < 0) return fail(BKV_EINVAL, "%s: n_units %lld < 0", fn, (long long)d->n_units);
+    if (d->group < 1 || d->group > 8)
+        return fail(d->group < 1 ? BKV_EINVAL : BKV_ENOTSUP,
+                    "%s: group %d not in [1, 8]", fn, d->group);
+    if (d->d_head != 64 && d->d_head != 128)
+        return fail(d->d_head <= 0 ? BKV_EINVAL : BKV_ENOTSUP,
+                    "%s: d_head %d not supported (64 or 128)", fn, d->d_head);
+    if (d->l_cap < 1) return fail(BKV_EINVAL, "%s: l_cap %lld < 1", fn, (long long)d->l_cap);
+    int64_t cells, elems;
+    if (!mul_ok(d->n_units, d->l_cap, &cells) || !mul_ok(cells, d->d_head, &elems) ||
+        elems > INT64_MAX / 4)
+        return fail(BKV_EINVAL, "%s: n_units * l_cap * d_head overflows", fn);
+    return BKV_OK;
+}
+
+int check_policy(const char* fn, const bkv_policy* p) {
+    if (!p) return fail(BKV_EINVAL, "%s: policy is NULL", fn);
+    if (p->flags != 0 || p->reserved != 0)
+        return fail(BKV_EINVAL, "%s: reserved policy fields must be 0", fn);
+    if (p->n_beacon != 16 || p->n_recent_q != 16)
+        return fail(BKV_ENOTSUP, "%s: n_beacon %d / n_recent_q %d: only 16 / 16 supported", fn,
+                    p->n_beacon, p->n_recent_q);
+    if (p->buf_cap < 1) return fail(BKV_EINVAL, "%s: buf_cap %d < 1", fn, p->buf_cap);
+    if (p->buf_cap > 256) return fail(BKV_ENOTSUP, "%s: buf_cap %d > 256", fn, p->buf_cap);
+    if (p->prefix < 0 || p->recent_tok < 0)
+        return fail(BKV_EINVAL, "%s: prefix %d / recent_tok %d must be >= 0", fn, p->prefix,
+                    p->recent_tok);
+    if (!(p->rope_theta > 0.0) || !isfinite(p->rope_theta))
+        return fail(BKV_EINVAL, "%s: rope_theta must be finite and > 0", fn);
+    if (!(p->sm_scale >= 0.f) || !isfinite(p->sm_scale) || p->sm_scale > 1e4f)
+        return fail(BKV_EINVAL, "%s: sm_scale must be in [0, 1e4]", fn);
+    return BKV_OK;
+}
+
+float scale_of(const bkv_dims* d, const bkv_policy* p) {
+    return p->sm_scale > 0.f ? p->sm_scale : (float)(1.0 / sqrt((double)d->d_head));
+}
+
+struct WsLayout {
+    size_t table = 0, score = 0, kept = 0, total = 0;
+};
+
+WsLayout ws_layout(const bkv_dims* d, const bkv_policy* p, int64_t b_kv) {
+    WsLayout w;
+    w.table = 0;
+    size_t off = align_up(bkv::rope_table_bytes(p->n_recent_q, d->d_head));
+    if (b_kv > 0) {
+        w.score = off;
+        off = align_up(off + (size_t)d->n_units * (size_t)d->l_cap * sizeof(float));
+        w.kept = off;
+        off = align_up(off + (size_t)d->n_units * (size_t)b_kv * sizeof(int32_t));
+    }
+    w.total = off;
+    return w;
+}
+
+int check_score_args(const char* fn, const bkv_dims* d, const bkv_policy* p, const void* K,
+                     const void* kpos, int64_t L, const void* beacons, const void* recents,
+                     int64_t t) {
+    if (!K || !kpos || !beacons || !recents)
+        return fail(BKV_EINVAL, "%s: NULL tensor pointer", fn);
+    if (L < p->n_recent_q || L > d->l_cap)
+        return fail(BKV_EINVAL, "%s: L %lld not in [n_recent_q=%d, l_cap=%lld]", fn,
+                    (long long)L, p->n_recent_q, (long long)d->l_cap);
+    if (p->buf_cap < p->n_beacon)
+        return fail(BKV_EINVAL, "%s: buf_cap %d < n_beacon %d", fn, p->buf_cap, p->n_beacon);
+    if (t < 0) return fail(BKV_EINVAL, "%s: t %lld < 0", fn, (long long)t);
+    return BKV_OK;
+}
+
+int check_select_args(const char* fn, const bkv_dims* d, const bkv_policy* p, int64_t L,
+                      int64_t b_kv) {
+    if (L < 1 || L > d->l_cap)
+        return fail(BKV_EINVAL, "%s: L %lld not in [1, l_cap=%lld]", fn, (long long)L,
+                    (long long)d->l_cap);
+    if (!((int64_t)p->prefix + p->recent_tok <= b_kv && b_kv < L))
+        return fail(BKV_EINVAL, "%s: need prefix + recent_tok (%d) <= b_kv (%lld) < L (%lld)", fn,
+                    p->prefix + p->recent_tok, (long long)b_kv, (long long)L);
+    if (L > INT32_MAX) return fail(BKV_ENOTSUP, "%s: L beyond int32 slots", fn);
+    return BKV_OK;
+}
+
+#define CHECK(x)                     \
+    do {                             \
+        int rc_ = (x);               \
+        if (rc_ != BKV_OK) return rc_; \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int bkv_abi_version(void) { return BKV_ABI_VERSION; }
+
+const char* bkv_last_error(void) { return g_err.c_str(); }
+
+size_t bkv_workspace_bytes(const bkv_dims* dims, const bkv_policy* pol, int64_t L,
+                           int64_t b_kv) {
+    const char* fn = "bkv_workspace_bytes";
+    if (check_dims(fn, dims) != BKV_OK || check_policy(fn, pol) != BKV_OK) return 0;
+    if (b_kv < 0 || L < 0 || L > dims->l_cap || (b_kv > 0 && b_kv >= L)) {
+        fail(BKV_EINVAL, "%s: need 0 <= b_kv < L <= l_cap", fn);
+        return 0;
+    }
+    ok();
+    return ws_layout(dims, pol, b_kv).total;
+}
+
+int bkv_fps_update(const bkv_dims* dims, const bkv_policy* pol, float* buf, int32_t* count,
+                   const float* new_q, int32_t n_new, int32_t trigger, int32_t m,
+                   int32_t* sel_order, int32_t* n_overflow, void* stream) {
+    const char* fn = "bkv_fps_update";
+    CHECK(check_dims(fn, dims));
+    CHECK(check_policy(fn, pol));
+    if (!buf || !count) return fail(BKV_EINVAL, "%s: NULL buf or count", fn);
+    if (n_new < 0 || n_new > pol->buf_cap)
+        return fail(BKV_EINVAL, "%s: n_new %d not in [0, buf_cap=%d]", fn, n_new, pol->buf_cap);
+    if ((new_q == nullptr) != (n_new == 0))
+        return fail(BKV_EINVAL, "%s: new_q must be NULL exactly when n_new == 0", fn);
+    if (!(1 <= m && m < trigger && trigger <= pol->buf_cap))
+        return fail(BKV_EINVAL, "%s: need 1 <= m (%d) < trigger (%d) <= buf_cap (%d)", fn, m,
+                    trigger, pol->buf_cap);
+    if (dims->n_units == 0) return ok();
+    if (fault_injected(fn)) return fail(BKV_EHIP, "%s: injected HIP failure", fn);
+    const int64_t n_heads = dims->n_units * dims->group;
+    return hip_result(bkv::launch_fps(buf, count, new_q, n_new, n_heads, dims->d_head,
+                                      pol->buf_cap, trigger, m, sel_order, n_overflow,
+                                      (hipStream_t)stream),
+                      fn);
+}
+
+int bkv_score(const bkv_dims* dims, const bkv_policy* pol, const uint16_t* K,
+              const int32_t* kpos, int64_t L, const float* beacons, const float* recents,
+              int64_t t, float* score, uint16_t* qobs_out, void* ws, size_t ws_bytes,
+              void* stream) {
+    const char* fn = "bkv_score";
+    CHECK(check_dims(fn, dims));
+    CHECK(check_policy(fn, pol));
+    CHECK(check_score_args(fn, dims, pol, K, kpos, L, beacons, recents, t));
+    if (!score) return fail(BKV_EINVAL, "%s: NULL score", fn);
+    const WsLayout w = ws_layout(dims, pol, 0);
+    if (!ws || ws_bytes < w.total)
+        return fail(BKV_ENOSPC, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, w.total);
+    if (dims->n_units == 0) return ok();
+    if (fault_injected(fn)) return fail(BKV_EHIP, "%s: injected HIP failure", fn);
+    hipStream_t s = (hipStream_t)stream;
+    double* table = (double*)((char*)ws + w.table);
+    hipError_t e = bkv::launch_rope_table(table, t, pol->n_recent_q, dims->d_head,
+                                          pol->rope_theta, s);
+    if (e == hipSuccess)
+        e = bkv::launch_score(K, kpos, dims->n_units, dims->group, dims->d_head, dims->l_cap,
+                              L, beacons, pol->buf_cap, recents, pol->n_beacon,
+                              pol->n_recent_q, t, pol->rope_theta, scale_of(dims, pol),
+                              table, score, qobs_out, s);
+    return hip_result(e, fn);
+}
+
+int bkv_select(const bkv_dims* dims, const bkv_policy* pol, const float* score, int64_t L,
+               int64_t b_kv, int32_t* kept, void* stream) {
+    const char* fn = "bkv_select";
+    CHECK(check_dims(fn, dims));
+    CHECK(check_policy(fn, pol));
+    CHECK(check_select_args(fn, dims, pol, L, b_kv));
+    if (!score || !kept) return fail(BKV_EINVAL, "%s: NULL score or kept", fn);
+    if (dims->n_units == 0) return ok();
+    if (fault_injected(fn)) return fail(BKV_EHIP, "%s: injected HIP failure", fn);
+    return hip_result(bkv::launch_select(score, dims->n_units, dims->l_cap, L, b_kv,
+                                         pol->prefix, pol->recent_tok, kept,
+                                         (hipStream_t)stream),
+                      fn);
+}
+
+int bkv_compact(const bkv_dims* dims, uint16_t* K, uint16_t* V, int32_t* kpos, int64_t L,
+                const int32_t* kept, int64_t b_kv, uint16_t* K_out, uint16_t* V_out,
+                int32_t* kpos_out, int64_t out_cap, void* stream) {
+    const char* fn = "bkv_compact";
+    CHECK(check_dims(fn, dims));
+    if (!K || !V || !kpos || !kept) return fail(BKV_EINVAL, "%s: NULL tensor pointer", fn);
+    if (!(0 < b_kv && b_kv <= L && L <= dims->l_cap))
+        return fail(BKV_EINVAL, "%s: need 0 < b_kv (%lld) <= L (%lld) <= l_cap (%lld)", fn,
+                    (long long)b_kv, (long long)L, (long long)dims->l_cap);
+    const int n_out = (K_out != nullptr) + (V_out != nullptr) + (kpos_out != nullptr);
+    if (n_out != 0 && n_out != 3)
+        return fail(BKV_EINVAL, "%s: K_out, V_out, kpos_out must be all NULL or all set", fn);
+    if (n_out == 3) {
+        int64_t cells, elems;
+        if (out_cap < b_kv || !mul_ok(dims->n_units, out_cap, &cells) ||
+            !mul_ok(cells, dims->d_head, &elems))
+            return fail(BKV_EINVAL, "%s: out_cap %lld < b_kv %lld", fn, (long long)out_cap,
+                        (long long)b_kv);
+        if (K_out == K || V_out == V || kpos_out == kpos)
+            return fail(BKV_EINVAL, "%s: outputs alias inputs; pass NULL for in place", fn);
+    }
+    if (dims->n_units == 0) return ok();
+    if (fault_injected(fn)) return fail(BKV_EHIP, "%s: injected HIP failure", fn);
+    return hip_result(bkv::launch_compact(K, V, kpos, dims->n_units, dims->d_head, dims->l_cap,
+                                          L, kept, b_kv, K_out, V_out, kpos_out,
+                                          n_out ? out_cap : dims->l_cap, (hipStream_t)stream),
+                      fn);
+}
+
+int bkv_evict(const bkv_dims* dims, const bkv_policy* pol, uint16_t* K, uint16_t* V,
+              int32_t* kpos, int64_t L, const float* beacons, const float* recents, int64_t t,
+              int64_t b_kv, float* buf, int32_t* count, float* score_out, int32_t* kept_out,
+              void* ws, size_t ws_bytes, void* stream) {
+    const char* fn = "bkv_evict";
+    CHECK(check_dims(fn, dims));
+    CHECK(check_policy(fn, pol));
+    CHECK(check_score_args(fn, dims, pol, K, kpos, L, beacons, recents, t));
+    CHECK(check_select_args(fn, dims, pol, L, b_kv));
+    if (!V) return fail(BKV_EINVAL, "%s: NULL V", fn);
+    if ((buf == nullptr) != (count == nullptr))
+        return fail(BKV_EINVAL, "%s: buf and count must both be set or both NULL", fn);
+    if (buf && pol->buf_cap < pol->n_beacon + pol->n_recent_q)
+        return fail(BKV_EINVAL, "%s: buf_cap %d cannot hold beacons + recents", fn,
+                    pol->buf_cap);
+    const WsLayout w = ws_layout(dims, pol, b_kv);
+    if (!ws || ws_bytes < w.total)
+        return fail(BKV_ENOSPC, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, w.total);
+    if (dims->n_units == 0) return ok();
+    if (fault_injected(fn)) return fail(BKV_EHIP, "%s: injected HIP failure", fn);
+    hipStream_t s = (hipStream_t)stream;
+    double* table = (double*)((char*)ws + w.table);
+    float* score = score_out ? score_out : (float*)((char*)ws + w.score);
+    int32_t* kept = kept_out ? kept_out : (int32_t*)((char*)ws + w.kept);
+    hipError_t e = bkv::launch_rope_table(table, t, pol->n_recent_q, dims->d_head,
+                                          pol->rope_theta, s);
+    if (e == hipSuccess)
+        e = bkv::launch_score(K, kpos, dims->n_units, dims->group, dims->d_head, dims->l_cap,
+                              L, beacons, pol->buf_cap, recents, pol->n_beacon,
+                              pol->n_recent_q, t, pol->rope_theta, scale_of(dims, pol),
+                              table, score, nullptr, s);
+    if (e == hipSuccess)
+        e = bkv::launch_select(score, dims->n_units, dims->l_cap, L, b_kv, pol->prefix,
+                               pol->recent_tok, kept, s);
+    if (e == hipSuccess)
+        e = bkv::launch_compact(K, V, kpos, dims->n_units, dims->d_head, dims->l_cap, L, kept,
+                                b_kv, nullptr, nullptr, nullptr, dims->l_cap, s);
+    if (e == hipSuccess && buf)
+        e = bkv::launch_fps(buf, count, recents, pol->n_recent_q,
+                            dims->n_units * dims->group, dims->d_head, pol->buf_cap,
+                            pol->n_beacon + pol->n_recent_q, pol->n_beacon, nullptr, nullptr, s);
+    return hip_result(e, fn);
+}
+
+}  // extern "C"

@@ -5,10 +5,13 @@ random numbers and converts them to the storage types (bfloat16 keys and
 values via torch's round-to-nearest-even cast, float32 queries).  Both the
 float64 oracle and the HIP library consume what it returns.
 
-Every tensor of every unit has its own numpy stream,
-``default_rng(SeedSequence([seed, workload_id, kind, index]))``, so any one
-unit can be regenerated on its own (the parity tests check sampled units of
-full-size workloads that way).
+Two generators share one recipe.  ``unit_inputs`` gives every tensor of
+every unit its own numpy stream,
+``default_rng(SeedSequence([seed, workload_id, kind, index]))``, so small
+cases are reproducible on any host.  ``device_inputs`` draws whole
+full-size workloads on the device with torch's seeded generator (thousands
+of units in well under a second); sampled units of such a workload are
+copied to the host for the oracle.
 
 Value structure (a stand-in for the reasoning traces the pages measure on;
 see the design notes for the recipe and its reasons):
@@ -22,7 +25,7 @@ see the design notes for the recipe and its reasons):
   p = its own position.
 """
 
-from dataclasses import dataclass, field, replace
+from dataclasses import dataclass, replace
 
 import numpy as np
 import torch
@@ -215,3 +218,101 @@ def workload_inputs(w, units=None):
            ("keys", "values", "kpos", "buf", "recents")}
     out["t"] = w.L
     return out
+
+
+# ---------------------------------------------------------------------------
+# Bulk generation on the device (full-size workloads).
+#
+# Same recipe as above, drawn with torch's seeded device generator in chunks
+# of units so that a 4608-unit cache is generated in well under a second.
+# The numpy per-unit streams and this generator produce different numbers;
+# each test or bench run uses one of them for both sides.  Sampled units of
+# a device-generated workload are copied to the host for the oracle.
+
+
+def _dev_gen(w, kind, chunk, device):
+    g = torch.Generator(device=device)
+    g.manual_seed(int(np.random.SeedSequence([w.seed, w.wid, kind, chunk]).generate_state(1)[0]))
+    return g
+
+
+def device_inputs(w, device="cuda", chunk_units=256, l_cap=None):
+    """Whole-workload inputs as device tensors.
+
+    Returns dict(keys, values: bf16 [U, l_cap, d]; kpos: int32 [U, l_cap];
+    buf: fp32 [U*g, buf_cap, d]; recents: fp32 [U*g, n_recent_q, d]; t).
+    Slots at and beyond L (when l_cap > L) hold zeros.
+    """
+    U, g, d, L = w.n_units, w.group, w.d_head, w.L
+    cap = l_cap or w.cap
+    dev = torch.device(device)
+    keys = torch.zeros((U, cap, d), dtype=torch.bfloat16, device=dev)
+    vals = torch.zeros((U, cap, d), dtype=torch.bfloat16, device=dev)
+    kpos = torch.zeros((U, cap), dtype=torch.int32, device=dev)
+    kpos[:, :L] = torch.arange(L, dtype=torch.int32, device=dev)
+    buf = torch.empty((U * g, w.buf_cap, d), dtype=torch.float32, device=dev)
+    rec = torch.empty((U * g, w.n_recent_q, d), dtype=torch.float32, device=dev)
+    hi = max(w.prefix + 1, L - 16)
+    for c0 in range(0, U, chunk_units):
+        c1 = min(U, c0 + chunk_units)
+        n = c1 - c0
+        ci = c0 // chunk_units
+        gk = _dev_gen(w, KIND_K, ci, dev)
+        k = torch.randn((n, L, d), generator=gk, device=dev, dtype=torch.float32)
+        if w.outlier_channels:
+            layers = torch.tensor([w.layer_of(u) for u in range(c0, c1)])
+            for layer in torch.unique(layers).tolist():
+                rows = (layers == layer).nonzero().flatten().to(dev)
+                ch = torch.from_numpy(outlier_channels(w, layer)).to(dev)
+                sub = k[rows]
+                sub[:, :, ch] *= w.outlier_scale
+                k[rows] = sub
+        kb = k.to(torch.bfloat16)
+        keys[c0:c1, :L] = kb
+        gv = _dev_gen(w, KIND_V, ci, dev)
+        vals[c0:c1, :L] = torch.randn((n, L, d), generator=gv, device=dev,
+                                      dtype=torch.float32).to(torch.bfloat16)
+        kf = kb.to(torch.float32)  # local queries copy the stored (bf16) keys
+        gq = _dev_gen(w, KIND_BUF, ci, dev)
+        nq = n * g
+        cen = torch.randn((nq, w.n_centres, d), generator=gq, device=dev)
+        cen = cen / cen.norm(dim=-1, keepdim=True)
+        unit_of = torch.arange(nq, device=dev) // g
+
+        def mixture(pos):
+            m = pos.shape[1]
+            is_g = torch.rand((nq, m), generator=gq, device=dev) < w.pi_global
+            which = torch.randint(0, w.n_centres, (nq, m), generator=gq, device=dev)
+            lo = torch.clamp(pos - 31, min=0)
+            j = lo + (torch.rand((nq, m), generator=gq, device=dev) *
+                      (pos - lo + 1).to(torch.float32)).to(torch.int64)
+            j = torch.minimum(j, pos)
+            local = kf[unit_of[:, None], j]
+            glob = 8.0 * torch.gather(cen, 1, which[..., None].expand(-1, -1, d))
+            q = torch.where(is_g[..., None], glob, local)
+            return q + 0.3 * torch.randn((nq, m, d), generator=gq, device=dev)
+
+        pos_b = torch.randint(w.prefix, hi, (nq, w.buf_cap), generator=gq, device=dev)
+        buf[c0 * g:c1 * g] = mixture(pos_b)
+        pos_r = torch.arange(L - w.n_recent_q, L, device=dev).expand(nq, -1)
+        rec[c0 * g:c1 * g] = mixture(pos_r)
+    return {"keys": keys, "values": vals, "kpos": kpos, "buf": buf, "recents": rec, "t": L}
+
+
+def to_device(inp, device="cuda", l_cap=None):
+    """Move host unit inputs (workload_inputs) to device tensors in library layout."""
+    dev = torch.device(device)
+    k = inp["keys"]
+    U, L, d = k.shape
+    cap = l_cap or L
+    keys = torch.zeros((U, cap, d), dtype=torch.bfloat16, device=dev)
+    vals = torch.zeros((U, cap, d), dtype=torch.bfloat16, device=dev)
+    kpos = torch.zeros((U, cap), dtype=torch.int32, device=dev)
+    keys[:, :L] = torch.from_numpy(k).to(dev).to(torch.bfloat16)
+    vals[:, :L] = torch.from_numpy(inp["values"]).to(dev).to(torch.bfloat16)
+    kpos[:, :L] = torch.from_numpy(inp["kpos"]).to(dev)
+    g = inp["buf"].shape[1]
+    buf = torch.from_numpy(inp["buf"].reshape(U * g, *inp["buf"].shape[2:])).to(dev)
+    rec = torch.from_numpy(inp["recents"].reshape(U * g, *inp["recents"].shape[2:])).to(dev)
+    return {"keys": keys, "values": vals, "kpos": kpos, "buf": buf.contiguous(),
+            "recents": rec.contiguous(), "t": inp["t"]}

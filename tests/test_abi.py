@@ -1,0 +1,146 @@
+"""Host-only checks of the C ABI: exports, validation, error codes.
+
+No call here reaches a kernel launch: every call either fails validation,
+has n_units == 0, or is stopped by the fault-injection hook, all of which
+return before the library touches the HIP runtime.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from reasoning_model_kv_amd import bkv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = ctypes.c_void_p(0x10000)  # never dereferenced by these calls
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return bkv.load_library()
+
+
+def _shape(**kw):
+    base = dict(n_units=4, group=4, d_head=128, l_cap=512, prefix=8, rope_theta=1e6)
+    base.update(kw)
+    return bkv.Shape(**base)
+
+
+def test_exports_every_declared_symbol(lib):
+    with open(os.path.join(ROOT, "include", "bkv.h")) as f:
+        header = f.read()
+    declared = set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(bkv_\w+)\(", header, re.M))
+    assert declared == set(bkv.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert lib.bkv_abi_version() == bkv.ABI_VERSION
+
+
+def _call_score(lib, shape, L=300, t=300, ws_bytes=1 << 20, K=FAKE, score=FAKE, ws=FAKE):
+    return lib.bkv_score(ctypes.byref(shape.dims()), ctypes.byref(shape.policy()), K, FAKE, L,
+                         FAKE, FAKE, t, score, None, ws, ws_bytes, None)
+
+
+def test_score_validation(lib):
+    s = _shape()
+    assert _call_score(lib, s, K=None) == bkv.BKV_EINVAL
+    assert _call_score(lib, s, L=600) == bkv.BKV_EINVAL          # L > l_cap
+    assert _call_score(lib, s, L=8) == bkv.BKV_EINVAL            # L < n_recent_q
+    assert _call_score(lib, s, t=-1) == bkv.BKV_EINVAL
+    assert _call_score(lib, s, ws_bytes=16) == bkv.BKV_ENOSPC
+    assert "workspace" in bkv.last_error()
+    assert _call_score(lib, _shape(d_head=96)) == bkv.BKV_ENOTSUP
+    assert _call_score(lib, _shape(group=9)) == bkv.BKV_ENOTSUP
+    assert _call_score(lib, _shape(group=0)) == bkv.BKV_EINVAL
+    assert _call_score(lib, _shape(n_beacon=8)) == bkv.BKV_ENOTSUP
+    assert _call_score(lib, _shape(rope_theta=0.0)) == bkv.BKV_EINVAL
+    assert _call_score(lib, _shape(buf_cap=300)) == bkv.BKV_ENOTSUP
+    assert _call_score(lib, _shape(n_units=0)) == bkv.BKV_OK     # no-op, no launch
+    assert bkv.last_error() == ""
+
+
+def test_select_validation(lib):
+    s = _shape(prefix=8)
+    call = lambda L, b: lib.bkv_select(ctypes.byref(s.dims()), ctypes.byref(s.policy()),
+                                        FAKE, L, b, FAKE, None)
+    assert call(300, 20) == bkv.BKV_EINVAL    # b_kv < P + R
+    assert call(300, 300) == bkv.BKV_EINVAL   # b_kv == L
+    assert call(600, 100) == bkv.BKV_EINVAL   # L > l_cap
+    s0 = _shape(n_units=0)
+    assert lib.bkv_select(ctypes.byref(s0.dims()), ctypes.byref(s0.policy()), FAKE, 300, 100,
+                          FAKE, None) == bkv.BKV_OK
+
+
+def test_compact_validation(lib):
+    s = _shape()
+    d = ctypes.byref(s.dims())
+    assert lib.bkv_compact(d, FAKE, FAKE, FAKE, 300, FAKE, 0, None, None, None, 0,
+                           None) == bkv.BKV_EINVAL
+    assert lib.bkv_compact(d, FAKE, FAKE, FAKE, 300, FAKE, 301, None, None, None, 0,
+                           None) == bkv.BKV_EINVAL
+    # partially given outputs
+    assert lib.bkv_compact(d, FAKE, FAKE, FAKE, 300, FAKE, 200, FAKE, None, None, 200,
+                           None) == bkv.BKV_EINVAL
+    # out_cap too small
+    o = ctypes.c_void_p(0x20000)
+    assert lib.bkv_compact(d, FAKE, FAKE, FAKE, 300, FAKE, 200, o, o, o, 100,
+                           None) == bkv.BKV_EINVAL
+    # aliasing outputs
+    assert lib.bkv_compact(d, FAKE, FAKE, FAKE, 300, FAKE, 200, FAKE, o, o, 200,
+                           None) == bkv.BKV_EINVAL
+
+
+def test_fps_validation(lib):
+    s = _shape()
+    call = lambda nq, n_new, trig, m: lib.bkv_fps_update(
+        ctypes.byref(s.dims()), ctypes.byref(s.policy()), FAKE, FAKE, nq, n_new, trig, m, None,
+        None, None)
+    assert call(None, 0, 32, 32) == bkv.BKV_EINVAL     # m == trigger
+    assert call(None, 0, 33, 16) == bkv.BKV_EINVAL     # trigger > buf_cap
+    assert call(None, 0, 32, 0) == bkv.BKV_EINVAL      # m < 1
+    assert call(FAKE, 0, 32, 16) == bkv.BKV_EINVAL     # new_q without rows
+    assert call(None, 1, 32, 16) == bkv.BKV_EINVAL     # rows without new_q
+    assert call(FAKE, 33, 32, 16) == bkv.BKV_EINVAL    # n_new > buf_cap
+
+
+def test_evict_validation_and_workspace(lib):
+    s = _shape(l_cap=2176)
+    need = bkv.workspace_bytes(s, 2176, 2048)
+    table = bkv.workspace_bytes(s, 2176, 0)
+    assert table >= 17 * 64 * 16
+    assert need >= table + 4 * 2176 * 4 + 4 * 2048 * 4
+    call = lambda ws_bytes, buf=None, count=None: lib.bkv_evict(
+        ctypes.byref(s.dims()), ctypes.byref(s.policy()), FAKE, FAKE, FAKE, 2176, FAKE, FAKE,
+        2176, 2048, buf, count, None, None, FAKE, ws_bytes, None)
+    assert call(need - 1) == bkv.BKV_ENOSPC
+    assert call(need, buf=FAKE) == bkv.BKV_EINVAL      # buf without count
+    with pytest.raises(bkv.BkvError):
+        bkv.workspace_bytes(s, 2176, 2176)
+
+
+def test_fault_injection_reports_hip_error(lib, monkeypatch):
+    s = _shape()
+    monkeypatch.setenv("BKV_FAULT_INJECT", "bkv_score")
+    assert _call_score(lib, s) == bkv.BKV_EHIP
+    assert "injected" in bkv.last_error()
+    monkeypatch.setenv("BKV_FAULT_INJECT", "all")
+    assert lib.bkv_select(ctypes.byref(s.dims()), ctypes.byref(s.policy()), FAKE, 300, 100,
+                          FAKE, None) == bkv.BKV_EHIP
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    import importlib
+    mod = importlib.import_module("reasoning_model_kv_amd.bkv")
+    with pytest.raises(ImportError):
+        mod.load_library.__wrapped__(str(tmp_path / "nope.so")) if hasattr(
+            mod.load_library, "__wrapped__") else _load_missing(mod, tmp_path)
+
+
+def _load_missing(mod, tmp_path):
+    saved = mod._lib
+    mod._lib = None
+    try:
+        mod.load_library(str(tmp_path / "nope.so"))
+    finally:
+        mod._lib = saved

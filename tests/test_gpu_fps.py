@@ -1,0 +1,126 @@
+"""FPS kernel (bkv_fps_update) against the float64 oracle on the GPU."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from parity_util import check_fps, log
+from reasoning_model_kv_amd import bkv
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _shape(w, **kw):
+    base = dict(n_units=w.n_units, group=w.group, d_head=w.d_head, l_cap=w.L,
+                prefix=w.prefix, rope_theta=w.theta)
+    base.update(kw)
+    return bkv.Shape(**base)
+
+
+@pytest.mark.parametrize("name", ["tiny", "qwen3_4b_layer"])
+def test_compress_32_to_16(name):
+    w = synth.WORKLOADS[name]
+    log(f"fps compress {name}: Uq={w.n_qheads} d={w.d_head}")
+    inp = synth.workload_inputs(w)
+    host = inp["buf"].reshape(w.n_qheads, 32, w.d_head)
+    buf = torch.from_numpy(host.copy()).to(DEV)
+    count = torch.full((w.n_qheads,), 32, dtype=torch.int32, device=DEV)
+    sel = torch.full((w.n_qheads, 16), -7, dtype=torch.int32, device=DEV)
+    bkv.fps_update(_shape(w), buf, count, trigger=32, m=16, sel_order=sel)
+    torch.cuda.synchronize()
+    assert torch.all(count == 16)
+    sel, out = sel.cpu().numpy(), buf.cpu().numpy()
+    exact = 0
+    for q in range(w.n_qheads):
+        exact += check_fps(host[q], sel[q], 16, f"{name} head {q}")
+        assert np.array_equal(out[q, :16], host[q][np.sort(sel[q])]), f"head {q} rows"
+    log(f"  {exact}/{w.n_qheads} heads outside near-ties matched exactly")
+
+
+def test_append_only_and_triggers():
+    w = synth.WORKLOADS["tiny"]
+    nq, d = w.n_qheads, w.d_head
+    r = np.random.default_rng(5)
+    host = r.standard_normal((nq, 32, d)).astype(np.float32)
+    shape = _shape(w)
+    # count 10 + 1 new row, trigger 32: append only.
+    buf = torch.from_numpy(host.copy()).to(DEV)
+    count = torch.full((nq,), 10, dtype=torch.int32, device=DEV)
+    newq = torch.from_numpy(r.standard_normal((nq, 1, d)).astype(np.float32)).to(DEV)
+    sel = torch.zeros((nq, 16), dtype=torch.int32, device=DEV)
+    bkv.fps_update(shape, buf, count, newq, trigger=32, m=16, sel_order=sel)
+    torch.cuda.synchronize()
+    out = buf.cpu().numpy()
+    assert torch.all(count == 11) and torch.all(sel == -1)
+    assert np.array_equal(out[:, 10], newq.cpu().numpy()[:, 0])
+    assert np.array_equal(np.delete(out, 10, axis=1), np.delete(host, 10, axis=1))
+    # Beacon fix on heads holding exactly 16: nothing changes.
+    buf = torch.from_numpy(host.copy()).to(DEV)
+    count = torch.full((nq,), 16, dtype=torch.int32, device=DEV)
+    bkv.fps_update(shape, buf, count, trigger=17, m=16)
+    torch.cuda.synchronize()
+    assert torch.all(count == 16) and np.array_equal(buf.cpu().numpy(), host)
+    # Mixed counts: 20 -> compress, 16 -> unchanged.
+    buf = torch.from_numpy(host.copy()).to(DEV)
+    cnt = np.array([20, 16, 20, 16][:nq], dtype=np.int32)
+    count = torch.from_numpy(cnt).to(DEV)
+    sel = torch.zeros((nq, 16), dtype=torch.int32, device=DEV)
+    bkv.fps_update(shape, buf, count, trigger=17, m=16, sel_order=sel)
+    torch.cuda.synchronize()
+    out, sel = buf.cpu().numpy(), sel.cpu().numpy()
+    for q in range(nq):
+        if cnt[q] == 20:
+            check_fps(host[q, :20], sel[q], 16, f"beacon fix head {q}")
+            assert np.array_equal(out[q, :16], host[q, :20][np.sort(sel[q])])
+        else:
+            assert np.all(sel[q] == -1) and np.array_equal(out[q], host[q])
+    # Merge: 16 beacons + 16 appended recents, trigger 32.
+    buf = torch.from_numpy(host.copy()).to(DEV)
+    count = torch.full((nq,), 16, dtype=torch.int32, device=DEV)
+    rec = r.standard_normal((nq, 16, d)).astype(np.float32)
+    sel = torch.zeros((nq, 16), dtype=torch.int32, device=DEV)
+    bkv.fps_update(shape, buf, count, torch.from_numpy(rec).to(DEV), trigger=32, m=16,
+                   sel_order=sel)
+    torch.cuda.synchronize()
+    merged = np.concatenate([host[:, :16], rec], axis=1)
+    out, sel = buf.cpu().numpy(), sel.cpu().numpy()
+    for q in range(nq):
+        check_fps(merged[q], sel[q], 16, f"merge head {q}")
+        assert np.array_equal(out[q, :16], merged[q][np.sort(sel[q])])
+
+
+def test_overflow_leaves_heads_unchanged():
+    w = synth.WORKLOADS["tiny"]
+    nq, d = w.n_qheads, w.d_head
+    host = np.random.default_rng(6).standard_normal((nq, 32, d)).astype(np.float32)
+    buf = torch.from_numpy(host.copy()).to(DEV)
+    count = torch.full((nq,), 31, dtype=torch.int32, device=DEV)
+    newq = torch.ones((nq, 2, d), dtype=torch.float32, device=DEV)
+    ovf = torch.zeros(1, dtype=torch.int32, device=DEV)
+    bkv.fps_update(_shape(w), buf, count, newq, trigger=32, m=16, n_overflow=ovf)
+    torch.cuda.synchronize()
+    assert int(ovf.item()) == nq
+    assert torch.all(count == 31) and np.array_equal(buf.cpu().numpy(), host)
+
+
+@pytest.mark.parametrize("d,n", [(128, 256), (64, 200), (128, 33)])
+def test_prefill_block_path(d, n):
+    """Buffers above 32 rows (prefill FPS over up to 256 queries)."""
+    nq, cap = 6, 256
+    log(f"fps prefill block path d={d} N={n}")
+    r = np.random.default_rng(n + d)
+    host = r.standard_normal((nq, cap, d)).astype(np.float32)
+    host[:, : n // 3] += 3.0 * r.standard_normal((nq, 1, d)).astype(np.float32)
+    shape = bkv.Shape(n_units=nq, group=1, d_head=d, l_cap=64, prefix=0, rope_theta=1e6,
+                      buf_cap=cap)
+    buf = torch.from_numpy(host.copy()).to(DEV)
+    count = torch.full((nq,), n, dtype=torch.int32, device=DEV)
+    sel = torch.zeros((nq, 16), dtype=torch.int32, device=DEV)
+    bkv.fps_update(shape, buf, count, trigger=17, m=16, sel_order=sel)
+    torch.cuda.synchronize()
+    assert torch.all(count == 16)
+    out, sel = buf.cpu().numpy(), sel.cpu().numpy()
+    for q in range(nq):
+        check_fps(host[q, :n], sel[q], 16, f"prefill head {q}")
+        assert np.array_equal(out[q, :16], host[q, :n][np.sort(sel[q])])

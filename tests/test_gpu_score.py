@@ -1,0 +1,60 @@
+"""Scoring kernel (bkv_score) against the float64 oracle on the GPU."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from parity_util import check_scores, log
+from reasoning_model_kv_amd import bkv
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _run(w, L=None, l_cap=None, t=None, kpos_offset=0):
+    L = L or w.L
+    l_cap = l_cap or L
+    w2 = synth.shrink(w, L=L)
+    inp = synth.workload_inputs(w2)
+    inp["kpos"] = inp["kpos"] + kpos_offset
+    t = t if t is not None else L + kpos_offset
+    dev = synth.to_device(inp, DEV, l_cap=l_cap)
+    shape = bkv.Shape(w.n_units, w.group, w.d_head, l_cap, w.prefix, w.theta)
+    score = torch.full((w.n_units, l_cap), -1.0, device=DEV)
+    qobs = torch.zeros((w.n_units, w.group * 32, w.d_head), dtype=torch.bfloat16, device=DEV)
+    bkv.score(shape, dev["keys"], dev["kpos"], L, dev["buf"], dev["recents"], t, score, qobs)
+    torch.cuda.synchronize()
+    return inp, score.cpu().numpy(), qobs.cpu(), t
+
+
+@pytest.mark.parametrize("name,L,l_cap,t_shift", [
+    ("tiny", None, None, 0),          # 256 slots, 4 full tiles
+    ("tiny", 203, 256, 0),            # ragged tail, l_cap > L
+    ("tiny", 40, 64, 0),              # one tile, recent rows masked inside it
+    ("tiny", 150, 150, 37),           # recent positions != t-16+i: direct RoPE path
+    ("qwen3_4b_layer", None, None, 0),
+])
+def test_score_matches_oracle(name, L, l_cap, t_shift):
+    w = synth.WORKLOADS[name]
+    log(f"score {name} L={L or w.L} l_cap={l_cap} t_shift={t_shift}")
+    inp, sc, qobs, t = _run(w, L, l_cap, None if not t_shift else (L or w.L) + t_shift)
+    L = L or w.L
+    worst = 0.0
+    flips = 0
+    for u in range(w.n_units):
+        beacons = inp["buf"][u][:, :16]
+        taus = inp["kpos"][u][L - 16:L]
+        ref, qhat, _, _ = oracle.score.score_unit(inp["keys"][u], beacons, inp["recents"][u],
+                                                  t, taus, w.theta, return_all=True)
+        worst = max(worst, check_scores(sc[u, :L], ref, f"{name} unit {u}"))
+        if sc.shape[1] > L:
+            assert np.all(sc[u, L:] == -1.0), "slots past L must be untouched"
+        got_q = qobs[u].float().numpy().reshape(w.group, 32, w.d_head)
+        neq = got_q != qhat
+        flips += int(neq.sum())
+        if neq.any():  # rounding-boundary flips only: one bf16 ulp
+            ulp = np.abs(qhat[neq]) * 2.0 ** -7
+            assert np.all(np.abs(got_q[neq] - qhat[neq]) <= ulp)
+    assert flips <= 1e-4 * qobs.numel()
+    log(f"  max rel err {worst:.3g}, bf16 rounding flips {flips}")

@@ -1,0 +1,83 @@
+"""Selection and compaction kernels against the oracle (bit-exact)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity_util import log
+from reasoning_model_kv_amd import bkv
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.mark.parametrize("L,b_kv,P,R,kind", [
+    (256, 128, 8, 16, "cont"),
+    (2176, 2048, 256, 16, "cont"),
+    (1000, 24, 8, 16, "cont"),      # nothing chosen: only forced slots
+    (1000, 999, 0, 16, "ties"),     # evict exactly one
+    (777, 300, 33, 16, "ties"),     # many equal scores around the cut
+    (4224, 4096, 512, 16, "ties"),
+    (300, 150, 0, 0, "zeros"),      # all-equal scores, no forced slots
+])
+def test_select_bit_exact(L, b_kv, P, R, kind):
+    U = 37
+    log(f"select L={L} b_kv={b_kv} P={P} R={R} {kind}")
+    r = np.random.default_rng(L + b_kv)
+    if kind == "cont":
+        s = r.random((U, L)).astype(np.float32) * 1e-3
+    elif kind == "ties":
+        s = r.choice(np.array([1e-6, 2e-6, 2e-6, 5e-4, 0.25, 0.0], np.float32), size=(U, L))
+    else:
+        s = np.zeros((U, L), np.float32)
+    l_cap = L + 5
+    sc = torch.zeros((U, l_cap), dtype=torch.float32, device=DEV)
+    sc[:, :L] = torch.from_numpy(s).to(DEV)
+    kept = torch.full((U, b_kv), -1, dtype=torch.int32, device=DEV)
+    shape = bkv.Shape(U, 1, 64, l_cap, P, 1e4, recent_tok=R)
+    bkv.select(shape, sc, L, b_kv, kept)
+    torch.cuda.synchronize()
+    k = kept.cpu().numpy()
+    for u in range(U):
+        ref = oracle.select.select(s[u].astype(np.float64), L, b_kv, P, R)
+        assert np.array_equal(k[u], ref), f"unit {u}"
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("L,b_kv", [(256, 128), (2176, 2048), (519, 301)])
+def test_compact_in_place_and_out_of_place(d, L, b_kv):
+    U = 13
+    log(f"compact d={d} L={L} b_kv={b_kv}")
+    r = np.random.default_rng(d + L)
+    l_cap = L + 3
+    K = r.standard_normal((U, l_cap, d)).astype(np.float32)
+    V = r.standard_normal((U, l_cap, d)).astype(np.float32)
+    kpos = (np.arange(l_cap)[None].repeat(U, 0) * 2 + 11).astype(np.int32)
+    kept = np.stack([np.sort(r.choice(L, b_kv, replace=False)) for _ in range(U)]).astype(np.int32)
+    kept[0] = np.arange(b_kv)           # nothing moves
+    kept[1, : b_kv - 1] = np.arange(b_kv - 1)
+    kept[1, -1] = L - 1                  # only the last entry moves
+    Kt = torch.from_numpy(K).to(torch.bfloat16).to(DEV)
+    Vt = torch.from_numpy(V).to(torch.bfloat16).to(DEV)
+    Pt = torch.from_numpy(kpos).to(DEV)
+    kt = torch.from_numpy(kept).to(DEV)
+    shape = bkv.Shape(U, 1, d, l_cap, 0, 1e4)
+    Ko = torch.zeros((U, b_kv, d), dtype=torch.bfloat16, device=DEV)
+    Vo = torch.zeros_like(Ko)
+    Po = torch.zeros((U, b_kv), dtype=torch.int32, device=DEV)
+    Kh, Vh = Kt.cpu(), Vt.cpu()
+    bkv.compact(shape, Kt, Vt, Pt, L, kt, b_kv, Ko, Vo, Po, out_cap=b_kv)
+    K2, V2, P2 = Kt.clone(), Vt.clone(), Pt.clone()
+    bkv.compact(shape, K2, V2, P2, L, kt, b_kv)
+    torch.cuda.synchronize()
+    for u in range(U):
+        ek, ev, ep = oracle.compact.compact(Kh[u].view(torch.int16).numpy(),
+                                            Vh[u].view(torch.int16).numpy(), kpos[u], kept[u])
+        assert np.array_equal(Ko[u].cpu().view(torch.int16).numpy(), ek)
+        assert np.array_equal(Vo[u].cpu().view(torch.int16).numpy(), ev)
+        assert np.array_equal(Po[u].cpu().numpy(), ep)
+    # In place equals out of place, and the tail past b_kv is untouched.
+    assert torch.equal(K2[:, :b_kv].view(torch.int16), Ko.view(torch.int16))
+    assert torch.equal(V2[:, :b_kv].view(torch.int16), Vo.view(torch.int16))
+    assert torch.equal(P2[:, :b_kv], Po)
+    assert torch.equal(K2[:, b_kv:].view(torch.int16), Kt[:, b_kv:].view(torch.int16))

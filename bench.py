@@ -1,0 +1,363 @@
+#!/usr/bin/env python3
+"""Benchmark of the BeaconKV eviction step on one MI355X.
+
+One step is one pass of the whole hot path over one batch of synthetic
+input, every stage through the C ABI on one stream:
+
+  1. bkv_fps_update  append this step's pre-RoPE query and Continual-FPS
+                     compress every head's buffer 32 -> 16        (a1, a2)
+  2. bkv_score       RoPE-align beacons/recents, Q_obs . K^T on bf16 MFMA,
+                     row softmax, max over the GQA group          (a4-a7)
+  3. bkv_select      forced prefix/recent slots + Top-K, ascending (a8)
+  4. bkv_compact     in-place gather of K, V, positions            (a9)
+  5. bkv_fps_update  merge the recent queries and compress 32 -> 16 (a10)
+
+bkv_evict launches exactly stages 2-5; the bench calls them one by one so
+that HIP events on the launch stream time every kernel inside the timed
+region.  Before each step the cache, positions and buffers are restored
+from pristine copies and a scratch buffer is overwritten to flush caches;
+both happen outside the timed step.  Each timed step is bracketed by
+torch.cuda.synchronize() on both sides.
+
+Prints ONE JSON line (stdout).  Diagnostics go to stderr.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+METRIC = "KV-head·key-tokens scored/s + evictions/s at Qwen3-4B shape; % of HBM peak"
+DEFAULT_WORKLOAD = "qwen3_4b_full_b2048"
+KERNEL_SOURCES = {
+    "fps_compress": "fps.hip", "score": "score.hip", "select": "select.hip",
+    "compact": "compact.hip", "fps_merge": "fps.hip",
+}
+
+
+def eprint(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=30)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="target CPU time of the oracle baseline sample (0 disables)")
+    p.add_argument("--no-check", action="store_true", help="skip the sampled parity check")
+    return p.parse_args()
+
+
+def stage_bytes(w, n_mv_total):
+    """Algorithmic HBM bytes per launch of each stage (what the method must move)."""
+    U, g, d, L, B = w.n_units, w.group, w.d_head, w.L, w.b_kv
+    nq = U * g
+    P, R = w.prefix, w.recent_tok
+    return {
+        # read 31 buffer rows + the new query, write 16 rows and the count
+        "fps_compress": nq * ((31 + 1 + 16) * d * 4 + 8),
+        # K rows, 32 observation rows per head, 16 recent positions, score out
+        "score": U * (L * d * 2 + g * 32 * d * 4 + 16 * 4 + L * 4),
+        # middle scores in, kept list out
+        "select": U * ((L - P - R) * 4 + B * 4),
+        # moved tokens: K and V row read + write, position read + write; kept in
+        "compact": n_mv_total * (4 * d * 2 + 8) + U * B * 4,
+        # 16 beacons + 16 recents in, 16 rows out, count
+        "fps_merge": nq * ((16 + 16 + 16) * d * 4 + 8),
+    }
+
+
+def source_digest(name):
+    path = os.path.join(ROOT, "reasoning_model_kv_amd", "csrc", name)
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profile(kernel, workload):
+    """HBM bytes per launch from a committed counter summary, if it still
+    matches the kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_sha256_16") != source_digest(KERNEL_SOURCES[kernel]):
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, seconds):
+    """The float64 oracle on a bounded sample of units, over the host cores.
+
+    Runs before the GPU is touched (the workers are forked from this
+    process).  Each worker generates a few units with the per-unit numpy
+    generator (same recipe and shapes as the GPU run), waits at a barrier,
+    then runs the oracle's full step over its share of the sample, cycling
+    through its units.  Throughput = sampled units x L over the wall time
+    from the barrier to the last worker's finish.
+    """
+    if seconds <= 0:
+        return None
+    import multiprocessing as mp
+    cores = min(len(os.sched_getaffinity(0)), 16)
+    unit0 = _host_unit(w, 0)
+    _oracle_step(w, unit0)  # warm imports and caches
+    t0 = time.perf_counter()
+    _oracle_step(w, unit0)
+    one = time.perf_counter() - t0
+    per_worker = max(1, int(seconds / max(one, 1e-3)))
+    ctx = mp.get_context("fork")
+    barrier = ctx.Barrier(cores + 1)
+    q = ctx.Queue()
+    procs = [ctx.Process(target=_cpu_worker, args=(w, i, per_worker, barrier, q))
+             for i in range(cores)]
+    for p in procs:
+        p.start()
+    barrier.wait()
+    t0 = time.perf_counter()
+    ends = [q.get() for _ in procs]
+    dt = max(ends) - t0
+    for p in procs:
+        p.join()
+    n = per_worker * cores
+    return {"value": round(n * w.L / dt, 1), "unit": "KV-head·key-tokens/s", "cores": cores,
+            "kind": "oracle",
+            "sample": (f"{n} unit-steps of {w.name} ({cores} workers x {per_worker}, each "
+                       f"cycling over up to 8 host-generated units of the same recipe); full "
+                       f"step per unit: FPS compress of {w.group} heads, score, select, compact, "
+                       f"merge FPS; float64 numpy, one BLAS thread per worker, {dt:.1f} s wall")}
+
+
+def _cpu_worker(w, i, n_steps, barrier, q):
+    _one_blas_thread()
+    units = [_host_unit(w, (i * 8 + k) % w.n_units) for k in range(min(8, n_steps))]
+    barrier.wait()
+    for k in range(n_steps):
+        _oracle_step(w, units[k % len(units)])
+    q.put(time.perf_counter())
+
+
+def _host_unit(w, u):
+    import synth
+    x = synth.unit_inputs(w, u)
+    return {k: x[k] for k in ("keys", "values", "kpos", "buf", "recents")}
+
+
+def _one_blas_thread():
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:
+        pass
+
+
+def _oracle_step(w, unit):
+    import numpy as np
+
+    import oracle
+    heads = []
+    for h in range(w.group):
+        _, keep = oracle.fps.fps(unit["buf"][h], 16)
+        heads.append(unit["buf"][h][keep])
+    beacons = np.stack(heads)
+    oracle.evict.evict_unit(unit["keys"], unit["values"], unit["kpos"], w.L, beacons,
+                            unit["recents"], w.L, w.b_kv, w.prefix, w.recent_tok, w.theta)
+    return True
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        eprint("bench.py measures one GPU only: this eviction-step library runs on a single "
+               "MI355X and has no multi-GPU path (every unit is independent; see the design "
+               "notes for how it would shard). Run with --gpus 1.")
+        sys.exit(2)
+
+    import numpy as np
+
+    import synth
+
+    w = synth.WORKLOADS[args.workload]
+    cpu = None
+    if args.cpu_seconds > 0:
+        eprint(f"[bench] oracle CPU baseline (~{args.cpu_seconds:.0f} s of CPU work per core)")
+        cpu = cpu_baseline(w, args.cpu_seconds)
+        eprint(f"[bench] cpu baseline: {cpu}")
+
+    import torch
+
+    from reasoning_model_kv_amd import bkv
+
+    bkv.load_library()
+    if not torch.cuda.is_available():
+        eprint("no GPU visible")
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    U, g, d, L, B = w.n_units, w.group, w.d_head, w.L, w.b_kv
+    nq = U * g
+    eprint(f"[bench] workload {w.name}: U={U} g={g} d={d} L={L} B_KV={B} P={w.prefix}")
+
+    t0 = time.perf_counter()
+    inp = synth.device_inputs(w, dev)
+    torch.cuda.synchronize()
+    eprint(f"[bench] inputs generated in {time.perf_counter() - t0:.2f} s")
+    K0, V0, P0 = inp["keys"], inp["values"], inp["kpos"]
+    buf0, rec = inp["buf"], inp["recents"]
+    newq = buf0[:, 31:32].clone()          # this step's query (appended at count 31)
+    K, V, kpos = torch.empty_like(K0), torch.empty_like(V0), torch.empty_like(P0)
+    buf = torch.empty_like(buf0)
+    count = torch.empty((nq,), dtype=torch.int32, device=dev)
+    score = torch.empty((U, L), dtype=torch.float32, device=dev)
+    kept = torch.empty((U, B), dtype=torch.int32, device=dev)
+    scrub = torch.empty(512 * 2**20 // 4, dtype=torch.float32, device=dev)
+    shape = bkv.Shape(U, g, d, L, w.prefix, w.theta, recent_tok=w.recent_tok)
+    ws = bkv.alloc_workspace(shape, L, 0, dev)
+    stream = torch.cuda.current_stream()
+
+    def restore():
+        K.copy_(K0)
+        V.copy_(V0)
+        kpos.copy_(P0)
+        buf.copy_(buf0)
+        count.fill_(31)
+        scrub.fill_(1.0)
+
+    names = ["fps_compress", "score", "select", "compact", "fps_merge"]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+
+    def step():
+        ev[0].record(stream)
+        bkv.fps_update(shape, buf, count, newq, trigger=32, m=16)
+        ev[1].record(stream)
+        bkv.score(shape, K, kpos, L, buf, rec, L, score, ws=ws)
+        ev[2].record(stream)
+        bkv.select(shape, score, L, B, kept)
+        ev[3].record(stream)
+        bkv.compact(shape, K, V, kpos, L, kept, B)
+        ev[4].record(stream)
+        bkv.fps_update(shape, buf, count, rec, trigger=32, m=16)
+        ev[5].record(stream)
+
+    for i in range(args.warmup):
+        restore()
+        torch.cuda.synchronize()
+        step()
+        torch.cuda.synchronize()
+    eprint(f"[bench] {args.warmup} warmup steps done")
+
+    # Moved tokens of this (deterministic) eviction, for the compaction bytes.
+    kept_host = kept.cpu().numpy()
+    n_mv = int(np.count_nonzero(kept_host != np.arange(B)[None, :]))
+
+    wall, stage_ms = [], {n: [] for n in names}
+    for i in range(args.steps):
+        restore()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        step()
+        torch.cuda.synchronize()
+        wall.append(time.perf_counter() - t0)
+        for j, n in enumerate(names):
+            stage_ms[n].append(ev[j].elapsed_time(ev[j + 1]))
+    eprint(f"[bench] {args.steps} timed steps done")
+
+    ms_step = 1e3 * float(np.mean(wall))
+    gpu_ms = {n: float(np.mean(v)) for n, v in stage_ms.items()}
+    gpu_step_ms = sum(gpu_ms.values())
+    sbytes = stage_bytes(w, n_mv)
+    total_bytes = sum(sbytes.values())
+    flops = 2.0 * U * g * 32 * d * L  # one pass of Q_obs . K^T per unit
+
+    stages = {}
+    for n in names:
+        t = gpu_ms[n] * 1e-3
+        gbs = sbytes[n] / t / 1e9
+        stages[n] = {"us": round(gpu_ms[n] * 1e3, 2), "alg_bytes": sbytes[n],
+                     "GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    stages["score"]["TFLOPs"] = round(flops / (gpu_ms["score"] * 1e-3) / 1e12, 2)
+    stages["score"]["mfma_frac"] = round(stages["score"]["TFLOPs"] / MFMA_BF16_PEAK_TFLOPS, 4)
+
+    dom = max(names, key=lambda n: gpu_ms[n])
+    achieved = sbytes[dom] / (gpu_ms[dom] * 1e-3) / 1e9
+    traffic = traffic_from_profile(dom, w.name)
+    roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic}
+
+    # Sampled parity check of one more step against the oracle.  The oracle
+    # scores with the beacons the GPU's FPS produced (near-ties in FPS may
+    # legitimately pick another set; FPS itself is checked by the tests).
+    check = None
+    if not args.no_check:
+        import oracle
+        sample_units = [0, U // 3, U - 1]
+        restore()
+        torch.cuda.synchronize()
+        bkv.fps_update(shape, buf, count, newq, trigger=32, m=16)
+        beacons = buf[:, :16].cpu().numpy()
+        bkv.score(shape, K, kpos, L, buf, rec, L, score, ws=ws)
+        bkv.select(shape, score, L, B, kept)
+        torch.cuda.synchronize()
+        worst, n_diff = 0.0, 0
+        for u in sample_units:
+            ref = oracle.evict.evict_unit(
+                K0[u].float().cpu().numpy(), V0[u].float().cpu().numpy(), P0[u].cpu().numpy(),
+                L, beacons[u * g:(u + 1) * g], rec[u * g:(u + 1) * g].cpu().numpy(), L, B,
+                w.prefix, w.recent_tok, w.theta, merge=False)
+            s_gpu = score[u].cpu().numpy()
+            worst = max(worst, float(np.max(np.abs(s_gpu - ref["score"]) /
+                                            (ref["score"] + 1e-30))))
+            n_diff += len(set(kept[u].cpu().numpy().tolist()) ^ set(ref["kept"].tolist()))
+        check = {"units": sample_units, "max_score_rel_err": worst, "kept_sym_diff": n_diff}
+        eprint(f"[bench] parity on units {sample_units}: {check}")
+
+    t_step = gpu_step_ms * 1e-3
+    out = {
+        "metric": METRIC,
+        "value": round(U * L / (ms_step * 1e-3), 1),
+        "unit": "KV-head·key-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "units": U, "layers": w.layers, "batch": w.batch,
+                   "kv_heads": w.h_kv, "group": g, "d_head": d, "L": L, "b_kv": B,
+                   "prefix": w.prefix, "recent": w.recent_tok, "rope_theta": w.theta},
+        "unit_evictions_per_s": round(U / (ms_step * 1e-3), 1),
+        "steps_per_s": round(1e3 / ms_step, 2),
+        "gpu_ms_per_step": round(gpu_step_ms, 4),
+        "alg_bytes_per_step": total_bytes,
+        "hbm_frac_step": round(total_bytes / t_step / 1e9 / HBM_PEAK_GBS, 4),
+        "moved_tokens": n_mv,
+        "stages": stages,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "parity": check,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

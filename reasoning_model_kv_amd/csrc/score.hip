@@ -148,6 +148,75 @@ __device__ __forceinline__ void build_queries(const ScoreArgs& a, int64_t u, int
     }
 }
 
+// RoPE alignment (paper text §4.3) as its own step: one wavefront per query
+// head rotates its 32 observation rows once and writes them as bf16 to
+// a.qobs ([U, g*32, d]); the scoring kernel reads them as MFMA A operands.
+template <int D>
+__global__ __launch_bounds__(256) void rope_align_kernel(ScoreArgs a, int g, int64_t n_heads) {
+    const int64_t qh = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
+    if (qh >= n_heads) return;
+    bf16x8 frag[D / 16];
+    build_queries<D>(a, qh / g, g, (int)(qh % g), threadIdx.x & 63, frag);
+}
+
+// A fragments of query head h of unit u: this lane's row (lane % 32) and
+// dims (16 s + 8 (lane / 32) .. + 8) of the bf16 observation rows.
+template <int D>
+__device__ __forceinline__ void load_frag(const uint16_t* qobs, int64_t u, int g, int h,
+                                          int lane, bf16x8 (&frag)[D / 16]) {
+    const uint16_t* qrow =
+        qobs + ((u * g + h) * 32 + (lane & 31)) * (int64_t)D + 8 * (lane >> 5);
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s)
+        frag[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qrow + 16 * s));
+}
+
+// Causal limit of accumulator entry v as an offset from the first recent
+// slot L - nrq: a key at offset d is visible iff d <= limit.  Beacon rows
+// see every live slot (offset nrq - 1 is slot L - 1); recent row i sees
+// slots up to its own, offset i.
+__device__ __forceinline__ int row_lim(int v, int lane, int nrq) {
+    const int r = acc_row(v, lane);
+    return r < 16 ? nrq - 1 : r - 16;
+}
+
+// exp2 without the denormal-range fix-up: results below 2^-126 flush to 0.
+// Used for the softmax sums, where such terms are negligible next to the
+// row maximum's term of 1.
+__device__ __forceinline__ float exp2_sum(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// s_waitcnt on the vector-memory counter only (expcnt and lgkmcnt at their
+// no-wait maxima): at most N vector memory operations of this wavefront may
+// still be outstanding; they complete in issue order.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Direct-to-LDS loads of one key tile by the first NL wavefronts: NPW
+// instructions per loader lane, in the same chunk order and XOR swizzle as
+// load_tile.
+template <int D, int NL>
+__device__ __forceinline__ void load_tile_nl(const uint16_t* Ku, int64_t L, int64_t base,
+                                             uint16_t* lds_tile, int wave, int lane) {
+    constexpr int CPR = D / 8;
+    constexpr int NPW = KT * CPR / (64 * NL);
+    static_assert(NPW * 64 * NL == KT * CPR, "tile split");
+#pragma unroll
+    for (int k = 0; k < NPW; ++k) {
+        const int p0 = (k * NL + wave) * 64;
+        const int p = p0 + lane;
+        const int j = p / CPR;
+        const int c = (p % CPR) ^ (j % CPR);
+        int64_t key = base + j;
+        key = key < L ? key : L - 1;
+        __builtin_amdgcn_global_load_lds(
+            (const void*)(Ku + key * D + 8 * c),
+            (__attribute__((address_space(3))) void*)(lds_tile + (int64_t)p0 * 8), 16, 0, 0);
+    }
+}
+
 // Issue the direct-to-LDS loads of one key tile.  LDS chunk p (16 bytes) of
 // the tile holds global chunk (row j, column c) with p = j*CPR + (c ^ (j%CPR)).
 template <int D>
@@ -195,15 +264,24 @@ __device__ __forceinline__ void tile_logits(const uint16_t* lds_tile, int lane,
     }
 }
 
-template <int D>
-__global__ __launch_bounds__(512) void score_kernel(ScoreArgs a, int g) {
-    __shared__ __attribute__((aligned(16))) uint16_t tiles[2][KT * D];
+// One workgroup per unit (one wavefront per query head); with about 140
+// VGPRs, 3 workgroups share a CU.
+template <int D, int NL>
+__global__ __launch_bounds__(512)
+void score_kernel(ScoreArgs a, int g) {
+    // Three separately declared tiles (not one array) so that the compiler
+    // can tell the tiles being loaded by the direct-to-LDS loads from the tile
+    // being read, and does not wait for the former before reading the latter.
+    __shared__ __attribute__((aligned(16))) uint16_t tile0[KT * D];
+    __shared__ __attribute__((aligned(16))) uint16_t tile1[KT * D];
+    __shared__ __attribute__((aligned(16))) uint16_t tile2[KT * D];
     __shared__ float red[8][KT];
+    constexpr int NPW = KT * (D / 8) / (64 * NL);  // loads per loader lane per tile
 
     const int tid = threadIdx.x;
-    const int nthreads = blockDim.x;
-    const int h = tid >> 6;
+    const int h = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int lane = tid & 63;
+    const bool loader = h < NL;
     const int64_t u = blockIdx.x;
     const int64_t L = a.L;
     const uint16_t* Ku = a.K + u * a.l_cap * D;
@@ -212,54 +290,83 @@ __global__ __launch_bounds__(512) void score_kernel(ScoreArgs a, int g) {
     const float c2 = a.c2;
 
     bf16x8 frag[D / 16];
-    build_queries<D>(a, u, g, h, lane, frag);
+    load_frag<D>(a.qobs, u, g, h, lane, frag);
+
+// One tile iteration: wait until tile `it` (in CUR) has landed while tile
+// it+1 may still be in flight (loader wavefronts; NST extra stores may be
+// younger than tile it+1's loads), start loading tile it+2 into NXT2, then
+// run BODY on CUR.  Lane-derived addresses are recomputed every iteration
+// (ti), not kept live across the loop.
+#define BKV_TILE_ITER(it, NST, CUR, NXT2, ...)                                     \
+    do {                                                                           \
+        int ti = tid;                                                              \
+        asm volatile("" : "+v"(ti));                                               \
+        if (loader) {                                                              \
+            if ((it) + 1 >= ntiles) wait_vm<0>();                                  \
+            else if (NST) wait_vm<NPW + 1>();                                      \
+            else wait_vm<NPW>();                                                   \
+        }                                                                          \
+        __syncthreads();                                                           \
+        if (loader && (it) + 2 < ntiles)                                           \
+            load_tile_nl<D, NL>(Ku, L, (int64_t)((it) + 2) * KT, NXT2, h, ti & 63); \
+        f32x16 acc0, acc1;                                                         \
+        tile_logits<D>(CUR, ti & 63, frag, acc0, acc1);                            \
+        const int64_t base = (int64_t)(it) * KT;                                   \
+        __VA_ARGS__;                                                               \
+    } while (0)
+// Tiles rotate through tile0, tile1, tile2; SDEL is 1 when wavefront 0
+// issues a score store in each iteration (pass 2), which the wait of the
+// next iteration must allow for.
+#define BKV_TILE_LOOP(SDEL, ...)                                                   \
+    do {                                                                           \
+        if (loader) {                                                              \
+            load_tile_nl<D, NL>(Ku, L, 0, tile0, h, lane);                          \
+            if (1 < ntiles) load_tile_nl<D, NL>(Ku, L, KT, tile1, h, lane);         \
+        }                                                                          \
+        for (int it = 0; it < ntiles; it += 3) {                                   \
+            BKV_TILE_ITER(it, (SDEL) && h == 0 && it > 0, tile0, tile2, __VA_ARGS__); \
+            if (it + 1 < ntiles)                                                   \
+                BKV_TILE_ITER(it + 1, (SDEL) && h == 0, tile1, tile0, __VA_ARGS__); \
+            if (it + 2 < ntiles)                                                   \
+                BKV_TILE_ITER(it + 2, (SDEL) && h == 0, tile2, tile1, __VA_ARGS__); \
+        }                                                                          \
+    } while (0)
 
     // ---------------- pass 1: per-row running max and sum of exp2 ----------
     float m[16], l[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) { m[v] = kNegBig; l[v] = 0.f; }
     const float thr = kRescaleLog2 / c2;
-
-    load_tile<D>(Ku, L, 0, tiles[0], tid, nthreads);
-    for (int it = 0; it < ntiles; ++it) {
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (it + 1 < ntiles)
-            load_tile<D>(Ku, L, (int64_t)(it + 1) * KT, tiles[(it + 1) & 1], tid, nthreads);
-        f32x16 acc0, acc1;
-        tile_logits<D>(tiles[it & 1], lane, frag, acc0, acc1);
-        const int64_t base = (int64_t)it * KT;
-        if (base + KT > mask_from) {
-            const int64_t k0 = base + (lane & 31), k1 = k0 + 32;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int r = acc_row(v, lane);
-                const int64_t lim = r < 16 ? L - 1 : L - a.n_recent_q + (r - 16);
-                if (k0 > lim) acc0[v] = -__builtin_inff();
-                if (k1 > lim) acc1[v] = -__builtin_inff();
-            }
-        }
-        bool need = false;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) need |= fmaxf(acc0[v], acc1[v]) > m[v] + thr;
-        if (__builtin_amdgcn_ballot_w64(need) != 0) {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                // Subtract before scaling: with the finite sentinel, m - mn is
-                // exactly 0 when nothing visible has been seen yet.
-                const float mn = fmaxf(m[v], fmaxf(acc0[v], acc1[v]));
-                l[v] = l[v] * exp2f((m[v] - mn) * c2) + exp2f((acc0[v] - mn) * c2) +
-                       exp2f((acc1[v] - mn) * c2);
-                m[v] = mn;
-            }
-        } else {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const float mc = m[v] * c2;
-                l[v] += exp2f(fmaf(acc0[v], c2, -mc)) + exp2f(fmaf(acc1[v], c2, -mc));
-            }
-        }
+#define BKV_PASS1                                                                  \
+    if (base + KT > mask_from) {                                                   \
+        const int ln = ti & 63;                                                    \
+        const int d0 = (int)(base - mask_from) + (ln & 31), d1 = d0 + 32;          \
+        _Pragma("unroll") for (int v = 0; v < 16; ++v) {                           \
+            const int lim = row_lim(v, ln, a.n_recent_q);                          \
+            if (d0 > lim) acc0[v] = -__builtin_inff();                             \
+            if (d1 > lim) acc1[v] = -__builtin_inff();                             \
+        }                                                                          \
+    }                                                                              \
+    bool need = false;                                                             \
+    _Pragma("unroll") for (int v = 0; v < 16; ++v)                                 \
+        need |= fmaxf(acc0[v], acc1[v]) > m[v] + thr;                              \
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {                                  \
+        /* Subtract before scaling: with the finite sentinel, m - mn is */         \
+        /* exactly 0 when nothing visible has been seen yet. */                    \
+        _Pragma("unroll") for (int v = 0; v < 16; ++v) {                           \
+            const float mn = fmaxf(m[v], fmaxf(acc0[v], acc1[v]));                 \
+            l[v] = l[v] * exp2_sum((m[v] - mn) * c2) + exp2_sum((acc0[v] - mn) * c2) + \
+                   exp2_sum((acc1[v] - mn) * c2);                                  \
+            m[v] = mn;                                                             \
+        }                                                                          \
+    } else {                                                                       \
+        _Pragma("unroll") for (int v = 0; v < 16; ++v) {                           \
+            const float mc = m[v] * c2;                                            \
+            l[v] += exp2_sum(fmaf(acc0[v], c2, -mc)) + exp2_sum(fmaf(acc1[v], c2, -mc)); \
+        }                                                                          \
     }
+    BKV_TILE_LOOP(0, BKV_PASS1);
+#undef BKV_PASS1
     // Merge the 32 lanes of each half: every lane ends with its rows' LSE.
 #pragma unroll
     for (int o = 1; o < 32; o <<= 1) {
@@ -268,7 +375,7 @@ __global__ __launch_bounds__(512) void score_kernel(ScoreArgs a, int g) {
             const float m2 = __shfl_xor(m[v], o);
             const float l2 = __shfl_xor(l[v], o);
             const float mn = fmaxf(m[v], m2);
-            l[v] = l[v] * exp2f((m[v] - mn) * c2) + l2 * exp2f((m2 - mn) * c2);
+            l[v] = l[v] * exp2_sum((m[v] - mn) * c2) + l2 * exp2_sum((m2 - mn) * c2);
             m[v] = mn;
         }
     }
@@ -277,51 +384,44 @@ __global__ __launch_bounds__(512) void score_kernel(ScoreArgs a, int g) {
     for (int v = 0; v < 16; ++v) lse[v] = fmaf(m[v], c2, log2f(l[v]));
 
     // ---------------- pass 2: max over rows of (s - LSE) -------------------
-    __syncthreads();  // everyone is done with both tile buffers
-    load_tile<D>(Ku, L, 0, tiles[0], tid, nthreads);
+    __syncthreads();  // everyone is done with the tiles
     float* score_u = a.score + u * a.l_cap;
-    for (int it = 0; it < ntiles; ++it) {
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (it + 1 < ntiles)
-            load_tile<D>(Ku, L, (int64_t)(it + 1) * KT, tiles[(it + 1) & 1], tid, nthreads);
-        f32x16 acc0, acc1;
-        tile_logits<D>(tiles[it & 1], lane, frag, acc0, acc1);
-        const int64_t base = (int64_t)it * KT;
-        float c0 = -__builtin_inff(), c1 = -__builtin_inff();
-        if (base + KT > mask_from) {
-            const int64_t k0 = base + (lane & 31), k1 = k0 + 32;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int r = acc_row(v, lane);
-                const int64_t lim = r < 16 ? L - 1 : L - a.n_recent_q + (r - 16);
-                const float y0 = fmaf(acc0[v], c2, -lse[v]);
-                const float y1 = fmaf(acc1[v], c2, -lse[v]);
-                if (k0 <= lim) c0 = fmaxf(c0, y0);
-                if (k1 <= lim) c1 = fmaxf(c1, y1);
-            }
-        } else {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                c0 = fmaxf(c0, fmaf(acc0[v], c2, -lse[v]));
-                c1 = fmaxf(c1, fmaf(acc1[v], c2, -lse[v]));
-            }
-        }
-        // Other half of the rows lives in lane ^ 32.
-        c0 = fmaxf(c0, __shfl_xor(c0, 32));
-        c1 = fmaxf(c1, __shfl_xor(c1, 32));
-        if (lane < 32) {
-            red[h][lane] = c0;
-            red[h][32 + lane] = c1;
-        }
-        __syncthreads();
-        if (tid < KT) {
-            float best = red[0][tid];
-            for (int w = 1; w < g; ++w) best = fmaxf(best, red[w][tid]);
-            const int64_t key = base + tid;
-            if (key < L) score_u[key] = exp2f(best);
-        }
+#define BKV_PASS2                                                                  \
+    float c0 = -__builtin_inff(), c1 = -__builtin_inff();                          \
+    if (base + KT > mask_from) {                                                   \
+        const int ln = ti & 63;                                                    \
+        const int d0 = (int)(base - mask_from) + (ln & 31), d1 = d0 + 32;          \
+        _Pragma("unroll") for (int v = 0; v < 16; ++v) {                           \
+            const int lim = row_lim(v, ln, a.n_recent_q);                          \
+            const float y0 = fmaf(acc0[v], c2, -lse[v]);                           \
+            const float y1 = fmaf(acc1[v], c2, -lse[v]);                           \
+            if (d0 <= lim) c0 = fmaxf(c0, y0);                                     \
+            if (d1 <= lim) c1 = fmaxf(c1, y1);                                     \
+        }                                                                          \
+    } else {                                                                       \
+        _Pragma("unroll") for (int v = 0; v < 16; ++v) {                           \
+            c0 = fmaxf(c0, fmaf(acc0[v], c2, -lse[v]));                            \
+            c1 = fmaxf(c1, fmaf(acc1[v], c2, -lse[v]));                            \
+        }                                                                          \
+    }                                                                              \
+    /* Other half of the rows lives in lane ^ 32. */                               \
+    c0 = fmaxf(c0, __shfl_xor(c0, 32));                                            \
+    c1 = fmaxf(c1, __shfl_xor(c1, 32));                                            \
+    if (lane < 32) {                                                               \
+        red[h][lane] = c0;                                                         \
+        red[h][32 + lane] = c1;                                                    \
+    }                                                                              \
+    __syncthreads();                                                               \
+    if (tid < KT) {                                                                \
+        float best = red[0][tid];                                                  \
+        for (int w = 1; w < g; ++w) best = fmaxf(best, red[w][tid]);               \
+        const int64_t key = base + tid;                                            \
+        if (key < L) score_u[key] = exp2f(best);                                   \
     }
+    BKV_TILE_LOOP(1, BKV_PASS2);
+#undef BKV_PASS2
+#undef BKV_TILE_LOOP
+#undef BKV_TILE_ITER
 }
 
 }  // namespace
@@ -338,7 +438,7 @@ hipError_t launch_score(const uint16_t* K, const int32_t* kpos, int64_t n_units,
                         const float* beacons, int buf_cap, const float* recents,
                         int n_beacon, int n_recent_q, int64_t t, double theta,
                         float sm_scale, const double* table, float* score,
-                        uint16_t* qobs_out, hipStream_t s) {
+                        uint16_t* qobs_out, uint16_t* qobs_ws, hipStream_t s) {
     (void)n_beacon;
     if (n_units <= 0) return hipSuccess;
     ScoreArgs a;
@@ -355,13 +455,28 @@ hipError_t launch_score(const uint16_t* K, const int32_t* kpos, int64_t n_units,
     a.c2 = sm_scale * 1.4426950408889634f;
     a.table = table;
     a.score = score;
-    a.qobs = qobs_out;
+    a.qobs = qobs_out ? qobs_out : qobs_ws;
+    const int64_t n_heads = n_units * g;
+    const unsigned rblocks = (unsigned)((n_heads + 3) / 4);
+    if (d == 128)
+        rope_align_kernel<128><<<rblocks, 256, 0, s>>>(a, g, n_heads);
+    else
+        rope_align_kernel<64><<<rblocks, 256, 0, s>>>(a, g, n_heads);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
     const dim3 grid((unsigned)n_units);
     const dim3 block(64 * g);
-    if (d == 128)
-        score_kernel<128><<<grid, block, 0, s>>>(a, g);
-    else
-        score_kernel<64><<<grid, block, 0, s>>>(a, g);
+    // Loader wavefronts: the largest power of two <= g, at most 4.
+    const int nl = g >= 4 ? 4 : (g >= 2 ? 2 : 1);
+    if (d == 128) {
+        if (nl == 4) score_kernel<128, 4><<<grid, block, 0, s>>>(a, g);
+        else if (nl == 2) score_kernel<128, 2><<<grid, block, 0, s>>>(a, g);
+        else score_kernel<128, 1><<<grid, block, 0, s>>>(a, g);
+    } else {
+        if (nl == 4) score_kernel<64, 4><<<grid, block, 0, s>>>(a, g);
+        else if (nl == 2) score_kernel<64, 2><<<grid, block, 0, s>>>(a, g);
+        else score_kernel<64, 1><<<grid, block, 0, s>>>(a, g);
+    }
     return hipGetLastError();
 }
 

@@ -1,4 +1,11 @@
-"""Scoring kernel (bkv_score) against the float64 oracle on the GPU."""
+"""Scoring kernel (bkv_score) against the float64 oracle on the GPU.
+
+The kernel streams each unit's keys in tiles of 64 through a ring of three
+LDS tiles (two passes); the cases cover a single tile, several tiles and
+ring turns, a ragged last tile, a last tile that some recent rows cannot
+see at all, recent positions that need the direct RoPE path, and groups of
+2, 4, 5 and 7 (which change the number of loader wavefronts).
+"""
 import numpy as np
 import pytest
 import torch
@@ -10,6 +17,15 @@ from reasoning_model_kv_amd import bkv
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
+
+
+def _workload(name):
+    if name == "tiny_g7":
+        return synth.shrink(synth.WORKLOADS["tiny"], group=7, d_head=128, theta=1e6)
+    if name == "tiny_g5":
+        return synth.shrink(synth.WORKLOADS["tiny"], group=5, d_head=128, theta=1e6,
+                            h_kv=3)
+    return synth.WORKLOADS[name]
 
 
 def _run(w, L=None, l_cap=None, t=None, kpos_offset=0):
@@ -28,15 +44,24 @@ def _run(w, L=None, l_cap=None, t=None, kpos_offset=0):
     return inp, score.cpu().numpy(), qobs.cpu(), t
 
 
-@pytest.mark.parametrize("name,L,l_cap,t_shift", [
-    ("tiny", None, None, 0),          # 256 slots, 4 full tiles
+CASES = [
+    ("tiny", None, None, 0),          # 256 slots: 4 tiles, one ring turn
     ("tiny", 203, 256, 0),            # ragged tail, l_cap > L
-    ("tiny", 40, 64, 0),              # one tile, recent rows masked inside it
+    ("tiny", 40, 64, 0),              # one tile; recent rows masked inside it
+    ("tiny", 64, 64, 0),              # exactly one full tile
+    ("tiny", 128, 128, 0),            # exactly two tiles
     ("tiny", 150, 150, 37),           # recent positions != t-16+i: direct RoPE path
+    ("tiny", 517, 600, 0),            # 5-key last tile, invisible to recent rows 0..10
+    ("tiny", 700, 700, 37),           # eleven tiles, direct RoPE path
+    ("tiny_g7", 300, 320, 0),         # group 7
+    ("tiny_g5", 1000, 1000, 0),       # group 5
     ("qwen3_4b_layer", None, None, 0),
-])
+]
+
+
+@pytest.mark.parametrize("name,L,l_cap,t_shift", CASES)
 def test_score_matches_oracle(name, L, l_cap, t_shift):
-    w = synth.WORKLOADS[name]
+    w = _workload(name)
     log(f"score {name} L={L or w.L} l_cap={l_cap} t_shift={t_shift}")
     inp, sc, qobs, t = _run(w, L, l_cap, None if not t_shift else (L or w.L) + t_shift)
     L = L or w.L

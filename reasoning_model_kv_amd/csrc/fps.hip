@@ -4,16 +4,13 @@
 // average cosine similarity picks the seed (lowest), then the row whose
 // largest cosine to the picked set is lowest joins it, until m rows remain.
 //
-// Mapping.  Buffers of up to 32 rows: one wavefront per query head, two
-// lanes per row, each lane holding half of the row (d/2 fp32 values) in
-// registers.  The unit-normalised rows are staged in LDS once; each pick
-// then broadcasts the new member's row from LDS to all lanes (same-address
-// reads, no bank conflicts), every lane pair forms its row's cosine with
-// it, and a wavefront argmin chooses the next pick.  The average cosine of
-// row i uses the sum of all normalised rows: sum_j cos(q_i, q_j) equals
-// q_i/|q_i| . sum_j q_j/|q_j|, one dot product instead of a row of the Gram
-// matrix.  Buffers of up to 256 rows (prefill) use one workgroup per head
-// and one thread per row.
+// Mapping.  Buffers of up to 32 rows: one wavefront per query head forms
+// the 32 x 32 cosine matrix once on fp32 MFMA and runs the greedy picks on
+// it (see fps_wave_kernel).  Buffers of up to 256 rows (prefill) use one
+// workgroup per head and one thread per row; there the average cosine of
+// row i uses the sum of all normalised rows (sum_j cos(q_i, q_j) equals
+// q_i/|q_i| . sum_j q_j/|q_j|) and each pick broadcasts the new member's
+// row through LDS.
 //
 // Arithmetic is fp32; ties go to the lower slot.
 
@@ -31,16 +28,39 @@ __device__ __forceinline__ void argmin_pair(float& v, int& i, float ov, int oi) 
     }
 }
 
-// Wavefront argmin over (value, index); every lane receives the result.
-// Lanes 2r and 2r+1 carry the same candidate, so xor 1 is skipped.
+// Cross-lane moves for the wavefront reductions: DPP within rows of 16
+// lanes, a bitmask swizzle for lane ^ 16 within 32.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x) {
+    return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __builtin_bit_cast(float, dpp_i<CTRL>(__builtin_bit_cast(int, x)));
+}
+__device__ __forceinline__ int swap16_i(int x) { return __builtin_amdgcn_ds_swizzle(x, 0x401F); }
+__device__ __forceinline__ float swap16_f(float x) {
+    return __builtin_bit_cast(float, swap16_i(__builtin_bit_cast(int, x)));
+}
+
+// Wavefront argmin over (value, index), returned wave-uniform.  Lanes 2r
+// and 2r+1 carry the same candidate, so lane ^ 1 is skipped: lane ^ 2
+// (quad_perm [2,3,0,1]), then the other quad of 8 (row_half_mirror), the
+// other 8 of 16 (row_mirror), lane ^ 16 (swizzle), and the two halves
+// (lanes 0 and 32).  (value, index) pairs compare lexicographically, so
+// the order of the steps does not change the result.
 __device__ __forceinline__ int wave_argmin_rows(float v, int i) {
-#pragma unroll
-    for (int o = 2; o < 64; o <<= 1) {
-        float ov = __shfl_xor(v, o);
-        int oi = __shfl_xor(i, o);
-        argmin_pair(v, i, ov, oi);
-    }
-    return i;
+    argmin_pair(v, i, dpp_f<0x4E>(v), dpp_i<0x4E>(i));
+    argmin_pair(v, i, dpp_f<0x141>(v), dpp_i<0x141>(i));
+    argmin_pair(v, i, dpp_f<0x140>(v), dpp_i<0x140>(i));
+    argmin_pair(v, i, swap16_f(v), swap16_i(i));
+    float v0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+    int i0 = __builtin_amdgcn_readlane(i, 0);
+    const float v1 =
+        __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+    const int i1 = __builtin_amdgcn_readlane(i, 32);
+    argmin_pair(v0, i0, v1, i1);
+    return i0;
 }
 
 __device__ __forceinline__ void wave_sync_lds() {
@@ -49,15 +69,47 @@ __device__ __forceinline__ void wave_sync_lds() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+// Wavefront argmin over (value, index) within each 32-lane half (both halves
+// hold the same 32 candidates, one per lane), returned wave-uniform:
+// lane ^ 1 and ^ 2 (quad_perm), the other quad of 8 (row_half_mirror), the
+// other 8 of 16 (row_mirror), lane ^ 16 (swizzle).  (value, index) pairs
+// compare lexicographically, so the order of the steps does not matter.
+__device__ __forceinline__ int half_argmin(float v, int i) {
+    argmin_pair(v, i, dpp_f<0xB1>(v), dpp_i<0xB1>(i));
+    argmin_pair(v, i, dpp_f<0x4E>(v), dpp_i<0x4E>(i));
+    argmin_pair(v, i, dpp_f<0x141>(v), dpp_i<0x141>(i));
+    argmin_pair(v, i, dpp_f<0x140>(v), dpp_i<0x140>(i));
+    argmin_pair(v, i, swap16_f(v), swap16_i(i));
+    return __builtin_amdgcn_readlane(i, 0);
+}
+
+// Buffers of up to 32 rows: one wavefront per query head.
+//  * Lane pair (2r, 2r+1) loads row r (half of its d fp32 values each) into
+//    registers, where the rows stay until the kept ones are written back.
+//  * The unit-normalised rows go to LDS transposed (dim-major), and the
+//    32 x 32 cosine matrix C = Qn Qn^T is formed with d/2 fp32 MFMAs
+//    (v_mfma_f32_32x32x2_f32; lane l supplies row l % 32, dim 2t + l / 32).
+//  * Lane l then stands for row l % 32.  The average cosine of row j is the
+//    sum of column j of C (C is symmetric) over N; the seed is its argmin.
+//    Each further pick p adds column p of C (one LDS read per lane) to the
+//    running max S, and the next pick is the argmin of S over the rows not
+//    yet picked.
 template <int D>
 __global__ __launch_bounds__(64) void fps_wave_kernel(
     float* __restrict__ buf, int32_t* __restrict__ count,
     const float* __restrict__ new_q, int n_new, int cap, int trigger, int m,
     int32_t* __restrict__ sel_order, int32_t* __restrict__ n_overflow) {
-    constexpr int HD = D / 2;       // dims held by one lane
-    constexpr int STRIDE = D + 4;   // LDS row stride (floats)
-    __shared__ float qn[32 * STRIDE];
-    __shared__ float svec[D];
+    constexpr int HD = D / 2;   // dims held by one lane of a pair
+    constexpr int TS = 33;      // LDS stride (floats) of the transposed rows and of C
+    constexpr int RS = D + 4;   // LDS stride (floats) of the raw rows
+    constexpr int C4 = D / 4;   // 16-byte chunks per row
+    constexpr int LDSF = D * TS > 32 * RS ? D * TS : 32 * RS;
+    // In turn: the raw rows (qt[row * RS + dim]), Qn^T (qt[dim * TS + row]),
+    // C (qt[i * TS + j]), and the raw rows again for the write-back.
+    __shared__ __attribute__((aligned(16))) float qt[LDSF];
+    __shared__ int keep[32];  // slots of the kept rows, ascending
 
     const int lane = threadIdx.x;
     const int64_t head = blockIdx.x;
@@ -83,7 +135,8 @@ __global__ __launch_bounds__(64) void fps_wave_kernel(
         return;
     }
 
-    // Load this lane's half row (rows >= N are padding).
+    // Load this lane's half row (rows >= N are padding); all 16-byte loads
+    // of a lane are in flight together.
     float x[HD];
     const bool valid = row < N;
     if (valid) {
@@ -102,60 +155,60 @@ __global__ __launch_bounds__(64) void fps_wave_kernel(
     float nn = 0.f;
 #pragma unroll
     for (int k = 0; k < HD; ++k) nn = fmaf(x[k], x[k], nn);
-    nn += __shfl_xor(nn, 1);
+    nn += dpp_f<0xB1>(nn);  // the lane pair's other half (quad_perm [1,0,3,2])
     const float inv = 1.0f / fmaxf(sqrtf(nn), kNormFloor);
 
-    float* myrow = qn + row * STRIDE + half * HD;
+    // Qn^T into LDS (padding rows are zero rows).
 #pragma unroll
-    for (int k = 0; k < HD; k += 4)
-        *reinterpret_cast<float4*>(myrow + k) =
-            make_float4(x[k] * inv, x[k + 1] * inv, x[k + 2] * inv, x[k + 3] * inv);
+    for (int k = 0; k < HD; ++k) qt[(half * HD + k) * TS + row] = x[k] * inv;
     wave_sync_lds();
 
-    // Sum of the normalised rows, one or two dims per lane.
-    for (int k = lane; k < D; k += 64) {
-        float s = 0.f;
-        for (int j = 0; j < N; ++j) s += qn[j * STRIDE + k];
-        svec[k] = s;
+    // C = Qn Qn^T: lane l holds C[i][l % 32] for i = 8 (v / 4) + 4 (l / 32) + v % 4.
+    const int r32 = lane & 31;
+    const int kk = lane >> 5;
+    f32x16 acc = f32x16{};
+#pragma unroll 8
+    for (int t = 0; t < HD; ++t) {
+        const float a = qt[(2 * t + kk) * TS + r32];
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, a, acc, 0, 0, 0);
     }
+    float colsum = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) colsum += acc[v];
+    colsum += __shfl_xor(colsum, 32);  // the other 16 rows of the column
+    wave_sync_lds();                   // every operand read of Qn^T is done
+#pragma unroll
+    for (int v = 0; v < 16; ++v) qt[(8 * (v >> 2) + 4 * kk + (v & 3)) * TS + r32] = acc[v];
     wave_sync_lds();
 
-    auto dot_with = [&](const float* v) {
-        float a = 0.f;
-#pragma unroll
-        for (int k = 0; k < HD; k += 4) {
-            float4 f = *reinterpret_cast<const float4*>(v + half * HD + k);
-            a = fmaf(x[k], f.x, a);
-            a = fmaf(x[k + 1], f.y, a);
-            a = fmaf(x[k + 2], f.z, a);
-            a = fmaf(x[k + 3], f.w, a);
-        }
-        a += __shfl_xor(a, 1);
-        return a * inv;
-    };
-
-    const float avg = dot_with(svec) / (float)N;
+    // Lane l stands for row l % 32 from here on.
+    const bool valid32 = r32 < N;
     const float inf = __builtin_inff();
-    int pick = wave_argmin_rows(valid ? avg : inf, row);
+    int pick = half_argmin(valid32 ? colsum / (float)N : inf, r32);
     uint32_t sel = 1u << pick;
     int my_pick = (lane == 0) ? pick : -1;
-    float S = dot_with(qn + pick * STRIDE);
-
+    float S = qt[pick * TS + r32];
     for (int it = 1; it < m; ++it) {
-        const bool cand = valid && !((sel >> row) & 1u);
-        pick = wave_argmin_rows(cand ? S : inf, row);
+        const bool cand = valid32 && !((sel >> r32) & 1u);
+        pick = half_argmin(cand ? S : inf, r32);
         sel |= 1u << pick;
         if (lane == it) my_pick = pick;
-        S = fmaxf(S, dot_with(qn + pick * STRIDE));
+        S = fmaxf(S, qt[pick * TS + r32]);
     }
 
-    // Keep the picked rows in ascending slot order, from registers.
-    if ((sel >> row) & 1u) {
-        const int rank = __popc(sel & ((1u << row) - 1u));
-        float* dst = hb + (int64_t)rank * D + half * HD;
+    // Keep the picked rows in ascending slot order: raw rows back to LDS
+    // (every read of C is done), then contiguous 16-byte stores.
+    wave_sync_lds();
 #pragma unroll
-        for (int k = 0; k < HD; k += 4)
-            *reinterpret_cast<float4*>(dst + k) = make_float4(x[k], x[k + 1], x[k + 2], x[k + 3]);
+    for (int k = 0; k < HD; k += 4)
+        *reinterpret_cast<float4*>(qt + row * RS + half * HD + k) =
+            make_float4(x[k], x[k + 1], x[k + 2], x[k + 3]);
+    if (lane < 32 && ((sel >> lane) & 1u)) keep[__popc(sel & ((1u << lane) - 1u))] = lane;
+    wave_sync_lds();
+    for (int id = lane; id < m * C4; id += 64) {
+        const int r = id / C4, c4 = id % C4;
+        *reinterpret_cast<float4*>(hb + (int64_t)r * D + 4 * c4) =
+            *reinterpret_cast<const float4*>(qt + keep[r] * RS + 4 * c4);
     }
     if (sel_order && lane < m) sel_order[head * m + lane] = my_pick;
     if (lane == 0) count[head] = m;

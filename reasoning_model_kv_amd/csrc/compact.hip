@@ -19,6 +19,14 @@ namespace bkv {
 namespace {
 
 constexpr int WAVES = 4;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Streaming (non-temporal) 16-byte store: the compacted rows are not read
+// again by this step.
+__device__ __forceinline__ void st_nt(uint16_t* p, uint4 v) {
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4*>(p));
+}
 constexpr int TPI = 16;  // tokens per iteration
 
 template <int D>
@@ -81,10 +89,10 @@ __global__ __launch_bounds__(64 * WAVES) void compact_kernel(
         if (s3 >= 0) { k3r = *(const uint4*)(Ks + (int64_t)s3 * D + off); v3r = *(const uint4*)(Vs + (int64_t)s3 * D + off); }
         int32_t pr = 0;
         if (psrc >= 0) pr = ps[psrc];
-        if (s0 >= 0) { *(uint4*)(Kd + kb * D + off) = k0r; *(uint4*)(Vd + kb * D + off) = v0r; }
-        if (s1 >= 0) { *(uint4*)(Kd + (kb + TPW) * D + off) = k1r; *(uint4*)(Vd + (kb + TPW) * D + off) = v1r; }
-        if (s2 >= 0) { *(uint4*)(Kd + (kb + 2 * TPW) * D + off) = k2r; *(uint4*)(Vd + (kb + 2 * TPW) * D + off) = v2r; }
-        if (s3 >= 0) { *(uint4*)(Kd + (kb + 3 * TPW) * D + off) = k3r; *(uint4*)(Vd + (kb + 3 * TPW) * D + off) = v3r; }
+        if (s0 >= 0) { st_nt(Kd + kb * D + off, k0r); st_nt(Vd + kb * D + off, v0r); }
+        if (s1 >= 0) { st_nt(Kd + (kb + TPW) * D + off, k1r); st_nt(Vd + (kb + TPW) * D + off, v1r); }
+        if (s2 >= 0) { st_nt(Kd + (kb + 2 * TPW) * D + off, k2r); st_nt(Vd + (kb + 2 * TPW) * D + off, v2r); }
+        if (s3 >= 0) { st_nt(Kd + (kb + 3 * TPW) * D + off, k3r); st_nt(Vd + (kb + 3 * TPW) * D + off, v3r); }
         if (psrc >= 0) pd[base + lane] = pr;
     }
 }

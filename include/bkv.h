@@ -112,9 +112,13 @@ size_t bkv_workspace_bytes(const bkv_dims* dims, const bkv_policy* pol,
  *      (heads that do not compress get -1 there).
  * Typical calls: trigger = buf_cap = 32, m = 16 (fill and compress);
  * trigger = m + 1 (beacon fix: compress only heads holding more than m);
- * n_new = 16 recents with trigger 32 after an eviction (merge).
- * Arithmetic is fp32.  Requires 0 <= n_new <= buf_cap, new_q NULL iff
- * n_new == 0, 1 <= m < trigger <= buf_cap <= 256, every count in
+ * n_new = 16 recents with trigger 32 after an eviction (merge);
+ * trigger = buf_cap + 1 (append only, never compress: collecting the recent
+ * queries, summary step (3), in a buffer of n_recent_q rows).
+ * The cosine matrix of a buffer of up to 32 rows is formed on fp32 MFMA
+ * (v_mfma_f32_32x32x2_f32); other arithmetic is fp32.  Requires
+ * 0 <= n_new <= buf_cap, new_q NULL iff n_new == 0,
+ * 1 <= m < trigger <= buf_cap + 1, buf_cap <= 256, every count in
  * [0, buf_cap] on entry.  buf and count are updated in place; new_q must not
  * overlap buf.
  */

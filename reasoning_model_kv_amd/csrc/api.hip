@@ -180,9 +180,9 @@ int bkv_fps_update(const bkv_dims* dims, const bkv_policy* pol, float* buf, int3
         return fail(BKV_EINVAL, "%s: n_new %d not in [0, buf_cap=%d]", fn, n_new, pol->buf_cap);
     if ((new_q == nullptr) != (n_new == 0))
         return fail(BKV_EINVAL, "%s: new_q must be NULL exactly when n_new == 0", fn);
-    if (!(1 <= m && m < trigger && trigger <= pol->buf_cap))
-        return fail(BKV_EINVAL, "%s: need 1 <= m (%d) < trigger (%d) <= buf_cap (%d)", fn, m,
-                    trigger, pol->buf_cap);
+    if (!(1 <= m && m < trigger && trigger <= pol->buf_cap + 1))
+        return fail(BKV_EINVAL, "%s: need 1 <= m (%d) < trigger (%d) <= buf_cap + 1 (%d)", fn, m,
+                    trigger, pol->buf_cap + 1);
     if (dims->n_units == 0) return ok();
     if (fault_injected(fn)) return fail(BKV_EHIP, "%s: injected HIP failure", fn);
     const int64_t n_heads = dims->n_units * dims->group;

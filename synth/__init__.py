@@ -56,6 +56,7 @@ class Workload:
     outlier_scale: float = 6.0
     seed: int = 0
     l_cap: int = 0      # slot stride; 0 means L
+    stream_steps: int = 0  # decode steps of a streaming run (L is then B_max)
 
     @property
     def n_units(self):
@@ -96,6 +97,19 @@ def _r1_qwen_7b():
                     theta=1e6)
 
 
+def _qwen3_14b_stream():
+    # Streaming run: prompt of `prefix` tokens, then decode steps; eviction
+    # fires when the cache reaches L = B_max = b_kv + 128.
+    return Workload("qwen3-14b-40L-b16-stream", 5, layers=40, batch=16, h_kv=8, group=5,
+                    d_head=128, L=4224, b_kv=4096, prefix=256, theta=1e6,
+                    stream_steps=32768)
+
+
+def _stream_small():
+    return Workload("stream-small", 6, layers=1, batch=2, h_kv=2, group=5, d_head=128,
+                    L=384, b_kv=256, prefix=32, theta=1e6, stream_steps=640)
+
+
 WORKLOADS = {
     "tiny": _tiny(),
     "qwen3_4b_layer": _qwen3_4b_layer(),
@@ -105,6 +119,8 @@ WORKLOADS = {
     "qwen3_4b_full_b2048": _qwen3_4b_full(2048),
     "qwen3_4b_full_b4096": _qwen3_4b_full(4096),
     "r1_qwen_7b": _r1_qwen_7b(),
+    "qwen3_14b_stream": _qwen3_14b_stream(),
+    "stream_small": _stream_small(),
 }
 
 
@@ -316,3 +332,88 @@ def to_device(inp, device="cuda", l_cap=None):
     rec = torch.from_numpy(inp["recents"].reshape(U * g, *inp["recents"].shape[2:])).to(dev)
     return {"keys": keys, "values": vals, "kpos": kpos, "buf": buf.contiguous(),
             "recents": rec.contiguous(), "t": inp["t"]}
+
+
+# ---------------------------------------------------------------------------
+# Streaming inputs (decode-time runs), generated on the device in chunks of
+# steps.  A prompt of `prefix` tokens, then one key, value (bf16) and
+# pre-RoPE query per query head (fp32) per unit and step.  Queries follow the
+# same mixture: local queries copy one of the 32 most recently generated keys
+# of their unit (+ noise), global ones a cluster centre of their head.
+
+KIND_SPRE, KIND_SSTEP = 8, 9
+
+
+class StreamInputs:
+    """Seeded per-step inputs of a streaming workload on ``device``.
+
+    prompt() -> keys, values [U, P, d] bf16; queries [U*g, P, d] fp32.
+    chunk(c, n) -> keys, values [n, U, d] bf16; queries [n, U*g, d] fp32 for
+    decode steps c*n .. c*n + n - 1 (chunks must be requested in order).
+    """
+
+    def __init__(self, w, device="cuda"):
+        self.w = w
+        self.dev = torch.device(device)
+        U, g, d = w.n_units, w.group, w.d_head
+        gc = _dev_gen(w, KIND_CENTRES, 0, self.dev)
+        cen = torch.randn((U * g, w.n_centres, d), generator=gc, device=self.dev)
+        self.centres = cen / cen.norm(dim=-1, keepdim=True)
+        self.window = None  # [U, 32, d] fp32: the 32 most recent keys of each unit
+        self.next_chunk = 0
+
+    def _queries(self, gen, n_steps, keys_at):
+        """keys_at(j): [n_steps, U*g, d] fp32, the key j (0..31) steps back from
+        each step's own token for each query head's unit."""
+        w = self.w
+        U, g, d = w.n_units, w.group, w.d_head
+        nq = U * g
+        is_g = torch.rand((n_steps, nq), generator=gen, device=self.dev) < w.pi_global
+        which = torch.randint(0, w.n_centres, (n_steps, nq), generator=gen, device=self.dev)
+        j = torch.randint(0, 32, (n_steps, nq), generator=gen, device=self.dev)
+        local = keys_at(j)
+        glob = 8.0 * self.centres[torch.arange(nq, device=self.dev)[None, :], which]
+        q = torch.where(is_g[..., None], glob, local)
+        return q + 0.3 * torch.randn((n_steps, nq, d), generator=gen, device=self.dev)
+
+    def _unit_of(self):
+        return torch.arange(self.w.n_units * self.w.group, device=self.dev) // self.w.group
+
+    def prompt(self):
+        w = self.w
+        U, g, d, P = w.n_units, w.group, w.d_head, w.prefix
+        gen = _dev_gen(w, KIND_SPRE, 0, self.dev)
+        k = torch.randn((U, P, d), generator=gen, device=self.dev).to(torch.bfloat16)
+        v = torch.randn((U, P, d), generator=gen, device=self.dev).to(torch.bfloat16)
+        kf = k.to(torch.float32)
+        unit_of = self._unit_of()
+        steps = torch.arange(P, device=self.dev)[:, None]
+
+        def keys_at(j):  # prompt query i sees keys max(0, i - 31) .. i
+            return kf[unit_of[None, :], torch.clamp(steps - j, min=0)]
+
+        q = self._queries(gen, P, keys_at).permute(1, 0, 2).contiguous()  # [U*g, P, d]
+        last = torch.clamp(torch.arange(P - 32, P, device=self.dev), min=0)
+        self.window = kf[:, last].contiguous()                            # last 32 keys
+        return k, v, q
+
+    def chunk(self, c, n):
+        if c != self.next_chunk:
+            raise ValueError("stream chunks must be generated in order")
+        self.next_chunk += 1
+        w = self.w
+        U, d = w.n_units, w.d_head
+        gen = _dev_gen(w, KIND_SSTEP, c, self.dev)
+        k = torch.randn((n, U, d), generator=gen, device=self.dev).to(torch.bfloat16)
+        v = torch.randn((n, U, d), generator=gen, device=self.dev).to(torch.bfloat16)
+        # keys of step s: allk[32 + s] is its own, allk[32 + s - j] is j steps back
+        allk = torch.cat([self.window.permute(1, 0, 2), k.to(torch.float32)], dim=0)  # [32+n, U, d]
+        unit_of = self._unit_of()
+        steps = torch.arange(n, device=self.dev)[:, None]
+
+        def keys_at(j):
+            return allk[32 + steps - j, unit_of[None, :]]
+
+        q = self._queries(gen, n, keys_at)
+        self.window = allk[-32:].permute(1, 0, 2).contiguous()
+        return k, v, q

@@ -97,7 +97,7 @@ def test_fps_validation(lib):
         ctypes.byref(s.dims()), ctypes.byref(s.policy()), FAKE, FAKE, nq, n_new, trig, m, None,
         None, None)
     assert call(None, 0, 32, 32) == bkv.BKV_EINVAL     # m == trigger
-    assert call(None, 0, 33, 16) == bkv.BKV_EINVAL     # trigger > buf_cap
+    assert call(None, 0, 34, 16) == bkv.BKV_EINVAL     # trigger > buf_cap + 1
     assert call(None, 0, 32, 0) == bkv.BKV_EINVAL      # m < 1
     assert call(FAKE, 0, 32, 16) == bkv.BKV_EINVAL     # new_q without rows
     assert call(None, 1, 32, 16) == bkv.BKV_EINVAL     # rows without new_q

@@ -1,0 +1,146 @@
+"""Decode-time streaming run (Stream driver over the C ABI) against the oracle.
+
+The policy's event cadence must equal the oracle state machine's
+(oracle.stream.UnitStream, same prompt length, B_max, B_KV).  Every event is
+checked on the GPU's own state just before it ("lockstep with resync"): each
+FPS compression by replaying its pick order in float64; each eviction by the
+oracle's scores and kept set on the pre-eviction cache, exact compaction
+with the GPU's kept set, and the merged buffer.  Small run: every unit and
+head.  Qwen3-14B shape (40 layers x batch 16 x 8 KV heads, group 5): the
+first two eviction intervals on sampled units and heads.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from parity_util import check_fps, check_kept, check_scores, log
+from reasoning_model_kv_amd import stream as bstream
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+class Checker:
+    """Observer: snapshots sampled state before each event, checks after."""
+
+    def __init__(self, w, units):
+        self.w, self.units = w, list(units)
+        self.heads = [u * w.group + h for u in self.units for h in range(w.group)]
+        self.pre = None
+        self.n = {"fps": 0, "evict": 0, "exact_fps": 0}
+        self.worst = 0.0
+
+    def __call__(self, kind, stage, st):
+        hi = torch.tensor(self.heads, device=st.buf.device)
+        if stage == "pre":
+            if kind == "prefill_fps":
+                self.pre = {"rows": st.prompt_queries[hi].cpu().numpy()}
+            elif kind in ("collect_fps", "beacon_fix_fps"):
+                rows = st.buf[hi].cpu().numpy()
+                n = st.rows
+                if kind == "collect_fps":  # the step's query is appended first
+                    rows[:, n] = st.last_q[hi].cpu().numpy()
+                    n += 1
+                self.pre = {"rows": rows[:, :n]}
+            else:
+                ui = torch.tensor(self.units, device=st.K.device)
+                self.pre = {"K": st.K[ui].float().cpu().numpy(),
+                            "V": st.V[ui].float().cpu().numpy(),
+                            "P": st.kpos[ui].cpu().numpy(), "L": st.L, "t": st.t,
+                            "beacons": st.buf[hi, :16].cpu().numpy(),
+                            "recents": st.recents[hi].cpu().numpy()}
+            return
+        if kind != "evict":
+            sel = st.sel[hi].cpu().numpy()
+            out = st.buf[hi, :16].cpu().numpy()
+            for i, q in enumerate(self.heads):
+                rows = self.pre["rows"][i]
+                self.n["exact_fps"] += check_fps(rows, sel[i], 16, f"{kind} head {q}")
+                assert np.array_equal(out[i], rows[np.sort(sel[i])]), f"{kind} head {q} rows"
+            self.n["fps"] += 1
+            return
+        w, pre, g = self.w, self.pre, self.w.group
+        L, b = pre["L"], w.b_kv
+        ui = torch.tensor(self.units, device=st.K.device)
+        K1, V1, P1 = (st.K[ui].float().cpu().numpy(), st.V[ui].float().cpu().numpy(),
+                      st.kpos[ui].cpu().numpy())
+        sc, kept = st.score[ui].cpu().numpy(), st.kept[ui].cpu().numpy()
+        merged_out = st.buf[hi, :16].cpu().numpy()
+        for i, u in enumerate(self.units):
+            hs = slice(i * g, (i + 1) * g)
+            ref = oracle.evict.evict_unit(pre["K"][i], pre["V"][i], pre["P"][i], L,
+                                          pre["beacons"][hs], pre["recents"][hs], pre["t"], b,
+                                          w.prefix, w.recent_tok, w.theta)
+            where = f"evict at L={L} unit {u}"
+            self.worst = max(self.worst, check_scores(sc[i, :L], ref["score"], where))
+            check_kept(kept[i], ref["score"], L, b, w.prefix, w.recent_tok, where)
+            assert np.array_equal(K1[i, :b], pre["K"][i][kept[i]]), where + " K"
+            assert np.array_equal(V1[i, :b], pre["V"][i][kept[i]]), where + " V"
+            assert np.array_equal(P1[i, :b], pre["P"][i][kept[i]]), where + " kpos"
+            for h in range(g):
+                merged = np.concatenate([pre["beacons"][i * g + h], pre["recents"][i * g + h]])
+                out = merged_out[i * g + h]
+                idx = [int(np.nonzero((merged == row).all(axis=1))[0][0]) for row in out]
+                assert idx == sorted(idx) and len(set(idx)) == 16, where + " merged rows"
+                if min(oracle.fps.fps_margins(merged, 16)) > 2e-3:
+                    order, _ = oracle.fps.fps(merged, 16)
+                    assert sorted(order) == idx, where + " merged FPS set"
+        self.n["evict"] += 1
+
+
+def _oracle_events(w, n_steps):
+    """Event cadence of the oracle state machine (values do not affect it)."""
+    st = oracle.stream.UnitStream(1, 4, w.L, w.b_kv, w.prefix, w.theta)
+    r = np.random.default_rng(0)
+    st.prefill(r.standard_normal((w.prefix, 4)), r.standard_normal((w.prefix, 4)),
+               r.standard_normal((1, w.prefix, 4)))
+    for _ in range(n_steps):
+        st.step(r.standard_normal(4), r.standard_normal(4), r.standard_normal((1, 4)))
+    return st.events
+
+
+def _run(w, n_steps, units, chunk=128):
+    chk = Checker(w, units)
+    st = bstream.Stream(w.n_units, w.group, w.d_head, w.L, w.b_kv, w.prefix, w.theta,
+                        device=DEV, observer=chk)
+    gen = synth.StreamInputs(w, DEV)
+    st.prefill(*gen.prompt())
+    done = 0
+    c = 0
+    while done < n_steps:
+        k, v, q = gen.chunk(c, chunk)
+        c += 1
+        for s in range(min(chunk, n_steps - done)):
+            st.step(k[s], v[s], q[s])
+        done += min(chunk, n_steps - done)
+    torch.cuda.synchronize()
+    return st, chk
+
+
+def test_stream_small_all_units():
+    w = synth.WORKLOADS["stream_small"]
+    n = w.stream_steps
+    log(f"stream {w.name}: U={w.n_units} g={w.group} B_max={w.L} B_KV={w.b_kv} steps={n}")
+    st, chk = _run(w, n, range(w.n_units))
+    assert st.events == _oracle_events(w, n)
+    first = w.L - w.prefix
+    assert st.n_evictions == 1 + (n - first) // 128
+    assert chk.n["evict"] == st.n_evictions and chk.n["fps"] > 10
+    log(f"  events {len(st.events)}, evictions {st.n_evictions}, FPS events {chk.n['fps']}, "
+        f"exact FPS sets {chk.n['exact_fps']}, max score rel err {chk.worst:.3g}")
+
+
+def test_stream_qwen3_14b_two_intervals_sampled():
+    w = synth.WORKLOADS["qwen3_14b_stream"]
+    n = (w.L - w.prefix) + 128 + 40  # two evictions, then into the third interval
+    units = [0, 2047, w.n_units - 1]
+    log(f"stream {w.name}: U={w.n_units} g={w.group} steps={n} sampled units {units}")
+    st, chk = _run(w, n, units)
+    assert st.events == _oracle_events(w, n)
+    assert st.n_evictions == 2 and chk.n["evict"] == 2
+    assert st.L == w.b_kv + 40
+    assert torch.all(st.count == 16 + 40 % 16)
+    log(f"  FPS events {chk.n['fps']}, exact FPS sets {chk.n['exact_fps']}, "
+        f"max score rel err {chk.worst:.3g}")

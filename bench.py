@@ -55,6 +55,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle baseline sample (0 disables)")
     p.add_argument("--no-check", action="store_true", help="skip the sampled parity check")
+    p.add_argument("--stream-steps", type=int, default=0,
+                   help="decode steps of a streaming workload (0: the workload's own)")
     return p.parse_args()
 
 
@@ -195,6 +197,9 @@ def main():
     import synth
 
     w = synth.WORKLOADS[args.workload]
+    if w.stream_steps:
+        stream_main(args, w)
+        return
     cpu = None
     if args.cpu_seconds > 0:
         eprint(f"[bench] oracle CPU baseline (~{args.cpu_seconds:.0f} s of CPU work per core)")
@@ -355,6 +360,106 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "parity": check,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def stream_main(args, w):
+    """Streaming decode run (the Qwen3-14B-shaped workload): the whole policy
+    over `stream_steps` decode steps of all units in lockstep.  Each chunk of
+    128 steps is generated on the device before its steps are timed; HIP
+    events on the launch stream time the chunks (decode-step upkeep:
+    writing each token's K/V, append / fill-and-compress, beacon fix, recent
+    capture, evictions) and, inside them, every eviction event."""
+    import numpy as np
+    import torch
+
+    import synth
+    from reasoning_model_kv_amd import bkv
+    from reasoning_model_kv_amd import stream as bstream
+
+    bkv.load_library()
+    if not torch.cuda.is_available():
+        eprint("no GPU visible")
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    n_steps = args.stream_steps or w.stream_steps
+    U, g, d = w.n_units, w.group, w.d_head
+    cs = torch.cuda.current_stream()
+    ev_marks = []
+
+    def observer(kind, stage, st):
+        if kind == "evict":
+            e = torch.cuda.Event(enable_timing=True)
+            e.record(cs)
+            ev_marks.append(e)
+
+    st = bstream.Stream(U, g, d, w.L, w.b_kv, w.prefix, w.theta, device=dev, observer=observer)
+    gen = synth.StreamInputs(w, dev)
+    st.prefill(*gen.prompt())
+    torch.cuda.synchronize()
+    eprint(f"[bench] stream {w.name}: U={U} g={g} B_max={w.L} B_KV={w.b_kv} P={w.prefix} "
+           f"steps={n_steps}")
+    chunk_ms, done, c, moved = [], 0, 0, []
+    t_wall = time.perf_counter()
+    while done < n_steps:
+        n = min(128, n_steps - done)
+        k, v, q = gen.chunk(c, 128)
+        c += 1
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(cs)
+        before = st.n_evictions
+        for s_ in range(n):
+            st.step(k[s_], v[s_], q[s_])
+        e1.record(cs)
+        torch.cuda.synchronize()
+        chunk_ms.append(e0.elapsed_time(e1))
+        if st.n_evictions > before and len(moved) < 4:
+            kept = st.kept.cpu().numpy()
+            moved.append(int(np.count_nonzero(kept != np.arange(w.b_kv)[None, :])))
+        done += n
+        if c % 32 == 0:
+            eprint(f"[bench] {done} steps, {st.n_evictions} evictions")
+    wall = time.perf_counter() - t_wall
+    evict_ms = [ev_marks[i].elapsed_time(ev_marks[i + 1]) for i in range(0, len(ev_marks), 2)]
+    gpu_ms = float(np.sum(chunk_ms))
+    n_ev = st.n_evictions
+    unit_ev = n_ev * U
+    mean_ev = float(np.mean(evict_ms)) if evict_ms else float("nan")
+    L = w.L
+    n_mv = float(np.mean(moved)) if moved else 0.0
+    ev_bytes = (U * (L * d * 2 + g * 32 * d * 4 + 16 * 4 + L * 4)       # score
+                + U * ((L - w.prefix - w.recent_tok) * 4 + w.b_kv * 4)  # select
+                + n_mv * (4 * d * 2 + 8) + U * w.b_kv * 4               # compaction
+                + U * g * ((16 + 16 + 16) * d * 4 + 8))                 # merge FPS
+    cache_bytes = 2 * U * L * d * 2
+    out = {
+        "metric": "unit-evictions/s sustained over a streaming decode run (Qwen3-14B shape)",
+        "value": round(unit_ev / (gpu_ms * 1e-3), 1),
+        "unit": "unit-evictions/s",
+        "n_gpus": 1,
+        "steps": n_steps,
+        "warmup": 0,
+        "ms_per_step": round(gpu_ms / n_steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "units": U, "layers": w.layers, "batch": w.batch,
+                   "kv_heads": w.h_kv, "group": g, "d_head": d, "B_max": L, "b_kv": w.b_kv,
+                   "prefix": w.prefix, "recent": w.recent_tok, "rope_theta": w.theta},
+        "evictions": n_ev,
+        "evict_ms_mean": round(mean_ev, 4),
+        "evict_hbm_frac": round(ev_bytes / (mean_ev * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "decode_upkeep_ms_per_step": round((gpu_ms - float(np.sum(evict_ms))) / n_steps, 5),
+        "gpu_s_total": round(gpu_ms * 1e-3, 3),
+        "wall_s_total": round(wall, 3),
+        "peak_cache_bytes": cache_bytes,
+        "full_cache_bytes_at_end": 2 * U * (w.prefix + n_steps) * d * 2,
+        "torch_max_memory_allocated": torch.cuda.max_memory_allocated(),
+        "moved_tokens_per_eviction": n_mv,
     }
     print(json.dumps(out), flush=True)
 

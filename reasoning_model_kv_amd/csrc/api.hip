@@ -128,6 +128,10 @@ int check_score_args(const char* fn, const bkv_dims* d, const bkv_policy* p, con
     if (p->buf_cap < p->n_beacon)
         return fail(BKV_EINVAL, "%s: buf_cap %d < n_beacon %d", fn, p->buf_cap, p->n_beacon);
     if (t < 0) return fail(BKV_EINVAL, "%s: t %lld < 0", fn, (long long)t);
+    // The scoring kernel addresses one unit's keys with 32-bit byte offsets.
+    if (L * d->d_head * 2 > INT32_MAX)
+        return fail(BKV_ENOTSUP, "%s: L %lld keys of d_head %d exceed 2^31 bytes per unit", fn,
+                    (long long)L, d->d_head);
     return BKV_OK;
 }
 

@@ -35,7 +35,9 @@ typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 constexpr int KT = 64;               // keys per tile
 constexpr float kNegBig = -1.0e30f;  // finite "no key seen yet" running max
-constexpr float kRescaleLog2 = 64.f; // lazy rescale threshold (log2 units)
+// Buffer-resource flags word (gfx9 family: raw 32-bit data, no swizzle).
+constexpr int kBufferFlags = 0x00020000;
+constexpr float kRescaleBig = 0x1p64f; // lazy rescale: largest tile term sum kept
 
 __device__ __forceinline__ void rope_cs(double pos, int i, int d, double theta,
                                         double* c, double* s) {
@@ -180,6 +182,16 @@ __device__ __forceinline__ int row_lim(int v, int lane, int nrq) {
     return r < 16 ? nrq - 1 : r - 16;
 }
 
+// Maximum of two or three floats as one v_maximum(3)_f32.  The operands are
+// logits, LSE offsets or their exp2 (never NaN for finite inputs); unlike
+// fmaxf this needs no canonicalisation of its inputs.
+__device__ __forceinline__ float vmax(float x, float y) {
+    return __builtin_elementwise_maximum(x, y);
+}
+__device__ __forceinline__ float vmax3(float x, float y, float z) {
+    return __builtin_elementwise_maximum(__builtin_elementwise_maximum(x, y), z);
+}
+
 // exp2 without the denormal-range fix-up: results below 2^-126 flush to 0.
 // Used for the softmax sums, where such terms are negligible next to the
 // row maximum's term of 1.
@@ -194,73 +206,87 @@ __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// Direct-to-LDS loads of one key tile by the first NL wavefronts: NPW
-// instructions per loader lane, in the same chunk order and XOR swizzle as
-// load_tile.
+// Key tiles in LDS: chunk p (16 bytes) of a tile holds global chunk (row j,
+// column c) of the tile's keys with p = j*CPR + (c ^ (j % CPR)), CPR = D/8
+// chunks per row; the XOR swizzle by row makes the 32 lanes that read one
+// chunk column for an MFMA B operand hit distinct banks.
+//
+// Loads go through a buffer resource whose base is the tile's first key and
+// whose size ends at key L - 1: chunks of keys at or past L read as zero
+// (the hardware range check, no memory access) and are masked later.  The
+// first NL wavefronts load, NPW direct-to-LDS instructions per lane and
+// tile; each lane's byte offsets within a tile are the same for every tile.
 template <int D, int NL>
-__device__ __forceinline__ void load_tile_nl(const uint16_t* Ku, int64_t L, int64_t base,
-                                             uint16_t* lds_tile, int wave, int lane) {
-    constexpr int CPR = D / 8;
-    constexpr int NPW = KT * CPR / (64 * NL);
+struct TileLoad {
+    static constexpr int CPR = D / 8;
+    static constexpr int NPW = KT * CPR / (64 * NL);
     static_assert(NPW * 64 * NL == KT * CPR, "tile split");
+    // One load instruction fills 64 / CPR key rows (1 KB).  Load k of
+    // wavefront w starts at row (k*NL + w) * 64/CPR; the swizzle term of a
+    // lane repeats with period NP in k, so NP offsets serve all NPW loads
+    // and the rest of the displacement (k * NL KB) moves the buffer base.
+    static constexpr int ROWS = 64 / CPR;
+    static constexpr int NP = (CPR / ROWS) / NL > 1 ? (CPR / ROWS) / NL : 1;
+    int voff[NP];
+
+    __device__ __forceinline__ TileLoad(int wave, int lane) {
 #pragma unroll
-    for (int k = 0; k < NPW; ++k) {
-        const int p0 = (k * NL + wave) * 64;
-        const int p = p0 + lane;
-        const int j = p / CPR;
-        const int c = (p % CPR) ^ (j % CPR);
-        int64_t key = base + j;
-        key = key < L ? key : L - 1;
-        __builtin_amdgcn_global_load_lds(
-            (const void*)(Ku + key * D + 8 * c),
-            (__attribute__((address_space(3))) void*)(lds_tile + (int64_t)p0 * 8), 16, 0, 0);
+        for (int k = 0; k < NP; ++k) {
+            const int j = (k * NL + wave) * ROWS + lane / CPR;
+            const int c = (lane % CPR) ^ (j % CPR);
+            voff[k] = (((k * NL + wave) * ROWS) * D + (lane / CPR) * D + 8 * c) * 2 - k * NL * 1024;
+        }
     }
-}
 
-// Issue the direct-to-LDS loads of one key tile.  LDS chunk p (16 bytes) of
-// the tile holds global chunk (row j, column c) with p = j*CPR + (c ^ (j%CPR)).
-template <int D>
-__device__ __forceinline__ void load_tile(const uint16_t* Ku, int64_t L, int64_t base,
-                                          uint16_t* lds_tile, int tid, int nthreads) {
-    constexpr int CPR = D / 8;  // 16-byte chunks per key row
-    constexpr int NCH = KT * CPR;
-    const int wave = tid >> 6, lane = tid & 63;
-    for (int p0 = wave * 64; p0 < NCH; p0 += nthreads) {
-        const int p = p0 + lane;
-        const int j = p / CPR;
-        const int c = (p % CPR) ^ (j % CPR);
-        int64_t key = base + j;
-        key = key < L ? key : L - 1;  // tail: any valid row, masked later
-        const uint16_t* gsrc = Ku + key * D + 8 * c;
-        __builtin_amdgcn_global_load_lds(
-            (const void*)gsrc,
-            (__attribute__((address_space(3))) void*)(lds_tile + (int64_t)p0 * 8), 16, 0, 0);
+    // Issue the loads of keys [base, base + KT) of Ku (L keys) into lds_tile.
+    __device__ __forceinline__ void issue(const uint16_t* Ku, int64_t L, int64_t base,
+                                          uint16_t* lds_tile, int wave) const {
+        const int bytes = (int)((L - base) * D * 2);
+#pragma unroll
+        for (int k = 0; k < NPW; ++k) {
+            const int shift = k * NL * 1024;
+            const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)((const char*)(Ku + base * D) + shift), 0,
+                bytes > shift ? bytes - shift : 0, kBufferFlags);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc,
+                (__attribute__((address_space(3))) void*)(lds_tile + (k * NL + wave) * 64 * 8),
+                16, voff[k % NP], 0, 0, 0);
+        }
     }
-}
+};
+
+// Byte offsets (within a tile) of this lane's B-operand chunks for MFMA
+// steps s = 0..D/16-1 of the first 32 keys; the second 32 keys are
+// 32*D*2 bytes further.
+template <int D>
+struct TileRead {
+    static constexpr int NS = D / 16;
+    uint32_t off[NS];
+    __device__ __forceinline__ explicit TileRead(int lane) {
+        constexpr int CPR = D / 8;
+        const int j = lane & 31, hh = lane >> 5;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) off[s] = (uint32_t)(j * D + 8 * ((2 * s + hh) ^ (j % CPR))) * 2;
+    }
+};
 
 template <int D>
-__device__ __forceinline__ void tile_logits(const uint16_t* lds_tile, int lane,
+__device__ __forceinline__ void tile_logits(const uint16_t* lds_tile, const TileRead<D>& rd,
                                             const bf16x8 (&frag)[D / 16], f32x16& acc0,
                                             f32x16& acc1) {
     constexpr int NS = D / 16;
-    constexpr int CPR = D / 8;
-    const int hh = lane >> 5;
+    const char* t = reinterpret_cast<const char*>(lds_tile);
     acc0 = f32x16{};
     acc1 = f32x16{};
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-        const int j = cb * 32 + (lane & 31);
-        const uint16_t* rowp = lds_tile + j * D;
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            const int c = (2 * s + hh) ^ (j % CPR);
-            const uint4 w = *reinterpret_cast<const uint4*>(rowp + 8 * c);
-            const bf16x8 b = __builtin_bit_cast(bf16x8, w);
-            if (cb == 0)
-                acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag[s], b, acc0, 0, 0, 0);
-            else
-                acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag[s], b, acc1, 0, 0, 0);
-        }
+    for (int s = 0; s < NS; ++s) {
+        const uint4 w0 = *reinterpret_cast<const uint4*>(t + rd.off[s]);
+        const uint4 w1 = *reinterpret_cast<const uint4*>(t + rd.off[s] + 32 * D * 2);
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag[s], __builtin_bit_cast(bf16x8, w0),
+                                                       acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag[s], __builtin_bit_cast(bf16x8, w1),
+                                                       acc1, 0, 0, 0);
     }
 }
 
@@ -276,7 +302,7 @@ void score_kernel(ScoreArgs a, int g) {
     __shared__ __attribute__((aligned(16))) uint16_t tile1[KT * D];
     __shared__ __attribute__((aligned(16))) uint16_t tile2[KT * D];
     __shared__ float red[8][KT];
-    constexpr int NPW = KT * (D / 8) / (64 * NL);  // loads per loader lane per tile
+    constexpr int NPW = TileLoad<D, NL>::NPW;  // loads per loader lane per tile
 
     const int tid = threadIdx.x;
     const int h = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -291,16 +317,15 @@ void score_kernel(ScoreArgs a, int g) {
 
     bf16x8 frag[D / 16];
     load_frag<D>(a.qobs, u, g, h, lane, frag);
+    const TileLoad<D, NL> ld(h, lane);
+    const TileRead<D> rd(lane);
 
 // One tile iteration: wait until tile `it` (in CUR) has landed while tile
 // it+1 may still be in flight (loader wavefronts; NST extra stores may be
 // younger than tile it+1's loads), start loading tile it+2 into NXT2, then
-// run BODY on CUR.  Lane-derived addresses are recomputed every iteration
-// (ti), not kept live across the loop.
+// run BODY on CUR.
 #define BKV_TILE_ITER(it, NST, CUR, NXT2, ...)                                     \
     do {                                                                           \
-        int ti = tid;                                                              \
-        asm volatile("" : "+v"(ti));                                               \
         if (loader) {                                                              \
             if ((it) + 1 >= ntiles) wait_vm<0>();                                  \
             else if (NST) wait_vm<NPW + 1>();                                      \
@@ -308,9 +333,9 @@ void score_kernel(ScoreArgs a, int g) {
         }                                                                          \
         __syncthreads();                                                           \
         if (loader && (it) + 2 < ntiles)                                           \
-            load_tile_nl<D, NL>(Ku, L, (int64_t)((it) + 2) * KT, NXT2, h, ti & 63); \
+            ld.issue(Ku, L, (int64_t)((it) + 2) * KT, NXT2, h);                    \
         f32x16 acc0, acc1;                                                         \
-        tile_logits<D>(CUR, ti & 63, frag, acc0, acc1);                            \
+        tile_logits<D>(CUR, rd, frag, acc0, acc1);                                 \
         const int64_t base = (int64_t)(it) * KT;                                   \
         __VA_ARGS__;                                                               \
     } while (0)
@@ -320,8 +345,8 @@ void score_kernel(ScoreArgs a, int g) {
 #define BKV_TILE_LOOP(SDEL, ...)                                                   \
     do {                                                                           \
         if (loader) {                                                              \
-            load_tile_nl<D, NL>(Ku, L, 0, tile0, h, lane);                          \
-            if (1 < ntiles) load_tile_nl<D, NL>(Ku, L, KT, tile1, h, lane);         \
+            ld.issue(Ku, L, 0, tile0, h);                                          \
+            if (1 < ntiles) ld.issue(Ku, L, KT, tile1, h);                         \
         }                                                                          \
         for (int it = 0; it < ntiles; it += 3) {                                   \
             BKV_TILE_ITER(it, (SDEL) && h == 0 && it > 0, tile0, tile2, __VA_ARGS__); \
@@ -333,13 +358,18 @@ void score_kernel(ScoreArgs a, int g) {
     } while (0)
 
     // ---------------- pass 1: per-row running max and sum of exp2 ----------
-    float m[16], l[16];
+    // mc[v]: running maximum of row v's logits in log2 units (logit * c2),
+    // starting at a finite sentinel; l[v]: sum of exp2(logit * c2 - mc[v]).
+    // The maximum is updated lazily: a tile whose terms stay below
+    // kRescaleBig (logits at most ~64 log2 units above mc) is summed against
+    // the stale mc; otherwise (and for the first tile, where every term
+    // overflows against the sentinel) the tile is redone with a rescale.
+    float mc[16], l[16];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) { m[v] = kNegBig; l[v] = 0.f; }
-    const float thr = kRescaleLog2 / c2;
+    for (int v = 0; v < 16; ++v) { mc[v] = kNegBig; l[v] = 0.f; }
 #define BKV_PASS1                                                                  \
     if (base + KT > mask_from) {                                                   \
-        const int ln = ti & 63;                                                    \
+        const int ln = lane;                                                       \
         const int d0 = (int)(base - mask_from) + (ln & 31), d1 = d0 + 32;          \
         _Pragma("unroll") for (int v = 0; v < 16; ++v) {                           \
             const int lim = row_lim(v, ln, a.n_recent_q);                          \
@@ -347,41 +377,48 @@ void score_kernel(ScoreArgs a, int g) {
             if (d1 > lim) acc1[v] = -__builtin_inff();                             \
         }                                                                          \
     }                                                                              \
-    bool need = false;                                                             \
-    _Pragma("unroll") for (int v = 0; v < 16; ++v)                                 \
-        need |= fmaxf(acc0[v], acc1[v]) > m[v] + thr;                              \
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {                                  \
-        /* Subtract before scaling: with the finite sentinel, m - mn is */         \
-        /* exactly 0 when nothing visible has been seen yet. */                    \
-        _Pragma("unroll") for (int v = 0; v < 16; ++v) {                           \
-            const float mn = fmaxf(m[v], fmaxf(acc0[v], acc1[v]));                 \
-            l[v] = l[v] * exp2_sum((m[v] - mn) * c2) + exp2_sum((acc0[v] - mn) * c2) + \
-                   exp2_sum((acc1[v] - mn) * c2);                                  \
-            m[v] = mn;                                                             \
+    BKV_PASS1_HALF(0);                                                             \
+    BKV_PASS1_HALF(8);
+// Rows v0..v0+7 of one tile: sum against the stale maxima if every term
+// stays below kRescaleBig, else rescale those rows.
+#define BKV_PASS1_HALF(v0)                                                         \
+    do {                                                                           \
+        float tsum[8];                                                             \
+        float big = 0.f;                                                           \
+        _Pragma("unroll") for (int v = 0; v < 8; ++v) {                            \
+            tsum[v] = exp2_sum(fmaf(acc0[(v0) + v], c2, -mc[(v0) + v])) +          \
+                      exp2_sum(fmaf(acc1[(v0) + v], c2, -mc[(v0) + v]));           \
+            if (v & 1) big = vmax3(big, tsum[v - 1], tsum[v]);                      \
         }                                                                          \
-    } else {                                                                       \
-        _Pragma("unroll") for (int v = 0; v < 16; ++v) {                           \
-            const float mc = m[v] * c2;                                            \
-            l[v] += exp2_sum(fmaf(acc0[v], c2, -mc)) + exp2_sum(fmaf(acc1[v], c2, -mc)); \
+        if (__builtin_amdgcn_ballot_w64(!(big <= kRescaleBig)) == 0) {             \
+            _Pragma("unroll") for (int v = 0; v < 8; ++v) l[(v0) + v] += tsum[v];  \
+        } else {                                                                   \
+            _Pragma("unroll") for (int v = (v0); v < (v0) + 8; ++v) {              \
+                const float mn = vmax3(mc[v], acc0[v] * c2, acc1[v] * c2);         \
+                l[v] = l[v] * exp2_sum(mc[v] - mn) + exp2_sum(fmaf(acc0[v], c2, -mn)) + \
+                       exp2_sum(fmaf(acc1[v], c2, -mn));                           \
+                mc[v] = mn;                                                        \
+            }                                                                      \
         }                                                                          \
-    }
+    } while (0)
     BKV_TILE_LOOP(0, BKV_PASS1);
 #undef BKV_PASS1
+#undef BKV_PASS1_HALF
     // Merge the 32 lanes of each half: every lane ends with its rows' LSE.
 #pragma unroll
     for (int o = 1; o < 32; o <<= 1) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-            const float m2 = __shfl_xor(m[v], o);
+            const float m2 = __shfl_xor(mc[v], o);
             const float l2 = __shfl_xor(l[v], o);
-            const float mn = fmaxf(m[v], m2);
-            l[v] = l[v] * exp2_sum((m[v] - mn) * c2) + l2 * exp2_sum((m2 - mn) * c2);
-            m[v] = mn;
+            const float mn = fmaxf(mc[v], m2);
+            l[v] = l[v] * exp2_sum(mc[v] - mn) + l2 * exp2_sum(m2 - mn);
+            mc[v] = mn;
         }
     }
     float lse[16];  // log2-domain LSE in units of (logit * c2)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) lse[v] = fmaf(m[v], c2, log2f(l[v]));
+    for (int v = 0; v < 16; ++v) lse[v] = mc[v] + log2f(l[v]);
 
     // ---------------- pass 2: max over rows of (s - LSE) -------------------
     __syncthreads();  // everyone is done with the tiles
@@ -389,24 +426,24 @@ void score_kernel(ScoreArgs a, int g) {
 #define BKV_PASS2                                                                  \
     float c0 = -__builtin_inff(), c1 = -__builtin_inff();                          \
     if (base + KT > mask_from) {                                                   \
-        const int ln = ti & 63;                                                    \
+        const int ln = lane;                                                       \
         const int d0 = (int)(base - mask_from) + (ln & 31), d1 = d0 + 32;          \
         _Pragma("unroll") for (int v = 0; v < 16; ++v) {                           \
             const int lim = row_lim(v, ln, a.n_recent_q);                          \
             const float y0 = fmaf(acc0[v], c2, -lse[v]);                           \
             const float y1 = fmaf(acc1[v], c2, -lse[v]);                           \
-            if (d0 <= lim) c0 = fmaxf(c0, y0);                                     \
-            if (d1 <= lim) c1 = fmaxf(c1, y1);                                     \
+            if (d0 <= lim) c0 = vmax(c0, y0);                                      \
+            if (d1 <= lim) c1 = vmax(c1, y1);                                      \
         }                                                                          \
     } else {                                                                       \
-        _Pragma("unroll") for (int v = 0; v < 16; ++v) {                           \
-            c0 = fmaxf(c0, fmaf(acc0[v], c2, -lse[v]));                            \
-            c1 = fmaxf(c1, fmaf(acc1[v], c2, -lse[v]));                            \
+        _Pragma("unroll") for (int v = 0; v < 16; v += 2) {                        \
+            c0 = vmax3(c0, fmaf(acc0[v], c2, -lse[v]), fmaf(acc0[v + 1], c2, -lse[v + 1])); \
+            c1 = vmax3(c1, fmaf(acc1[v], c2, -lse[v]), fmaf(acc1[v + 1], c2, -lse[v + 1])); \
         }                                                                          \
     }                                                                              \
     /* Other half of the rows lives in lane ^ 32. */                               \
-    c0 = fmaxf(c0, __shfl_xor(c0, 32));                                            \
-    c1 = fmaxf(c1, __shfl_xor(c1, 32));                                            \
+    c0 = vmax(c0, __shfl_xor(c0, 32));                                             \
+    c1 = vmax(c1, __shfl_xor(c1, 32));                                             \
     if (lane < 32) {                                                               \
         red[h][lane] = c0;                                                         \
         red[h][32 + lane] = c1;                                                    \
@@ -414,7 +451,7 @@ void score_kernel(ScoreArgs a, int g) {
     __syncthreads();                                                               \
     if (tid < KT) {                                                                \
         float best = red[0][tid];                                                  \
-        for (int w = 1; w < g; ++w) best = fmaxf(best, red[w][tid]);               \
+        for (int w = 1; w < g; ++w) best = vmax(best, red[w][tid]);                \
         const int64_t key = base + tid;                                            \
         if (key < L) score_u[key] = exp2f(best);                                   \
     }

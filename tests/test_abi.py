@@ -56,6 +56,9 @@ def test_score_validation(lib):
     assert _call_score(lib, _shape(n_beacon=8)) == bkv.BKV_ENOTSUP
     assert _call_score(lib, _shape(rope_theta=0.0)) == bkv.BKV_EINVAL
     assert _call_score(lib, _shape(buf_cap=300)) == bkv.BKV_ENOTSUP
+    big = _shape(n_units=1, l_cap=1 << 23)                        # 2^31 key bytes per unit
+    assert _call_score(lib, big, L=1 << 23, t=1 << 23) == bkv.BKV_ENOTSUP
+    assert "2^31" in bkv.last_error()
     assert _call_score(lib, _shape(n_units=0)) == bkv.BKV_OK     # no-op, no launch
     assert bkv.last_error() == ""
 

@@ -6,21 +6,22 @@
 // current cache, max-pooled over all queries and heads of the KV group
 // (summary step (4); review §4.3: Score[j] = max_{h in g} max_q W[h,q,j]).
 //
-// Mapping (one workgroup per KV group, one wavefront per query head):
-//  * A wavefront owns its head's 32 observation rows (16 beacons, 16
-//    recents).  It rotates them in fp64 straight into the A operand of
-//    v_mfma_f32_32x32x16_bf16: lane (row i = lane % 32, half h = lane / 32)
-//    holds dims 16 s + 8 h + e for MFMA step s, element e; the RoPE partner
-//    of dim k < d/2 (dim k + d/2) sits in the same lane at step s + d/32.
-//  * Keys stream through LDS in tiles of 64 (double-buffered, loaded with
-//    global_load_lds_dwordx4, 16-byte chunks XOR-swizzled by row so the
-//    32 lanes that read one chunk column hit distinct banks).  All g
+// Two kernels:
+//  * rope_align_kernel (one wavefront per query head) rotates the head's 32
+//    observation rows (16 beacons, 16 recents) once in fp64 and writes them
+//    as bf16 rows, the A operands of v_mfma_f32_32x32x16_bf16.
+//  * score_kernel (one workgroup per KV group, one wavefront per query
+//    head) holds its head's rows in registers as A fragments (lane: row
+//    lane % 32, dims 16 s + 8 (lane / 32) .. + 8 for MFMA step s).  Keys
+//    stream through a ring of three LDS tiles of 64 keys, loaded two tiles
+//    ahead by buffer_load ... lds (16-byte chunks XOR-swizzled by row so the
+//    32 lanes that read one chunk column hit distinct banks); all g
 //    wavefronts of the group read the same tile.
-//  * Pass 1: per 64-key tile each wavefront forms a 32 x 64 logit block and
-//    keeps a per-lane running (max, sum of exp2) for its 16 rows; the 32
-//    lanes of a half are merged once at the end into each row's LSE.
+//  * Pass 1: per tile each wavefront forms a 32 x 64 logit block and keeps a
+//    per-lane running (max, sum of exp2) for its 16 rows; the 32 lanes of a
+//    half are merged once at the end into each row's LSE.
 //  * Pass 2: the logits are formed again, shifted by the row LSE, reduced
-//    over the lane's 16 rows, the other half (permlane32 swap) and the g
+//    over the lane's 16 rows, the other half (lane ^ 32) and the g
 //    wavefronts (LDS), and written as score = exp2(max).
 //  Output layout of the 32x32 MFMA: lane l, accumulator v holds
 //  row 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32.
@@ -79,86 +80,60 @@ __device__ __forceinline__ int acc_row(int v, int lane) {
     return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
 }
 
-// Build this lane's A fragments (bf16) for MFMA steps 0..D/16-1.
+// RoPE alignment (paper text §4.3) as its own step, one wavefront per query
+// head: lane k owns the RoPE pair (k, k + D/2) (for D = 64 the two halves of
+// the wavefront take two rows at a time), walks the head's 32 observation
+// rows (16 beacons at position t, 16 recents at their own positions) and
+// writes them as bf16 rows to a.qobs ([U, g*32, D]), the MFMA A operands of
+// the scoring kernel.  Rotation in fp64 (products rounded separately, as
+// the plain definition computes them), then fp64 -> fp32 -> bf16, both
+// round-to-nearest-even.  The cos/sin pairs come from the table for t and
+// t-16..t-1; a recent row at any other position computes its own.
 template <int D>
-__device__ __forceinline__ void build_queries(const ScoreArgs& a, int64_t u, int g,
-                                              int h, int lane, bf16x8 (&frag)[D / 16]) {
+__global__ __launch_bounds__(256) void rope_align_kernel(ScoreArgs a, int g, int64_t n_heads) {
 #pragma clang fp contract(off)
-    constexpr int NS = D / 16;
-    const int i = lane & 31;
-    const int hh = lane >> 5;
-    const int64_t qh = u * g + h;
-    const float* src;
-    int64_t pos;
-    const double* tab = nullptr;
-    if (i < 16) {
-        src = a.beacons + (qh * a.buf_cap + i) * (int64_t)D;
-        pos = a.t;
-        tab = a.table;
-    } else {
-        const int r = i - 16;
-        src = a.recents + (qh * a.n_recent_q + r) * (int64_t)D;
-        pos = a.kpos[u * a.l_cap + a.L - a.n_recent_q + r];
-        if (pos == a.t - a.n_recent_q + r) tab = a.table + (int64_t)(1 + r) * D;
-    }
-    uint16_t out[NS][8];
-#pragma unroll
-    for (int s = 0; s < NS / 2; ++s) {
-        const int d0 = 16 * s + 8 * hh;
-        float x1[8], x2[8];
-        const float4 p0 = *reinterpret_cast<const float4*>(src + d0);
-        const float4 p1 = *reinterpret_cast<const float4*>(src + d0 + 4);
-        const float4 q0 = *reinterpret_cast<const float4*>(src + d0 + D / 2);
-        const float4 q1 = *reinterpret_cast<const float4*>(src + d0 + D / 2 + 4);
-        x1[0] = p0.x; x1[1] = p0.y; x1[2] = p0.z; x1[3] = p0.w;
-        x1[4] = p1.x; x1[5] = p1.y; x1[6] = p1.z; x1[7] = p1.w;
-        x2[0] = q0.x; x2[1] = q0.y; x2[2] = q0.z; x2[3] = q0.w;
-        x2[4] = q1.x; x2[5] = q1.y; x2[6] = q1.z; x2[7] = q1.w;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int k = d0 + e;
-            double c, sn;
-            if (tab) {
-                c = tab[2 * k];
-                sn = tab[2 * k + 1];
+    constexpr int HALF = D / 2;
+    constexpr int RPS = 64 / HALF;  // rows per step
+    const int64_t qh = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
+    if (qh >= n_heads) return;
+    const int lane = threadIdx.x & 63;
+    const int k = lane % HALF, sub = lane / HALF;
+    const int64_t u = qh / g;
+    const int h = (int)(qh % g);
+    const double2 cs_t = reinterpret_cast<const double2*>(a.table)[k];
+    uint16_t* out = a.qobs + (u * g + h) * 32 * (int64_t)D;
+    const int32_t* kp = a.kpos + u * a.l_cap + a.L - a.n_recent_q;
+#pragma unroll 4
+    for (int i0 = 0; i0 < 32; i0 += RPS) {
+        const int i = i0 + sub;
+        const float* src;
+        double c, sn;
+        if (i < 16) {
+            src = a.beacons + (qh * a.buf_cap + i) * (int64_t)D;
+            c = cs_t.x;
+            sn = cs_t.y;
+        } else {
+            const int r = i - 16;
+            src = a.recents + (qh * a.n_recent_q + r) * (int64_t)D;
+            const int64_t pos = kp[r];
+            if (pos == a.t - a.n_recent_q + r) {
+                const double2 v = reinterpret_cast<const double2*>(a.table)[(1 + r) * HALF + k];
+                c = v.x;
+                sn = v.y;
             } else {
                 rope_cs((double)pos, k, D, a.theta, &c, &sn);
             }
-            const double a1 = (double)x1[e], a2 = (double)x2[e];
-            const double p = a1 * c;
-            const double q = a2 * sn;
-            const double y1 = p - q;
-            const double r1 = a2 * c;
-            const double r2 = a1 * sn;
-            const double y2 = r1 + r2;
-            out[s][e] = f32_to_bf16_rne((float)y1);
-            out[s + NS / 2][e] = f32_to_bf16_rne((float)y2);
         }
+        const double x1 = (double)src[k], x2 = (double)src[k + HALF];
+        const double p = x1 * c;
+        const double q = x2 * sn;
+        const double y1 = p - q;
+        const double r1 = x2 * c;
+        const double r2 = x1 * sn;
+        const double y2 = r1 + r2;
+        out[i * D + k] = f32_to_bf16_rne((float)y1);
+        out[i * D + k + HALF] = f32_to_bf16_rne((float)y2);
     }
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-        uint4 w;
-        w.x = (uint32_t)out[s][0] | ((uint32_t)out[s][1] << 16);
-        w.y = (uint32_t)out[s][2] | ((uint32_t)out[s][3] << 16);
-        w.z = (uint32_t)out[s][4] | ((uint32_t)out[s][5] << 16);
-        w.w = (uint32_t)out[s][6] | ((uint32_t)out[s][7] << 16);
-        frag[s] = __builtin_bit_cast(bf16x8, w);
-        if (a.qobs) {
-            const int64_t row = (int64_t)h * 32 + i;
-            *reinterpret_cast<uint4*>(a.qobs + ((u * g * 32) + row) * D + 16 * s + 8 * hh) = w;
-        }
-    }
-}
-
-// RoPE alignment (paper text §4.3) as its own step: one wavefront per query
-// head rotates its 32 observation rows once and writes them as bf16 to
-// a.qobs ([U, g*32, d]); the scoring kernel reads them as MFMA A operands.
-template <int D>
-__global__ __launch_bounds__(256) void rope_align_kernel(ScoreArgs a, int g, int64_t n_heads) {
-    const int64_t qh = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
-    if (qh >= n_heads) return;
-    bf16x8 frag[D / 16];
-    build_queries<D>(a, qh / g, g, (int)(qh % g), threadIdx.x & 63, frag);
 }
 
 // A fragments of query head h of unit u: this lane's row (lane % 32) and

@@ -90,49 +90,76 @@ __device__ __forceinline__ int acc_row(int v, int lane) {
 // round-to-nearest-even.  The cos/sin pairs come from the table for t and
 // t-16..t-1; a recent row at any other position computes its own.
 template <int D>
-__global__ __launch_bounds__(256) void rope_align_kernel(ScoreArgs a, int g, int64_t n_heads) {
+__device__ __forceinline__ void rotate_store(uint16_t* row, int k, float x1f, float x2f,
+                                             double c, double sn) {
 #pragma clang fp contract(off)
+    const double x1 = (double)x1f, x2 = (double)x2f;
+    const double p = x1 * c;
+    const double q = x2 * sn;
+    const double y1 = p - q;
+    const double r1 = x2 * c;
+    const double r2 = x1 * sn;
+    const double y2 = r1 + r2;
+    row[k] = f32_to_bf16_rne((float)y1);
+    row[k + D / 2] = f32_to_bf16_rne((float)y2);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void rope_align_kernel(ScoreArgs a, int g, int64_t n_heads) {
     constexpr int HALF = D / 2;
     constexpr int RPS = 64 / HALF;  // rows per step
+    constexpr int NB = 16 / RPS;    // steps per 16 rows
     const int64_t qh = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
     if (qh >= n_heads) return;
     const int lane = threadIdx.x & 63;
     const int k = lane % HALF, sub = lane / HALF;
     const int64_t u = qh / g;
     const int h = (int)(qh % g);
-    const double2 cs_t = reinterpret_cast<const double2*>(a.table)[k];
+    const double2* tab = reinterpret_cast<const double2*>(a.table);
     uint16_t* out = a.qobs + (u * g + h) * 32 * (int64_t)D;
-    const int32_t* kp = a.kpos + u * a.l_cap + a.L - a.n_recent_q;
-#pragma unroll 4
-    for (int i0 = 0; i0 < 32; i0 += RPS) {
-        const int i = i0 + sub;
-        const float* src;
-        double c, sn;
-        if (i < 16) {
-            src = a.beacons + (qh * a.buf_cap + i) * (int64_t)D;
-            c = cs_t.x;
-            sn = cs_t.y;
-        } else {
-            const int r = i - 16;
-            src = a.recents + (qh * a.n_recent_q + r) * (int64_t)D;
-            const int64_t pos = kp[r];
-            if (pos == a.t - a.n_recent_q + r) {
-                const double2 v = reinterpret_cast<const double2*>(a.table)[(1 + r) * HALF + k];
-                c = v.x;
-                sn = v.y;
-            } else {
-                rope_cs((double)pos, k, D, a.theta, &c, &sn);
-            }
+    // Positions of the 16 recent rows: lane r (mod 16) holds row r's.
+    const int64_t rpos = a.kpos[u * a.l_cap + a.L - a.n_recent_q + (lane & 15)];
+
+    // Beacons (rows 0..15) at position t.  All loads are issued before any
+    // arithmetic so that they overlap.
+    {
+        float x1[NB], x2[NB];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            const float* src = a.beacons + (qh * a.buf_cap + j * RPS + sub) * (int64_t)D;
+            x1[j] = src[k];
+            x2[j] = src[k + HALF];
         }
-        const double x1 = (double)src[k], x2 = (double)src[k + HALF];
-        const double p = x1 * c;
-        const double q = x2 * sn;
-        const double y1 = p - q;
-        const double r1 = x2 * c;
-        const double r2 = x1 * sn;
-        const double y2 = r1 + r2;
-        out[i * D + k] = f32_to_bf16_rne((float)y1);
-        out[i * D + k + HALF] = f32_to_bf16_rne((float)y2);
+        const double2 cs = tab[k];
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+            rotate_store<D>(out + (j * RPS + sub) * D, k, x1[j], x2[j], cs.x, cs.y);
+    }
+    // Recents (rows 16..31): recent r at its own position, tabulated when it
+    // is t - 16 + r, else computed here.
+    {
+        float x1[NB], x2[NB];
+        double2 cs[NB];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            const int r = j * RPS + sub;
+            const float* src = a.recents + (qh * a.n_recent_q + r) * (int64_t)D;
+            x1[j] = src[k];
+            x2[j] = src[k + HALF];
+            cs[j] = tab[(1 + r) * HALF + k];
+        }
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            const int r = j * RPS + sub;
+            const int64_t pos = __shfl(rpos, r);
+            if (pos != a.t - a.n_recent_q + r) {
+                double c, sn;
+                rope_cs((double)pos, k, D, a.theta, &c, &sn);
+                cs[j].x = c;
+                cs[j].y = sn;
+            }
+            rotate_store<D>(out + (16 + r) * D, k, x1[j], x2[j], cs[j].x, cs[j].y);
+        }
     }
 }
 

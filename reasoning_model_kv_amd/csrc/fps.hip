@@ -88,28 +88,33 @@ __device__ __forceinline__ int half_argmin(float v, int i) {
 // Buffers of up to 32 rows: one wavefront per query head.
 //  * Lane pair (2r, 2r+1) loads row r (half of its d fp32 values each) into
 //    registers, where the rows stay until the kept ones are written back.
-//  * The unit-normalised rows go to LDS transposed (dim-major), and the
-//    32 x 32 cosine matrix C = Qn Qn^T is formed with d/2 fp32 MFMAs
-//    (v_mfma_f32_32x32x2_f32; lane l supplies row l % 32, dim 2t + l / 32).
+//  * The unit-normalised rows go to LDS transposed (dim-major), one half of
+//    the dims at a time, and the 32 x 32 cosine matrix C = Qn Qn^T is formed
+//    with d/2 fp32 MFMAs (v_mfma_f32_32x32x2_f32; lane l supplies row
+//    l % 32, dim 2t + l / 32 of the half in LDS).
 //  * Lane l then stands for row l % 32.  The average cosine of row j is the
 //    sum of column j of C (C is symmetric) over N; the seed is its argmin.
 //    Each further pick p adds column p of C (one LDS read per lane) to the
 //    running max S, and the next pick is the argmin of S over the rows not
 //    yet picked.
+//  * The kept rows leave through LDS, eight at a time, as contiguous stores.
+//  LDS stays at about 8 KB (d = 128), so some 18 wavefronts share a CU.
 template <int D>
-__global__ __launch_bounds__(64) void fps_wave_kernel(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(5))) void fps_wave_kernel(
     float* __restrict__ buf, int32_t* __restrict__ count,
     const float* __restrict__ new_q, int n_new, int cap, int trigger, int m,
     int32_t* __restrict__ sel_order, int32_t* __restrict__ n_overflow) {
     constexpr int HD = D / 2;   // dims held by one lane of a pair
     constexpr int TS = 33;      // LDS stride (floats) of the transposed rows and of C
-    constexpr int RS = D + 4;   // LDS stride (floats) of the raw rows
+    constexpr int RS = D + 4;   // LDS stride (floats) of a staged output row
     constexpr int C4 = D / 4;   // 16-byte chunks per row
-    constexpr int LDSF = D * TS > 32 * RS ? D * TS : 32 * RS;
-    // In turn: the raw rows (qt[row * RS + dim]), Qn^T (qt[dim * TS + row]),
-    // C (qt[i * TS + j]), and the raw rows again for the write-back.
+    constexpr int SR = 8;       // output rows staged per write-back round
+    constexpr int LDSF = HD * TS;
+    static_assert(LDSF >= 32 * TS && LDSF >= SR * RS, "LDS reuse");
+    // In turn: Qn^T of one half of the dims (qt[dim * TS + row]), C
+    // (qt[i * TS + j]), and output rows (qt[r * RS + dim]) for the write-back.
+    // Half the transposed rows at a time keeps the footprint at 8 KB (d = 128).
     __shared__ __attribute__((aligned(16))) float qt[LDSF];
-    __shared__ int keep[32];  // slots of the kept rows, ascending
 
     const int lane = threadIdx.x;
     const int64_t head = blockIdx.x;
@@ -158,19 +163,26 @@ __global__ __launch_bounds__(64) void fps_wave_kernel(
     nn += dpp_f<0xB1>(nn);  // the lane pair's other half (quad_perm [1,0,3,2])
     const float inv = 1.0f / fmaxf(sqrtf(nn), kNormFloor);
 
-    // Qn^T into LDS (padding rows are zero rows).
-#pragma unroll
-    for (int k = 0; k < HD; ++k) qt[(half * HD + k) * TS + row] = x[k] * inv;
-    wave_sync_lds();
-
-    // C = Qn Qn^T: lane l holds C[i][l % 32] for i = 8 (v / 4) + 4 (l / 32) + v % 4.
+    // C = Qn Qn^T over two rounds, one per half of the dims: the lanes holding
+    // that half store it transposed to LDS (padding rows are zero rows), then
+    // d/4 MFMAs add it.  Lane l ends with C[i][l % 32] for
+    // i = 8 (v / 4) + 4 (l / 32) + v % 4.
     const int r32 = lane & 31;
     const int kk = lane >> 5;
     f32x16 acc = f32x16{};
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+        if (hf) wave_sync_lds();  // the first round's operand reads are done
+        if (half == hf) {
+#pragma unroll
+            for (int k = 0; k < HD; ++k) qt[k * TS + row] = x[k] * inv;
+        }
+        wave_sync_lds();
 #pragma unroll 8
-    for (int t = 0; t < HD; ++t) {
-        const float a = qt[(2 * t + kk) * TS + r32];
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, a, acc, 0, 0, 0);
+        for (int t = 0; t < HD / 2; ++t) {
+            const float a = qt[(2 * t + kk) * TS + r32];
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, a, acc, 0, 0, 0);
+        }
     }
     float colsum = 0.f;
 #pragma unroll
@@ -196,19 +208,25 @@ __global__ __launch_bounds__(64) void fps_wave_kernel(
         S = fmaxf(S, qt[pick * TS + r32]);
     }
 
-    // Keep the picked rows in ascending slot order: raw rows back to LDS
-    // (every read of C is done), then contiguous 16-byte stores.
-    wave_sync_lds();
+    // Keep the picked rows in ascending slot order: SR output rows at a time
+    // go from registers to LDS (in C's place), then out with contiguous
+    // 16-byte stores.  Every row was loaded before any store.
+    const int dst = ((sel >> row) & 1u) ? __popc(sel & ((1u << row) - 1u)) : -1;
+    for (int r0 = 0; r0 < m; r0 += SR) {
+        wave_sync_lds();  // C's last reads, or the previous round's stores
+        if (dst >= r0 && dst < r0 + SR) {
 #pragma unroll
-    for (int k = 0; k < HD; k += 4)
-        *reinterpret_cast<float4*>(qt + row * RS + half * HD + k) =
-            make_float4(x[k], x[k + 1], x[k + 2], x[k + 3]);
-    if (lane < 32 && ((sel >> lane) & 1u)) keep[__popc(sel & ((1u << lane) - 1u))] = lane;
-    wave_sync_lds();
-    for (int id = lane; id < m * C4; id += 64) {
-        const int r = id / C4, c4 = id % C4;
-        *reinterpret_cast<float4*>(hb + (int64_t)r * D + 4 * c4) =
-            *reinterpret_cast<const float4*>(qt + keep[r] * RS + 4 * c4);
+            for (int k = 0; k < HD; k += 4)
+                *reinterpret_cast<float4*>(qt + (dst - r0) * RS + half * HD + k) =
+                    make_float4(x[k], x[k + 1], x[k + 2], x[k + 3]);
+        }
+        wave_sync_lds();
+        const int nrow = m - r0 < SR ? m - r0 : SR;
+        for (int id = lane; id < nrow * C4; id += 64) {
+            const int r = id / C4, c4 = id % C4;
+            *reinterpret_cast<float4*>(hb + (int64_t)(r0 + r) * D + 4 * c4) =
+                *reinterpret_cast<const float4*>(qt + r * RS + 4 * c4);
+        }
     }
     if (sel_order && lane < m) sel_order[head * m + lane] = my_pick;
     if (lane == 0) count[head] = m;

@@ -1,4 +1,8 @@
-"""Selection and compaction kernels against the oracle (bit-exact)."""
+"""Selection and compaction kernels against the oracle (bit-exact).
+
+Selection runs on one wavefront per unit up to L = 8192 and on a workgroup
+per unit beyond; both are covered.
+"""
 import numpy as np
 import pytest
 import torch
@@ -19,6 +23,9 @@ DEV = "cuda"
     (777, 300, 33, 16, "ties"),     # many equal scores around the cut
     (4224, 4096, 512, 16, "ties"),
     (300, 150, 0, 0, "zeros"),      # all-equal scores, no forced slots
+    (8192, 8000, 8, 16, "cont"),    # largest unit of the one-wavefront kernel
+    (8193, 7000, 8, 16, "ties"),    # beyond it: the workgroup kernel
+    (9001, 5000, 8, 16, "cont"),
 ])
 def test_select_bit_exact(L, b_kv, P, R, kind):
     U = 37

@@ -105,6 +105,8 @@ def _all_unit_properties(w, kept):
 
 @pytest.mark.parametrize("name,samples", [
     ("qwen3_4b_full_b2048", [0, 1, 777, 2303, 4095, 4607]),
+    ("qwen3_4b_full_b128", [0, 2304, 4607]),    # L = 256: a unit of four key tiles
+    ("qwen3_4b_full_b4096", [0, 3001, 4607]),   # L = 4224
     ("r1_qwen_7b", [0, 1791, 3583]),
 ])
 def test_evict_full_size_sampled(name, samples):

@@ -74,6 +74,8 @@ struct ScoreArgs {
     const double* table;
     float* score;
     uint16_t* qobs;
+    int64_t n_units;
+    int split;  // 1: each unit's heads are scored by two workgroups (scores pre-zeroed, max-combined)
 };
 
 __device__ __forceinline__ int acc_row(int v, int lane) {
@@ -115,6 +117,13 @@ __global__ __launch_bounds__(256) void rope_align_kernel(ScoreArgs a, int g, int
     const int k = lane % HALF, sub = lane / HALF;
     const int64_t u = qh / g;
     const int h = (int)(qh % g);
+    if (a.split) {
+        // The two workgroups of a split unit combine their scores with an
+        // atomic maximum: clear the unit's score slots first (the g waves of
+        // the unit take interleaved runs of 64).
+        float* su = a.score + u * a.l_cap;
+        for (int64_t j = (int64_t)h * 64 + lane; j < a.L; j += (int64_t)g * 64) su[j] = 0.f;
+    }
     const double2* tab = reinterpret_cast<const double2*>(a.table);
     uint16_t* out = a.qobs + (u * g + h) * 32 * (int64_t)D;
     // Positions of the 16 recent rows: lane r (mod 16) holds row r's.
@@ -292,11 +301,17 @@ __device__ __forceinline__ void tile_logits(const uint16_t* lds_tile, const Tile
     }
 }
 
-// One workgroup per unit (one wavefront per query head); with about 140
-// VGPRs, 3 workgroups share a CU.
-template <int D, int NL>
+// One workgroup per unit, one wavefront per query head; with 162 VGPRs, 12
+// wavefronts share a CU.  For g > 4 (a.split) a unit's heads are shared by
+// two workgroups of hs wavefronts each (the second may have an idle
+// wavefront, which loads and keeps the barriers but computes nothing), so
+// that more than one group fits on a CU; the pair runs on one XCD
+// (blocks b and b + 8), where the second read of each key tile is likely to
+// hit L2, and combines its column maxima with an atomic maximum on the
+// score bits (non-negative floats order like their bit patterns).
+template <int D, int NL, bool SPLIT>
 __global__ __launch_bounds__(512)
-void score_kernel(ScoreArgs a, int g) {
+void score_kernel(ScoreArgs a, int g, int hs) {
     // Three separately declared tiles (not one array) so that the compiler
     // can tell the tiles being loaded by the direct-to-LDS loads from the tile
     // being read, and does not wait for the former before reading the latter.
@@ -310,7 +325,16 @@ void score_kernel(ScoreArgs a, int g) {
     const int h = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int lane = tid & 63;
     const bool loader = h < NL;
-    const int64_t u = blockIdx.x;
+    int64_t u = blockIdx.x;
+    int hg = h;  // query head of the group this wavefront scores
+    if (SPLIT) {
+        const int64_t b = blockIdx.x;
+        u = (b / 16) * 8 + (b % 8);
+        hg = (int)((b / 8) & 1) * hs + h;
+        if (u >= a.n_units) return;  // whole workgroup, before any barrier
+    }
+    const bool active = !SPLIT || hg < g;
+    const int nw = (int)(blockDim.x / 64);
     const int64_t L = a.L;
     const uint16_t* Ku = a.K + u * a.l_cap * D;
     const int ntiles = (int)((L + KT - 1) / KT);
@@ -318,7 +342,7 @@ void score_kernel(ScoreArgs a, int g) {
     const float c2 = a.c2;
 
     bf16x8 frag[D / 16];
-    load_frag<D>(a.qobs, u, g, h, lane, frag);
+    if (active) load_frag<D>(a.qobs, u, g, hg, lane, frag);
     const TileLoad<D, NL> ld(h, lane);
     const TileRead<D> rd(lane);
 
@@ -337,7 +361,8 @@ void score_kernel(ScoreArgs a, int g) {
         if (loader && (it) + 2 < ntiles)                                           \
             ld.issue(Ku, L, (int64_t)((it) + 2) * KT, NXT2, h);                    \
         f32x16 acc0, acc1;                                                         \
-        tile_logits<D>(CUR, rd, frag, acc0, acc1);                                 \
+        if (SPLIT && !active) { acc0 = f32x16{}; acc1 = f32x16{}; }                \
+        else tile_logits<D>(CUR, rd, frag, acc0, acc1);                            \
         const int64_t base = (int64_t)(it) * KT;                                   \
         __VA_ARGS__;                                                               \
     } while (0)
@@ -370,6 +395,7 @@ void score_kernel(ScoreArgs a, int g) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) { mc[v] = kNegBig; l[v] = 0.f; }
 #define BKV_PASS1                                                                  \
+    if (active) {                                                                  \
     if (base + KT > mask_from) {                                                   \
         const int ln = lane;                                                       \
         const int d0 = (int)(base - mask_from) + (ln & 31), d1 = d0 + 32;          \
@@ -380,7 +406,8 @@ void score_kernel(ScoreArgs a, int g) {
         }                                                                          \
     }                                                                              \
     BKV_PASS1_HALF(0);                                                             \
-    BKV_PASS1_HALF(8);
+    BKV_PASS1_HALF(8);                                                             \
+    }
 // Rows v0..v0+7 of one tile: sum against the stale maxima if every term
 // stays below kRescaleBig, else rescale those rows.
 #define BKV_PASS1_HALF(v0)                                                         \
@@ -447,21 +474,42 @@ void score_kernel(ScoreArgs a, int g) {
     c0 = vmax(c0, __shfl_xor(c0, 32));                                             \
     c1 = vmax(c1, __shfl_xor(c1, 32));                                             \
     if (lane < 32) {                                                               \
-        red[h][lane] = c0;                                                         \
-        red[h][32 + lane] = c1;                                                    \
+        red[h][lane] = active ? c0 : -__builtin_inff();                            \
+        red[h][32 + lane] = active ? c1 : -__builtin_inff();                       \
     }                                                                              \
     __syncthreads();                                                               \
     if (tid < KT) {                                                                \
         float best = red[0][tid];                                                  \
-        for (int w = 1; w < g; ++w) best = vmax(best, red[w][tid]);                \
+        for (int w = 1; w < nw; ++w) best = vmax(best, red[w][tid]);               \
         const int64_t key = base + tid;                                            \
-        if (key < L) score_u[key] = exp2f(best);                                   \
+        if (key < L) {                                                             \
+            if (SPLIT)                                                             \
+                atomicMax(reinterpret_cast<unsigned int*>(score_u + key),          \
+                          __float_as_uint(exp2f(best)));                           \
+            else                                                                   \
+                score_u[key] = exp2f(best);                                        \
+        }                                                                          \
     }
     BKV_TILE_LOOP(1, BKV_PASS2);
 #undef BKV_PASS2
 #undef BKV_TILE_LOOP
 #undef BKV_TILE_ITER
 }
+
+// Every variant is instantiated explicitly, so each gets its host launch stub
+// even though it is launched from one branch of a conditional.
+template __global__ void score_kernel<128, 4, false>(ScoreArgs, int, int);
+template __global__ void score_kernel<128, 2, false>(ScoreArgs, int, int);
+template __global__ void score_kernel<128, 1, false>(ScoreArgs, int, int);
+template __global__ void score_kernel<64, 4, false>(ScoreArgs, int, int);
+template __global__ void score_kernel<64, 2, false>(ScoreArgs, int, int);
+template __global__ void score_kernel<64, 1, false>(ScoreArgs, int, int);
+template __global__ void score_kernel<128, 4, true>(ScoreArgs, int, int);
+template __global__ void score_kernel<128, 2, true>(ScoreArgs, int, int);
+template __global__ void score_kernel<128, 1, true>(ScoreArgs, int, int);
+template __global__ void score_kernel<64, 4, true>(ScoreArgs, int, int);
+template __global__ void score_kernel<64, 2, true>(ScoreArgs, int, int);
+template __global__ void score_kernel<64, 1, true>(ScoreArgs, int, int);
 
 }  // namespace
 
@@ -495,6 +543,10 @@ hipError_t launch_score(const uint16_t* K, const int32_t* kpos, int64_t n_units,
     a.table = table;
     a.score = score;
     a.qobs = qobs_out ? qobs_out : qobs_ws;
+    a.n_units = n_units;
+    // Groups of more than 4 heads: two workgroups per unit (see score_kernel).
+    a.split = g > 4 ? 1 : 0;
+    const int hs = a.split ? (g + 1) / 2 : g;
     const int64_t n_heads = n_units * g;
     const unsigned rblocks = (unsigned)((n_heads + 3) / 4);
     if (d == 128)
@@ -503,19 +555,25 @@ hipError_t launch_score(const uint16_t* K, const int32_t* kpos, int64_t n_units,
         rope_align_kernel<64><<<rblocks, 256, 0, s>>>(a, g, n_heads);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const dim3 grid((unsigned)n_units);
-    const dim3 block(64 * g);
-    // Loader wavefronts: the largest power of two <= g, at most 4.
-    const int nl = g >= 4 ? 4 : (g >= 2 ? 2 : 1);
+    const dim3 grid(a.split ? (unsigned)((n_units + 7) / 8 * 16) : (unsigned)n_units);
+    const dim3 block(64 * hs);
+    // Loader wavefronts: the largest power of two <= hs, at most 4.
+    const int nl = hs >= 4 ? 4 : (hs >= 2 ? 2 : 1);
+#define BKV_LAUNCH(DD, NN)                                                        \
+    do {                                                                          \
+        if (a.split) score_kernel<DD, NN, true><<<grid, block, 0, s>>>(a, g, hs);  \
+        else score_kernel<DD, NN, false><<<grid, block, 0, s>>>(a, g, hs);         \
+    } while (0)
     if (d == 128) {
-        if (nl == 4) score_kernel<128, 4><<<grid, block, 0, s>>>(a, g);
-        else if (nl == 2) score_kernel<128, 2><<<grid, block, 0, s>>>(a, g);
-        else score_kernel<128, 1><<<grid, block, 0, s>>>(a, g);
+        if (nl == 4) BKV_LAUNCH(128, 4);
+        else if (nl == 2) BKV_LAUNCH(128, 2);
+        else BKV_LAUNCH(128, 1);
     } else {
-        if (nl == 4) score_kernel<64, 4><<<grid, block, 0, s>>>(a, g);
-        else if (nl == 2) score_kernel<64, 2><<<grid, block, 0, s>>>(a, g);
-        else score_kernel<64, 1><<<grid, block, 0, s>>>(a, g);
+        if (nl == 4) BKV_LAUNCH(64, 4);
+        else if (nl == 2) BKV_LAUNCH(64, 2);
+        else BKV_LAUNCH(64, 1);
     }
+#undef BKV_LAUNCH
     return hipGetLastError();
 }
 

@@ -365,6 +365,32 @@ __global__ __launch_bounds__(256) void fps_block_kernel(
     if (tid == 0) count[head] = m;
 }
 
+// Append only (trigger > buf_cap, so no head can compress), when one head's
+// new rows are at most 64 16-byte chunks: CPH lanes (a power of two) per
+// head, 256 / CPH heads per workgroup.  All lanes of a head are in one
+// wavefront and read count before its chunk-0 lane writes the new count.
+template <int CPH>
+__global__ __launch_bounds__(256) void fps_append_kernel(
+    float* __restrict__ buf, int32_t* __restrict__ count, const float* __restrict__ new_q,
+    int n_new, int d, int cap, int m, int32_t* __restrict__ sel_order,
+    int32_t* __restrict__ n_overflow, int64_t n_heads) {
+    const int64_t head = ((int64_t)blockIdx.x * 256 + threadIdx.x) / CPH;
+    const int c = threadIdx.x % CPH;
+    if (head >= n_heads) return;
+    const int nch = n_new * d / 4;  // 16-byte chunks to append
+    const int cnt = count[head];
+    if (sel_order)
+        for (int i = c; i < m; i += CPH) sel_order[head * m + i] = -1;
+    if (cnt < 0 || cnt + n_new > cap) {
+        if (c == 0 && n_overflow) atomicAdd(n_overflow, 1);
+        return;
+    }
+    if (c < nch)
+        reinterpret_cast<float4*>(buf + (head * cap + cnt) * (int64_t)d)[c] =
+            reinterpret_cast<const float4*>(new_q + head * (int64_t)n_new * d)[c];
+    if (c == 0) count[head] = cnt + n_new;
+}
+
 }  // namespace
 
 hipError_t launch_fps(float* buf, int32_t* count, const float* new_q,
@@ -372,6 +398,19 @@ hipError_t launch_fps(float* buf, int32_t* count, const float* new_q,
                       int trigger, int m, int32_t* sel_order,
                       int32_t* n_overflow, hipStream_t s) {
     if (n_heads <= 0) return hipSuccess;
+    const int nch = n_new * d / 4;
+    if (trigger > buf_cap && n_new > 0 && nch <= 64) {
+        // Append only: many heads per workgroup.
+        const unsigned blocks32 = (unsigned)((n_heads * 32 + 255) / 256);
+        const unsigned blocks64 = (unsigned)((n_heads * 64 + 255) / 256);
+        if (nch <= 32)
+            fps_append_kernel<32><<<blocks32, 256, 0, s>>>(buf, count, new_q, n_new, d, buf_cap,
+                                                           m, sel_order, n_overflow, n_heads);
+        else
+            fps_append_kernel<64><<<blocks64, 256, 0, s>>>(buf, count, new_q, n_new, d, buf_cap,
+                                                           m, sel_order, n_overflow, n_heads);
+        return hipGetLastError();
+    }
     const dim3 grid((unsigned)n_heads);
     if (buf_cap <= 32) {
         if (d == 128)

@@ -95,7 +95,10 @@ class Stream:
             compress = self.rows + 1 >= 32
             if compress:
                 self._note("collect_fps", "pre")
-            bkv.fps_update(self.shape, self.buf, self.count, q[:, None], trigger=32, m=16,
+            # Every head holds the same number of rows, so the host knows when the
+            # buffer fills: other steps append only (trigger past the capacity).
+            bkv.fps_update(self.shape, self.buf, self.count, q[:, None],
+                           trigger=32 if compress else self.shape.buf_cap + 1, m=16,
                            sel_order=self.sel if compress else None)
             self.rows = 16 if compress else self.rows + 1
             if compress:

@@ -90,6 +90,43 @@ def test_append_only_and_triggers():
         assert np.array_equal(out[q, :16], merged[q][np.sort(sel[q])])
 
 
+@pytest.mark.parametrize("name,n_new", [("tiny", 1), ("tiny", 3), ("qwen3_4b_layer", 1),
+                                         ("qwen3_4b_layer", 2), ("qwen3_4b_layer", 3)])
+def test_append_only_many_heads_per_workgroup(name, n_new):
+    """trigger = buf_cap + 1 (append only): rows land at each head's count,
+    counts advance, heads without room are left unchanged and counted as
+    overflow, sel_order reads -1.  New rows of up to 64 16-byte chunks per
+    head take the batched append kernel (tiny: 1 and 3 rows; d = 128: 1 and 2
+    rows); 3 rows at d = 128 take the per-head kernel."""
+    w = synth.WORKLOADS[name]
+    nq, d = w.n_qheads, w.d_head
+    r = np.random.default_rng(11 + n_new)
+    host = r.standard_normal((nq, 32, d)).astype(np.float32)
+    shape = _shape(w)
+    cnt = np.array([(7 * q) % 33 for q in range(nq)], dtype=np.int32)  # some heads are full
+    buf = torch.from_numpy(host.copy()).to(DEV)
+    count = torch.from_numpy(cnt.copy()).to(DEV)
+    newq = r.standard_normal((nq, n_new, d)).astype(np.float32)
+    sel = torch.zeros((nq, 16), dtype=torch.int32, device=DEV)
+    ovf = torch.zeros((1,), dtype=torch.int32, device=DEV)
+    bkv.fps_update(shape, buf, count, torch.from_numpy(newq).to(DEV), trigger=33, m=16,
+                   sel_order=sel, n_overflow=ovf)
+    torch.cuda.synchronize()
+    out, cnt2 = buf.cpu().numpy(), count.cpu().numpy()
+    fits = cnt + n_new <= 32
+    assert int(ovf.item()) == int((~fits).sum())
+    assert torch.all(sel == -1)
+    for q in range(nq):
+        if fits[q]:
+            assert cnt2[q] == cnt[q] + n_new
+            assert np.array_equal(out[q, cnt[q]:cnt[q] + n_new], newq[q])
+            rest = np.delete(out[q], np.arange(cnt[q], cnt[q] + n_new), axis=0)
+            assert np.array_equal(rest, np.delete(host[q], np.arange(cnt[q], cnt[q] + n_new),
+                                                  axis=0))
+        else:
+            assert cnt2[q] == cnt[q] and np.array_equal(out[q], host[q])
+
+
 def test_overflow_leaves_heads_unchanged():
     w = synth.WORKLOADS["tiny"]
     nq, d = w.n_qheads, w.d_head

@@ -43,26 +43,6 @@ __device__ __forceinline__ float swap16_f(float x) {
     return __builtin_bit_cast(float, swap16_i(__builtin_bit_cast(int, x)));
 }
 
-// Wavefront argmin over (value, index), returned wave-uniform.  Lanes 2r
-// and 2r+1 carry the same candidate, so lane ^ 1 is skipped: lane ^ 2
-// (quad_perm [2,3,0,1]), then the other quad of 8 (row_half_mirror), the
-// other 8 of 16 (row_mirror), lane ^ 16 (swizzle), and the two halves
-// (lanes 0 and 32).  (value, index) pairs compare lexicographically, so
-// the order of the steps does not change the result.
-__device__ __forceinline__ int wave_argmin_rows(float v, int i) {
-    argmin_pair(v, i, dpp_f<0x4E>(v), dpp_i<0x4E>(i));
-    argmin_pair(v, i, dpp_f<0x141>(v), dpp_i<0x141>(i));
-    argmin_pair(v, i, dpp_f<0x140>(v), dpp_i<0x140>(i));
-    argmin_pair(v, i, swap16_f(v), swap16_i(i));
-    float v0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
-    int i0 = __builtin_amdgcn_readlane(i, 0);
-    const float v1 =
-        __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
-    const int i1 = __builtin_amdgcn_readlane(i, 32);
-    argmin_pair(v0, i0, v1, i1);
-    return i0;
-}
-
 __device__ __forceinline__ void wave_sync_lds() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();

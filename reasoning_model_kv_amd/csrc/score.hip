@@ -450,7 +450,7 @@ void score_kernel(ScoreArgs a, int g, int hs) {
     for (int v = 0; v < 16; ++v) lse[v] = mc[v] + log2f(l[v]);
 
     // ---------------- pass 2: max over rows of (s - LSE) -------------------
-    __syncthreads();  // everyone is done with the tiles
+    __syncthreads();
     float* score_u = a.score + u * a.l_cap;
 #define BKV_PASS2                                                                  \
     float c0 = -__builtin_inff(), c1 = -__builtin_inff();                          \
@@ -490,7 +490,42 @@ void score_kernel(ScoreArgs a, int g, int hs) {
                 score_u[key] = exp2f(best);                                        \
         }                                                                          \
     }
-    BKV_TILE_LOOP(1, BKV_PASS2);
+// Pass 2 walks the tiles backwards: at the end of pass 1 the last three
+// tiles are still in LDS (tile T in buffer T % 3), so they are scored
+// without being read again, and the rest stream in from the end with the
+// same ring, two tiles ahead.  Iteration j scores tile T = ntiles - 1 - j
+// from CUR and loads tile T - 2 into NXT (the buffer tile T + 1 used).
+#define BKV_REV_ITER(j, CUR, NXT, ...)                                             \
+    do {                                                                           \
+        const int T = ntiles - 1 - (j);                                            \
+        if (loader && T < ntiles - 3) {                                            \
+            if (T == 0) wait_vm<0>();                                              \
+            else if (h == 0) wait_vm<NPW + 1>();                                   \
+            else wait_vm<NPW>();                                                   \
+        }                                                                          \
+        __syncthreads();                                                           \
+        if (loader && T - 2 >= 0 && T - 2 < ntiles - 3)                            \
+            ld.issue(Ku, L, (int64_t)(T - 2) * KT, NXT, h);                        \
+        f32x16 acc0, acc1;                                                         \
+        if (SPLIT && !active) { acc0 = f32x16{}; acc1 = f32x16{}; }                \
+        else tile_logits<D>(CUR, rd, frag, acc0, acc1);                            \
+        const int64_t base = (int64_t)T * KT;                                      \
+        __VA_ARGS__;                                                               \
+    } while (0)
+#define BKV_REV_LOOP(B0, B1, B2, ...)                                              \
+    for (int j = 0; j < ntiles; j += 3) {                                          \
+        BKV_REV_ITER(j, B0, B1, __VA_ARGS__);                                      \
+        if (j + 1 < ntiles) BKV_REV_ITER(j + 1, B2, B0, __VA_ARGS__);              \
+        if (j + 2 < ntiles) BKV_REV_ITER(j + 2, B1, B2, __VA_ARGS__);              \
+    }
+    // Buffers visited from the last tile down: tile T lives in buffer T % 3.
+    switch ((ntiles - 1) % 3) {
+        case 0: BKV_REV_LOOP(tile0, tile1, tile2, BKV_PASS2); break;
+        case 1: BKV_REV_LOOP(tile1, tile2, tile0, BKV_PASS2); break;
+        default: BKV_REV_LOOP(tile2, tile0, tile1, BKV_PASS2); break;
+    }
+#undef BKV_REV_LOOP
+#undef BKV_REV_ITER
 #undef BKV_PASS2
 #undef BKV_TILE_LOOP
 #undef BKV_TILE_ITER

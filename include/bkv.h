@@ -86,9 +86,8 @@ int bkv_abi_version(void);
 const char* bkv_last_error(void);
 
 /* Workspace bytes.  With b_kv == 0: what bkv_score needs (the RoPE angle
- * table and the bf16 observation rows, U * g * 32 * d * 2 bytes, used when
- * qobs_out is NULL).  With b_kv > 0: what bkv_evict needs for (L, b_kv),
- * which also covers the score and kept arrays when the caller passes none.
+ * table).  With b_kv > 0: what bkv_evict needs for (L, b_kv), which also
+ * covers the score and kept arrays when the caller passes none.
  * Returns 0 on invalid arguments (see bkv_last_error).  The workspace holds
  * nothing between calls; calls that share a workspace must not overlap. */
 size_t bkv_workspace_bytes(const bkv_dims* dims, const bkv_policy* pol,

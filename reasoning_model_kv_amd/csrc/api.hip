@@ -96,17 +96,14 @@ float scale_of(const bkv_dims* d, const bkv_policy* p) {
 }
 
 struct WsLayout {
-    size_t table = 0, qobs = 0, score = 0, kept = 0, total = 0;
+    size_t table = 0, score = 0, kept = 0, total = 0;
 };
 
-// Workspace: RoPE angle table, bf16 observation rows, then (bkv_evict) the
-// score and kept arrays.
+// Workspace: RoPE angle table, then (bkv_evict) the score and kept arrays.
 WsLayout ws_layout(const bkv_dims* d, const bkv_policy* p, int64_t b_kv) {
     WsLayout w;
     w.table = 0;
     size_t off = align_up(bkv::rope_table_bytes(p->n_recent_q, d->d_head));
-    w.qobs = off;
-    off = align_up(off + bkv::qobs_bytes(d->n_units, d->group, d->d_head));
     if (b_kv > 0) {
         w.score = off;
         off = align_up(off + (size_t)d->n_units * (size_t)d->l_cap * sizeof(float));
@@ -218,7 +215,7 @@ int bkv_score(const bkv_dims* dims, const bkv_policy* pol, const uint16_t* K,
         e = bkv::launch_score(K, kpos, dims->n_units, dims->group, dims->d_head, dims->l_cap,
                               L, beacons, pol->buf_cap, recents, pol->n_beacon,
                               pol->n_recent_q, t, pol->rope_theta, scale_of(dims, pol),
-                              table, score, qobs_out, (uint16_t*)((char*)ws + w.qobs), s);
+                              table, score, qobs_out, s);
     return hip_result(e, fn);
 }
 
@@ -296,7 +293,7 @@ int bkv_evict(const bkv_dims* dims, const bkv_policy* pol, uint16_t* K, uint16_t
         e = bkv::launch_score(K, kpos, dims->n_units, dims->group, dims->d_head, dims->l_cap,
                               L, beacons, pol->buf_cap, recents, pol->n_beacon,
                               pol->n_recent_q, t, pol->rope_theta, scale_of(dims, pol),
-                              table, score, nullptr, (uint16_t*)((char*)ws + w.qobs), s);
+                              table, score, nullptr, s);
     if (e == hipSuccess)
         e = bkv::launch_select(score, dims->n_units, dims->l_cap, L, b_kv, pol->prefix,
                                pol->recent_tok, kept, s);

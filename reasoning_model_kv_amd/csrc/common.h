@@ -22,12 +22,7 @@ hipError_t launch_score(const uint16_t* K, const int32_t* kpos, int64_t n_units,
                         const float* beacons, int buf_cap, const float* recents,
                         int n_beacon, int n_recent_q, int64_t t, double theta,
                         float sm_scale, const double* table, float* score,
-                        uint16_t* qobs_out, uint16_t* qobs_ws, hipStream_t s);
-
-// Bytes of the bf16 observation rows, [U, g*32, d].
-inline size_t qobs_bytes(int64_t n_units, int g, int d) {
-    return (size_t)n_units * (size_t)g * 32 * (size_t)d * 2;
-}
+                        uint16_t* qobs_out, hipStream_t s);
 
 hipError_t launch_select(const float* score, int64_t n_units, int64_t l_cap,
                          int64_t L, int64_t b_kv, int prefix, int recent_tok,

@@ -6,23 +6,26 @@
 // current cache, max-pooled over all queries and heads of the KV group
 // (summary step (4); review §4.3: Score[j] = max_{h in g} max_q W[h,q,j]).
 //
-// Two kernels:
-//  * rope_align_kernel (one wavefront per query head) rotates the head's 32
-//    observation rows (16 beacons, 16 recents) once in fp64 and writes them
-//    as bf16 rows, the A operands of v_mfma_f32_32x32x16_bf16.
-//  * score_kernel (one workgroup per KV group, one wavefront per query
-//    head) holds its head's rows in registers as A fragments (lane: row
-//    lane % 32, dims 16 s + 8 (lane / 32) .. + 8 for MFMA step s).  Keys
-//    stream through a ring of three LDS tiles of 64 keys, loaded two tiles
-//    ahead by buffer_load ... lds (16-byte chunks XOR-swizzled by row so the
-//    32 lanes that read one chunk column hit distinct banks); all g
+// Mapping: one workgroup per KV group, one wavefront per query head.
+//  * Prologue: the cos/sin table rows go to LDS and each wavefront loads its
+//    head's 32 observation rows (16 beacons, 16 recents) ahead of the first
+//    two key tiles; while those are in flight it rotates the rows in fp64
+//    (lane = 4 RoPE pairs of a row), stages them as bf16 in LDS and reads
+//    them back as the A operands of v_mfma_f32_32x32x16_bf16 (lane: row
+//    lane % 32, dims 16 s + 8 (lane / 32) .. + 8 for MFMA step s).
+//  * Keys stream through a ring of three LDS tiles of 64 keys, loaded two
+//    tiles ahead by buffer_load ... lds (16-byte chunks XOR-swizzled by row
+//    so the 32 lanes that read one chunk column hit distinct banks); all
 //    wavefronts of the group read the same tile.
 //  * Pass 1: per tile each wavefront forms a 32 x 64 logit block and keeps a
 //    per-lane running (max, sum of exp2) for its 16 rows; the 32 lanes of a
 //    half are merged once at the end into each row's LSE.
-//  * Pass 2: the logits are formed again, shifted by the row LSE, reduced
-//    over the lane's 16 rows, the other half (lane ^ 32) and the g
-//    wavefronts (LDS), and written as score = exp2(max).
+//  * Pass 2 walks the tiles backwards (the last three are still in LDS): the
+//    logits are formed again, shifted by the row LSE, reduced over the
+//    lane's 16 rows, the other half (lane ^ 32) and the wavefronts (LDS),
+//    and written as score = exp2(max).
+//  * Groups of more than four heads are shared by two workgroups on one XCD
+//    that combine their maxima with an atomic maximum.
 //  Output layout of the 32x32 MFMA: lane l, accumulator v holds
 //  row 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32.
 
@@ -32,6 +35,8 @@ namespace bkv {
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 constexpr int KT = 64;               // keys per tile
@@ -82,106 +87,142 @@ __device__ __forceinline__ int acc_row(int v, int lane) {
     return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
 }
 
-// RoPE alignment (paper text §4.3) as its own step, one wavefront per query
-// head: lane k owns the RoPE pair (k, k + D/2) (for D = 64 the two halves of
-// the wavefront take two rows at a time), walks the head's 32 observation
-// rows (16 beacons at position t, 16 recents at their own positions) and
-// writes them as bf16 rows to a.qobs ([U, g*32, D]), the MFMA A operands of
-// the scoring kernel.  Rotation in fp64 (products rounded separately, as
-// the plain definition computes them), then fp64 -> fp32 -> bf16, both
-// round-to-nearest-even.  The cos/sin pairs come from the table for t and
-// t-16..t-1; a recent row at any other position computes its own.
-template <int D>
-__device__ __forceinline__ void rotate_store(uint16_t* row, int k, float x1f, float x2f,
-                                             double c, double sn) {
+// RoPE alignment (paper text §4.3) of one query head's 32 observation rows
+// (16 beacons at position t, 16 recents at their own positions), done by
+// the head's wavefront in the scoring kernel's prologue.
+//
+// rotate4: rotation of four RoPE pairs (x1[p], x2[p]) by (cs[p].x, cs[p].y)
+// in fp64, each product rounded separately as the plain definition computes
+// them, then fp64 -> fp32 -> bf16, both round-to-nearest-even (the hardware
+// conversions in the default rounding mode).  Returns the four rotated
+// first halves (two packed words, lower pair index in the low half) then
+// the four second halves.
+__device__ __forceinline__ uint4 rotate4(float4 x1, float4 x2, const double2 (&cs)[4]) {
 #pragma clang fp contract(off)
-    const double x1 = (double)x1f, x2 = (double)x2f;
-    const double p = x1 * c;
-    const double q = x2 * sn;
-    const double y1 = p - q;
-    const double r1 = x2 * c;
-    const double r2 = x1 * sn;
-    const double y2 = r1 + r2;
-    row[k] = f32_to_bf16_rne((float)y1);
-    row[k + D / 2] = f32_to_bf16_rne((float)y2);
+    const float a1[4] = {x1.x, x1.y, x1.z, x1.w}, a2[4] = {x2.x, x2.y, x2.z, x2.w};
+    float y1[4], y2[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const double u1 = (double)a1[p], u2 = (double)a2[p];
+        const double m1 = u1 * cs[p].x;
+        const double m2 = u2 * cs[p].y;
+        const double m3 = u2 * cs[p].x;
+        const double m4 = u1 * cs[p].y;
+        y1[p] = (float)(m1 - m2);
+        y2[p] = (float)(m3 + m4);
+    }
+    const auto pk = [](float lo, float hi) {
+        const f32x2 v = {lo, hi};
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+    };
+    return uint4{pk(y1[0], y1[1]), pk(y1[2], y1[3]), pk(y2[0], y2[1]), pk(y2[2], y2[3])};
 }
 
+// The rows as loaded: lane = (row sub of each step, pairs 4q .. 4q+3 of
+// the D/2 RoPE pairs (k, k + D/2)).  Loading and rotating are separate
+// steps so that the loads can be in flight together with the first key
+// tiles.
 template <int D>
-__global__ __launch_bounds__(256) void rope_align_kernel(ScoreArgs a, int g, int64_t n_heads) {
-    constexpr int HALF = D / 2;
-    constexpr int RPS = 64 / HALF;  // rows per step
-    constexpr int NB = 16 / RPS;    // steps per 16 rows
-    const int64_t qh = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
-    if (qh >= n_heads) return;
-    const int lane = threadIdx.x & 63;
-    const int k = lane % HALF, sub = lane / HALF;
-    const int64_t u = qh / g;
-    const int h = (int)(qh % g);
-    if (a.split) {
-        // The two workgroups of a split unit combine their scores with an
-        // atomic maximum: clear the unit's score slots first (the g waves of
-        // the unit take interleaved runs of 64).
-        float* su = a.score + u * a.l_cap;
-        for (int64_t j = (int64_t)h * 64 + lane; j < a.L; j += (int64_t)g * 64) su[j] = 0.f;
-    }
-    const double2* tab = reinterpret_cast<const double2*>(a.table);
-    uint16_t* out = a.qobs + (u * g + h) * 32 * (int64_t)D;
-    // Positions of the 16 recent rows: lane r (mod 16) holds row r's.
-    const int64_t rpos = a.kpos[u * a.l_cap + a.L - a.n_recent_q + (lane & 15)];
+struct ObsRows {
+    static constexpr int HALF = D / 2;
+    static constexpr int QPR = HALF / 4;  // lanes per row
+    static constexpr int RPS = 64 / QPR;  // rows per step
+    static constexpr int NB = 16 / RPS;   // steps per 16 rows
+    float4 bx1[NB], bx2[NB], rx1[NB], rx2[NB];
 
-    // Beacons (rows 0..15) at position t.  All loads are issued before any
-    // arithmetic so that they overlap.
-    {
-        float x1[NB], x2[NB];
+    __device__ __forceinline__ void load(const ScoreArgs& a, int64_t qh, int lane) {
+        const int q = lane % QPR, sub = lane / QPR;
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
-            const float* src = a.beacons + (qh * a.buf_cap + j * RPS + sub) * (int64_t)D;
-            x1[j] = src[k];
-            x2[j] = src[k + HALF];
+            const float* src = a.beacons + (qh * a.buf_cap + j * RPS + sub) * (int64_t)D + 4 * q;
+            bx1[j] = *reinterpret_cast<const float4*>(src);
+            bx2[j] = *reinterpret_cast<const float4*>(src + HALF);
         }
-        const double2 cs = tab[k];
 #pragma unroll
-        for (int j = 0; j < NB; ++j)
-            rotate_store<D>(out + (j * RPS + sub) * D, k, x1[j], x2[j], cs.x, cs.y);
+        for (int j = 0; j < NB; ++j) {
+            const float* src =
+                a.recents + (qh * a.n_recent_q + j * RPS + sub) * (int64_t)D + 4 * q;
+            rx1[j] = *reinterpret_cast<const float4*>(src);
+            rx2[j] = *reinterpret_cast<const float4*>(src + HALF);
+        }
     }
-    // Recents (rows 16..31): recent r at its own position, tabulated when it
-    // is t - 16 + r, else computed here.
-    {
-        float x1[NB], x2[NB];
-        double2 cs[NB];
+
+    // out[j]: beacon row j * RPS + sub; out[NB + j]: recent row (row 16 +)
+    // j * RPS + sub; each as rotate4 returns it.  tab0 ([D/2] double2) and
+    // rtab ([16][D/2]): the cos/sin pairs for t and for the recent rows'
+    // positions, in LDS.
+    __device__ __forceinline__ void rotate(int lane, const double2* tab0, const double2* rtab,
+                                           uint4 (&out)[2 * NB]) const {
+        const int q = lane % QPR, sub = lane / QPR;
+        double2 cs[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) cs[p] = tab0[4 * q + p];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) out[j] = rotate4(bx1[j], bx2[j], cs);
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
+            // One row's cos/sin pairs at a time (the scheduler would
+            // otherwise read all of them up front, 16 registers a row).
+            __builtin_amdgcn_sched_barrier(0);
             const int r = j * RPS + sub;
-            const float* src = a.recents + (qh * a.n_recent_q + r) * (int64_t)D;
-            x1[j] = src[k];
-            x2[j] = src[k + HALF];
-            cs[j] = tab[(1 + r) * HALF + k];
-        }
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            const int r = j * RPS + sub;
-            const int64_t pos = __shfl(rpos, r);
-            if (pos != a.t - a.n_recent_q + r) {
-                double c, sn;
-                rope_cs((double)pos, k, D, a.theta, &c, &sn);
-                cs[j].x = c;
-                cs[j].y = sn;
-            }
-            rotate_store<D>(out + (16 + r) * D, k, x1[j], x2[j], cs[j].x, cs[j].y);
+            for (int p = 0; p < 4; ++p) cs[p] = rtab[r * HALF + 4 * q + p];
+            out[NB + j] = rotate4(rx1[j], rx2[j], cs);
         }
+    }
+};
+
+// The table holds the cos/sin pairs for positions t-16..t-1; recent rows
+// of the unit at other positions (lane r (mod 16) holds row r's position
+// in rpos) get theirs computed into rtab ([16][D/2] double2, LDS) by the
+// whole workgroup.  Every wavefront of the workgroup sees the same
+// positions, so all take the same branch.  Returns whether any row moved.
+template <int D>
+__device__ __forceinline__ bool fix_recent_table(const ScoreArgs& a, int64_t u, int32_t rpos,
+                                                 int lane, int tid, int nthreads,
+                                                 double2* rtab) {
+    const int32_t first = (int32_t)(a.t - a.n_recent_q);
+    if (__ballot(rpos != first + (lane & 15)) == 0) return false;
+    const int32_t* rp = a.kpos + u * a.l_cap + a.L - a.n_recent_q;
+    for (int e = tid; e < 16 * (D / 2); e += nthreads) {
+        const int r = e / (D / 2), k = e % (D / 2);
+        const int32_t pos = rp[r];
+        if (pos != first + r) {
+            double c, sn;
+            rope_cs((double)pos, k, D, a.theta, &c, &sn);
+            rtab[e] = double2{c, sn};
+        }
+    }
+    __syncthreads();
+    return true;
+}
+
+// Writes rotated rows to `stage` (LDS, 32 rows in the swizzled layout of a
+// key tile): per row, 4 consecutive dims of each half.
+template <int D>
+__device__ __forceinline__ void put_rows(const uint4 (&v)[2 * ObsRows<D>::NB], int lane,
+                                         uint16_t* stage) {
+    using O = ObsRows<D>;
+    constexpr int CPR = D / 8;
+    const int q = lane % O::QPR, sub = lane / O::QPR;
+#pragma unroll
+    for (int i = 0; i < 2 * O::NB; ++i) {
+        const int r = (i / O::NB) * 16 + (i % O::NB) * O::RPS + sub;
+        const int c1 = q >> 1, c2 = O::HALF / 8 + (q >> 1), e = 4 * (q & 1);
+        *reinterpret_cast<uint2*>(stage + (r * CPR + (c1 ^ (r % CPR))) * 8 + e) =
+            uint2{v[i].x, v[i].y};
+        *reinterpret_cast<uint2*>(stage + (r * CPR + (c2 ^ (r % CPR))) * 8 + e) =
+            uint2{v[i].z, v[i].w};
     }
 }
 
-// A fragments of query head h of unit u: this lane's row (lane % 32) and
-// dims (16 s + 8 (lane / 32) .. + 8) of the bf16 observation rows.
-template <int D>
-__device__ __forceinline__ void load_frag(const uint16_t* qobs, int64_t u, int g, int h,
-                                          int lane, bf16x8 (&frag)[D / 16]) {
-    const uint16_t* qrow =
-        qobs + ((u * g + h) * 32 + (lane & 31)) * (int64_t)D + 8 * (lane >> 5);
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s)
-        frag[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qrow + 16 * s));
+// Clears the score slots [0, L) of every unit; groups split over two
+// workgroups combine their scores there with an atomic maximum.
+__global__ __launch_bounds__(256) void zero_scores_kernel(float* score, int64_t l_cap, int64_t L,
+                                                          int64_t n_units) {
+    const int64_t n = n_units * L;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+        score[(i / L) * l_cap + i % L] = 0.f;
 }
 
 // Causal limit of accumulator entry v as an offset from the first recent
@@ -341,10 +382,103 @@ void score_kernel(ScoreArgs a, int g, int hs) {
     const int64_t mask_from = L - a.n_recent_q;  // tiles reaching past this need masks
     const float c2 = a.c2;
 
-    bf16x8 frag[D / 16];
-    if (active) load_frag<D>(a.qobs, u, g, hg, lane, frag);
     const TileLoad<D, NL> ld(h, lane);
-    const TileRead<D> rd(lane);
+
+    // Prologue.  The table's cos/sin rows for t-16..t-1 (16 x D/2 pairs of
+    // doubles, one tile buffer's size) go to the third tile buffer and the
+    // row for t to the reduction buffer by direct-to-LDS loads, each
+    // wavefront loads its head's observation rows, then the loader
+    // wavefronts issue the first two key tiles and wait for everything
+    // older.  The rows are rotated while the tiles are in flight and staged,
+    // two heads at a time, through the third tile buffer, from where each
+    // wavefront reads its MFMA A fragments (lane: row lane % 32, dims
+    // 16 s + 8 (lane / 32) .. + 8 for step s; the same swizzled layout as a
+    // key tile).
+    const int64_t qh = u * g + hg;
+    {
+        constexpr int NI = KT * D * 2 / 1024;  // 1 KB load instructions, rows t-16..t-1
+        static_assert(D / 2 * 16 <= (int)sizeof(red), "table row for t fits the reduction buffer");
+        const char* tab = reinterpret_cast<const char*>(a.table);
+        for (int i = h; i <= NI; i += nw) {
+            const bool row0 = i == NI;
+            const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(tab + (row0 ? 0 : (D / 2) * 16 + i * 1024)), 0, row0 ? (D / 2) * 16 : 1024,
+                kBufferFlags);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc,
+                (__attribute__((address_space(3))) void*)(row0 ? (void*)&red[0][0]
+                                                               : (void*)(tile2 + i * 512)),
+                16, lane * 16, 0, 0, 0);
+        }
+    }
+    const int32_t rpos = a.kpos[u * a.l_cap + L - a.n_recent_q + (lane & 15)];
+    ObsRows<D> obs;
+    if (active) obs.load(a, qh, lane);
+    if (loader) {
+        ld.issue(Ku, L, 0, tile0, h);
+        if (1 < ntiles) {
+            ld.issue(Ku, L, KT, tile1, h);
+            wait_vm<2 * NPW>();
+        } else {
+            wait_vm<NPW>();
+        }
+    } else {
+        wait_vm<0>();
+    }
+    __syncthreads();  // the cos/sin rows have landed
+    if (fix_recent_table<D>(a, u, rpos, lane, tid, 64 * nw, reinterpret_cast<double2*>(tile2))) {
+        // Rare path: the rows are loaded again, so that their first copy is
+        // dead while the cos/sin pairs are computed and its registers free.
+        if (active) obs.load(a, qh, lane);
+    }
+    bf16x8 frag[D / 16];
+    {
+        uint4 rows[2 * ObsRows<D>::NB];
+        if (active)
+            obs.rotate(lane, reinterpret_cast<const double2*>(&red[0][0]),
+                       reinterpret_cast<const double2*>(tile2), rows);
+        // The rotated words pass through an empty asm before the barrier, so
+        // the arithmetic stays ahead of it (sunk past it, it would keep every
+        // cos/sin pair read before the barrier in registers at once).
+#pragma unroll
+        for (int i = 0; i < 2 * ObsRows<D>::NB; ++i)
+            asm volatile("" : "+v"(rows[i].x), "+v"(rows[i].y), "+v"(rows[i].z), "+v"(rows[i].w));
+        __syncthreads();  // the cos/sin rows are no longer needed
+        uint16_t* stage = tile2 + (h & 1) * 32 * D;
+        for (int rnd = 0; 2 * rnd < nw; ++rnd) {
+            const bool mine = active && (h >> 1) == rnd;
+            // A fresh copy of the lane index per round keeps the staging
+            // addresses from being hoisted out of the loop into registers.
+            int ln = lane;
+            asm volatile("" : "+v"(ln));
+            if (mine) put_rows<D>(rows, ln, stage);
+            __syncthreads();
+            if (mine) {
+                const TileRead<D> rs(ln);
+                const char* st = reinterpret_cast<const char*>(stage);
+#pragma unroll
+                for (int s = 0; s < D / 16; ++s)
+                    frag[s] = __builtin_bit_cast(
+                        bf16x8, *reinterpret_cast<const uint4*>(st + rs.off[s]));
+                // Observation rows out (a.qobs: [U, g*32, D] bf16): lane
+                // holds 8 consecutive dims per step.
+                if (a.qobs) {
+                    uint16_t* q = a.qobs + (qh * 32 + (ln & 31)) * (int64_t)D + 8 * (ln >> 5);
+#pragma unroll
+                    for (int s = 0; s < D / 16; ++s)
+                        *reinterpret_cast<uint4*>(q + 16 * s) = __builtin_bit_cast(uint4, frag[s]);
+                }
+            }
+            __syncthreads();
+        }
+    }
+
+    // Per-lane LDS offsets of the key tiles' B operands, formed after the
+    // prologue (from a fresh copy of the lane index) so that they do not
+    // occupy registers during it.
+    int lane_rd = lane;
+    asm volatile("" : "+v"(lane_rd));
+    const TileRead<D> rd(lane_rd);
 
 // One tile iteration: wait until tile `it` (in CUR) has landed while tile
 // it+1 may still be in flight (loader wavefronts; NST extra stores may be
@@ -366,15 +500,11 @@ void score_kernel(ScoreArgs a, int g, int hs) {
         const int64_t base = (int64_t)(it) * KT;                                   \
         __VA_ARGS__;                                                               \
     } while (0)
-// Tiles rotate through tile0, tile1, tile2; SDEL is 1 when wavefront 0
-// issues a score store in each iteration (pass 2), which the wait of the
-// next iteration must allow for.
+// Tiles rotate through tile0, tile1, tile2 (tiles 0 and 1 are issued by the
+// prologue); SDEL is 1 when wavefront 0 issues a score store in each
+// iteration, which the wait of the next iteration must allow for.
 #define BKV_TILE_LOOP(SDEL, ...)                                                   \
     do {                                                                           \
-        if (loader) {                                                              \
-            ld.issue(Ku, L, 0, tile0, h);                                          \
-            if (1 < ntiles) ld.issue(Ku, L, KT, tile1, h);                         \
-        }                                                                          \
         for (int it = 0; it < ntiles; it += 3) {                                   \
             BKV_TILE_ITER(it, (SDEL) && h == 0 && it > 0, tile0, tile2, __VA_ARGS__); \
             if (it + 1 < ntiles)                                                   \
@@ -560,7 +690,7 @@ hipError_t launch_score(const uint16_t* K, const int32_t* kpos, int64_t n_units,
                         const float* beacons, int buf_cap, const float* recents,
                         int n_beacon, int n_recent_q, int64_t t, double theta,
                         float sm_scale, const double* table, float* score,
-                        uint16_t* qobs_out, uint16_t* qobs_ws, hipStream_t s) {
+                        uint16_t* qobs_out, hipStream_t s) {
     (void)n_beacon;
     if (n_units <= 0) return hipSuccess;
     ScoreArgs a;
@@ -577,19 +707,18 @@ hipError_t launch_score(const uint16_t* K, const int32_t* kpos, int64_t n_units,
     a.c2 = sm_scale * 1.4426950408889634f;
     a.table = table;
     a.score = score;
-    a.qobs = qobs_out ? qobs_out : qobs_ws;
+    a.qobs = qobs_out;
     a.n_units = n_units;
     // Groups of more than 4 heads: two workgroups per unit (see score_kernel).
     a.split = g > 4 ? 1 : 0;
     const int hs = a.split ? (g + 1) / 2 : g;
-    const int64_t n_heads = n_units * g;
-    const unsigned rblocks = (unsigned)((n_heads + 3) / 4);
-    if (d == 128)
-        rope_align_kernel<128><<<rblocks, 256, 0, s>>>(a, g, n_heads);
-    else
-        rope_align_kernel<64><<<rblocks, 256, 0, s>>>(a, g, n_heads);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (a.split) {
+        const int64_t n = n_units * L;
+        const unsigned zb = (unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
+        zero_scores_kernel<<<zb, 256, 0, s>>>(score, l_cap, L, n_units);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     const dim3 grid(a.split ? (unsigned)((n_units + 7) / 8 * 16) : (unsigned)n_units);
     const dim3 block(64 * hs);
     // Loader wavefronts: the largest power of two <= hs, at most 4.

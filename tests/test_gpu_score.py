@@ -3,7 +3,8 @@
 The kernel streams each unit's keys in tiles of 64 through a ring of three
 LDS tiles (two passes); the cases cover a single tile, several tiles and
 ring turns, a ragged last tile, a last tile that some recent rows cannot
-see at all, recent positions that need the direct RoPE path, and groups of
+see at all, recent positions that need the direct RoPE path (all or some of
+the rows), and groups of
 2, 4, 5 and 7 (which change the number of loader wavefronts).
 """
 import numpy as np
@@ -28,12 +29,14 @@ def _workload(name):
     return synth.WORKLOADS[name]
 
 
-def _run(w, L=None, l_cap=None, t=None, kpos_offset=0):
+def _run(w, L=None, l_cap=None, t=None, kpos_offset=0, shift_first_recents=0):
     L = L or w.L
     l_cap = l_cap or L
     w2 = synth.shrink(w, L=L)
     inp = synth.workload_inputs(w2)
     inp["kpos"] = inp["kpos"] + kpos_offset
+    if shift_first_recents:  # recent rows 0..7 earlier, rows 8..15 at t-8..t-1
+        inp["kpos"][:, L - 16:L - 8] -= shift_first_recents
     t = t if t is not None else L + kpos_offset
     dev = synth.to_device(inp, DEV, l_cap=l_cap)
     shape = bkv.Shape(w.n_units, w.group, w.d_head, l_cap, w.prefix, w.theta)
@@ -53,6 +56,7 @@ CASES = [
     ("tiny", 150, 150, 37),           # recent positions != t-16+i: direct RoPE path
     ("tiny", 517, 600, 0),            # 5-key last tile, invisible to recent rows 0..10
     ("tiny", 700, 700, 37),           # eleven tiles, direct RoPE path
+    ("tiny", 300, 300, "partial"),    # recent rows 0..7 moved, 8..15 from the table
     ("tiny_g7", 300, 320, 0),         # group 7
     ("tiny_g5", 1000, 1000, 0),       # group 5
     ("qwen3_4b_layer", None, None, 0),
@@ -63,7 +67,10 @@ CASES = [
 def test_score_matches_oracle(name, L, l_cap, t_shift):
     w = _workload(name)
     log(f"score {name} L={L or w.L} l_cap={l_cap} t_shift={t_shift}")
-    inp, sc, qobs, t = _run(w, L, l_cap, None if not t_shift else (L or w.L) + t_shift)
+    if t_shift == "partial":
+        inp, sc, qobs, t = _run(w, L, l_cap, shift_first_recents=3)
+    else:
+        inp, sc, qobs, t = _run(w, L, l_cap, None if not t_shift else (L or w.L) + t_shift)
     L = L or w.L
     worst = 0.0
     flips = 0

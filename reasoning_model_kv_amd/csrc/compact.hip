@@ -5,8 +5,9 @@
 //
 // Mapping: one wavefront per KV group walks its kept list in ascending
 // order, 16 tokens per iteration (a bf16 row of d = 128 is 16 lanes x 16
-// bytes, so one load instruction moves 4 rows).  In place, tokens before
-// the first evicted slot do not move and are skipped.  The walk is safe in
+// bytes, so one load instruction moves 4 rows), with the next iteration's
+// rows in flight while this one's are stored.  In place, tokens before the
+// first evicted slot do not move and are skipped.  The walk is safe in
 // place without any barrier: kept is strictly ascending, so the source of
 // token k is at a slot >= k and every destination written by an iteration
 // lies below every source read by later iterations; a destination can only
@@ -28,6 +29,12 @@ __device__ __forceinline__ void st_nt(uint16_t* p, uint4 v) {
     __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4*>(p));
 }
 constexpr int TPI = 16;  // tokens per iteration
+
+// Write-only sink for the stores of tokens past the end of the kept list (or
+// of malformed entries): every store is issued unconditionally, so that the
+// compiler's vmcnt waits count exactly (a conditional store makes it assume
+// the store may be missing and wait for loads still in flight).  Never read.
+__device__ uint4 g_sink[64];
 
 template <int D>
 __global__ __launch_bounds__(64 * WAVES) void compact_kernel(
@@ -67,33 +74,70 @@ __global__ __launch_bounds__(64 * WAVES) void compact_kernel(
 
     const int st = lane / LPT;  // token within an instruction
     const int ch = lane % LPT;  // 16-byte chunk within the row
-    for (int64_t base = k0; base < b_kv; base += TPI) {
-        // Source slots of this lane's NI tokens (kept[k] >= 0 always; -1 = past the end).
-        // Entries outside [0, L) (a malformed kept list) are skipped, never followed.
-        auto src_of = [&](int64_t k) -> int32_t {
-            if (k >= b_kv) return -1;
-            const int32_t v = ku[k];
-            return (v >= 0 && v < L) ? v : -1;
-        };
-        const int64_t kb = base + st;
-        const int32_t s0 = src_of(kb);
-        const int32_t s1 = NI > 1 ? src_of(kb + TPW) : -1;
-        const int32_t s2 = NI > 2 ? src_of(kb + 2 * TPW) : -1;
-        const int32_t s3 = NI > 3 ? src_of(kb + 3 * TPW) : -1;
-        const int32_t psrc = lane < TPI ? src_of(base + lane) : -1;
-        uint4 k0r{}, k1r{}, k2r{}, k3r{}, v0r{}, v1r{}, v2r{}, v3r{};
-        const int64_t off = 8 * ch;
-        if (s0 >= 0) { k0r = *(const uint4*)(Ks + (int64_t)s0 * D + off); v0r = *(const uint4*)(Vs + (int64_t)s0 * D + off); }
-        if (s1 >= 0) { k1r = *(const uint4*)(Ks + (int64_t)s1 * D + off); v1r = *(const uint4*)(Vs + (int64_t)s1 * D + off); }
-        if (s2 >= 0) { k2r = *(const uint4*)(Ks + (int64_t)s2 * D + off); v2r = *(const uint4*)(Vs + (int64_t)s2 * D + off); }
-        if (s3 >= 0) { k3r = *(const uint4*)(Ks + (int64_t)s3 * D + off); v3r = *(const uint4*)(Vs + (int64_t)s3 * D + off); }
-        int32_t pr = 0;
-        if (psrc >= 0) pr = ps[psrc];
-        if (s0 >= 0) { st_nt(Kd + kb * D + off, k0r); st_nt(Vd + kb * D + off, v0r); }
-        if (s1 >= 0) { st_nt(Kd + (kb + TPW) * D + off, k1r); st_nt(Vd + (kb + TPW) * D + off, v1r); }
-        if (s2 >= 0) { st_nt(Kd + (kb + 2 * TPW) * D + off, k2r); st_nt(Vd + (kb + 2 * TPW) * D + off, v2r); }
-        if (s3 >= 0) { st_nt(Kd + (kb + 3 * TPW) * D + off, k3r); st_nt(Vd + (kb + 3 * TPW) * D + off, v3r); }
-        if (psrc >= 0) pd[base + lane] = pr;
+    const int64_t off = 8 * ch;
+    // Kept entries of tokens [base, base + TPI): lane j (mod TPI) holds
+    // kept[base + j], or -1 past b_kv or for an entry outside [0, L) (a
+    // malformed list is skipped, never followed).  One load per lane.
+    auto load_kept = [&](int64_t base) -> int32_t {
+        const int64_t k = base + (lane & (TPI - 1));
+        const int32_t v = ku[k < b_kv ? k : b_kv - 1];
+        return (k < b_kv && v >= 0 && v < L) ? v : -1;
+    };
+    // One iteration's rows and positions.  Invalid tokens load slot 0 (the
+    // loads stay unconditional, so the compiler's waits count exactly) and
+    // are stored into the sink.
+    struct Batch {
+        uint4 k[NI], v[NI];
+        int32_t s[NI];
+        int32_t p;
+        bool pv;
+    };
+    auto load_rows = [&](int32_t kv, Batch& b) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            b.s[i] = __shfl(kv, st + i * TPW);
+            const int64_t r = b.s[i] >= 0 ? b.s[i] : 0;
+            b.k[i] = *(const uint4*)(Ks + r * D + off);
+            b.v[i] = *(const uint4*)(Vs + r * D + off);
+        }
+        b.pv = kv >= 0;
+        b.p = ps[kv >= 0 ? kv : 0];
+    };
+    // Every lane stores: invalid tokens into the sink; lanes TPI.. repeat the
+    // position stores of lanes 0..TPI-1 (same address, same value).
+    auto store_rows = [&](int64_t base, const Batch& b) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int64_t kb = base + st + i * TPW;
+            const bool ok = b.s[i] >= 0;
+            st_nt(ok ? Kd + kb * D + off : reinterpret_cast<uint16_t*>(&g_sink[lane]), b.k[i]);
+            st_nt(ok ? Vd + kb * D + off : reinterpret_cast<uint16_t*>(&g_sink[lane]), b.v[i]);
+        }
+        *(b.pv ? pd + base + (lane & (TPI - 1)) : reinterpret_cast<int32_t*>(&g_sink[lane])) = b.p;
+    };
+
+    // Software pipeline: the kept entries of the iteration after next and
+    // the rows of the next iteration are loaded before this iteration's rows
+    // are stored.  Unrolled by two
+    // over two buffers, so that no register with a load in flight is ever
+    // copied (a copy would wait for the load).  Safe in place: every
+    // destination written by an iteration lies below every source read by
+    // the later ones (kept is strictly ascending and kept[k] >= k).
+    Batch A, B;
+    int32_t kvA = load_kept(k0);
+    load_rows(kvA, A);
+    int32_t kvB = load_kept(k0 + TPI);
+    for (int64_t base = k0;;) {
+        kvA = load_kept(base + 2 * TPI);
+        load_rows(kvB, B);
+        store_rows(base, A);
+        base += TPI;
+        if (base >= b_kv) break;
+        kvB = load_kept(base + 2 * TPI);
+        load_rows(kvA, A);
+        store_rows(base, B);
+        base += TPI;
+        if (base >= b_kv) break;
     }
 }
 

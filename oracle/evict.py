@@ -19,8 +19,10 @@ from .select import select
 
 
 def evict_unit(keys, values, kpos, L, beacons, recents, t, b_kv, prefix,
-               recent_tok, theta, n_min=16, scale=None, merge=True):
+               recent_tok, theta, n_min=16, scale=None, merge=True, aggregate="max"):
     """keys/values: [>=L, d]; kpos: [>=L]; beacons/recents: [g, 16, d].
+
+    aggregate: the pooling of the scores, "max" (the method) or "mean".
 
     Returns a dict with score [L], kept [b_kv], the compacted keys, values
     and positions, and (with merge) the merged buffer [g, n_min, d] plus the
@@ -31,7 +33,7 @@ def evict_unit(keys, values, kpos, L, beacons, recents, t, b_kv, prefix,
     kpos = np.asarray(kpos, dtype=np.int64)[:L]
     n_recent = np.asarray(recents).shape[1]
     taus = kpos[L - n_recent:L]
-    sc = score_unit(keys, beacons, recents, t, taus, theta, scale)
+    sc = score_unit(keys, beacons, recents, t, taus, theta, scale, aggregate=aggregate)
     kept = select(sc, L, b_kv, prefix, recent_tok)
     k2, v2, p2 = compact(keys, values, kpos, kept)
     out = {"score": sc, "kept": kept, "keys": k2, "values": v2, "kpos": p2}

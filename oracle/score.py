@@ -1,5 +1,7 @@
 """Observation-set scoring: RoPE alignment, attention weights, max pooling.
 
+(Mean pooling, the pages' ablation of the pooling step, is an option.)
+
 Paper text, §4.3: when the cache is full at decoding step t, the observation
 set combines the beacon queries, rotated to t, and the most recent queries,
 kept at their own positions tau; its attention weights W over the current
@@ -66,16 +68,30 @@ def attention_weights(s, vis):
     return e / e.sum(axis=-1, keepdims=True)
 
 
-def pooled_score(w):
-    """Score[j] = max over heads and observation rows of W[h, r, j]."""
-    return w.reshape(-1, w.shape[-1]).max(axis=0)
+def pooled_score(w, aggregate="max"):
+    """Pool W[h, r, j] over every head and observation row of the group.
+
+    "max": Score[j] = max over (h, r) of W[h, r, j] (the method's pooling,
+    paper text §4.3).  "mean": Score[j] = the average of W[h, r, j] over all
+    N = heads x rows of the group, rows that cannot see slot j counting with
+    weight 0 (the mean-aggregation ablation, paper text §5.3 / Table 2, and
+    the average form of the importance score in §2.2; over a group the
+    average runs over all queries and heads, as the max does).
+    """
+    flat = w.reshape(-1, w.shape[-1])
+    if aggregate == "max":
+        return flat.max(axis=0)
+    if aggregate == "mean":
+        return flat.sum(axis=0) / flat.shape[0]
+    raise ValueError(f"aggregate must be 'max' or 'mean', not {aggregate!r}")
 
 
 def score_unit(keys, beacons, recents, t, taus, theta, scale=None,
-               return_all=False):
+               return_all=False, aggregate="max"):
     """Score every slot of one KV group's cache.
 
     keys: [L, d] (bfloat16 values widened to float64).
+    aggregate: "max" (the method) or "mean" (the ablation), see pooled_score.
     Returns score [L] (and, with return_all, qhat, logits and weights).
     """
     keys = np.asarray(keys, dtype=np.float64)
@@ -87,7 +103,7 @@ def score_unit(keys, beacons, recents, t, taus, theta, scale=None,
     qhat = observation_set(beacons, recents, t, taus, theta)
     s = logits(qhat, keys, scale)
     w = attention_weights(s, visibility(L, n_beacon, n_recent))
-    sc = pooled_score(w)
+    sc = pooled_score(w, aggregate)
     if return_all:
         return sc, qhat, s, w
     return sc

@@ -113,3 +113,59 @@ def test_pooled_score_and_weights_shapes():
     s = np.zeros((2, 32, 40))
     w = attention_weights(s, visibility(40, 16, 16))
     assert pooled_score(w).shape == (40,)
+
+
+def test_mean_pooling_sums_to_one_and_brute_force():
+    # Every softmax row sums to 1, so the average of the rows sums to 1 over
+    # the slots; and each slot's value is the plain average over all
+    # g x 32 rows, hidden rows counting as 0.
+    keys, b, rc, taus = _case(7, g=3, L=70, d=8)
+    L = keys.shape[0]
+    sc, _, _, w = score_unit(keys, b, rc, L, taus, 1e4, return_all=True, aggregate="mean")
+    assert abs(sc.sum() - 1.0) < 1e-12
+    vis = visibility(L, 16, 16)
+    for j in (0, 17, L - 16, L - 9, L - 1):
+        tot = 0.0
+        for h in range(3):
+            for r_ in range(32):
+                tot += w[h, r_, j] if vis[r_, j] else 0.0
+        assert abs(sc[j] - tot / 96) < 1e-15
+    mx = score_unit(keys, b, rc, L, taus, 1e4)
+    assert np.all(sc <= mx) and np.all(sc >= mx / 96 - 1e-18)
+
+
+def test_mean_pooling_identical_keys_closed_form():
+    # Uniform rows: beacon rows give 1/L to every slot, recent row i gives
+    # 1/(L-15+i) to slots 0..L-16+i.  The mean over the 2 x 32 rows is
+    # (16/L + sum over recent rows that see j of 1/(L-15+i)) / 32.
+    L, d = 80, 16
+    r = np.random.default_rng(8)
+    keys = np.tile(r.standard_normal(d), (L, 1))
+    b, rc = r.standard_normal((2, 16, d)), r.standard_normal((2, 16, d))
+    sc = score_unit(keys, b, rc, L, np.arange(L - 16, L), 1e4, aggregate="mean")
+    want = np.empty(L)
+    for j in range(L):
+        tot = 16.0 / L
+        for i in range(16):
+            if j <= L - 16 + i:
+                tot += 1.0 / (L - 15 + i)
+        want[j] = tot / 32
+    assert np.allclose(sc, want, rtol=1e-12, atol=0)
+
+
+def test_mean_equals_max_for_a_single_row():
+    # One head, one recent row and no beacons: both poolings return that row.
+    r = np.random.default_rng(9)
+    L, d = 30, 8
+    keys = r.standard_normal((L, d))
+    b = np.zeros((1, 0, d))
+    rc = r.standard_normal((1, 1, d))
+    a = score_unit(keys, b, rc, L, [L - 1], 1e4, aggregate="mean")
+    m = score_unit(keys, b, rc, L, [L - 1], 1e4)
+    assert np.array_equal(a, m)
+    try:
+        pooled_score(np.zeros((1, 1, 3)), "median")
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("unknown pooling must be rejected")

@@ -55,6 +55,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle baseline sample (0 disables)")
     p.add_argument("--no-check", action="store_true", help="skip the sampled parity check")
+    p.add_argument("--aggregate", choices=("max", "mean"), default="max",
+                   help="pooling of the attention weights: the method's max, or the mean of "
+                        "the aggregation ablation")
     p.add_argument("--stream-steps", type=int, default=0,
                    help="decode steps of a streaming workload (0: the workload's own)")
     return p.parse_args()
@@ -232,7 +235,8 @@ def main():
     score = torch.empty((U, L), dtype=torch.float32, device=dev)
     kept = torch.empty((U, B), dtype=torch.int32, device=dev)
     scrub = torch.empty(512 * 2**20 // 4, dtype=torch.float32, device=dev)
-    shape = bkv.Shape(U, g, d, L, w.prefix, w.theta, recent_tok=w.recent_tok)
+    shape = bkv.Shape(U, g, d, L, w.prefix, w.theta, recent_tok=w.recent_tok,
+                      aggregate=args.aggregate)
     ws = bkv.alloc_workspace(shape, L, 0, dev)
     stream = torch.cuda.current_stream()
 
@@ -350,7 +354,7 @@ def main():
             ref = oracle.evict.evict_unit(
                 K0[u].float().cpu().numpy(), V0[u].float().cpu().numpy(), P0[u].cpu().numpy(),
                 L, beacons[u * g:(u + 1) * g], rec[u * g:(u + 1) * g].cpu().numpy(), L, B,
-                w.prefix, w.recent_tok, w.theta, merge=False)
+                w.prefix, w.recent_tok, w.theta, merge=False, aggregate=args.aggregate)
             s_gpu = score[u].cpu().numpy()
             worst = max(worst, float(np.max(np.abs(s_gpu - ref["score"]) /
                                             (ref["score"] + 1e-30))))
@@ -374,7 +378,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "units": U, "layers": w.layers, "batch": w.batch,
                    "kv_heads": w.h_kv, "group": g, "d_head": d, "L": L, "b_kv": B,
-                   "prefix": w.prefix, "recent": w.recent_tok, "rope_theta": w.theta},
+                   "prefix": w.prefix, "recent": w.recent_tok, "rope_theta": w.theta,
+                   "pooling": args.aggregate},
         "unit_evictions_per_s": round(U / (ms_step * 1e-3), 1),
         "steps_per_s": round(1e3 / ms_step, 2),
         "step": "bkv_fps_update (compress) + bkv_evict",

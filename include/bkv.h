@@ -63,6 +63,12 @@ typedef struct bkv_dims {
     int64_t l_cap;   /* slot stride of K, V, kpos and score (>= L) */
 } bkv_dims;
 
+/* Policy flags.  BKV_FLAG_MEAN: pool the attention weights by their mean
+ * over the group's rows instead of their maximum (the mean-aggregation
+ * ablation: paper text §5.3 and Table 2; the average form of the importance
+ * score, paper text §2.2). */
+#define BKV_FLAG_MEAN 1
+
 /* Method parameters.  Paper text §5.1 ("Implementation Details"): beacon
  * budget max 32 / min 16, recent query budget 16; summary step (5): prefix
  * and recent tokens always kept. */
@@ -72,7 +78,7 @@ typedef struct bkv_policy {
     int32_t buf_cap;    /* rows per head in buf (32; up to 256 for prefill) */
     int32_t prefix;     /* P: leading slots always kept */
     int32_t recent_tok; /* R: trailing slots always kept */
-    int32_t flags;      /* reserved, must be 0 */
+    int32_t flags;      /* 0, or BKV_FLAG_MEAN */
     double rope_theta;  /* RoPE base theta (> 0) */
     float sm_scale;     /* softmax scale; 0 means 1/sqrt(d_head) */
     int32_t reserved;   /* must be 0 */
@@ -139,8 +145,9 @@ int bkv_fps_update(const bkv_dims* dims, const bkv_policy* pol, float* buf,
  *   computed in fp64 and rounded to fp32 and then to bf16 (both RNE).
  *   logits s = q . k * sm_scale against K[u, 0..L) (bf16 in, fp32 accumulate);
  *   recent row i sees slots 0..L-n_recent_q+i, beacon rows see all L slots;
- *   W = row softmax over the visible slots;
- *   score[u, j] = max over the g*(n_beacon+n_recent_q) rows of W[row, j].
+ *   W = row softmax over the visible slots (hidden entries are 0);
+ *   score[u, j] = max over the g*(n_beacon+n_recent_q) rows of W[row, j],
+ *   or with BKV_FLAG_MEAN their average (sum over the rows / that count).
  * Writes score[u, 0..L); other slots are untouched.  If qobs_out is non-NULL
  * it receives the bf16 observation rows, [U, g*(n_beacon+n_recent_q), d],
  * row = h*(n_beacon+n_recent_q) + (beacons first, then recents).

@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libbkv.so")
 
 BKV_OK, BKV_EINVAL, BKV_ENOTSUP, BKV_ENOSPC, BKV_EHIP = 0, -1, -2, -3, -4
 ABI_VERSION = 1
+BKV_FLAG_MEAN = 1  # policy flag: mean pooling (include/bkv.h)
 
 EXPORTS = ("bkv_abi_version", "bkv_last_error", "bkv_workspace_bytes", "bkv_fps_update",
            "bkv_score", "bkv_select", "bkv_compact", "bkv_evict")
@@ -57,13 +58,17 @@ class Shape:
     n_beacon: int = 16
     n_recent_q: int = 16
     sm_scale: float = 0.0
+    aggregate: str = "max"  # pooling of the attention weights: "max" or "mean"
 
     def dims(self):
         return Dims(self.n_units, self.group, self.d_head, self.l_cap)
 
     def policy(self):
+        if self.aggregate not in ("max", "mean"):
+            raise ValueError(f"aggregate must be 'max' or 'mean', not {self.aggregate!r}")
+        flags = BKV_FLAG_MEAN if self.aggregate == "mean" else 0
         return Policy(self.n_beacon, self.n_recent_q, self.buf_cap, self.prefix,
-                      self.recent_tok, 0, float(self.rope_theta), float(self.sm_scale), 0)
+                      self.recent_tok, flags, float(self.rope_theta), float(self.sm_scale), 0)
 
     @property
     def scale(self):

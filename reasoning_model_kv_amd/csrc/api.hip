@@ -74,8 +74,8 @@ int check_dims(const char* fn, const bkv_dims* d) {
 
 int check_policy(const char* fn, const bkv_policy* p) {
     if (!p) return fail(BKV_EINVAL, "%s: policy is NULL", fn);
-    if (p->flags != 0 || p->reserved != 0)
-        return fail(BKV_EINVAL, "%s: reserved policy fields must be 0", fn);
+    if ((p->flags & ~BKV_FLAG_MEAN) != 0 || p->reserved != 0)
+        return fail(BKV_EINVAL, "%s: unknown policy flags or reserved field not 0", fn);
     if (p->n_beacon != 16 || p->n_recent_q != 16)
         return fail(BKV_ENOTSUP, "%s: n_beacon %d / n_recent_q %d: only 16 / 16 supported", fn,
                     p->n_beacon, p->n_recent_q);
@@ -215,7 +215,7 @@ int bkv_score(const bkv_dims* dims, const bkv_policy* pol, const uint16_t* K,
         e = bkv::launch_score(K, kpos, dims->n_units, dims->group, dims->d_head, dims->l_cap,
                               L, beacons, pol->buf_cap, recents, pol->n_beacon,
                               pol->n_recent_q, t, pol->rope_theta, scale_of(dims, pol),
-                              table, score, qobs_out, s);
+                              (pol->flags & BKV_FLAG_MEAN) != 0, table, score, qobs_out, s);
     return hip_result(e, fn);
 }
 
@@ -293,7 +293,7 @@ int bkv_evict(const bkv_dims* dims, const bkv_policy* pol, uint16_t* K, uint16_t
         e = bkv::launch_score(K, kpos, dims->n_units, dims->group, dims->d_head, dims->l_cap,
                               L, beacons, pol->buf_cap, recents, pol->n_beacon,
                               pol->n_recent_q, t, pol->rope_theta, scale_of(dims, pol),
-                              table, score, nullptr, s);
+                              (pol->flags & BKV_FLAG_MEAN) != 0, table, score, nullptr, s);
     if (e == hipSuccess)
         e = bkv::launch_select(score, dims->n_units, dims->l_cap, L, b_kv, pol->prefix,
                                pol->recent_tok, kept, s);

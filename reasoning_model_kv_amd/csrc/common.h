@@ -21,7 +21,7 @@ hipError_t launch_score(const uint16_t* K, const int32_t* kpos, int64_t n_units,
                         int g, int d, int64_t l_cap, int64_t L,
                         const float* beacons, int buf_cap, const float* recents,
                         int n_beacon, int n_recent_q, int64_t t, double theta,
-                        float sm_scale, const double* table, float* score,
+                        float sm_scale, bool mean, const double* table, float* score,
                         uint16_t* qobs_out, hipStream_t s);
 
 hipError_t launch_select(const float* score, int64_t n_units, int64_t l_cap,

@@ -80,7 +80,8 @@ struct ScoreArgs {
     float* score;
     uint16_t* qobs;
     int64_t n_units;
-    int split;  // 1: each unit's heads are scored by two workgroups (scores pre-zeroed, max-combined)
+    int split;  // 1: each unit's heads are scored by two workgroups (scores pre-zeroed, combined atomically)
+    float inv_rows;  // 1 / (g * 32): the mean pooling's divisor
 };
 
 __device__ __forceinline__ int acc_row(int v, int lane) {
@@ -350,7 +351,7 @@ __device__ __forceinline__ void tile_logits(const uint16_t* lds_tile, const Tile
 // (blocks b and b + 8), where the second read of each key tile is likely to
 // hit L2, and combines its column maxima with an atomic maximum on the
 // score bits (non-negative floats order like their bit patterns).
-template <int D, int NL, bool SPLIT>
+template <int D, int NL, bool SPLIT, bool MEAN>
 __global__ __launch_bounds__(512)
 void score_kernel(ScoreArgs a, int g, int hs) {
     // Three separately declared tiles (not one array) so that the compiler
@@ -583,6 +584,14 @@ void score_kernel(ScoreArgs a, int g, int hs) {
     __syncthreads();
     float* score_u = a.score + u * a.l_cap;
 #define BKV_PASS2                                                                  \
+    if constexpr (MEAN) {                                                          \
+        BKV_PASS2_MEAN;                                                            \
+    } else {                                                                       \
+        BKV_PASS2_MAX;                                                             \
+    }
+// Max pooling: the largest (s - LSE) over the lane's rows, the other half
+// and the wavefronts, then one exp2 per key.
+#define BKV_PASS2_MAX                                                              \
     float c0 = -__builtin_inff(), c1 = -__builtin_inff();                          \
     if (base + KT > mask_from) {                                                   \
         const int ln = lane;                                                       \
@@ -618,6 +627,47 @@ void score_kernel(ScoreArgs a, int g, int hs) {
                           __float_as_uint(exp2f(best)));                           \
             else                                                                   \
                 score_u[key] = exp2f(best);                                        \
+        }                                                                          \
+    }
+// Mean pooling: the sum of exp2(s - LSE) = W over the lane's rows (hidden
+// entries add nothing), the other half and the wavefronts, divided by the
+// group's g * 32 rows; a split group adds its two halves atomically (two
+// addends: the result does not depend on their order).  Terms below 2^-126
+// flush to zero, far below any score that matters (at most 224 of them).
+#define BKV_PASS2_MEAN                                                             \
+    float c0 = 0.f, c1 = 0.f;                                                      \
+    if (base + KT > mask_from) {                                                   \
+        const int ln = lane;                                                       \
+        const int d0 = (int)(base - mask_from) + (ln & 31), d1 = d0 + 32;          \
+        _Pragma("unroll") for (int v = 0; v < 16; ++v) {                           \
+            const int lim = row_lim(v, ln, a.n_recent_q);                          \
+            const float e0 = exp2_sum(fmaf(acc0[v], c2, -lse[v]));                 \
+            const float e1 = exp2_sum(fmaf(acc1[v], c2, -lse[v]));                 \
+            c0 += d0 <= lim ? e0 : 0.f;                                            \
+            c1 += d1 <= lim ? e1 : 0.f;                                            \
+        }                                                                          \
+    } else {                                                                       \
+        _Pragma("unroll") for (int v = 0; v < 16; ++v) {                           \
+            c0 += exp2_sum(fmaf(acc0[v], c2, -lse[v]));                            \
+            c1 += exp2_sum(fmaf(acc1[v], c2, -lse[v]));                            \
+        }                                                                          \
+    }                                                                              \
+    c0 += __shfl_xor(c0, 32);                                                      \
+    c1 += __shfl_xor(c1, 32);                                                      \
+    if (lane < 32) {                                                               \
+        red[h][lane] = active ? c0 : 0.f;                                          \
+        red[h][32 + lane] = active ? c1 : 0.f;                                     \
+    }                                                                              \
+    __syncthreads();                                                               \
+    if (tid < KT) {                                                                \
+        float tot = red[0][tid];                                                   \
+        for (int w = 1; w < nw; ++w) tot += red[w][tid];                           \
+        const int64_t key = base + tid;                                            \
+        if (key < L) {                                                             \
+            if (SPLIT)                                                             \
+                atomicAdd(score_u + key, tot * a.inv_rows);                        \
+            else                                                                   \
+                score_u[key] = tot * a.inv_rows;                                   \
         }                                                                          \
     }
 // Pass 2 walks the tiles backwards: at the end of pass 1 the last three
@@ -657,24 +707,38 @@ void score_kernel(ScoreArgs a, int g, int hs) {
 #undef BKV_REV_LOOP
 #undef BKV_REV_ITER
 #undef BKV_PASS2
+#undef BKV_PASS2_MAX
+#undef BKV_PASS2_MEAN
 #undef BKV_TILE_LOOP
 #undef BKV_TILE_ITER
 }
 
 // Every variant is instantiated explicitly, so each gets its host launch stub
 // even though it is launched from one branch of a conditional.
-template __global__ void score_kernel<128, 4, false>(ScoreArgs, int, int);
-template __global__ void score_kernel<128, 2, false>(ScoreArgs, int, int);
-template __global__ void score_kernel<128, 1, false>(ScoreArgs, int, int);
-template __global__ void score_kernel<64, 4, false>(ScoreArgs, int, int);
-template __global__ void score_kernel<64, 2, false>(ScoreArgs, int, int);
-template __global__ void score_kernel<64, 1, false>(ScoreArgs, int, int);
-template __global__ void score_kernel<128, 4, true>(ScoreArgs, int, int);
-template __global__ void score_kernel<128, 2, true>(ScoreArgs, int, int);
-template __global__ void score_kernel<128, 1, true>(ScoreArgs, int, int);
-template __global__ void score_kernel<64, 4, true>(ScoreArgs, int, int);
-template __global__ void score_kernel<64, 2, true>(ScoreArgs, int, int);
-template __global__ void score_kernel<64, 1, true>(ScoreArgs, int, int);
+template __global__ void score_kernel<128, 4, false, false>(ScoreArgs, int, int);
+template __global__ void score_kernel<128, 2, false, false>(ScoreArgs, int, int);
+template __global__ void score_kernel<128, 1, false, false>(ScoreArgs, int, int);
+template __global__ void score_kernel<64, 4, false, false>(ScoreArgs, int, int);
+template __global__ void score_kernel<64, 2, false, false>(ScoreArgs, int, int);
+template __global__ void score_kernel<64, 1, false, false>(ScoreArgs, int, int);
+template __global__ void score_kernel<128, 4, true, false>(ScoreArgs, int, int);
+template __global__ void score_kernel<128, 2, true, false>(ScoreArgs, int, int);
+template __global__ void score_kernel<128, 1, true, false>(ScoreArgs, int, int);
+template __global__ void score_kernel<64, 4, true, false>(ScoreArgs, int, int);
+template __global__ void score_kernel<64, 2, true, false>(ScoreArgs, int, int);
+template __global__ void score_kernel<64, 1, true, false>(ScoreArgs, int, int);
+template __global__ void score_kernel<128, 4, false, true>(ScoreArgs, int, int);
+template __global__ void score_kernel<128, 2, false, true>(ScoreArgs, int, int);
+template __global__ void score_kernel<128, 1, false, true>(ScoreArgs, int, int);
+template __global__ void score_kernel<64, 4, false, true>(ScoreArgs, int, int);
+template __global__ void score_kernel<64, 2, false, true>(ScoreArgs, int, int);
+template __global__ void score_kernel<64, 1, false, true>(ScoreArgs, int, int);
+template __global__ void score_kernel<128, 4, true, true>(ScoreArgs, int, int);
+template __global__ void score_kernel<128, 2, true, true>(ScoreArgs, int, int);
+template __global__ void score_kernel<128, 1, true, true>(ScoreArgs, int, int);
+template __global__ void score_kernel<64, 4, true, true>(ScoreArgs, int, int);
+template __global__ void score_kernel<64, 2, true, true>(ScoreArgs, int, int);
+template __global__ void score_kernel<64, 1, true, true>(ScoreArgs, int, int);
 
 }  // namespace
 
@@ -689,7 +753,7 @@ hipError_t launch_score(const uint16_t* K, const int32_t* kpos, int64_t n_units,
                         int g, int d, int64_t l_cap, int64_t L,
                         const float* beacons, int buf_cap, const float* recents,
                         int n_beacon, int n_recent_q, int64_t t, double theta,
-                        float sm_scale, const double* table, float* score,
+                        float sm_scale, bool mean, const double* table, float* score,
                         uint16_t* qobs_out, hipStream_t s) {
     (void)n_beacon;
     if (n_units <= 0) return hipSuccess;
@@ -711,6 +775,7 @@ hipError_t launch_score(const uint16_t* K, const int32_t* kpos, int64_t n_units,
     a.n_units = n_units;
     // Groups of more than 4 heads: two workgroups per unit (see score_kernel).
     a.split = g > 4 ? 1 : 0;
+    a.inv_rows = 1.0f / (float)(g * 32);
     const int hs = a.split ? (g + 1) / 2 : g;
     if (a.split) {
         const int64_t n = n_units * L;
@@ -723,10 +788,15 @@ hipError_t launch_score(const uint16_t* K, const int32_t* kpos, int64_t n_units,
     const dim3 block(64 * hs);
     // Loader wavefronts: the largest power of two <= hs, at most 4.
     const int nl = hs >= 4 ? 4 : (hs >= 2 ? 2 : 1);
-#define BKV_LAUNCH(DD, NN)                                                        \
-    do {                                                                          \
-        if (a.split) score_kernel<DD, NN, true><<<grid, block, 0, s>>>(a, g, hs);  \
-        else score_kernel<DD, NN, false><<<grid, block, 0, s>>>(a, g, hs);         \
+#define BKV_LAUNCH_M(DD, NN, MM)                                                   \
+    do {                                                                           \
+        if (a.split) score_kernel<DD, NN, true, MM><<<grid, block, 0, s>>>(a, g, hs); \
+        else score_kernel<DD, NN, false, MM><<<grid, block, 0, s>>>(a, g, hs);     \
+    } while (0)
+#define BKV_LAUNCH(DD, NN)                                                         \
+    do {                                                                           \
+        if (mean) BKV_LAUNCH_M(DD, NN, true);                                      \
+        else BKV_LAUNCH_M(DD, NN, false);                                          \
     } while (0)
     if (d == 128) {
         if (nl == 4) BKV_LAUNCH(128, 4);
@@ -738,6 +808,7 @@ hipError_t launch_score(const uint16_t* K, const int32_t* kpos, int64_t n_units,
         else BKV_LAUNCH(64, 1);
     }
 #undef BKV_LAUNCH
+#undef BKV_LAUNCH_M
     return hipGetLastError();
 }
 

@@ -55,6 +55,15 @@ def test_score_validation(lib):
     assert _call_score(lib, _shape(group=0)) == bkv.BKV_EINVAL
     assert _call_score(lib, _shape(n_beacon=8)) == bkv.BKV_ENOTSUP
     assert _call_score(lib, _shape(rope_theta=0.0)) == bkv.BKV_EINVAL
+    bad_flags = _shape()
+    pol = bad_flags.policy()
+    pol.flags = 2                                                 # unknown flag bit
+    assert lib.bkv_score(ctypes.byref(bad_flags.dims()), ctypes.byref(pol), FAKE, FAKE, 300,
+                         FAKE, FAKE, 300, FAKE, None, FAKE, 1 << 20, None) == bkv.BKV_EINVAL
+    assert "flags" in bkv.last_error()
+    assert _call_score(lib, _shape(n_units=0, aggregate="mean")) == bkv.BKV_OK
+    with pytest.raises(ValueError):
+        _shape(aggregate="median").policy()
     assert _call_score(lib, _shape(buf_cap=300)) == bkv.BKV_ENOTSUP
     big = _shape(n_units=1, l_cap=1 << 23)                        # 2^31 key bytes per unit
     assert _call_score(lib, big, L=1 << 23, t=1 << 23) == bkv.BKV_ENOTSUP

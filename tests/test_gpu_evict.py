@@ -18,14 +18,14 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def _shape(w, l_cap):
+def _shape(w, l_cap, aggregate="max"):
     return bkv.Shape(w.n_units, w.group, w.d_head, l_cap, w.prefix, w.theta,
-                     recent_tok=w.recent_tok)
+                     recent_tok=w.recent_tok, aggregate=aggregate)
 
 
-def _step(w, dev, l_cap):
+def _step(w, dev, l_cap, aggregate="max"):
     """The benchmark's step: Continual-FPS compress, then evict with merge."""
-    shape = _shape(w, l_cap)
+    shape = _shape(w, l_cap, aggregate)
     nq = w.n_qheads
     count = torch.full((nq,), 31, dtype=torch.int32, device=DEV)
     newq = dev["buf"][:, 31:32].contiguous()
@@ -43,7 +43,7 @@ def _step(w, dev, l_cap):
                 K0=K0, V0=V0, P0=P0, count=count)
 
 
-def _check_unit(w, u, inp_u, res, where):
+def _check_unit(w, u, inp_u, res, where, aggregate="max"):
     L = w.L
     g = w.group
     qh = slice(u * g, (u + 1) * g)
@@ -53,7 +53,8 @@ def _check_unit(w, u, inp_u, res, where):
         check_fps(buf0[h, :32], sel[h], 16, f"{where} fps head {h}")
     beacons = res["beacons"][qh].cpu().numpy()
     ref = oracle.evict.evict_unit(inp_u["keys"], inp_u["values"], inp_u["kpos"], L, beacons,
-                                  inp_u["recents"], L, w.b_kv, w.prefix, w.recent_tok, w.theta)
+                                  inp_u["recents"], L, w.b_kv, w.prefix, w.recent_tok, w.theta,
+                                  aggregate=aggregate)
     rel = check_scores(res["score"][u, :L].cpu().numpy(), ref["score"], where)
     kept = res["kept"][u].cpu().numpy()
     nd = check_kept(kept, ref["score"], L, w.b_kv, w.prefix, w.recent_tok, where)
@@ -89,6 +90,40 @@ def test_evict_small_all_units(name):
     for u in range(w.n_units):
         unit = {k: inp[k][u] for k in ("keys", "values", "kpos", "recents")}
         rel, nd = _check_unit(w, u, unit, res, f"{name} unit {u}")
+        worst, ndiff = max(worst, rel), ndiff + nd
+    log(f"  max score rel err {worst:.3g}; kept-set tie-band differences {ndiff}")
+
+
+@pytest.mark.parametrize("name,samples", [
+    ("tiny", None),
+    ("qwen3_4b_layer", None),
+    ("r1_qwen_7b", [0, 1791, 3583]),   # group 7: two workgroups per unit add their sums
+])
+def test_evict_mean_pooling(name, samples):
+    """The mean-aggregation ablation through the whole step."""
+    w = synth.WORKLOADS[name]
+    log(f"evict mean pooling {name}: U={w.n_units} g={w.group} L={w.L} B={w.b_kv}")
+    if samples is None:
+        inp = synth.workload_inputs(w)
+        dev = synth.to_device(inp, DEV)
+        samples = list(range(w.n_units))
+        host = {u: {k: inp[k][u] for k in ("keys", "values", "kpos", "recents")}
+                for u in samples}
+    else:
+        dev = synth.device_inputs(w, DEV)
+        host = {u: {"keys": dev["keys"][u].float().cpu().numpy(),
+                    "values": dev["values"][u].float().cpu().numpy(),
+                    "kpos": dev["kpos"][u].cpu().numpy(),
+                    "recents": dev["recents"][u * w.group:(u + 1) * w.group].cpu().numpy()}
+                for u in samples}
+    res = _step(w, dev, w.L, aggregate="mean")
+    res.update(K1=dev["keys"], V1=dev["values"], P1=dev["kpos"], buf1=dev["buf"])
+    # Every unit: the average of softmax rows sums to 1 over the slots.
+    tot = res["score"][:, :w.L].double().sum(dim=1)
+    assert torch.all((tot - 1).abs() < 1e-3), float((tot - 1).abs().max())
+    worst, ndiff = 0.0, 0
+    for u in samples:
+        rel, nd = _check_unit(w, u, host[u], res, f"{name} mean unit {u}", aggregate="mean")
         worst, ndiff = max(worst, rel), ndiff + nd
     log(f"  max score rel err {worst:.3g}; kept-set tie-band differences {ndiff}")
 

@@ -29,7 +29,7 @@ def _workload(name):
     return synth.WORKLOADS[name]
 
 
-def _run(w, L=None, l_cap=None, t=None, kpos_offset=0, shift_first_recents=0):
+def _run(w, L=None, l_cap=None, t=None, kpos_offset=0, shift_first_recents=0, aggregate="max"):
     L = L or w.L
     l_cap = l_cap or L
     w2 = synth.shrink(w, L=L)
@@ -39,7 +39,8 @@ def _run(w, L=None, l_cap=None, t=None, kpos_offset=0, shift_first_recents=0):
         inp["kpos"][:, L - 16:L - 8] -= shift_first_recents
     t = t if t is not None else L + kpos_offset
     dev = synth.to_device(inp, DEV, l_cap=l_cap)
-    shape = bkv.Shape(w.n_units, w.group, w.d_head, l_cap, w.prefix, w.theta)
+    shape = bkv.Shape(w.n_units, w.group, w.d_head, l_cap, w.prefix, w.theta,
+                      aggregate=aggregate)
     score = torch.full((w.n_units, l_cap), -1.0, device=DEV)
     qobs = torch.zeros((w.n_units, w.group * 32, w.d_head), dtype=torch.bfloat16, device=DEV)
     bkv.score(shape, dev["keys"], dev["kpos"], L, dev["buf"], dev["recents"], t, score, qobs)
@@ -90,3 +91,31 @@ def test_score_matches_oracle(name, L, l_cap, t_shift):
             assert np.all(np.abs(got_q[neq] - qhat[neq]) <= ulp)
     assert flips <= 1e-4 * qobs.numel()
     log(f"  max rel err {worst:.3g}, bf16 rounding flips {flips}")
+
+
+MEAN_CASES = [
+    ("tiny", 203, 256),       # ragged tail, l_cap > L
+    ("tiny", 40, 64),         # one tile, recent rows masked inside it
+    ("tiny_g7", 300, 320),    # group 7: two workgroups add their sums
+    ("tiny_g5", 1000, 1000),  # group 5
+    ("qwen3_4b_layer", None, None),
+]
+
+
+@pytest.mark.parametrize("name,L,l_cap", MEAN_CASES)
+def test_score_mean_pooling_matches_oracle(name, L, l_cap):
+    w = _workload(name)
+    log(f"score mean pooling {name} L={L or w.L} l_cap={l_cap}")
+    inp, sc, _, t = _run(w, L, l_cap, aggregate="mean")
+    L = L or w.L
+    worst = 0.0
+    for u in range(w.n_units):
+        beacons = inp["buf"][u][:, :16]
+        taus = inp["kpos"][u][L - 16:L]
+        ref = oracle.score.score_unit(inp["keys"][u], beacons, inp["recents"][u], t, taus,
+                                      w.theta, aggregate="mean")
+        worst = max(worst, check_scores(sc[u, :L], ref, f"{name} mean unit {u}"))
+        assert abs(sc[u, :L].astype(np.float64).sum() - 1.0) < 1e-4
+        if sc.shape[1] > L:
+            assert np.all(sc[u, L:] == -1.0), "slots past L must be untouched"
+    log(f"  max rel err {worst:.3g}")

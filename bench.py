@@ -58,6 +58,10 @@ def parse():
     p.add_argument("--aggregate", choices=("max", "mean"), default="max",
                    help="pooling of the attention weights: the method's max, or the mean of "
                         "the aggregation ablation")
+    p.add_argument("--observe", choices=("beacons", "recent32"), default="beacons",
+                   help="observation set: the method's 16 beacons + 16 recent queries, or the "
+                        "baselines' 32 most recent queries (no beacons, no FPS, 32 recent "
+                        "tokens kept)")
     p.add_argument("--stream-steps", type=int, default=0,
                    help="decode steps of a streaming workload (0: the workload's own)")
     return p.parse_args()
@@ -71,8 +75,8 @@ def stage_bytes(w, n_mv_total):
     return {
         # read 31 buffer rows + the new query, write 16 rows and the count
         "fps_compress": nq * ((31 + 1 + 16) * d * 4 + 8),
-        # K rows, 32 observation rows per head, 16 recent positions, score out
-        "score": U * (L * d * 2 + g * 32 * d * 4 + 16 * 4 + L * 4),
+        # K rows, 32 observation rows per head, the recent positions, score out
+        "score": U * (L * d * 2 + g * 32 * d * 4 + w.n_recent_q * 4 + L * 4),
         # middle scores in, kept list out
         "select": U * ((L - P - R) * 4 + B * 4),
         # moved tokens: K and V row read + write, position read + write; kept in
@@ -177,6 +181,11 @@ def _oracle_step(w, unit):
     import numpy as np
 
     import oracle
+    if w.n_beacon == 0:  # the 32-query window: no FPS, no merge
+        oracle.evict.evict_unit(unit["keys"], unit["values"], unit["kpos"], w.L,
+                                np.zeros((w.group, 0, w.d_head)), unit["recents"], w.L, w.b_kv,
+                                w.prefix, w.recent_tok, w.theta, merge=False)
+        return True
     heads = []
     for h in range(w.group):
         _, keep = oracle.fps.fps(unit["buf"][h], 16)
@@ -203,6 +212,9 @@ def main():
     if w.stream_steps:
         stream_main(args, w)
         return
+    window = args.observe == "recent32"
+    if window:
+        w = synth.shrink(w, n_beacon=0, n_recent_q=32, recent_tok=32)
     cpu = None
     if args.cpu_seconds > 0:
         eprint(f"[bench] oracle CPU baseline (~{args.cpu_seconds:.0f} s of CPU work per core)")
@@ -236,7 +248,7 @@ def main():
     kept = torch.empty((U, B), dtype=torch.int32, device=dev)
     scrub = torch.empty(512 * 2**20 // 4, dtype=torch.float32, device=dev)
     shape = bkv.Shape(U, g, d, L, w.prefix, w.theta, recent_tok=w.recent_tok,
-                      aggregate=args.aggregate)
+                      n_beacon=w.n_beacon, n_recent_q=w.n_recent_q, aggregate=args.aggregate)
     ws = bkv.alloc_workspace(shape, L, 0, dev)
     stream = torch.cuda.current_stream()
 
@@ -255,29 +267,36 @@ def main():
 
     def step_evict():
         eva[0].record(stream)
-        bkv.fps_update(shape, buf, count, newq, trigger=32, m=16)
+        if not window:
+            bkv.fps_update(shape, buf, count, newq, trigger=32, m=16)
         eva[1].record(stream)
-        bkv.evict(shape, K, V, kpos, L, buf, rec, L, B, buf=buf, count=count,
-                  score_out=score, kept_out=kept, ws=ws_e)
+        if window:
+            bkv.evict(shape, K, V, kpos, L, None, rec, L, B, score_out=score, kept_out=kept,
+                      ws=ws_e)
+        else:
+            bkv.evict(shape, K, V, kpos, L, buf, rec, L, B, buf=buf, count=count,
+                      score_out=score, kept_out=kept, ws=ws_e)
         eva[2].record(stream)
 
     # The same work as separate calls, with events between them, for the
     # per-stage breakdown and the roofline of the dominant kernel.
-    names = ["fps_compress", "score", "select", "compact", "fps_merge"]
+    names = (["score", "select", "compact"] if window else
+             ["fps_compress", "score", "select", "compact", "fps_merge"])
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
 
     def step():
+        calls = {
+            "fps_compress": lambda: bkv.fps_update(shape, buf, count, newq, trigger=32, m=16),
+            "score": lambda: bkv.score(shape, K, kpos, L, None if window else buf, rec, L,
+                                       score, ws=ws),
+            "select": lambda: bkv.select(shape, score, L, B, kept),
+            "compact": lambda: bkv.compact(shape, K, V, kpos, L, kept, B),
+            "fps_merge": lambda: bkv.fps_update(shape, buf, count, rec, trigger=32, m=16),
+        }
         ev[0].record(stream)
-        bkv.fps_update(shape, buf, count, newq, trigger=32, m=16)
-        ev[1].record(stream)
-        bkv.score(shape, K, kpos, L, buf, rec, L, score, ws=ws)
-        ev[2].record(stream)
-        bkv.select(shape, score, L, B, kept)
-        ev[3].record(stream)
-        bkv.compact(shape, K, V, kpos, L, kept, B)
-        ev[4].record(stream)
-        bkv.fps_update(shape, buf, count, rec, trigger=32, m=16)
-        ev[5].record(stream)
+        for j, n in enumerate(names):
+            calls[n]()
+            ev[j + 1].record(stream)
 
     for i in range(args.warmup):
         for fn in (step_evict, step):
@@ -315,7 +334,7 @@ def main():
     ms_step = 1e3 * float(np.mean(wall))
     gpu_ms = {n: float(np.mean(v)) for n, v in stage_ms.items()}
     gpu_step_ms = float(np.mean(gpu_fps_c)) + float(np.mean(gpu_evict))
-    sbytes = stage_bytes(w, n_mv)
+    sbytes = {n: b for n, b in stage_bytes(w, n_mv).items() if n in names}
     total_bytes = sum(sbytes.values())
     flops = 2.0 * U * g * 32 * d * L  # one pass of Q_obs . K^T per unit
 
@@ -344,9 +363,12 @@ def main():
         sample_units = [0, U // 3, U - 1]
         restore()
         torch.cuda.synchronize()
-        bkv.fps_update(shape, buf, count, newq, trigger=32, m=16)
-        beacons = buf[:, :16].cpu().numpy()
-        bkv.score(shape, K, kpos, L, buf, rec, L, score, ws=ws)
+        if window:
+            beacons = np.zeros((U * g, 0, d))
+        else:
+            bkv.fps_update(shape, buf, count, newq, trigger=32, m=16)
+            beacons = buf[:, :16].cpu().numpy()
+        bkv.score(shape, K, kpos, L, None if window else buf, rec, L, score, ws=ws)
         bkv.select(shape, score, L, B, kept)
         torch.cuda.synchronize()
         worst, n_diff = 0.0, 0
@@ -379,10 +401,12 @@ def main():
         "config": {"workload": w.name, "units": U, "layers": w.layers, "batch": w.batch,
                    "kv_heads": w.h_kv, "group": g, "d_head": d, "L": L, "b_kv": B,
                    "prefix": w.prefix, "recent": w.recent_tok, "rope_theta": w.theta,
-                   "pooling": args.aggregate},
+                   "pooling": args.aggregate,
+                   "observation": "recent32" if window else "beacons16+recent16"},
         "unit_evictions_per_s": round(U / (ms_step * 1e-3), 1),
         "steps_per_s": round(1e3 / ms_step, 2),
-        "step": "bkv_fps_update (compress) + bkv_evict",
+        "step": ("bkv_evict (32-query window, no FPS)" if window else
+                 "bkv_fps_update (compress) + bkv_evict"),
         "gpu_ms_per_step": round(gpu_step_ms, 4),
         "gpu_ms_evict": round(float(np.mean(gpu_evict)), 4),
         "gpu_ms_separate_calls": round(sum(gpu_ms.values()), 4),

@@ -73,8 +73,11 @@ typedef struct bkv_dims {
  * budget max 32 / min 16, recent query budget 16; summary step (5): prefix
  * and recent tokens always kept. */
 typedef struct bkv_policy {
-    int32_t n_beacon;   /* beacon rows per query head used for scoring: 16 */
-    int32_t n_recent_q; /* recent queries per query head: 16 */
+    int32_t n_beacon;   /* beacon rows per query head used for scoring: 16, or 0
+                         * with n_recent_q = 32 (no beacons: the window of the 32
+                         * most recent queries the baselines observe, paper
+                         * text §2.2 and §3.2) */
+    int32_t n_recent_q; /* recent queries per query head: 16 (or 32, above) */
     int32_t buf_cap;    /* rows per head in buf (32; up to 256 for prefill) */
     int32_t prefix;     /* P: leading slots always kept */
     int32_t recent_tok; /* R: trailing slots always kept */
@@ -151,6 +154,7 @@ int bkv_fps_update(const bkv_dims* dims, const bkv_policy* pol, float* buf,
  * Writes score[u, 0..L); other slots are untouched.  If qobs_out is non-NULL
  * it receives the bf16 observation rows, [U, g*(n_beacon+n_recent_q), d],
  * row = h*(n_beacon+n_recent_q) + (beacons first, then recents).
+ * beacons may be NULL when n_beacon == 0.
  * Requires n_recent_q <= L <= l_cap, t >= 0,
  * ws_bytes >= bkv_workspace_bytes(dims, pol, L, 0).
  */
@@ -200,6 +204,7 @@ int bkv_compact(const bkv_dims* dims, uint16_t* K, uint16_t* V, int32_t* kpos,
  * queries are appended to each head's buffer (which must hold exactly the
  * n_beacon beacons, count == n_beacon) and the buffer is compressed back to
  * n_beacon rows with FPS.  `beacons` is normally `buf` itself.
+ * With n_beacon == 0 there is no rolling update and buf must be NULL.
  * score_out / kept_out, if non-NULL, receive the scores and kept slots;
  * otherwise they live in the workspace.
  * Requires what the three calls require and

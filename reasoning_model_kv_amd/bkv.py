@@ -205,7 +205,7 @@ def score(shape, K, kpos, L, beacons, recents, t, score_out, qobs_out=None, ws=N
         ws = alloc_workspace(shape, L, 0, K.device)
     _check(lib.bkv_score(
         ctypes.byref(shape.dims()), ctypes.byref(shape.policy()), _bits(K, "K"),
-        _ptr(kpos, torch.int32, "kpos"), int(L), _ptr(beacons, torch.float32, "beacons"),
+        _ptr(kpos, torch.int32, "kpos"), int(L), _ptr(beacons, torch.float32, "beacons", shape.n_beacon == 0),
         _ptr(recents, torch.float32, "recents"), int(t), _ptr(score_out, torch.float32, "score"),
         _bits(qobs_out, "qobs_out", True), _ptr(ws, torch.uint8, "ws"), ws.numel(),
         _stream(stream)))
@@ -252,7 +252,7 @@ def evict(shape, K, V, kpos, L, beacons, recents, t, b_kv, buf=None, count=None,
         ws = alloc_workspace(shape, L, b_kv, K.device)
     _check(lib.bkv_evict(
         ctypes.byref(shape.dims()), ctypes.byref(shape.policy()), _bits(K, "K"), _bits(V, "V"),
-        _ptr(kpos, torch.int32, "kpos"), int(L), _ptr(beacons, torch.float32, "beacons"),
+        _ptr(kpos, torch.int32, "kpos"), int(L), _ptr(beacons, torch.float32, "beacons", shape.n_beacon == 0),
         _ptr(recents, torch.float32, "recents"), int(t), int(b_kv),
         _ptr(buf, torch.float32, "buf", True), _ptr(count, torch.int32, "count", True),
         _ptr(score_out, torch.float32, "score_out", True),

@@ -76,8 +76,11 @@ int check_policy(const char* fn, const bkv_policy* p) {
     if (!p) return fail(BKV_EINVAL, "%s: policy is NULL", fn);
     if ((p->flags & ~BKV_FLAG_MEAN) != 0 || p->reserved != 0)
         return fail(BKV_EINVAL, "%s: unknown policy flags or reserved field not 0", fn);
-    if (p->n_beacon != 16 || p->n_recent_q != 16)
-        return fail(BKV_ENOTSUP, "%s: n_beacon %d / n_recent_q %d: only 16 / 16 supported", fn,
+    // The observation set is 32 rows per query head: 16 beacons + 16 recent
+    // queries (the method), or 32 recent queries (the baselines' window).
+    if (!((p->n_beacon == 16 && p->n_recent_q == 16) || (p->n_beacon == 0 && p->n_recent_q == 32)))
+        return fail(BKV_ENOTSUP,
+                    "%s: n_beacon %d / n_recent_q %d: only 16 / 16 or 0 / 32 supported", fn,
                     p->n_beacon, p->n_recent_q);
     if (p->buf_cap < 1) return fail(BKV_EINVAL, "%s: buf_cap %d < 1", fn, p->buf_cap);
     if (p->buf_cap > 256) return fail(BKV_ENOTSUP, "%s: buf_cap %d > 256", fn, p->buf_cap);
@@ -117,7 +120,7 @@ WsLayout ws_layout(const bkv_dims* d, const bkv_policy* p, int64_t b_kv) {
 int check_score_args(const char* fn, const bkv_dims* d, const bkv_policy* p, const void* K,
                      const void* kpos, int64_t L, const void* beacons, const void* recents,
                      int64_t t) {
-    if (!K || !kpos || !beacons || !recents)
+    if (!K || !kpos || !recents || (!beacons && p->n_beacon > 0))
         return fail(BKV_EINVAL, "%s: NULL tensor pointer", fn);
     if (L < p->n_recent_q || L > d->l_cap)
         return fail(BKV_EINVAL, "%s: L %lld not in [n_recent_q=%d, l_cap=%lld]", fn,
@@ -275,6 +278,8 @@ int bkv_evict(const bkv_dims* dims, const bkv_policy* pol, uint16_t* K, uint16_t
     if (!V) return fail(BKV_EINVAL, "%s: NULL V", fn);
     if ((buf == nullptr) != (count == nullptr))
         return fail(BKV_EINVAL, "%s: buf and count must both be set or both NULL", fn);
+    if (buf && pol->n_beacon == 0)
+        return fail(BKV_EINVAL, "%s: no beacons (n_beacon 0): pass buf = NULL", fn);
     if (buf && pol->buf_cap < pol->n_beacon + pol->n_recent_q)
         return fail(BKV_EINVAL, "%s: buf_cap %d cannot hold beacons + recents", fn,
                     pol->buf_cap);

@@ -120,9 +120,12 @@ __device__ __forceinline__ uint4 rotate4(float4 x1, float4 x2, const double2 (&c
 }
 
 // The rows as loaded: lane = (row sub of each step, pairs 4q .. 4q+3 of
-// the D/2 RoPE pairs (k, k + D/2)).  Loading and rotating are separate
-// steps so that the loads can be in flight together with the first key
-// tiles.
+// the D/2 RoPE pairs (k, k + D/2)).  Observation rows 0..15 come from src1
+// (the beacons, or the first 16 recent queries when the window is 32
+// recent queries) and rows 16..31 from src2 (the last 16 recent queries);
+// each is 16 consecutive rows of D floats.  Loading and rotating are
+// separate steps so that the loads can be in flight together with the
+// first key tiles.
 template <int D>
 struct ObsRows {
     static constexpr int HALF = D / 2;
@@ -131,35 +134,38 @@ struct ObsRows {
     static constexpr int NB = 16 / RPS;   // steps per 16 rows
     float4 bx1[NB], bx2[NB], rx1[NB], rx2[NB];
 
-    __device__ __forceinline__ void load(const ScoreArgs& a, int64_t qh, int lane) {
+    __device__ __forceinline__ void load(const float* src1, const float* src2, int lane) {
         const int q = lane % QPR, sub = lane / QPR;
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
-            const float* src = a.beacons + (qh * a.buf_cap + j * RPS + sub) * (int64_t)D + 4 * q;
+            const float* src = src1 + (j * RPS + sub) * (int64_t)D + 4 * q;
             bx1[j] = *reinterpret_cast<const float4*>(src);
             bx2[j] = *reinterpret_cast<const float4*>(src + HALF);
         }
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
-            const float* src =
-                a.recents + (qh * a.n_recent_q + j * RPS + sub) * (int64_t)D + 4 * q;
+            const float* src = src2 + (j * RPS + sub) * (int64_t)D + 4 * q;
             rx1[j] = *reinterpret_cast<const float4*>(src);
             rx2[j] = *reinterpret_cast<const float4*>(src + HALF);
         }
     }
 
-    // out[j]: beacon row j * RPS + sub; out[NB + j]: recent row (row 16 +)
-    // j * RPS + sub; each as rotate4 returns it.  tab0 ([D/2] double2) and
-    // rtab ([16][D/2]): the cos/sin pairs for t and for the recent rows'
-    // positions, in LDS.
-    __device__ __forceinline__ void rotate(int lane, const double2* tab0, const double2* rtab,
-                                           uint4 (&out)[2 * NB]) const {
+    // out[j]: observation row j * RPS + sub; out[NB + j]: row 16 + j * RPS +
+    // sub; each as rotate4 returns it.  Row r < 16 takes its cos/sin pairs
+    // from tab1[r * stride1 + pair] (stride1 = 0: the beacons' single row for
+    // t), row 16 + r from tab2[r * D/2 + pair]; all in LDS.
+    __device__ __forceinline__ void rotate(int lane, const double2* tab1, int stride1,
+                                           const double2* tab2, uint4 (&out)[2 * NB]) const {
         const int q = lane % QPR, sub = lane / QPR;
         double2 cs[4];
 #pragma unroll
-        for (int p = 0; p < 4; ++p) cs[p] = tab0[4 * q + p];
+        for (int j = 0; j < NB; ++j) {
+            __builtin_amdgcn_sched_barrier(0);
+            const int r = j * RPS + sub;
 #pragma unroll
-        for (int j = 0; j < NB; ++j) out[j] = rotate4(bx1[j], bx2[j], cs);
+            for (int p = 0; p < 4; ++p) cs[p] = tab1[r * stride1 + 4 * q + p];
+            out[j] = rotate4(bx1[j], bx2[j], cs);
+        }
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
             // One row's cos/sin pairs at a time (the scheduler would
@@ -167,31 +173,34 @@ struct ObsRows {
             __builtin_amdgcn_sched_barrier(0);
             const int r = j * RPS + sub;
 #pragma unroll
-            for (int p = 0; p < 4; ++p) cs[p] = rtab[r * HALF + 4 * q + p];
+            for (int p = 0; p < 4; ++p) cs[p] = tab2[r * HALF + 4 * q + p];
             out[NB + j] = rotate4(rx1[j], rx2[j], cs);
         }
     }
 };
 
-// The table holds the cos/sin pairs for positions t-16..t-1; recent rows
-// of the unit at other positions (lane r (mod 16) holds row r's position
-// in rpos) get theirs computed into rtab ([16][D/2] double2, LDS) by the
-// whole workgroup.  Every wavefront of the workgroup sees the same
-// positions, so all take the same branch.  Returns whether any row moved.
+// The table holds the cos/sin pairs for positions t-nrq..t-1 (nrq = 16 or
+// 32 recent queries); recent rows of the unit at other positions (lane r
+// (mod nrq) holds row r's position in rpos) get theirs computed into the
+// LDS copy (rows 0..15 at rtab_lo, rows 16..31 at rtab_hi, [16][D/2]
+// double2 each) by the whole workgroup.  Every wavefront of the workgroup
+// sees the same positions, so all take the same branch.  Returns whether
+// any row moved.
 template <int D>
 __device__ __forceinline__ bool fix_recent_table(const ScoreArgs& a, int64_t u, int32_t rpos,
                                                  int lane, int tid, int nthreads,
-                                                 double2* rtab) {
-    const int32_t first = (int32_t)(a.t - a.n_recent_q);
-    if (__ballot(rpos != first + (lane & 15)) == 0) return false;
-    const int32_t* rp = a.kpos + u * a.l_cap + a.L - a.n_recent_q;
-    for (int e = tid; e < 16 * (D / 2); e += nthreads) {
+                                                 double2* rtab_lo, double2* rtab_hi) {
+    const int nrq = a.n_recent_q;
+    const int32_t first = (int32_t)(a.t - nrq);
+    if (__ballot(rpos != first + (lane & (nrq - 1))) == 0) return false;
+    const int32_t* rp = a.kpos + u * a.l_cap + a.L - nrq;
+    for (int e = tid; e < nrq * (D / 2); e += nthreads) {
         const int r = e / (D / 2), k = e % (D / 2);
         const int32_t pos = rp[r];
         if (pos != first + r) {
             double c, sn;
             rope_cs((double)pos, k, D, a.theta, &c, &sn);
-            rtab[e] = double2{c, sn};
+            (r < 16 ? rtab_lo : rtab_hi)[(r % 16) * (D / 2) + k] = double2{c, sn};
         }
     }
     __syncthreads();
@@ -229,10 +238,14 @@ __global__ __launch_bounds__(256) void zero_scores_kernel(float* score, int64_t 
 // Causal limit of accumulator entry v as an offset from the first recent
 // slot L - nrq: a key at offset d is visible iff d <= limit.  Beacon rows
 // see every live slot (offset nrq - 1 is slot L - 1); recent row i sees
-// slots up to its own, offset i.
+// slots up to its own, offset i.  nrq is 16 (after 16 beacon rows) or 32.
 __device__ __forceinline__ int row_lim(int v, int lane, int nrq) {
     const int r = acc_row(v, lane);
-    return r < 16 ? nrq - 1 : r - 16;
+    // 32 recent rows: row r is recent row r.  16 beacons + 16 recents: the
+    // beacons are rows 0..15, i.e. accumulator entries v < 8 (a compile-time
+    // fact once v is unrolled).
+    if (nrq == 32) return r;
+    return v < 8 ? nrq - 1 : r - 16;
 }
 
 // Maximum of two or three floats as one v_maximum(3)_f32.  The operands are
@@ -385,39 +398,46 @@ void score_kernel(ScoreArgs a, int g, int hs) {
 
     const TileLoad<D, NL> ld(h, lane);
 
-    // Prologue.  The table's cos/sin rows for t-16..t-1 (16 x D/2 pairs of
-    // doubles, one tile buffer's size) go to the third tile buffer and the
-    // row for t to the reduction buffer by direct-to-LDS loads, each
+    // Prologue.  The table's cos/sin rows for the recent positions
+    // t-nrq..t-1 (nrq x D/2 pairs of doubles: one tile buffer per 16 rows)
+    // go to the third tile buffer (and, for 32 recent queries, the second)
+    // and the row for t to the reduction buffer by direct-to-LDS loads, each
     // wavefront loads its head's observation rows, then the loader
-    // wavefronts issue the first two key tiles and wait for everything
-    // older.  The rows are rotated while the tiles are in flight and staged,
-    // two heads at a time, through the third tile buffer, from where each
-    // wavefront reads its MFMA A fragments (lane: row lane % 32, dims
-    // 16 s + 8 (lane / 32) .. + 8 for step s; the same swizzled layout as a
-    // key tile).
+    // wavefronts issue the first key tiles (two, unless the second buffer
+    // holds table rows) and wait for everything older.  The rows are rotated
+    // while the tiles are in flight and staged, two heads at a time, through
+    // the third tile buffer, from where each wavefront reads its MFMA A
+    // fragments (lane: row lane % 32, dims 16 s + 8 (lane / 32) .. + 8 for
+    // step s; the same swizzled layout as a key tile).
     const int64_t qh = u * g + hg;
+    const int nrq = a.n_recent_q;
+    const bool wide = nrq == 32;  // window of 32 recent queries, no beacons
     {
-        constexpr int NI = KT * D * 2 / 1024;  // 1 KB load instructions, rows t-16..t-1
+        constexpr int NIT = KT * D * 2 / 1024;  // 1 KB loads per tile buffer (16 table rows)
         static_assert(D / 2 * 16 <= (int)sizeof(red), "table row for t fits the reduction buffer");
+        const int NI = wide ? 2 * NIT : NIT;
         const char* tab = reinterpret_cast<const char*>(a.table);
         for (int i = h; i <= NI; i += nw) {
             const bool row0 = i == NI;
             const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
                 (void*)(tab + (row0 ? 0 : (D / 2) * 16 + i * 1024)), 0, row0 ? (D / 2) * 16 : 1024,
                 kBufferFlags);
+            uint16_t* dst = (i < NIT ? tile2 : tile1) + (i % NIT) * 512;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rsrc,
-                (__attribute__((address_space(3))) void*)(row0 ? (void*)&red[0][0]
-                                                               : (void*)(tile2 + i * 512)),
+                (__attribute__((address_space(3))) void*)(row0 ? (void*)&red[0][0] : (void*)dst),
                 16, lane * 16, 0, 0, 0);
         }
     }
-    const int32_t rpos = a.kpos[u * a.l_cap + L - a.n_recent_q + (lane & 15)];
+    const int32_t rpos = a.kpos[u * a.l_cap + L - nrq + (lane & (nrq - 1))];
+    const float* src1 = wide ? a.recents + qh * nrq * (int64_t)D
+                             : a.beacons + qh * a.buf_cap * (int64_t)D;
+    const float* src2 = a.recents + (qh * nrq + nrq - 16) * (int64_t)D;
     ObsRows<D> obs;
-    if (active) obs.load(a, qh, lane);
+    if (active) obs.load(src1, src2, lane);
     if (loader) {
         ld.issue(Ku, L, 0, tile0, h);
-        if (1 < ntiles) {
+        if (!wide && 1 < ntiles) {
             ld.issue(Ku, L, KT, tile1, h);
             wait_vm<2 * NPW>();
         } else {
@@ -427,17 +447,22 @@ void score_kernel(ScoreArgs a, int g, int hs) {
         wait_vm<0>();
     }
     __syncthreads();  // the cos/sin rows have landed
-    if (fix_recent_table<D>(a, u, rpos, lane, tid, 64 * nw, reinterpret_cast<double2*>(tile2))) {
+    double2* rtab_lo = reinterpret_cast<double2*>(tile2);
+    double2* rtab_hi = reinterpret_cast<double2*>(tile1);
+    if (fix_recent_table<D>(a, u, rpos, lane, tid, 64 * nw, rtab_lo, rtab_hi)) {
         // Rare path: the rows are loaded again, so that their first copy is
         // dead while the cos/sin pairs are computed and its registers free.
-        if (active) obs.load(a, qh, lane);
+        if (active) obs.load(src1, src2, lane);
     }
     bf16x8 frag[D / 16];
     {
         uint4 rows[2 * ObsRows<D>::NB];
-        if (active)
-            obs.rotate(lane, reinterpret_cast<const double2*>(&red[0][0]),
-                       reinterpret_cast<const double2*>(tile2), rows);
+        if (active) {
+            // Rows 0..15: the beacons' row for t, or recent rows 0..15; rows
+            // 16..31: the last 16 recent rows.
+            const double2* tab1 = wide ? rtab_lo : reinterpret_cast<const double2*>(&red[0][0]);
+            obs.rotate(lane, tab1, wide ? D / 2 : 0, wide ? rtab_hi : rtab_lo, rows);
+        }
         // The rotated words pass through an empty asm before the barrier, so
         // the arithmetic stays ahead of it (sunk past it, it would keep every
         // cos/sin pair read before the barrier in registers at once).
@@ -473,6 +498,10 @@ void score_kernel(ScoreArgs a, int g, int hs) {
             __syncthreads();
         }
     }
+
+    // With 32 recent queries the second tile buffer held table rows: its key
+    // tile is issued now.
+    if (loader && wide && 1 < ntiles) ld.issue(Ku, L, KT, tile1, h);
 
     // Per-lane LDS offsets of the key tiles' B operands, formed after the
     // prologue (from a fresh copy of the lane index) so that they do not
@@ -528,7 +557,8 @@ void score_kernel(ScoreArgs a, int g, int hs) {
 #define BKV_PASS1                                                                  \
     if (active) {                                                                  \
     if (base + KT > mask_from) {                                                   \
-        const int ln = lane;                                                       \
+        int ln = lane; /* fresh copy: the limits are not hoisted */                \
+        asm volatile("" : "+v"(ln));                                              \
         const int d0 = (int)(base - mask_from) + (ln & 31), d1 = d0 + 32;          \
         _Pragma("unroll") for (int v = 0; v < 16; ++v) {                           \
             const int lim = row_lim(v, ln, a.n_recent_q);                          \
@@ -594,7 +624,8 @@ void score_kernel(ScoreArgs a, int g, int hs) {
 #define BKV_PASS2_MAX                                                              \
     float c0 = -__builtin_inff(), c1 = -__builtin_inff();                          \
     if (base + KT > mask_from) {                                                   \
-        const int ln = lane;                                                       \
+        int ln = lane; /* fresh copy: the limits are not hoisted */                \
+        asm volatile("" : "+v"(ln));                                              \
         const int d0 = (int)(base - mask_from) + (ln & 31), d1 = d0 + 32;          \
         _Pragma("unroll") for (int v = 0; v < 16; ++v) {                           \
             const int lim = row_lim(v, ln, a.n_recent_q);                          \
@@ -637,7 +668,8 @@ void score_kernel(ScoreArgs a, int g, int hs) {
 #define BKV_PASS2_MEAN                                                             \
     float c0 = 0.f, c1 = 0.f;                                                      \
     if (base + KT > mask_from) {                                                   \
-        const int ln = lane;                                                       \
+        int ln = lane; /* fresh copy: the limits are not hoisted */                \
+        asm volatile("" : "+v"(ln));                                              \
         const int d0 = (int)(base - mask_from) + (ln & 31), d1 = d0 + 32;          \
         _Pragma("unroll") for (int v = 0; v < 16; ++v) {                           \
             const int lim = row_lim(v, ln, a.n_recent_q);                          \

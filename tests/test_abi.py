@@ -54,6 +54,8 @@ def test_score_validation(lib):
     assert _call_score(lib, _shape(group=9)) == bkv.BKV_ENOTSUP
     assert _call_score(lib, _shape(group=0)) == bkv.BKV_EINVAL
     assert _call_score(lib, _shape(n_beacon=8)) == bkv.BKV_ENOTSUP
+    assert _call_score(lib, _shape(n_beacon=0)) == bkv.BKV_ENOTSUP    # 0 beacons needs 32 recents
+    assert _call_score(lib, _shape(n_units=0, n_beacon=0, n_recent_q=32)) == bkv.BKV_OK
     assert _call_score(lib, _shape(rope_theta=0.0)) == bkv.BKV_EINVAL
     bad_flags = _shape()
     pol = bad_flags.policy()
@@ -127,6 +129,12 @@ def test_evict_validation_and_workspace(lib):
         2176, 2048, buf, count, None, None, FAKE, ws_bytes, None)
     assert call(need - 1) == bkv.BKV_ENOSPC
     assert call(need, buf=FAKE) == bkv.BKV_EINVAL      # buf without count
+    w32 = _shape(l_cap=2176, n_beacon=0, n_recent_q=32, recent_tok=32)
+    need32 = bkv.workspace_bytes(w32, 2176, 2048)
+    assert lib.bkv_evict(ctypes.byref(w32.dims()), ctypes.byref(w32.policy()), FAKE, FAKE, FAKE,
+                         2176, None, FAKE, 2176, 2048, FAKE, FAKE, None, None, FAKE, need32,
+                         None) == bkv.BKV_EINVAL            # no beacons: no rolling update
+    assert "buf" in bkv.last_error()
     with pytest.raises(bkv.BkvError):
         bkv.workspace_bytes(s, 2176, 2176)
 

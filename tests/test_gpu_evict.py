@@ -128,6 +128,55 @@ def test_evict_mean_pooling(name, samples):
     log(f"  max score rel err {worst:.3g}; kept-set tie-band differences {ndiff}")
 
 
+@pytest.mark.parametrize("name,samples", [
+    ("tiny", None),
+    ("qwen3_4b_layer", None),
+    ("r1_qwen_7b", [0, 1791, 3583]),
+])
+def test_evict_recent_window(name, samples):
+    """The baselines' observation set (32 most recent queries, no beacons, the
+    last 32 tokens kept): score, select and compact, no rolling update."""
+    w = synth.shrink(synth.WORKLOADS[name], n_beacon=0, n_recent_q=32, recent_tok=32)
+    log(f"evict 32-query window {name}: U={w.n_units} g={w.group} L={w.L} B={w.b_kv}")
+    if samples is None:
+        inp = synth.workload_inputs(w)
+        dev = synth.to_device(inp, DEV)
+        samples = list(range(w.n_units))
+        host = {u: {k: inp[k][u] for k in ("keys", "values", "kpos", "recents")}
+                for u in samples}
+    else:
+        dev = synth.device_inputs(w, DEV)
+        host = {u: {"keys": dev["keys"][u].float().cpu().numpy(),
+                    "values": dev["values"][u].float().cpu().numpy(),
+                    "kpos": dev["kpos"][u].cpu().numpy(),
+                    "recents": dev["recents"][u * w.group:(u + 1) * w.group].cpu().numpy()}
+                for u in samples}
+    shape = bkv.Shape(w.n_units, w.group, w.d_head, w.L, w.prefix, w.theta, recent_tok=32,
+                      n_beacon=0, n_recent_q=32)
+    score = torch.zeros((w.n_units, w.L), device=DEV)
+    kept = torch.zeros((w.n_units, w.b_kv), dtype=torch.int32, device=DEV)
+    K0, V0, P0 = dev["keys"].clone(), dev["values"].clone(), dev["kpos"].clone()
+    bkv.evict(shape, dev["keys"], dev["values"], dev["kpos"], w.L, None, dev["recents"],
+              dev["t"], w.b_kv, score_out=score, kept_out=kept)
+    torch.cuda.synchronize()
+    _all_unit_properties(w, kept)
+    worst, ndiff = 0.0, 0
+    for u in samples:
+        hu = host[u]
+        ref = oracle.evict.evict_unit(hu["keys"], hu["values"], hu["kpos"], w.L,
+                                      np.zeros((w.group, 0, w.d_head)), hu["recents"], w.L,
+                                      w.b_kv, w.prefix, 32, w.theta, merge=False)
+        worst = max(worst, check_scores(score[u].cpu().numpy(), ref["score"], f"{name} {u}"))
+        ku = kept[u].cpu().numpy()
+        ndiff += check_kept(ku, ref["score"], w.L, w.b_kv, w.prefix, 32, f"{name} {u}")
+        k16 = K0[u].view(torch.int16).cpu().numpy()
+        assert np.array_equal(dev["keys"][u, :w.b_kv].view(torch.int16).cpu().numpy(), k16[ku])
+        v16 = V0[u].view(torch.int16).cpu().numpy()
+        assert np.array_equal(dev["values"][u, :w.b_kv].view(torch.int16).cpu().numpy(), v16[ku])
+        assert np.array_equal(dev["kpos"][u, :w.b_kv].cpu().numpy(), P0[u].cpu().numpy()[ku])
+    log(f"  max score rel err {worst:.3g}; kept-set tie-band differences {ndiff}")
+
+
 def _all_unit_properties(w, kept):
     P, R, L = w.prefix, w.recent_tok, w.L
     assert torch.all(kept[:, 1:] > kept[:, :-1])

@@ -40,10 +40,12 @@ def _run(w, L=None, l_cap=None, t=None, kpos_offset=0, shift_first_recents=0, ag
     t = t if t is not None else L + kpos_offset
     dev = synth.to_device(inp, DEV, l_cap=l_cap)
     shape = bkv.Shape(w.n_units, w.group, w.d_head, l_cap, w.prefix, w.theta,
+                      recent_tok=w.recent_tok, n_beacon=w.n_beacon, n_recent_q=w.n_recent_q,
                       aggregate=aggregate)
     score = torch.full((w.n_units, l_cap), -1.0, device=DEV)
     qobs = torch.zeros((w.n_units, w.group * 32, w.d_head), dtype=torch.bfloat16, device=DEV)
-    bkv.score(shape, dev["keys"], dev["kpos"], L, dev["buf"], dev["recents"], t, score, qobs)
+    beacons = dev["buf"] if w.n_beacon else None
+    bkv.score(shape, dev["keys"], dev["kpos"], L, beacons, dev["recents"], t, score, qobs)
     torch.cuda.synchronize()
     return inp, score.cpu().numpy(), qobs.cpu(), t
 
@@ -119,3 +121,53 @@ def test_score_mean_pooling_matches_oracle(name, L, l_cap):
         if sc.shape[1] > L:
             assert np.all(sc[u, L:] == -1.0), "slots past L must be untouched"
     log(f"  max rel err {worst:.3g}")
+
+
+def _window(w):
+    """The baselines' observation set: the 32 most recent queries, no beacons."""
+    return synth.shrink(w, n_beacon=0, n_recent_q=32, recent_tok=32)
+
+
+WINDOW_CASES = [
+    ("tiny", None, None, 0),          # 4 tiles
+    ("tiny", 203, 256, 0),            # ragged tail, l_cap > L
+    ("tiny", 40, 64, 0),              # one tile: 32 recent rows masked inside it
+    ("tiny", 517, 600, 0),            # 5-key last tile
+    ("tiny", 300, 300, 37),           # positions != t-32+i: direct RoPE path, all rows
+    ("tiny", 300, 300, "partial"),    # rows 0..7 moved
+    ("tiny_g7", 300, 320, 0),         # group 7 (two workgroups per unit)
+    ("tiny_g5", 1000, 1000, 0),       # group 5
+    ("qwen3_4b_layer", None, None, 0),
+]
+
+
+@pytest.mark.parametrize("aggregate", ["max", "mean"])
+@pytest.mark.parametrize("name,L,l_cap,t_shift", WINDOW_CASES)
+def test_score_recent_window_matches_oracle(name, L, l_cap, t_shift, aggregate):
+    w = _window(_workload(name))
+    log(f"score 32-query window {name} L={L or w.L} l_cap={l_cap} t_shift={t_shift} "
+        f"{aggregate}")
+    if t_shift == "partial":
+        inp, sc, qobs, t = _run(w, L, l_cap, shift_first_recents=3, aggregate=aggregate)
+    else:
+        inp, sc, qobs, t = _run(w, L, l_cap, None if not t_shift else (L or w.L) + t_shift,
+                                aggregate=aggregate)
+    L = L or w.L
+    worst, flips = 0.0, 0
+    for u in range(w.n_units):
+        none = np.zeros((w.group, 0, w.d_head))
+        taus = inp["kpos"][u][L - 32:L]
+        ref, qhat, _, _ = oracle.score.score_unit(inp["keys"][u], none, inp["recents"][u], t,
+                                                  taus, w.theta, return_all=True,
+                                                  aggregate=aggregate)
+        worst = max(worst, check_scores(sc[u, :L], ref, f"{name} unit {u}"))
+        if sc.shape[1] > L:
+            assert np.all(sc[u, L:] == -1.0), "slots past L must be untouched"
+        got_q = qobs[u].float().numpy().reshape(w.group, 32, w.d_head)
+        neq = got_q != qhat
+        flips += int(neq.sum())
+        if neq.any():
+            ulp = np.abs(qhat[neq]) * 2.0 ** -7
+            assert np.all(np.abs(got_q[neq] - qhat[neq]) <= ulp)
+    assert flips <= 1e-4 * qobs.numel()
+    log(f"  max rel err {worst:.3g}, bf16 rounding flips {flips}")

@@ -19,6 +19,12 @@ Readings: positions are 0-based and the next token's position is t; the
 query of the token that brings the cache to B_max - n_recent still goes to
 the buffer; the cache is trimmed to the workload's B_KV (the pages' 7/8
 rule is one choice of B_KV).
+
+``beacons="initial"`` is the Initial+Recent comparison of paper text §5.3
+(Table 3): the historical reference set is the first n_beacon queries
+generated after the prompt, kept as they are for the whole run (no FPS, no
+merge); everything else -- recents, scoring with the references rotated to
+t, selection, compaction -- is unchanged.
 """
 
 import numpy as np
@@ -31,7 +37,10 @@ class UnitStream:
     """Exact per-unit replay of the decode-time policy (slow; small units)."""
 
     def __init__(self, g, d, b_max, b_kv, prefix, theta, recent_tok=16,
-                 n_recent_q=16, buf_min=16, buf_max=32):
+                 n_recent_q=16, buf_min=16, buf_max=32, beacons="fps"):
+        if beacons not in ("fps", "initial"):
+            raise ValueError(f"beacons must be 'fps' or 'initial', not {beacons!r}")
+        self.policy = beacons
         self.g, self.d = g, d
         self.b_max, self.b_kv, self.prefix = b_max, b_kv, prefix
         self.theta, self.recent_tok = theta, recent_tok
@@ -52,6 +61,9 @@ class UnitStream:
         self.values = np.asarray(values, np.float64).copy()
         self.kpos = np.arange(p, dtype=np.int64)
         self.t = p
+        if self.policy == "initial":  # references come from the generation
+            self.events.append(("prefill", p))
+            return
         for h in range(self.g):
             _, keep = fps(queries[h], self.buf_min)
             self.buf[h] = np.asarray(queries[h], np.float64)[keep]
@@ -69,6 +81,24 @@ class UnitStream:
         self.values = np.vstack([self.values, np.asarray(v, np.float64)[None]])
         self.kpos = np.append(self.kpos, self.t)
         L = self.keys.shape[0]
+        if self.policy == "initial":
+            if self.phase == "collect":
+                if self.buf[0].shape[0] < self.buf_min:
+                    for h in range(self.g):
+                        self.buf[h] = np.vstack([self.buf[h],
+                                                 np.asarray(q[h], np.float64)[None]])
+                    if self.buf[0].shape[0] == self.buf_min:
+                        self.events.append(("initial_set", L))
+                if L == self.b_max - self.n_recent_q:
+                    self.events.append(("recent_start", L))
+                    self.phase = "recent"
+            else:
+                for h in range(self.g):
+                    self.recents[h].append(np.asarray(q[h], np.float64))
+            self.t += 1
+            if L == self.b_max:
+                self._evict()
+            return
         if self.phase == "collect":
             for h in range(self.g):
                 self.buf[h] = np.vstack([self.buf[h], np.asarray(q[h], np.float64)[None]])
@@ -91,15 +121,18 @@ class UnitStream:
         L = self.keys.shape[0]
         beacons = np.stack(self.buf)
         recents = np.stack([np.stack(r) for r in self.recents])
+        initial = self.policy == "initial"
         out = evict_unit(self.keys, self.values, self.kpos, L, beacons, recents,
                          self.t, self.b_kv, self.prefix, self.recent_tok,
-                         self.theta, n_min=self.buf_min)
+                         self.theta, n_min=self.buf_min, merge=not initial)
         self.keys, self.values, self.kpos = out["keys"], out["values"], out["kpos"]
-        self.buf = [out["buf"][h] for h in range(self.g)]
+        if not initial:
+            self.buf = [out["buf"][h] for h in range(self.g)]
         self.recents = [[] for _ in range(self.g)]
         self.phase = "collect"
         self.events.append(("evict", L))
-        self.events.append(("merge_fps", self.keys.shape[0]))
+        if not initial:
+            self.events.append(("merge_fps", self.keys.shape[0]))
         self.last_evict = out
         return out
 

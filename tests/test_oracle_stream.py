@@ -61,3 +61,46 @@ def test_evict_unit_invariants_and_merge():
     assert np.array_equal(out["keys"], keys[kept])
     assert out["buf"].shape == (g, 16, d)
     assert 0 <= moved_tokens(kept) <= b - P
+
+
+def test_initial_recent_policy_keeps_the_first_generated_queries():
+    # Initial+Recent (paper text §5.3, Table 3): the reference rows are the
+    # first 16 queries generated after the prompt, unchanged by evictions;
+    # the recents are the last 16 queries before each eviction, and the
+    # eviction scores with exactly those two sets.
+    g, d, b_kv, P = 2, 8, 64, 4
+    st = UnitStream(g, d, b_max=b_kv + 128, b_kv=b_kv, prefix=P, theta=1e4, beacons="initial")
+    r = np.random.default_rng(5)
+    st.prefill(r.standard_normal((P, d)), r.standard_normal((P, d)),
+               r.standard_normal((g, P, d)))
+    qs = []
+    first = (b_kv + 128) - P
+    for _ in range(first + 128 + 5):
+        k, v, q = r.standard_normal(d), r.standard_normal(d), r.standard_normal((g, d))
+        qs.append(q)
+        if len(qs) == first:  # about to evict: check what it will score with
+            pre = (st.keys.copy(), st.values.copy(), st.kpos.copy(), st.t)
+        st.step(k, v, q)
+        if len(qs) == first:
+            keys, vals, kpos, t = pre
+            keys = np.vstack([keys, k[None]])
+            vals = np.vstack([vals, v[None]])
+            kpos = np.append(kpos, t)
+            beacons = np.stack([np.stack([qs[i][h] for i in range(16)]) for h in range(g)])
+            recents = np.stack([np.stack([qs[i][h] for i in range(first - 16, first)])
+                                for h in range(g)])
+            ref = evict_unit(keys, vals, kpos, b_kv + 128, beacons, recents, t + 1, b_kv, P,
+                             16, 1e4, merge=False)
+            assert np.array_equal(st.last_evict["kept"], ref["kept"])
+            assert np.array_equal(st.last_evict["score"], ref["score"])
+    want = np.stack([np.stack([qs[i][h] for i in range(16)]) for h in range(g)])
+    assert np.array_equal(np.stack(st.buf), want)
+    ev = [e for e, _ in st.events]
+    assert ev.count("evict") == 2 and "merge_fps" not in ev and "collect_fps" not in ev
+    assert ev[:2] == ["prefill", "initial_set"] and ev.count("recent_start") == 2
+    try:
+        UnitStream(g, d, 192, 64, P, 1e4, beacons="random")
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("unknown beacon policy must be rejected")

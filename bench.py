@@ -62,6 +62,9 @@ def parse():
                    help="observation set: the method's 16 beacons + 16 recent queries, or the "
                         "baselines' 32 most recent queries (no beacons, no FPS, 32 recent "
                         "tokens kept)")
+    p.add_argument("--beacon-policy", choices=("fps", "initial"), default="fps",
+                   help="streaming workloads: the method's Continual FPS, or the Initial+Recent "
+                        "comparison (the first 16 generated queries as fixed references)")
     p.add_argument("--stream-steps", type=int, default=0,
                    help="decode steps of a streaming workload (0: the workload's own)")
     return p.parse_args()
@@ -451,7 +454,8 @@ def stream_main(args, w):
             e.record(cs)
             ev_marks.append(e)
 
-    st = bstream.Stream(U, g, d, w.L, w.b_kv, w.prefix, w.theta, device=dev, observer=observer)
+    st = bstream.Stream(U, g, d, w.L, w.b_kv, w.prefix, w.theta, device=dev, observer=observer,
+                        beacon_policy=args.beacon_policy)
     gen = synth.StreamInputs(w, dev)
     st.prefill(*gen.prompt())
     torch.cuda.synchronize()
@@ -506,7 +510,9 @@ def stream_main(args, w):
         "data": "synthetic",
         "config": {"workload": w.name, "units": U, "layers": w.layers, "batch": w.batch,
                    "kv_heads": w.h_kv, "group": g, "d_head": d, "B_max": L, "b_kv": w.b_kv,
-                   "prefix": w.prefix, "recent": w.recent_tok, "rope_theta": w.theta},
+                   "prefix": w.prefix, "recent": w.recent_tok, "rope_theta": w.theta,
+                   "beacons": "continual FPS" if args.beacon_policy == "fps" else
+                              "first 16 generated queries (Initial+Recent)"},
         "evictions": n_ev,
         "evict_ms_mean": round(mean_ev, 4),
         "evict_hbm_frac": round(ev_bytes / (mean_ev * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),

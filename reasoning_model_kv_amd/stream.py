@@ -14,6 +14,11 @@ call covers all units at each point of the policy:
 4.-6. when the cache reaches B_max, bkv_evict scores, selects and compacts
    the cache to B_KV and merges beacons and recents back to 16 rows.
 
+With beacon_policy="initial" (the Initial+Recent comparison, paper text
+§5.3 and Table 3) the reference rows are instead the first 16 queries
+generated after the prompt, appended and then left alone: no FPS at any
+point and no merge after an eviction.
+
 Writing the new token's key, value and position into the cache is the
 decoder's own work and is done here with plain tensor writes; every step of
 the policy runs in the library.  An optional observer is called with
@@ -29,9 +34,12 @@ from . import bkv
 
 class Stream:
     def __init__(self, n_units, group, d_head, b_max, b_kv, prefix, theta, recent_tok=16,
-                 device="cuda", observer=None):
+                 device="cuda", observer=None, beacon_policy="fps"):
         if b_max - b_kv < recent_tok or b_kv < prefix + recent_tok:
             raise ValueError("need prefix + recent_tok <= b_kv <= b_max - recent_tok")
+        if beacon_policy not in ("fps", "initial"):
+            raise ValueError(f"beacon_policy must be 'fps' or 'initial', not {beacon_policy!r}")
+        self.policy = beacon_policy
         dev = torch.device(device)
         self.shape = bkv.Shape(n_units, group, d_head, b_max, prefix, theta,
                                recent_tok=recent_tok)
@@ -71,6 +79,14 @@ class Stream:
         self.V[:, :P] = values
         self.kpos[:, :P] = torch.arange(P, dtype=torch.int32, device=self.K.device)
         self.L = self.t = P
+        if self.policy == "initial":  # the references come from the generation
+            if self.b_max - self.recent_tok - P < 16:
+                raise ValueError("prompt too long: 16 generated queries must precede the "
+                                 "recent window")
+            self.count.zero_()
+            self.rows = 0
+            self.events.append(("prefill", P))
+            return
         pshape = replace(self.shape, buf_cap=P)
         qbuf = queries.contiguous().clone()
         pcount = torch.full_like(self.count, P)
@@ -91,7 +107,9 @@ class Stream:
         self.V[:, L] = v
         self.kpos[:, L] = self.t
         self.L = L = L + 1
-        if self.phase == "collect":
+        if self.policy == "initial":
+            self._step_initial(q, L)
+        elif self.phase == "collect":
             compress = self.rows + 1 >= 32
             if compress:
                 self._note("collect_fps", "pre")
@@ -124,16 +142,36 @@ class Stream:
         if L == self.b_max:
             self._evict()
 
+    def _step_initial(self, q, L):
+        if self.phase == "collect":
+            if self.rows < 16:  # one of the first 16 generated queries: append only
+                bkv.fps_update(self.shape, self.buf, self.count, q[:, None],
+                               trigger=self.shape.buf_cap + 1, m=16)
+                self.rows += 1
+                if self.rows == 16:
+                    self.events.append(("initial_set", L))
+            if L == self.b_max - self.recent_tok:
+                self.events.append(("recent_start", L))
+                self.phase = "recent"
+                self.rcount.zero_()
+        else:
+            bkv.fps_update(self.rshape, self.recents, self.rcount, q[:, None],
+                           trigger=self.rshape.buf_cap + 1, m=16)
+
     def _evict(self):
         L = self.L
+        initial = self.policy == "initial"
         self._note("evict", "pre")
         bkv.evict(self.shape, self.K, self.V, self.kpos, L, self.buf, self.recents, self.t,
-                  self.b_kv, buf=self.buf, count=self.count, score_out=self.score,
+                  self.b_kv, buf=None if initial else self.buf,
+                  count=None if initial else self.count, score_out=self.score,
                   kept_out=self.kept, ws=self.ws)
         self.L = self.b_kv
-        self.rows = 16
+        if not initial:
+            self.rows = 16
         self.phase = "collect"
         self.n_evictions += 1
         self.events.append(("evict", L))
-        self.events.append(("merge_fps", self.b_kv))
+        if not initial:
+            self.events.append(("merge_fps", self.b_kv))
         self._note("evict", "post")

@@ -6,7 +6,8 @@ checked on the GPU's own state just before it ("lockstep with resync"): each
 FPS compression by replaying its pick order in float64; each eviction by the
 oracle's scores and kept set on the pre-eviction cache, exact compaction
 with the GPU's kept set, and the merged buffer.  Small run: every unit and
-head.  Qwen3-14B shape (40 layers x batch 16 x 8 KV heads, group 5): the
+head, under the method's Continual FPS and under the Initial+Recent
+comparison (the first 16 generated queries as fixed references).  Qwen3-14B shape (40 layers x batch 16 x 8 KV heads, group 5): the
 first two eviction intervals on sampled units and heads.
 """
 import numpy as np
@@ -25,8 +26,8 @@ DEV = "cuda"
 class Checker:
     """Observer: snapshots sampled state before each event, checks after."""
 
-    def __init__(self, w, units):
-        self.w, self.units = w, list(units)
+    def __init__(self, w, units, policy="fps"):
+        self.w, self.units, self.policy = w, list(units), policy
         self.heads = [u * w.group + h for u in self.units for h in range(w.group)]
         self.pre = None
         self.n = {"fps": 0, "evict": 0, "exact_fps": 0}
@@ -70,15 +71,19 @@ class Checker:
         merged_out = st.buf[hi, :16].cpu().numpy()
         for i, u in enumerate(self.units):
             hs = slice(i * g, (i + 1) * g)
+            initial = self.policy == "initial"
             ref = oracle.evict.evict_unit(pre["K"][i], pre["V"][i], pre["P"][i], L,
                                           pre["beacons"][hs], pre["recents"][hs], pre["t"], b,
-                                          w.prefix, w.recent_tok, w.theta)
+                                          w.prefix, w.recent_tok, w.theta, merge=not initial)
             where = f"evict at L={L} unit {u}"
             self.worst = max(self.worst, check_scores(sc[i, :L], ref["score"], where))
             check_kept(kept[i], ref["score"], L, b, w.prefix, w.recent_tok, where)
             assert np.array_equal(K1[i, :b], pre["K"][i][kept[i]]), where + " K"
             assert np.array_equal(V1[i, :b], pre["V"][i][kept[i]]), where + " V"
             assert np.array_equal(P1[i, :b], pre["P"][i][kept[i]]), where + " kpos"
+            if initial:  # no merge: the reference rows stay as they were
+                assert np.array_equal(merged_out[hs], pre["beacons"][hs]), where + " refs"
+                continue
             for h in range(g):
                 merged = np.concatenate([pre["beacons"][i * g + h], pre["recents"][i * g + h]])
                 out = merged_out[i * g + h]
@@ -90,9 +95,9 @@ class Checker:
         self.n["evict"] += 1
 
 
-def _oracle_events(w, n_steps):
+def _oracle_events(w, n_steps, policy="fps"):
     """Event cadence of the oracle state machine (values do not affect it)."""
-    st = oracle.stream.UnitStream(1, 4, w.L, w.b_kv, w.prefix, w.theta)
+    st = oracle.stream.UnitStream(1, 4, w.L, w.b_kv, w.prefix, w.theta, beacons=policy)
     r = np.random.default_rng(0)
     st.prefill(r.standard_normal((w.prefix, 4)), r.standard_normal((w.prefix, 4)),
                r.standard_normal((1, w.prefix, 4)))
@@ -101,10 +106,10 @@ def _oracle_events(w, n_steps):
     return st.events
 
 
-def _run(w, n_steps, units, chunk=128):
-    chk = Checker(w, units)
+def _run(w, n_steps, units, chunk=128, policy="fps"):
+    chk = Checker(w, units, policy)
     st = bstream.Stream(w.n_units, w.group, w.d_head, w.L, w.b_kv, w.prefix, w.theta,
-                        device=DEV, observer=chk)
+                        device=DEV, observer=chk, beacon_policy=policy)
     gen = synth.StreamInputs(w, DEV)
     st.prefill(*gen.prompt())
     done = 0
@@ -144,3 +149,15 @@ def test_stream_qwen3_14b_two_intervals_sampled():
     assert torch.all(st.count == 16 + 40 % 16)
     log(f"  FPS events {chk.n['fps']}, exact FPS sets {chk.n['exact_fps']}, "
         f"max score rel err {chk.worst:.3g}")
+
+
+def test_stream_small_initial_recent_all_units():
+    """Initial+Recent: the first 16 generated queries are the references."""
+    w = synth.WORKLOADS["stream_small"]
+    n = w.stream_steps
+    log(f"stream {w.name} (Initial+Recent): U={w.n_units} g={w.group} steps={n}")
+    st, chk = _run(w, n, range(w.n_units), policy="initial")
+    assert st.events == _oracle_events(w, n, "initial")
+    assert chk.n["evict"] == st.n_evictions >= 2 and chk.n["fps"] == 0
+    assert torch.all(st.count == 16)
+    log(f"  evictions {st.n_evictions}, max score rel err {chk.worst:.3g}")

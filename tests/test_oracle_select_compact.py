@@ -58,3 +58,41 @@ def test_compact_matches_loop():
         assert np.array_equal(k2[i], k[j]) and np.array_equal(v2[i], v[j])
         assert p2[i] == kpos[j]
     assert np.all(np.diff(p2) > 0)
+
+
+def test_fill_holes_hand_example():
+    # b_kv = 5 of L = 8 slots, kept = [0, 2, 3, 6, 7]: the holes below 5 are
+    # slots 1 and 4, the kept slots at or past 5 are 6 and 7, so slot 1
+    # takes token 6 and slot 4 takes token 7; slots 0, 2, 3 stay.
+    from oracle.compact import fill_holes
+    keys = np.arange(8.0)[:, None] * np.ones((1, 2))
+    kpos = np.arange(100, 108)
+    k, v, p, moves = fill_holes(keys, -keys, kpos, [0, 2, 3, 6, 7], 5)
+    assert moves == [(1, 6), (4, 7)]
+    assert k[:, 0].tolist() == [0, 6, 2, 3, 7]
+    assert v[:, 0].tolist() == [0, -6, -2, -3, -7]
+    assert p.tolist() == [100, 106, 102, 103, 107]
+
+
+def test_fill_holes_is_a_permutation_of_the_sorted_compaction():
+    # Same kept rows, any order: sorting the output by position gives the
+    # position-ordered compaction; kept slots below b_kv never move; every
+    # move goes from a slot >= b_kv to an evicted slot < b_kv.
+    from oracle.compact import compact, fill_holes
+    from oracle.select import select
+    r = np.random.default_rng(11)
+    for L, b in ((300, 200), (256, 128), (97, 96), (64, 16)):
+        keys = r.standard_normal((L, 4))
+        vals = r.standard_normal((L, 4))
+        kpos = np.arange(L) * 3 + 5
+        sc = r.random(L)
+        kept = select(sc, L, b, 4, 8)
+        k, v, p, moves = fill_holes(keys, vals, kpos, kept, b)
+        ks, vs, ps = compact(keys, vals, kpos, kept)
+        order = np.argsort(p)
+        assert np.array_equal(p[order], ps) and np.array_equal(k[order], ks)
+        assert np.array_equal(v[order], vs)
+        stay = [j for j in kept if j < b]
+        assert np.array_equal(k[stay], keys[stay])
+        assert len(moves) == sum(1 for j in kept if j >= b)
+        assert all(s >= b > h and h not in set(kept.tolist()) for h, s in moves)

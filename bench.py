@@ -62,6 +62,9 @@ def parse():
                    help="observation set: the method's 16 beacons + 16 recent queries, or the "
                         "baselines' 32 most recent queries (no beacons, no FPS, 32 recent "
                         "tokens kept)")
+    p.add_argument("--compaction", choices=("sorted", "unsorted"), default="sorted",
+                   help="position-ordered compaction (the method), or the unsorted variant "
+                        "that fills the evicted slots with the kept tokens past B_KV")
     p.add_argument("--beacon-policy", choices=("fps", "initial"), default="fps",
                    help="streaming workloads: the method's Continual FPS, or the Initial+Recent "
                         "comparison (the first 16 generated queries as fixed references)")
@@ -251,7 +254,8 @@ def main():
     kept = torch.empty((U, B), dtype=torch.int32, device=dev)
     scrub = torch.empty(512 * 2**20 // 4, dtype=torch.float32, device=dev)
     shape = bkv.Shape(U, g, d, L, w.prefix, w.theta, recent_tok=w.recent_tok,
-                      n_beacon=w.n_beacon, n_recent_q=w.n_recent_q, aggregate=args.aggregate)
+                      n_beacon=w.n_beacon, n_recent_q=w.n_recent_q, aggregate=args.aggregate,
+                      unsorted=args.compaction == "unsorted")
     ws = bkv.alloc_workspace(shape, L, 0, dev)
     stream = torch.cuda.current_stream()
 
@@ -293,7 +297,8 @@ def main():
             "score": lambda: bkv.score(shape, K, kpos, L, None if window else buf, rec, L,
                                        score, ws=ws),
             "select": lambda: bkv.select(shape, score, L, B, kept),
-            "compact": lambda: bkv.compact(shape, K, V, kpos, L, kept, B),
+            "compact": lambda: (bkv.compact_unsorted(shape, K, V, kpos, L, kept, B)
+                                if shape.unsorted else bkv.compact(shape, K, V, kpos, L, kept, B)),
             "fps_merge": lambda: bkv.fps_update(shape, buf, count, rec, trigger=32, m=16),
         }
         ev[0].record(stream)
@@ -311,7 +316,10 @@ def main():
 
     # Moved tokens of this (deterministic) eviction, for the compaction bytes.
     kept_host = kept.cpu().numpy()
-    n_mv = int(np.count_nonzero(kept_host != np.arange(B)[None, :]))
+    if shape.unsorted:  # only the kept tokens past B_KV move
+        n_mv = int(np.count_nonzero(kept_host >= B))
+    else:
+        n_mv = int(np.count_nonzero(kept_host != np.arange(B)[None, :]))
 
     wall, gpu_evict, gpu_fps_c = [], [], []
     for i in range(args.steps):
@@ -404,7 +412,7 @@ def main():
         "config": {"workload": w.name, "units": U, "layers": w.layers, "batch": w.batch,
                    "kv_heads": w.h_kv, "group": g, "d_head": d, "L": L, "b_kv": B,
                    "prefix": w.prefix, "recent": w.recent_tok, "rope_theta": w.theta,
-                   "pooling": args.aggregate,
+                   "pooling": args.aggregate, "compaction": args.compaction,
                    "observation": "recent32" if window else "beacons16+recent16"},
         "unit_evictions_per_s": round(U / (ms_step * 1e-3), 1),
         "steps_per_s": round(1e3 / ms_step, 2),

@@ -68,6 +68,10 @@ typedef struct bkv_dims {
  * ablation: paper text §5.3 and Table 2; the average form of the importance
  * score, paper text §2.2). */
 #define BKV_FLAG_MEAN 1
+/* BKV_FLAG_UNSORTED: bkv_evict compacts with bkv_compact_unsorted (kept
+ * tokens past b_kv fill the evicted slots below it; the cache is no longer in
+ * position order). */
+#define BKV_FLAG_UNSORTED 2
 
 /* Method parameters.  Paper text §5.1 ("Implementation Details"): beacon
  * budget max 32 / min 16, recent query budget 16; summary step (5): prefix
@@ -81,7 +85,7 @@ typedef struct bkv_policy {
     int32_t buf_cap;    /* rows per head in buf (32; up to 256 for prefill) */
     int32_t prefix;     /* P: leading slots always kept */
     int32_t recent_tok; /* R: trailing slots always kept */
-    int32_t flags;      /* 0, or BKV_FLAG_MEAN */
+    int32_t flags;      /* 0, or BKV_FLAG_MEAN | BKV_FLAG_UNSORTED */
     double rope_theta;  /* RoPE base theta (> 0) */
     float sm_scale;     /* softmax scale; 0 means 1/sqrt(d_head) */
     int32_t reserved;   /* must be 0 */
@@ -197,9 +201,27 @@ int bkv_compact(const bkv_dims* dims, uint16_t* K, uint16_t* V, int32_t* kpos,
                 void* stream);
 
 /*
+ * bkv_compact_unsorted -- fill the evicted slots instead of shifting.
+ *
+ * Unsorted variant of bkv_compact, in place.  The ThinKV pages note that
+ * attention is invariant to the order of the cached tokens and reuse evicted
+ * slots where they are.  Here every kept slot below b_kv keeps its token;
+ * the kept tokens at slots >= b_kv move into the evicted slots below b_kv,
+ * the i-th lowest such slot taking the i-th lowest such token (K, V and
+ * kpos).  Afterwards slots [0, b_kv) hold the kept set, not in position
+ * order, and at most L - b_kv tokens have moved.  kept must be the ascending
+ * keep set bkv_select writes; the kernel bounds-checks every access, so a
+ * malformed list moves nothing outside [0, L) (some slots may then be left
+ * as they were).  Requires 0 < b_kv <= L <= l_cap.
+ */
+int bkv_compact_unsorted(const bkv_dims* dims, uint16_t* K, uint16_t* V, int32_t* kpos,
+                         int64_t L, const int32_t* kept, int64_t b_kv, void* stream);
+
+/*
  * bkv_evict -- one full eviction event (summary steps (4)-(6)).
  *
- * Runs bkv_score, bkv_select and an in-place bkv_compact on K, V, kpos; then,
+ * Runs bkv_score, bkv_select and an in-place bkv_compact (bkv_compact_unsorted
+ * with BKV_FLAG_UNSORTED) on K, V, kpos; then,
  * if buf is non-NULL, the rolling update of summary step (6): the recent
  * queries are appended to each head's buffer (which must hold exactly the
  * n_beacon beacons, count == n_beacon) and the buffer is compressed back to

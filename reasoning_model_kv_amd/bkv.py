@@ -19,10 +19,11 @@ LIB_PATH = os.path.join(_HERE, "libbkv.so")
 
 BKV_OK, BKV_EINVAL, BKV_ENOTSUP, BKV_ENOSPC, BKV_EHIP = 0, -1, -2, -3, -4
 ABI_VERSION = 1
-BKV_FLAG_MEAN = 1  # policy flag: mean pooling (include/bkv.h)
+BKV_FLAG_MEAN = 1      # policy flag: mean pooling (include/bkv.h)
+BKV_FLAG_UNSORTED = 2  # policy flag: bkv_evict fills holes instead of shifting
 
 EXPORTS = ("bkv_abi_version", "bkv_last_error", "bkv_workspace_bytes", "bkv_fps_update",
-           "bkv_score", "bkv_select", "bkv_compact", "bkv_evict")
+           "bkv_score", "bkv_select", "bkv_compact", "bkv_compact_unsorted", "bkv_evict")
 
 
 class BkvError(RuntimeError):
@@ -59,6 +60,7 @@ class Shape:
     n_recent_q: int = 16
     sm_scale: float = 0.0
     aggregate: str = "max"  # pooling of the attention weights: "max" or "mean"
+    unsorted: bool = False  # bkv_evict compacts by filling holes (not in position order)
 
     def dims(self):
         return Dims(self.n_units, self.group, self.d_head, self.l_cap)
@@ -66,7 +68,8 @@ class Shape:
     def policy(self):
         if self.aggregate not in ("max", "mean"):
             raise ValueError(f"aggregate must be 'max' or 'mean', not {self.aggregate!r}")
-        flags = BKV_FLAG_MEAN if self.aggregate == "mean" else 0
+        flags = (BKV_FLAG_MEAN if self.aggregate == "mean" else 0) | (
+            BKV_FLAG_UNSORTED if self.unsorted else 0)
         return Policy(self.n_beacon, self.n_recent_q, self.buf_cap, self.prefix,
                       self.recent_tok, flags, float(self.rope_theta), float(self.sm_scale), 0)
 
@@ -108,6 +111,8 @@ def load_library(path=LIB_PATH):
     lib.bkv_select.argtypes = [_PD, _PP, _VP, _I64, _I64, _VP, _VP]
     lib.bkv_compact.restype = ctypes.c_int
     lib.bkv_compact.argtypes = [_PD, _VP, _VP, _VP, _I64, _VP, _I64, _VP, _VP, _VP, _I64, _VP]
+    lib.bkv_compact_unsorted.restype = ctypes.c_int
+    lib.bkv_compact_unsorted.argtypes = [_PD, _VP, _VP, _VP, _I64, _VP, _I64, _VP]
     lib.bkv_evict.restype = ctypes.c_int
     lib.bkv_evict.argtypes = [_PD, _PP, _VP, _VP, _VP, _I64, _VP, _VP, _I64, _I64, _VP, _VP,
                               _VP, _VP, _VP, ctypes.c_size_t, _VP]
@@ -237,6 +242,19 @@ def compact(shape, K, V, kpos, L, kept, b_kv, K_out=None, V_out=None, kpos_out=N
         int(L), _ptr(kept, torch.int32, "kept"), int(b_kv), _bits(K_out, "K_out", True),
         _bits(V_out, "V_out", True), _ptr(kpos_out, torch.int32, "kpos_out", True),
         int(out_cap), _stream(stream)))
+
+
+def compact_unsorted(shape, K, V, kpos, L, kept, b_kv, stream=None):
+    """In place: kept tokens past b_kv fill the evicted slots below it."""
+    lib = load_library()
+    U, d, cap = shape.n_units, shape.d_head, shape.l_cap
+    _need(K, U * cap * d, "K")
+    _need(V, U * cap * d, "V")
+    _need(kpos, U * cap, "kpos")
+    _need(kept, U * int(b_kv), "kept")
+    _check(lib.bkv_compact_unsorted(
+        ctypes.byref(shape.dims()), _bits(K, "K"), _bits(V, "V"), _ptr(kpos, torch.int32, "kpos"),
+        int(L), _ptr(kept, torch.int32, "kept"), int(b_kv), _stream(stream)))
 
 
 def evict(shape, K, V, kpos, L, beacons, recents, t, b_kv, buf=None, count=None,

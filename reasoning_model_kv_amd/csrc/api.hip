@@ -74,7 +74,7 @@ int check_dims(const char* fn, const bkv_dims* d) {
 
 int check_policy(const char* fn, const bkv_policy* p) {
     if (!p) return fail(BKV_EINVAL, "%s: policy is NULL", fn);
-    if ((p->flags & ~BKV_FLAG_MEAN) != 0 || p->reserved != 0)
+    if ((p->flags & ~(BKV_FLAG_MEAN | BKV_FLAG_UNSORTED)) != 0 || p->reserved != 0)
         return fail(BKV_EINVAL, "%s: unknown policy flags or reserved field not 0", fn);
     // The observation set is 32 rows per query head: 16 beacons + 16 recent
     // queries (the method), or 32 recent queries (the baselines' window).
@@ -237,6 +237,22 @@ int bkv_select(const bkv_dims* dims, const bkv_policy* pol, const float* score, 
                       fn);
 }
 
+int bkv_compact_unsorted(const bkv_dims* dims, uint16_t* K, uint16_t* V, int32_t* kpos,
+                         int64_t L, const int32_t* kept, int64_t b_kv, void* stream) {
+    const char* fn = "bkv_compact_unsorted";
+    CHECK(check_dims(fn, dims));
+    if (!K || !V || !kpos || !kept) return fail(BKV_EINVAL, "%s: NULL tensor pointer", fn);
+    if (!(0 < b_kv && b_kv <= L && L <= dims->l_cap))
+        return fail(BKV_EINVAL, "%s: need 0 < b_kv (%lld) <= L (%lld) <= l_cap (%lld)", fn,
+                    (long long)b_kv, (long long)L, (long long)dims->l_cap);
+    if (L > INT32_MAX) return fail(BKV_ENOTSUP, "%s: L beyond int32 slots", fn);
+    if (dims->n_units == 0) return ok();
+    if (fault_injected(fn)) return fail(BKV_EHIP, "%s: injected HIP failure", fn);
+    return hip_result(bkv::launch_compact_fill(K, V, kpos, dims->n_units, dims->d_head,
+                                               dims->l_cap, L, kept, b_kv, (hipStream_t)stream),
+                      fn);
+}
+
 int bkv_compact(const bkv_dims* dims, uint16_t* K, uint16_t* V, int32_t* kpos, int64_t L,
                 const int32_t* kept, int64_t b_kv, uint16_t* K_out, uint16_t* V_out,
                 int32_t* kpos_out, int64_t out_cap, void* stream) {
@@ -302,7 +318,10 @@ int bkv_evict(const bkv_dims* dims, const bkv_policy* pol, uint16_t* K, uint16_t
     if (e == hipSuccess)
         e = bkv::launch_select(score, dims->n_units, dims->l_cap, L, b_kv, pol->prefix,
                                pol->recent_tok, kept, s);
-    if (e == hipSuccess)
+    if (e == hipSuccess && (pol->flags & BKV_FLAG_UNSORTED))
+        e = bkv::launch_compact_fill(K, V, kpos, dims->n_units, dims->d_head, dims->l_cap, L,
+                                     kept, b_kv, s);
+    else if (e == hipSuccess)
         e = bkv::launch_compact(K, V, kpos, dims->n_units, dims->d_head, dims->l_cap, L, kept,
                                 b_kv, nullptr, nullptr, nullptr, dims->l_cap, s);
     if (e == hipSuccess && buf)

@@ -28,6 +28,11 @@ hipError_t launch_select(const float* score, int64_t n_units, int64_t l_cap,
                          int64_t L, int64_t b_kv, int prefix, int recent_tok,
                          int32_t* kept, hipStream_t s);
 
+// Unsorted compaction in place: kept tokens at slots >= b_kv fill the
+// evicted slots below b_kv.
+hipError_t launch_compact_fill(uint16_t* K, uint16_t* V, int32_t* kpos, int64_t n_units, int d,
+                               int64_t l_cap, int64_t L, const int32_t* kept, int64_t b_kv,
+                               hipStream_t s);
 hipError_t launch_compact(uint16_t* K, uint16_t* V, int32_t* kpos,
                           int64_t n_units, int d, int64_t l_cap, int64_t L,
                           const int32_t* kept, int64_t b_kv, uint16_t* K_out,

@@ -141,6 +141,129 @@ __global__ __launch_bounds__(64 * WAVES) void compact_kernel(
     }
 }
 
+// Wavefront-wide synchronisation of LDS between the lanes of one wavefront.
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Holes handled per pass of the unsorted compaction (LDS per wavefront).
+constexpr int kFillPass = 1024;
+
+// Unsorted compaction (hole filling): the kept tokens at slots >= b_kv move
+// into the evicted slots below b_kv -- the i-th lowest such hole takes the
+// i-th lowest such token -- and every other kept token stays where it is.
+// One wavefront per KV group:
+//  * c = the number of kept entries below b_kv (kept is ascending), by 64
+//    probes and then a scan of the one block they narrow it to;
+//  * the holes just below kept entry k are the slots between kept[k-1] and
+//    kept[k] (kept[c] taken as b_kv), and hole h there has rank h - k (the
+//    slots below it less the kept entries below it), so every lane walks its
+//    own entry's gap and records hole[rank] = h in LDS, no prefix sums;
+//  * the moves read token kept[c + rank] and write it to hole[rank]: sources
+//    are all >= b_kv and destinations < b_kv, so they are independent; 16
+//    lanes move one 256-byte row, four rows per instruction.
+// Ranks are handled kFillPass at a time.  Every access is bounds-checked: a
+// kept list that is not strictly ascending within [0, L) moves nothing
+// outside [0, L) (it may leave holes unfilled).
+template <int D>
+__global__ __launch_bounds__(64 * WAVES) void fill_kernel(uint16_t* K, uint16_t* V,
+                                                          int32_t* kpos, int64_t l_cap,
+                                                          const int32_t* __restrict__ kept,
+                                                          int64_t L, int64_t b_kv,
+                                                          int64_t n_units) {
+    constexpr int LPT = D / 8;     // lanes per token row
+    constexpr int TPW = 64 / LPT;  // rows per instruction
+    __shared__ int32_t hole_lds[WAVES][kFillPass];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int64_t u = (int64_t)blockIdx.x * WAVES + wv;
+    if (u >= n_units) return;
+    int32_t* hole = hole_lds[wv];
+    const int32_t* ku = kept + u * b_kv;
+    uint16_t* Ku = K + u * l_cap * D;
+    uint16_t* Vu = V + u * l_cap * D;
+    int32_t* pu = kpos + u * l_cap;
+    const int32_t b = (int32_t)b_kv;
+
+    // c: first index whose entry is >= b (b if none).  Probe i reads entry
+    // i * step (step = ceil(b / 64), so the probes cover [0, b)); the first
+    // probe at or above b, f, bounds c to (probe f-1, probe f]; with none,
+    // c lies after the last probe.  One scan of at most step - 1 entries
+    // finishes it.
+    int32_t c;
+    {
+        const int32_t step = (b + 63) / 64;
+        const int32_t pi = lane * step;
+        const uint64_t m = __ballot(pi < b && ku[pi] >= b);
+        int32_t lo, hi;
+        if (m == 0) {
+            const int32_t last = ((b - 1) / step) * step;  // last probe below b
+            lo = last + 1;
+            hi = b;
+        } else {
+            const int32_t f = (int32_t)__builtin_ctzll(m);
+            lo = f == 0 ? 0 : (f - 1) * step + 1;
+            hi = f * step;
+        }
+        c = hi;
+        for (int32_t k0 = lo; k0 < hi; k0 += 64) {
+            const int32_t k = k0 + lane;
+            const uint64_t mm = __ballot(k < hi && ku[k] >= b);
+            if (mm) {
+                c = k0 + (int32_t)__builtin_ctzll(mm);
+                break;
+            }
+        }
+    }
+    const int32_t n_tail = b - c;
+    const int st = lane / LPT, ch = lane % LPT;
+    const int64_t off = 8 * ch;
+    for (int32_t base = 0; base < n_tail; base += kFillPass) {
+        const int32_t n = n_tail - base < kFillPass ? n_tail - base : kFillPass;
+        for (int i = lane; i < kFillPass; i += 64) hole[i] = -1;
+        wave_sync();
+        // Gaps of entries 0..c (entry c stands for b): ranks [base, base + n).
+        int32_t carry = -1;  // entry before the chunk
+        for (int32_t k0 = 0; k0 <= c; k0 += 64) {
+            const int32_t k = k0 + lane;
+            const int32_t cur = k < c ? ku[k] : (k == c ? b : 0);
+            int32_t prev = __shfl_up(cur, 1);
+            if (lane == 0) prev = carry;
+            carry = __shfl(cur, 63);
+            if (k <= c) {
+                // holes h in (prev, cur) with rank h - k in [base, base + n)
+                int32_t h0 = prev + 1, h1 = cur - 1;
+                if (h0 < base + k) h0 = base + k;
+                if (h1 > base + n - 1 + k) h1 = base + n - 1 + k;
+                if (h1 >= b) h1 = b - 1;
+                for (int32_t h = h0; h <= h1; ++h) hole[h - k - base] = h;
+            }
+        }
+        wave_sync();
+        // Moves: 64 holes per round, TPW rows per instruction.
+        for (int32_t i0 = 0; i0 < n; i0 += 64) {
+            const int32_t my = i0 + lane;
+            const int32_t hsrc = my < n ? ku[c + base + my] : -1;  // source of rank base+my
+#pragma unroll 4
+            for (int r0 = 0; r0 < 64; r0 += TPW) {
+                const int j = r0 + st;  // row within the round
+                const int32_t s_ = __shfl(hsrc, j);
+                const int32_t h = i0 + j < n ? hole[i0 + j] : -1;
+                const bool ok = i0 + j < n && h >= 0 && h < b && s_ >= b && s_ < L;
+                if (ok) {
+                    const uint4 kr = *(const uint4*)(Ku + (int64_t)s_ * D + off);
+                    const uint4 vr = *(const uint4*)(Vu + (int64_t)s_ * D + off);
+                    st_nt(Ku + (int64_t)h * D + off, kr);
+                    st_nt(Vu + (int64_t)h * D + off, vr);
+                    if (ch == 0) pu[h] = pu[s_];
+                }
+            }
+        }
+        wave_sync();
+    }
+}
+
 }  // namespace
 
 hipError_t launch_compact(uint16_t* K, uint16_t* V, int32_t* kpos,
@@ -156,6 +279,22 @@ hipError_t launch_compact(uint16_t* K, uint16_t* V, int32_t* kpos,
     else
         compact_kernel<64><<<grid, 64 * WAVES, 0, s>>>(K, V, kpos, l_cap, kept, L, b_kv, K_out,
                                                        V_out, kpos_out, out_cap, n_units);
+    return hipGetLastError();
+}
+
+}  // namespace bkv
+
+namespace bkv {
+
+hipError_t launch_compact_fill(uint16_t* K, uint16_t* V, int32_t* kpos, int64_t n_units, int d,
+                               int64_t l_cap, int64_t L, const int32_t* kept, int64_t b_kv,
+                               hipStream_t s) {
+    if (n_units <= 0) return hipSuccess;
+    const dim3 grid((unsigned)((n_units + WAVES - 1) / WAVES));
+    if (d == 128)
+        fill_kernel<128><<<grid, 64 * WAVES, 0, s>>>(K, V, kpos, l_cap, kept, L, b_kv, n_units);
+    else
+        fill_kernel<64><<<grid, 64 * WAVES, 0, s>>>(K, V, kpos, l_cap, kept, L, b_kv, n_units);
     return hipGetLastError();
 }
 

@@ -59,7 +59,7 @@ def test_score_validation(lib):
     assert _call_score(lib, _shape(rope_theta=0.0)) == bkv.BKV_EINVAL
     bad_flags = _shape()
     pol = bad_flags.policy()
-    pol.flags = 2                                                 # unknown flag bit
+    pol.flags = 4                                                 # unknown flag bit
     assert lib.bkv_score(ctypes.byref(bad_flags.dims()), ctypes.byref(pol), FAKE, FAKE, 300,
                          FAKE, FAKE, 300, FAKE, None, FAKE, 1 << 20, None) == bkv.BKV_EINVAL
     assert "flags" in bkv.last_error()
@@ -103,6 +103,19 @@ def test_compact_validation(lib):
     # aliasing outputs
     assert lib.bkv_compact(d, FAKE, FAKE, FAKE, 300, FAKE, 200, FAKE, o, o, 200,
                            None) == bkv.BKV_EINVAL
+
+
+def test_compact_unsorted_validation(lib):
+    s = _shape()
+    d = ctypes.byref(s.dims())
+    call = lambda K, L, b: lib.bkv_compact_unsorted(d, K, FAKE, FAKE, L, FAKE, b, None)
+    assert call(None, 300, 200) == bkv.BKV_EINVAL    # NULL K
+    assert call(FAKE, 300, 0) == bkv.BKV_EINVAL      # b_kv = 0
+    assert call(FAKE, 300, 301) == bkv.BKV_EINVAL    # b_kv > L
+    assert call(FAKE, 600, 200) == bkv.BKV_EINVAL    # L > l_cap
+    s0 = _shape(n_units=0)
+    assert lib.bkv_compact_unsorted(ctypes.byref(s0.dims()), FAKE, FAKE, FAKE, 300, FAKE, 200,
+                                    None) == bkv.BKV_OK
 
 
 def test_fps_validation(lib):

@@ -177,6 +177,66 @@ def test_evict_recent_window(name, samples):
     log(f"  max score rel err {worst:.3g}; kept-set tie-band differences {ndiff}")
 
 
+@pytest.mark.parametrize("name,samples", [
+    ("tiny", None),
+    ("qwen3_4b_layer", None),
+    ("qwen3_4b_full_b2048", [0, 2303, 4607]),
+])
+def test_evict_unsorted_compaction(name, samples):
+    """bkv_evict with BKV_FLAG_UNSORTED: scores, kept set and merge as usual;
+    the cache holds the kept tokens with the tail ones in the evicted slots."""
+    w = synth.WORKLOADS[name]
+    log(f"evict unsorted {name}: U={w.n_units} g={w.group} L={w.L} B={w.b_kv}")
+    if samples is None:
+        inp = synth.workload_inputs(w)
+        dev = synth.to_device(inp, DEV)
+        samples = list(range(w.n_units))
+        host = {u: {k: inp[k][u] for k in ("keys", "values", "kpos", "recents")}
+                for u in samples}
+    else:
+        dev = synth.device_inputs(w, DEV)
+        host = {u: {"keys": dev["keys"][u].float().cpu().numpy(),
+                    "values": dev["values"][u].float().cpu().numpy(),
+                    "kpos": dev["kpos"][u].cpu().numpy(),
+                    "recents": dev["recents"][u * w.group:(u + 1) * w.group].cpu().numpy()}
+                for u in samples}
+    shape = bkv.Shape(w.n_units, w.group, w.d_head, w.L, w.prefix, w.theta,
+                      recent_tok=w.recent_tok, unsorted=True)
+    nq = w.n_qheads
+    count = torch.full((nq,), 31, dtype=torch.int32, device=DEV)
+    bkv.fps_update(shape, dev["buf"], count, dev["buf"][:, 31:32].contiguous(), trigger=32, m=16)
+    beacons = dev["buf"][:, :16].clone()
+    score = torch.zeros((w.n_units, w.L), device=DEV)
+    kept = torch.zeros((w.n_units, w.b_kv), dtype=torch.int32, device=DEV)
+    K0, V0, P0 = dev["keys"].clone(), dev["values"].clone(), dev["kpos"].clone()
+    bkv.evict(shape, dev["keys"], dev["values"], dev["kpos"], w.L, dev["buf"], dev["recents"],
+              dev["t"], w.b_kv, buf=dev["buf"], count=count, score_out=score, kept_out=kept)
+    torch.cuda.synchronize()
+    _all_unit_properties(w, kept)
+    # Every unit: the positions in [0, b_kv) are exactly the kept tokens' positions.
+    got_pos = torch.sort(dev["kpos"][:, :w.b_kv], dim=1).values
+    want_pos = torch.gather(P0, 1, kept.long())
+    assert torch.equal(got_pos, want_pos)
+    worst = 0.0
+    for u in samples:
+        hu = host[u]
+        g = w.group
+        ref = oracle.evict.evict_unit(hu["keys"], hu["values"], hu["kpos"], w.L,
+                                      beacons[u * g:(u + 1) * g].cpu().numpy(), hu["recents"],
+                                      w.L, w.b_kv, w.prefix, w.recent_tok, w.theta, merge=False)
+        worst = max(worst, check_scores(score[u].cpu().numpy(), ref["score"], f"{name} {u}"))
+        ku = kept[u].cpu().numpy()
+        check_kept(ku, ref["score"], w.L, w.b_kv, w.prefix, w.recent_tok, f"{name} {u}")
+        ek, ev, ep, _ = oracle.compact.fill_holes(K0[u].view(torch.int16).cpu().numpy(),
+                                                  V0[u].view(torch.int16).cpu().numpy(),
+                                                  P0[u].cpu().numpy(), ku, w.b_kv)
+        assert np.array_equal(dev["keys"][u, :w.b_kv].view(torch.int16).cpu().numpy(), ek)
+        assert np.array_equal(dev["values"][u, :w.b_kv].view(torch.int16).cpu().numpy(), ev)
+        assert np.array_equal(dev["kpos"][u, :w.b_kv].cpu().numpy(), ep)
+    assert torch.all(count == 16)
+    log(f"  max score rel err {worst:.3g}")
+
+
 def _all_unit_properties(w, kept):
     P, R, L = w.prefix, w.recent_tok, w.L
     assert torch.all(kept[:, 1:] > kept[:, :-1])

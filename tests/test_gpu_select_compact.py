@@ -88,3 +88,43 @@ def test_compact_in_place_and_out_of_place(d, L, b_kv):
     assert torch.equal(V2[:, :b_kv].view(torch.int16), Vo.view(torch.int16))
     assert torch.equal(P2[:, :b_kv], Po)
     assert torch.equal(K2[:, b_kv:].view(torch.int16), Kt[:, b_kv:].view(torch.int16))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("L,b_kv", [(256, 128), (2176, 2048), (519, 301), (5000, 1000),
+                                    (70, 65)])
+def test_compact_unsorted_bit_exact(d, L, b_kv):
+    """Hole filling against the oracle's fill_holes, every unit, bit for bit.
+
+    (5000, 1000): 3,800+ holes per unit, more than one pass of the kernel's
+    1024-hole window; units 0-2: nothing moves, one move, every kept slot at
+    or past b_kv but the first."""
+    U = 13
+    log(f"compact unsorted d={d} L={L} b_kv={b_kv}")
+    r = np.random.default_rng(3 * d + L)
+    l_cap = L + 3
+    K = r.standard_normal((U, l_cap, d)).astype(np.float32)
+    V = r.standard_normal((U, l_cap, d)).astype(np.float32)
+    kpos = (np.arange(l_cap)[None].repeat(U, 0) * 2 + 11).astype(np.int32)
+    kept = np.stack([np.sort(r.choice(L, b_kv, replace=False)) for _ in range(U)]).astype(np.int32)
+    kept[0] = np.arange(b_kv)                       # nothing moves
+    kept[1, : b_kv - 1] = np.arange(b_kv - 1)
+    kept[1, -1] = L - 1                             # one move
+    kept[2, 0] = 0
+    kept[2, 1:] = np.arange(L - b_kv + 1, L)        # all but slot 0 come from the tail
+    Kt = torch.from_numpy(K).to(torch.bfloat16).to(DEV)
+    Vt = torch.from_numpy(V).to(torch.bfloat16).to(DEV)
+    Pt = torch.from_numpy(kpos).to(DEV)
+    kt = torch.from_numpy(kept).to(DEV)
+    Kh, Vh = Kt.cpu().view(torch.int16).numpy(), Vt.cpu().view(torch.int16).numpy()
+    shape = bkv.Shape(U, 1, d, l_cap, 0, 1e4)
+    bkv.compact_unsorted(shape, Kt, Vt, Pt, L, kt, b_kv)
+    torch.cuda.synchronize()
+    Kg, Vg, Pg = Kt.cpu().view(torch.int16).numpy(), Vt.cpu().view(torch.int16).numpy(), Pt.cpu()
+    for u in range(U):
+        ek, ev, ep, moves = oracle.compact.fill_holes(Kh[u], Vh[u], kpos[u], kept[u], b_kv)
+        assert np.array_equal(Kg[u, :b_kv], ek), f"unit {u} K"
+        assert np.array_equal(Vg[u, :b_kv], ev), f"unit {u} V"
+        assert np.array_equal(Pg[u, :b_kv].numpy(), ep), f"unit {u} kpos"
+        # slots at and past b_kv are read, never written
+        assert np.array_equal(Kg[u, b_kv:], Kh[u, b_kv:]), f"unit {u} tail"

@@ -463,7 +463,8 @@ def stream_main(args, w):
             ev_marks.append(e)
 
     st = bstream.Stream(U, g, d, w.L, w.b_kv, w.prefix, w.theta, device=dev, observer=observer,
-                        beacon_policy=args.beacon_policy)
+                        beacon_policy=args.beacon_policy,
+                        unsorted=args.compaction == "unsorted")
     gen = synth.StreamInputs(w, dev)
     st.prefill(*gen.prompt())
     torch.cuda.synchronize()
@@ -486,7 +487,8 @@ def stream_main(args, w):
         chunk_ms.append(e0.elapsed_time(e1))
         if st.n_evictions > before and len(moved) < 4:
             kept = st.kept.cpu().numpy()
-            moved.append(int(np.count_nonzero(kept != np.arange(w.b_kv)[None, :])))
+            moved.append(int(np.count_nonzero(kept >= w.b_kv)) if st.shape.unsorted else
+                         int(np.count_nonzero(kept != np.arange(w.b_kv)[None, :])))
         done += n
         if c % 32 == 0:
             eprint(f"[bench] {done} steps, {st.n_evictions} evictions")
@@ -520,7 +522,8 @@ def stream_main(args, w):
                    "kv_heads": w.h_kv, "group": g, "d_head": d, "B_max": L, "b_kv": w.b_kv,
                    "prefix": w.prefix, "recent": w.recent_tok, "rope_theta": w.theta,
                    "beacons": "continual FPS" if args.beacon_policy == "fps" else
-                              "first 16 generated queries (Initial+Recent)"},
+                              "first 16 generated queries (Initial+Recent)",
+                   "compaction": args.compaction},
         "evictions": n_ev,
         "evict_ms_mean": round(mean_ev, 4),
         "evict_hbm_frac": round(ev_bytes / (mean_ev * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),

@@ -12,17 +12,20 @@ fps), each pinned separately.
 
 import numpy as np
 
-from .compact import compact
+from .compact import compact, fill_holes
 from .fps import fps
 from .score import score_unit
 from .select import select
 
 
 def evict_unit(keys, values, kpos, L, beacons, recents, t, b_kv, prefix,
-               recent_tok, theta, n_min=16, scale=None, merge=True, aggregate="max"):
+               recent_tok, theta, n_min=16, scale=None, merge=True, aggregate="max",
+               unsorted=False):
     """keys/values: [>=L, d]; kpos: [>=L]; beacons/recents: [g, 16, d].
 
     aggregate: the pooling of the scores, "max" (the method) or "mean".
+    unsorted: compact by filling the evicted slots (compact.fill_holes)
+    instead of in position order.
 
     Returns a dict with score [L], kept [b_kv], the compacted keys, values
     and positions, and (with merge) the merged buffer [g, n_min, d] plus the
@@ -35,7 +38,10 @@ def evict_unit(keys, values, kpos, L, beacons, recents, t, b_kv, prefix,
     taus = kpos[L - n_recent:L]
     sc = score_unit(keys, beacons, recents, t, taus, theta, scale, aggregate=aggregate)
     kept = select(sc, L, b_kv, prefix, recent_tok)
-    k2, v2, p2 = compact(keys, values, kpos, kept)
+    if unsorted:
+        k2, v2, p2, _ = fill_holes(keys, values, kpos, kept, b_kv)
+    else:
+        k2, v2, p2 = compact(keys, values, kpos, kept)
     out = {"score": sc, "kept": kept, "keys": k2, "values": v2, "kpos": p2}
     if merge:
         bufs, orders = [], []

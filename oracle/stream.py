@@ -37,10 +37,11 @@ class UnitStream:
     """Exact per-unit replay of the decode-time policy (slow; small units)."""
 
     def __init__(self, g, d, b_max, b_kv, prefix, theta, recent_tok=16,
-                 n_recent_q=16, buf_min=16, buf_max=32, beacons="fps"):
+                 n_recent_q=16, buf_min=16, buf_max=32, beacons="fps", unsorted=False):
         if beacons not in ("fps", "initial"):
             raise ValueError(f"beacons must be 'fps' or 'initial', not {beacons!r}")
         self.policy = beacons
+        self.unsorted = unsorted  # compact by filling holes (cache not in position order)
         self.g, self.d = g, d
         self.b_max, self.b_kv, self.prefix = b_max, b_kv, prefix
         self.theta, self.recent_tok = theta, recent_tok
@@ -124,7 +125,8 @@ class UnitStream:
         initial = self.policy == "initial"
         out = evict_unit(self.keys, self.values, self.kpos, L, beacons, recents,
                          self.t, self.b_kv, self.prefix, self.recent_tok,
-                         self.theta, n_min=self.buf_min, merge=not initial)
+                         self.theta, n_min=self.buf_min, merge=not initial,
+                         unsorted=self.unsorted)
         self.keys, self.values, self.kpos = out["keys"], out["values"], out["kpos"]
         if not initial:
             self.buf = [out["buf"][h] for h in range(self.g)]

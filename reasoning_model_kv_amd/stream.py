@@ -17,7 +17,10 @@ call covers all units at each point of the policy:
 With beacon_policy="initial" (the Initial+Recent comparison, paper text
 §5.3 and Table 3) the reference rows are instead the first 16 queries
 generated after the prompt, appended and then left alone: no FPS at any
-point and no merge after an eviction.
+point and no merge after an eviction.  With unsorted=True the evictions
+compact by filling the evicted slots (bkv_compact_unsorted): the cache is
+then not in position order, which scoring and the slot-based masks do not
+need (every slot below the recent window holds an older token).
 
 Writing the new token's key, value and position into the cache is the
 decoder's own work and is done here with plain tensor writes; every step of
@@ -34,7 +37,7 @@ from . import bkv
 
 class Stream:
     def __init__(self, n_units, group, d_head, b_max, b_kv, prefix, theta, recent_tok=16,
-                 device="cuda", observer=None, beacon_policy="fps"):
+                 device="cuda", observer=None, beacon_policy="fps", unsorted=False):
         if b_max - b_kv < recent_tok or b_kv < prefix + recent_tok:
             raise ValueError("need prefix + recent_tok <= b_kv <= b_max - recent_tok")
         if beacon_policy not in ("fps", "initial"):
@@ -42,7 +45,7 @@ class Stream:
         self.policy = beacon_policy
         dev = torch.device(device)
         self.shape = bkv.Shape(n_units, group, d_head, b_max, prefix, theta,
-                               recent_tok=recent_tok)
+                               recent_tok=recent_tok, unsorted=unsorted)
         self.rshape = replace(self.shape, buf_cap=self.shape.n_recent_q)
         U, nq = n_units, n_units * group
         self.b_max, self.b_kv, self.recent_tok = b_max, b_kv, recent_tok

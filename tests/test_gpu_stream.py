@@ -26,8 +26,8 @@ DEV = "cuda"
 class Checker:
     """Observer: snapshots sampled state before each event, checks after."""
 
-    def __init__(self, w, units, policy="fps"):
-        self.w, self.units, self.policy = w, list(units), policy
+    def __init__(self, w, units, policy="fps", unsorted=False):
+        self.w, self.units, self.policy, self.unsorted = w, list(units), policy, unsorted
         self.heads = [u * w.group + h for u in self.units for h in range(w.group)]
         self.pre = None
         self.n = {"fps": 0, "evict": 0, "exact_fps": 0}
@@ -78,9 +78,15 @@ class Checker:
             where = f"evict at L={L} unit {u}"
             self.worst = max(self.worst, check_scores(sc[i, :L], ref["score"], where))
             check_kept(kept[i], ref["score"], L, b, w.prefix, w.recent_tok, where)
-            assert np.array_equal(K1[i, :b], pre["K"][i][kept[i]]), where + " K"
-            assert np.array_equal(V1[i, :b], pre["V"][i][kept[i]]), where + " V"
-            assert np.array_equal(P1[i, :b], pre["P"][i][kept[i]]), where + " kpos"
+            if self.unsorted:
+                ek, ev, ep, _ = oracle.compact.fill_holes(pre["K"][i], pre["V"][i], pre["P"][i],
+                                                          kept[i], b)
+            else:
+                ek, ev, ep = oracle.compact.compact(pre["K"][i], pre["V"][i], pre["P"][i],
+                                                    kept[i])
+            assert np.array_equal(K1[i, :b], ek), where + " K"
+            assert np.array_equal(V1[i, :b], ev), where + " V"
+            assert np.array_equal(P1[i, :b], ep), where + " kpos"
             if initial:  # no merge: the reference rows stay as they were
                 assert np.array_equal(merged_out[hs], pre["beacons"][hs]), where + " refs"
                 continue
@@ -106,10 +112,10 @@ def _oracle_events(w, n_steps, policy="fps"):
     return st.events
 
 
-def _run(w, n_steps, units, chunk=128, policy="fps"):
-    chk = Checker(w, units, policy)
+def _run(w, n_steps, units, chunk=128, policy="fps", unsorted=False):
+    chk = Checker(w, units, policy, unsorted)
     st = bstream.Stream(w.n_units, w.group, w.d_head, w.L, w.b_kv, w.prefix, w.theta,
-                        device=DEV, observer=chk, beacon_policy=policy)
+                        device=DEV, observer=chk, beacon_policy=policy, unsorted=unsorted)
     gen = synth.StreamInputs(w, DEV)
     st.prefill(*gen.prompt())
     done = 0
@@ -160,4 +166,21 @@ def test_stream_small_initial_recent_all_units():
     assert st.events == _oracle_events(w, n, "initial")
     assert chk.n["evict"] == st.n_evictions >= 2 and chk.n["fps"] == 0
     assert torch.all(st.count == 16)
+    log(f"  evictions {st.n_evictions}, max score rel err {chk.worst:.3g}")
+
+
+def test_stream_small_unsorted_compaction_all_units():
+    """Evictions that fill holes: same cadence, exact hole filling at every
+    eviction, and the cache stays a permutation with the prefix in place."""
+    w = synth.WORKLOADS["stream_small"]
+    n = w.stream_steps
+    log(f"stream {w.name} (unsorted compaction): U={w.n_units} steps={n}")
+    st, chk = _run(w, n, range(w.n_units), unsorted=True)
+    assert st.events == _oracle_events(w, n)
+    assert chk.n["evict"] == st.n_evictions >= 2
+    P = w.prefix
+    assert torch.equal(st.kpos[:, :P], torch.arange(P, dtype=torch.int32,
+                                                    device=st.kpos.device).expand(w.n_units, -1))
+    live = st.kpos[:, :st.L]
+    assert torch.all(torch.sort(live, dim=1).values[:, 1:] > torch.sort(live, dim=1).values[:, :-1])
     log(f"  evictions {st.n_evictions}, max score rel err {chk.worst:.3g}")

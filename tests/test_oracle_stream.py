@@ -104,3 +104,29 @@ def test_initial_recent_policy_keeps_the_first_generated_queries():
         pass
     else:
         raise AssertionError("unknown beacon policy must be rejected")
+
+
+def test_unsorted_compaction_keeps_the_same_evictions():
+    # Filling holes only permutes the kept tokens, and scoring, selection
+    # (up to the slot order of ties) and the causal masks do not depend on
+    # the order of the older tokens: over three eviction intervals the kept
+    # positions, as sets, match the position-ordered run.
+    g, d, b_kv, P = 1, 8, 64, 4
+    runs = {}
+    for unsorted in (False, True):
+        st = UnitStream(g, d, b_max=b_kv + 128, b_kv=b_kv, prefix=P, theta=1e4, unsorted=unsorted)
+        r = np.random.default_rng(21)
+        st.prefill(r.standard_normal((P, d)), r.standard_normal((P, d)),
+                   r.standard_normal((g, P, d)))
+        kept_sets = []
+        for _ in range((b_kv + 128 - P) + 2 * 128 + 3):
+            n_ev = st.events.count(("evict", b_kv + 128))
+            st.step(r.standard_normal(d), r.standard_normal(d), r.standard_normal((g, d)))
+            if st.events.count(("evict", b_kv + 128)) > n_ev:
+                kept_sets.append(sorted(st.kpos.tolist()))
+        runs[unsorted] = (kept_sets, st)
+    assert runs[False][0] == runs[True][0] and len(runs[True][0]) == 3
+    # The unsorted cache is a permutation with the prefix in place.
+    st = runs[True][1]
+    assert st.kpos[:P].tolist() == list(range(P))
+    assert sorted(st.kpos.tolist()) != st.kpos.tolist()

@@ -82,7 +82,8 @@ typedef struct bkv_policy {
                          * most recent queries the baselines observe, paper
                          * text §2.2 and §3.2) */
     int32_t n_recent_q; /* recent queries per query head: 16 (or 32, above) */
-    int32_t buf_cap;    /* rows per head in buf (32; up to 256 for prefill) */
+    int32_t buf_cap;    /* rows per head in buf (32; up to 8192 for a prefill over a
+                         * long prompt; beyond 256 rows, m <= 64) */
     int32_t prefix;     /* P: leading slots always kept */
     int32_t recent_tok; /* R: trailing slots always kept */
     int32_t flags;      /* 0, or BKV_FLAG_MEAN | BKV_FLAG_UNSORTED */
@@ -130,7 +131,8 @@ size_t bkv_workspace_bytes(const bkv_dims* dims, const bkv_policy* pol,
  * The cosine matrix of a buffer of up to 32 rows is formed on fp32 MFMA
  * (v_mfma_f32_32x32x2_f32); other arithmetic is fp32.  Requires
  * 0 <= n_new <= buf_cap, new_q NULL iff n_new == 0,
- * 1 <= m < trigger <= buf_cap + 1, buf_cap <= 256, every count in
+ * 1 <= m < trigger <= buf_cap + 1, buf_cap <= 8192 (and m <= 64 when
+ * buf_cap > 256 and heads can compress), every count in
  * [0, buf_cap] on entry.  buf and count are updated in place; new_q must not
  * overlap buf.
  */

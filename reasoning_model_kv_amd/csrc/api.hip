@@ -83,7 +83,7 @@ int check_policy(const char* fn, const bkv_policy* p) {
                     "%s: n_beacon %d / n_recent_q %d: only 16 / 16 or 0 / 32 supported", fn,
                     p->n_beacon, p->n_recent_q);
     if (p->buf_cap < 1) return fail(BKV_EINVAL, "%s: buf_cap %d < 1", fn, p->buf_cap);
-    if (p->buf_cap > 256) return fail(BKV_ENOTSUP, "%s: buf_cap %d > 256", fn, p->buf_cap);
+    if (p->buf_cap > 8192) return fail(BKV_ENOTSUP, "%s: buf_cap %d > 8192", fn, p->buf_cap);
     if (p->prefix < 0 || p->recent_tok < 0)
         return fail(BKV_EINVAL, "%s: prefix %d / recent_tok %d must be >= 0", fn, p->prefix,
                     p->recent_tok);
@@ -187,6 +187,9 @@ int bkv_fps_update(const bkv_dims* dims, const bkv_policy* pol, float* buf, int3
     if (!(1 <= m && m < trigger && trigger <= pol->buf_cap + 1))
         return fail(BKV_EINVAL, "%s: need 1 <= m (%d) < trigger (%d) <= buf_cap + 1 (%d)", fn, m,
                     trigger, pol->buf_cap + 1);
+    if (pol->buf_cap > 256 && m > 64 && trigger <= pol->buf_cap)
+        return fail(BKV_ENOTSUP, "%s: buffers of more than 256 rows keep at most 64 (m = %d)", fn,
+                    m);
     if (dims->n_units == 0) return ok();
     if (fault_injected(fn)) return fail(BKV_EHIP, "%s: injected HIP failure", fn);
     const int64_t n_heads = dims->n_units * dims->group;

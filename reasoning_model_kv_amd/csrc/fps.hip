@@ -10,7 +10,8 @@
 // workgroup per head and one thread per row; there the average cosine of
 // row i uses the sum of all normalised rows (sum_j cos(q_i, q_j) equals
 // q_i/|q_i| . sum_j q_j/|q_j|) and each pick broadcasts the new member's
-// row through LDS.
+// row through LDS.  Longer buffers (up to 8192 rows) stream their rows on
+// every pass (fps_long_kernel).
 //
 // Arithmetic is fp32; ties go to the lower slot.
 
@@ -345,6 +346,224 @@ __global__ __launch_bounds__(256) void fps_block_kernel(
     if (tid == 0) count[head] = m;
 }
 
+// Buffers of more than 256 rows (up to kLongCap; the prefill FPS over a
+// long prompt, or FPS over a whole query history): one workgroup per head,
+// with the rows left in memory and streamed on every pass.  A wavefront
+// instruction reads RPI = 64 / (D/4) whole rows, one float4 per lane, and a
+// row's dot products reduce over its D/4 lanes with xor shuffles; the row's
+// norm is re-formed from the same loads on every pass, so LDS holds only
+// the running maxima S (4 bytes per row).
+//  * pass 1: the sum of the normalised rows (then the average cosine of row
+//    i is q_i/|q_i| . sum / N, as in fps_block_kernel);
+//  * pass 2: the average cosines; the seed is their argmin;
+//  * each further pass: the cosine of every row with the last pick (the
+//    pick's column of the Gram matrix), S = max(S, it), and the argmin of S
+//    over the rows not yet picked (a picked row holds S = +inf).
+// m + 1 passes over the N rows in all.  The picked rows are staged in
+// registers before they are written back to rows 0..m-1 (a destination row
+// can be another pick's source).
+constexpr int kLongCap = 8192;
+constexpr int kLongM = 64;
+
+template <int D>
+__global__ __launch_bounds__(256) void fps_long_kernel(
+    float* __restrict__ buf, int32_t* __restrict__ count, const float* __restrict__ new_q,
+    int n_new, int cap, int trigger, int m, int32_t* __restrict__ sel_order,
+    int32_t* __restrict__ n_overflow) {
+    extern __shared__ float S[];  // [cap]
+    __shared__ float bc[D];
+    __shared__ float part[4][D];
+    __shared__ float red_v[4];
+    __shared__ int red_i[4];
+    __shared__ int picks[kLongM];
+    constexpr int C4 = D / 4;       // float4 chunks per row
+    constexpr int RPI = 64 / C4;    // rows per wavefront instruction
+    constexpr int STEP = 4 * RPI;   // rows per pass iteration of the workgroup
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int sub = lane / C4, c4 = lane % C4;
+    const int64_t head = blockIdx.x;
+    float* hb = buf + head * (int64_t)cap * D;
+    const float* nq = new_q ? new_q + head * (int64_t)n_new * D : nullptr;
+
+    const int cnt = count[head];
+    const int N = cnt + n_new;
+    const bool compress = (cnt >= 0 && N <= cap && N >= trigger && N > m);
+    if (sel_order && !compress)
+        for (int i = tid; i < m; i += 256) sel_order[head * m + i] = -1;
+    if (cnt < 0 || N > cap) {
+        if (tid == 0 && n_overflow) atomicAdd(n_overflow, 1);
+        return;
+    }
+    if (!compress) {
+        for (int e = tid * 4; e < n_new * D; e += 256 * 4)
+            *reinterpret_cast<float4*>(hb + (int64_t)cnt * D + e) =
+                *reinterpret_cast<const float4*>(nq + e);
+        if (tid == 0) count[head] = N;
+        return;
+    }
+
+    auto row_ptr = [&](int j) -> const float* {
+        return j < cnt ? hb + (int64_t)j * D : nq + (int64_t)(j - cnt) * D;
+    };
+    auto load4 = [&](int j) -> float4 {
+        return j < N ? *reinterpret_cast<const float4*>(row_ptr(j) + 4 * c4)
+                     : make_float4(0.f, 0.f, 0.f, 0.f);
+    };
+    auto row_sum = [&](float x) {  // over the C4 lanes of a row
+#pragma unroll
+        for (int o = 1; o < C4; o <<= 1) x += __shfl_xor(x, o);
+        return x;
+    };
+    auto dot4 = [](float4 a, float4 b) { return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w; };
+    auto inv_norm = [&](float4 v) {
+        return 1.0f / fmaxf(sqrtf(row_sum(dot4(v, v))), kNormFloor);
+    };
+    // (value, index) argmin where index kNone means "no candidate": any
+    // candidate beats none, so the result is a real row even if every value
+    // is NaN (garbage in, but never an index out of range).
+    constexpr int kNone = 0x7fffffff;
+    auto take = [](float& v, int& i, float ov, int oi) {
+        if (oi != kNone && (i == kNone || ov < v || (ov == v && oi < i))) {
+            v = ov;
+            i = oi;
+        }
+    };
+    auto block_argmin = [&](float v, int i) -> int {
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const float ov = __shfl_xor(v, o);
+            const int oi = __shfl_xor(i, o);
+            take(v, i, ov, oi);
+        }
+        if (lane == 0) {
+            red_v[wave] = v;
+            red_i[wave] = i;
+        }
+        __syncthreads();
+        float bv = red_v[0];
+        int bi = red_i[0];
+        for (int w = 1; w < 4; ++w) take(bv, bi, red_v[w], red_i[w]);
+        __syncthreads();  // red_* are free again
+        return bi;
+    };
+    const float inf = __builtin_inff();
+
+    // Pass 1: sum of the normalised rows.
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j0 = wave * RPI; j0 < N; j0 += STEP) {
+        const int j = j0 + sub;
+        const float4 v = load4(j);
+        const float inv = inv_norm(v);
+        if (j < N) {
+            acc.x = fmaf(v.x, inv, acc.x);
+            acc.y = fmaf(v.y, inv, acc.y);
+            acc.z = fmaf(v.z, inv, acc.z);
+            acc.w = fmaf(v.w, inv, acc.w);
+        }
+    }
+#pragma unroll
+    for (int o = C4; o < 64; o <<= 1) {
+        acc.x += __shfl_xor(acc.x, o);
+        acc.y += __shfl_xor(acc.y, o);
+        acc.z += __shfl_xor(acc.z, o);
+        acc.w += __shfl_xor(acc.w, o);
+    }
+    if (sub == 0) *reinterpret_cast<float4*>(&part[wave][4 * c4]) = acc;
+    __syncthreads();
+    if (tid < D) bc[tid] = part[0][tid] + part[1][tid] + part[2][tid] + part[3][tid];
+    __syncthreads();
+
+    // Pass 2: average cosines; S starts at -inf.
+    const float invN = 1.0f / (float)N;
+    float bv = inf;
+    int bi = kNone;
+    {
+        const float4 sv = *reinterpret_cast<const float4*>(&bc[4 * c4]);
+        for (int j0 = wave * RPI; j0 < N; j0 += STEP) {
+            const int j = j0 + sub;
+            const float4 v = load4(j);
+            const float inv = inv_norm(v);
+            const float a = row_sum(dot4(v, sv)) * inv * invN;
+            if (j < N) {
+                take(bv, bi, a, j);
+                if (c4 == 0) S[j] = -inf;
+            }
+        }
+    }
+    int p = block_argmin(bv, bi);
+
+    // Greedy picks: each pass adds the last pick's cosines to S.
+    for (int it = 0;; ++it) {
+        if (tid == 0) {
+            picks[it] = p;
+            S[p] = inf;
+            if (sel_order) sel_order[head * m + it] = p;
+        }
+        if (it + 1 == m) break;
+        if (wave == 0) {  // the pick's normalised row
+            const float4 v = sub == 0 ? *reinterpret_cast<const float4*>(row_ptr(p) + 4 * c4)
+                                      : make_float4(0.f, 0.f, 0.f, 0.f);
+            const float inv = inv_norm(v);
+            if (sub == 0)
+                *reinterpret_cast<float4*>(&bc[4 * c4]) =
+                    make_float4(v.x * inv, v.y * inv, v.z * inv, v.w * inv);
+        }
+        __syncthreads();
+        const float4 b4 = *reinterpret_cast<const float4*>(&bc[4 * c4]);
+        bv = inf;
+        bi = kNone;
+        for (int j0 = wave * RPI; j0 < N; j0 += STEP) {
+            const int j = j0 + sub;
+            const float4 v = load4(j);
+            const float inv = inv_norm(v);
+            const float c = row_sum(dot4(v, b4)) * inv;
+            if (j < N) {
+                const float so = S[j];
+                if (so != inf) {
+                    const float sn = fmaxf(so, c);
+                    if (c4 == 0) S[j] = sn;
+                    take(bv, bi, sn, j);
+                }
+            }
+        }
+        p = block_argmin(bv, bi);  // its barriers also order the bc reads before the next write
+    }
+
+    // Write back the picks in ascending slot order.
+    __syncthreads();
+    if (tid == 0) {
+        for (int a = 1; a < m; ++a) {
+            const int x = picks[a];
+            int b = a - 1;
+            while (b >= 0 && picks[b] > x) {
+                picks[b + 1] = picks[b];
+                --b;
+            }
+            picks[b + 1] = x;
+        }
+    }
+    __syncthreads();
+    // (Native vector type: an array of the float4 struct would live in scratch.)
+    typedef float v4f __attribute__((ext_vector_type(4)));
+    constexpr int KS = kLongM * C4 / 256;  // staged chunks per thread
+    v4f stg[KS];
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+        const int e = tid + 256 * k;
+        stg[k] = e < m * C4
+                     ? *reinterpret_cast<const v4f*>(row_ptr(picks[e / C4]) + 4 * (e % C4))
+                     : v4f{0.f, 0.f, 0.f, 0.f};
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+        const int e = tid + 256 * k;
+        if (e < m * C4)
+            *reinterpret_cast<v4f*>(hb + (int64_t)(e / C4) * D + 4 * (e % C4)) = stg[k];
+    }
+    if (tid == 0) count[head] = m;
+}
+
 // Append only (trigger > buf_cap, so no head can compress), when one head's
 // new rows are at most 64 16-byte chunks: CPH lanes (a power of two) per
 // head, 256 / CPH heads per workgroup.  All lanes of a head are in one
@@ -399,13 +618,22 @@ hipError_t launch_fps(float* buf, int32_t* count, const float* new_q,
         else
             fps_wave_kernel<64><<<grid, 64, 0, s>>>(buf, count, new_q, n_new, buf_cap,
                                                     trigger, m, sel_order, n_overflow);
-    } else {
+    } else if (buf_cap <= 256) {
         if (d == 128)
             fps_block_kernel<128><<<grid, 256, 0, s>>>(buf, count, new_q, n_new, buf_cap,
                                                        trigger, m, sel_order, n_overflow);
         else
             fps_block_kernel<64><<<grid, 256, 0, s>>>(buf, count, new_q, n_new, buf_cap,
                                                       trigger, m, sel_order, n_overflow);
+    } else {
+        if (buf_cap > kLongCap || (m > kLongM && trigger <= buf_cap)) return hipErrorInvalidValue;
+        const size_t lds = (size_t)buf_cap * sizeof(float);
+        if (d == 128)
+            fps_long_kernel<128><<<grid, 256, lds, s>>>(buf, count, new_q, n_new, buf_cap,
+                                                        trigger, m, sel_order, n_overflow);
+        else
+            fps_long_kernel<64><<<grid, 256, lds, s>>>(buf, count, new_q, n_new, buf_cap,
+                                                       trigger, m, sel_order, n_overflow);
     }
     return hipGetLastError();
 }

@@ -74,9 +74,9 @@ class Stream:
             self.observer(kind, stage, self)
 
     def prefill(self, keys, values, queries):
-        """keys, values: bf16 [U, P, d]; queries: fp32 [U*g, P, d] (P <= 256)."""
+        """keys, values: bf16 [U, P, d]; queries: fp32 [U*g, P, d] (P <= 8192)."""
         P = keys.shape[1]
-        if P < 17 or P > 256 or P >= self.b_max - self.recent_tok:
+        if P < 17 or P > 8192 or P >= self.b_max - self.recent_tok:
             raise ValueError(f"prompt length {P} not supported")
         self.K[:, :P] = keys
         self.V[:, :P] = values

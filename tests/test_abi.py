@@ -66,7 +66,7 @@ def test_score_validation(lib):
     assert _call_score(lib, _shape(n_units=0, aggregate="mean")) == bkv.BKV_OK
     with pytest.raises(ValueError):
         _shape(aggregate="median").policy()
-    assert _call_score(lib, _shape(buf_cap=300)) == bkv.BKV_ENOTSUP
+    assert _call_score(lib, _shape(buf_cap=9000)) == bkv.BKV_ENOTSUP
     big = _shape(n_units=1, l_cap=1 << 23)                        # 2^31 key bytes per unit
     assert _call_score(lib, big, L=1 << 23, t=1 << 23) == bkv.BKV_ENOTSUP
     assert "2^31" in bkv.last_error()
@@ -129,6 +129,13 @@ def test_fps_validation(lib):
     assert call(FAKE, 0, 32, 16) == bkv.BKV_EINVAL     # new_q without rows
     assert call(None, 1, 32, 16) == bkv.BKV_EINVAL     # rows without new_q
     assert call(FAKE, 33, 32, 16) == bkv.BKV_EINVAL    # n_new > buf_cap
+    # (n_units = 0: validation only, nothing is launched)
+    long = _shape(buf_cap=1000, n_units=0)
+    lcall = lambda trig, m: lib.bkv_fps_update(
+        ctypes.byref(long.dims()), ctypes.byref(long.policy()), FAKE, FAKE, None, 0, trig, m,
+        None, None, None)
+    assert lcall(1000, 65) == bkv.BKV_ENOTSUP          # long buffers keep at most 64
+    assert lcall(1001, 65) == bkv.BKV_OK               # append only: no limit on m
 
 
 def test_evict_validation_and_workspace(lib):

@@ -161,3 +161,53 @@ def test_prefill_block_path(d, n):
     for q in range(nq):
         check_fps(host[q, :n], sel[q], 16, f"prefill head {q}")
         assert np.array_equal(out[q, :16], host[q, :n][np.sort(sel[q])])
+
+
+@pytest.mark.parametrize("d,n,cap,nq,m,n_new", [
+    (128, 257, 300, 8, 16, 0),     # just past the workgroup-per-row path
+    (64, 1000, 1000, 6, 16, 1),    # the last row arrives as a new query
+    (128, 2000, 2048, 4, 64, 0),   # the largest kept set of the long path
+    (128, 4096, 4096, 3, 16, 5),
+    (64, 8192, 8192, 1, 16, 0),    # the largest buffer
+])
+def test_long_buffer_fps(d, n, cap, nq, m, n_new):
+    """Buffers of more than 256 rows (prefill FPS over a long prompt): rows
+    streamed from memory on every pass."""
+    log(f"fps long buffer d={d} N={n} cap={cap} heads={nq} m={m} n_new={n_new}")
+    r = np.random.default_rng(n + d + m)
+    host = r.standard_normal((nq, cap, d)).astype(np.float32)
+    host[:, : n // 4] += 3.0 * r.standard_normal((nq, 1, d)).astype(np.float32)
+    host[:, n // 2: n // 2 + 50] += 5.0 * r.standard_normal((nq, 1, d)).astype(np.float32)
+    shape = bkv.Shape(n_units=nq, group=1, d_head=d, l_cap=64, prefix=0, rope_theta=1e6,
+                      buf_cap=cap)
+    buf = torch.from_numpy(host.copy()).to(DEV)
+    count = torch.full((nq,), n - n_new, dtype=torch.int32, device=DEV)
+    newq = (torch.from_numpy(host[:, n - n_new:n].copy()).to(DEV) if n_new else None)
+    sel = torch.full((nq, m), -7, dtype=torch.int32, device=DEV)
+    bkv.fps_update(shape, buf, count, newq, trigger=n, m=m, sel_order=sel)
+    torch.cuda.synchronize()
+    assert torch.all(count == m)
+    out, sel = buf.cpu().numpy(), sel.cpu().numpy()
+    exact = 0
+    for q in range(nq):
+        exact += check_fps(host[q, :n], sel[q], m, f"long head {q}")
+        assert np.array_equal(out[q, :m], host[q, :n][np.sort(sel[q])]), f"head {q} rows"
+    log(f"  {exact}/{nq} heads outside near-ties matched exactly")
+
+
+def test_long_buffer_append_only():
+    d, cap, nq = 128, 600, 5
+    r = np.random.default_rng(3)
+    host = r.standard_normal((nq, cap, d)).astype(np.float32)
+    shape = bkv.Shape(n_units=nq, group=1, d_head=d, l_cap=64, prefix=0, rope_theta=1e6,
+                      buf_cap=cap)
+    buf = torch.from_numpy(host.copy()).to(DEV)
+    count = torch.full((nq,), 500, dtype=torch.int32, device=DEV)
+    newq = torch.from_numpy(r.standard_normal((nq, 40, d)).astype(np.float32)).to(DEV)
+    bkv.fps_update(shape, buf, count, newq, trigger=cap + 1, m=16)
+    torch.cuda.synchronize()
+    assert torch.all(count == 540)
+    got = buf.cpu().numpy()
+    assert np.array_equal(got[:, 500:540], newq.cpu().numpy())
+    assert np.array_equal(got[:, :500], host[:, :500])
+    assert np.array_equal(got[:, 540:], host[:, 540:])

@@ -184,3 +184,16 @@ def test_stream_small_unsorted_compaction_all_units():
     live = st.kpos[:, :st.L]
     assert torch.all(torch.sort(live, dim=1).values[:, 1:] > torch.sort(live, dim=1).values[:, :-1])
     log(f"  evictions {st.n_evictions}, max score rel err {chk.worst:.3g}")
+
+
+def test_stream_long_prompt_prefill():
+    """A 1000-token prompt: the prefill FPS runs on the long-buffer path."""
+    w = synth.shrink(synth.WORKLOADS["stream_small"], prefix=1000, L=1280, b_kv=1152,
+                     stream_steps=300)
+    n = w.stream_steps
+    log(f"stream long prompt: U={w.n_units} g={w.group} P={w.prefix} B_max={w.L} steps={n}")
+    st, chk = _run(w, n, range(w.n_units))
+    assert st.events == _oracle_events(w, n)
+    assert st.n_evictions == 1 and chk.n["evict"] == 1 and chk.n["fps"] > 5
+    log(f"  FPS events {chk.n['fps']}, exact FPS sets {chk.n['exact_fps']}, "
+        f"max score rel err {chk.worst:.3g}")

@@ -52,18 +52,29 @@ __device__ __forceinline__ void wave_sync_lds() {
 
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
-// Wavefront argmin over (value, index) within each 32-lane half (both halves
-// hold the same 32 candidates, one per lane), returned wave-uniform:
-// lane ^ 1 and ^ 2 (quad_perm), the other quad of 8 (row_half_mirror), the
-// other 8 of 16 (row_mirror), lane ^ 16 (swizzle).  (value, index) pairs
-// compare lexicographically, so the order of the steps does not matter.
-__device__ __forceinline__ int half_argmin(float v, int i) {
-    argmin_pair(v, i, dpp_f<0xB1>(v), dpp_i<0xB1>(i));
-    argmin_pair(v, i, dpp_f<0x4E>(v), dpp_i<0x4E>(i));
-    argmin_pair(v, i, dpp_f<0x141>(v), dpp_i<0x141>(i));
-    argmin_pair(v, i, dpp_f<0x140>(v), dpp_i<0x140>(i));
-    argmin_pair(v, i, swap16_f(v), swap16_i(i));
-    return __builtin_amdgcn_readlane(i, 0);
+// A candidate as one 32-bit key that orders like (value, row): the float's
+// bits made monotone (larger value, larger key), the low 5 mantissa bits
+// replaced by the row (0..31).  Values within 32 ulps (2^-18 relative)
+// compare equal and go to the lower row, well inside the method's
+// tolerance and about the size of the fp32 cosines' own rounding.
+// kNoCandidate is larger than every real key (+inf included).
+constexpr uint32_t kNoCandidate = 0xFFFFFFFFu;
+__device__ __forceinline__ uint32_t pick_key(float v, int row) {
+    uint32_t b = __float_as_uint(v);
+    b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    return (b & ~31u) | (uint32_t)row;
+}
+
+// Minimum key over each 32-lane half (both halves hold the same 32
+// candidates), one v_min_u32 per step with the cross-lane move as its DPP
+// operand where the compiler can fold it; returns the winning row.
+__device__ __forceinline__ int half_argmin_key(uint32_t k) {
+    k = min(k, (uint32_t)dpp_i<0xB1>((int)k));
+    k = min(k, (uint32_t)dpp_i<0x4E>((int)k));
+    k = min(k, (uint32_t)dpp_i<0x141>((int)k));
+    k = min(k, (uint32_t)dpp_i<0x140>((int)k));
+    k = min(k, (uint32_t)swap16_i((int)k));
+    return __builtin_amdgcn_readlane((int)k, 0) & 31;
 }
 
 // Buffers of up to 32 rows: one wavefront per query head.
@@ -177,13 +188,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(5))) void fp
     // Lane l stands for row l % 32 from here on.
     const bool valid32 = r32 < N;
     const float inf = __builtin_inff();
-    int pick = half_argmin(valid32 ? colsum / (float)N : inf, r32);
+    int pick = half_argmin_key(valid32 ? pick_key(colsum / (float)N, r32) : kNoCandidate);
     uint32_t sel = 1u << pick;
     int my_pick = (lane == 0) ? pick : -1;
     float S = qt[pick * TS + r32];
     for (int it = 1; it < m; ++it) {
         const bool cand = valid32 && !((sel >> r32) & 1u);
-        pick = half_argmin(cand ? S : inf, r32);
+        pick = half_argmin_key(cand ? pick_key(S, r32) : kNoCandidate);
         sel |= 1u << pick;
         if (lane == it) my_pick = pick;
         S = fmaxf(S, qt[pick * TS + r32]);

@@ -28,6 +28,11 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void st_nt(uint16_t* p, uint4 v) {
     __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4*>(p));
 }
+// Streaming (non-temporal) 16-byte load: each moved row is read once.
+__device__ __forceinline__ uint4 ld_nt(const uint16_t* p) {
+    return __builtin_bit_cast(uint4,
+                              __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
+}
 constexpr int TPI = 16;  // tokens per iteration
 
 // Write-only sink for the stores of tokens past the end of the kept list (or
@@ -97,8 +102,8 @@ __global__ __launch_bounds__(64 * WAVES) void compact_kernel(
         for (int i = 0; i < NI; ++i) {
             b.s[i] = __shfl(kv, st + i * TPW);
             const int64_t r = b.s[i] >= 0 ? b.s[i] : 0;
-            b.k[i] = *(const uint4*)(Ks + r * D + off);
-            b.v[i] = *(const uint4*)(Vs + r * D + off);
+            b.k[i] = ld_nt(Ks + r * D + off);
+            b.v[i] = ld_nt(Vs + r * D + off);
         }
         b.pv = kv >= 0;
         b.p = ps[kv >= 0 ? kv : 0];

@@ -35,4 +35,4 @@ worked example).  One composite is NOT separately pinned:
   no worked eviction with numbers.
 """
 
-from . import bf16, rope, fps, score, select, compact, evict, stream  # noqa: F401
+from . import bf16, rope, fps, score, select, compact, evict, stream, decode  # noqa: F401

@@ -170,6 +170,56 @@ int bkv_score(const bkv_dims* dims, const bkv_policy* pol, const uint16_t* K,
               uint16_t* qobs_out, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * bkv_score_lse -- bkv_score with the softmax denominators already known.
+ *
+ * Summary "未来方向" (fold beacon scoring into the attention kernel, so the
+ * eviction step loses its extra pass); paper text §4.3 for the scores.  The
+ * same scores as bkv_score (max pooling, or the average with
+ * BKV_FLAG_MEAN), where lse_in[u, h, r] (float32, [U, g, 32], row r as in
+ * bkv_score: beacons first) gives the natural-log log-sum-exp of row r's
+ * scaled logits:
+ *   - beacon rows: over slots [0, lse_from) only; slots [lse_from, L) are
+ *     added here (bkv_decode_attend's lse_obs at the step the cache held
+ *     lse_from slots, the beacons then being fixed);
+ *   - recent rows: complete (each recent query's own bkv_decode_attend
+ *     lse_q: that step's cache is exactly the slots the row sees).
+ * The kernel then reads the keys once more for the scores instead of twice.
+ * A beacon value may be -inf (no slots before lse_from) only if
+ * lse_from < L; all values must otherwise be finite.
+ * Requires 0 <= lse_from <= L and what bkv_score requires; no qobs output.
+ */
+int bkv_score_lse(const bkv_dims* dims, const bkv_policy* pol, const uint16_t* K,
+                  const int32_t* kpos, int64_t L, const float* beacons,
+                  const float* recents, int64_t t, const float* lse_in,
+                  int64_t lse_from, float* score, void* ws, size_t ws_bytes,
+                  void* stream);
+
+/*
+ * bkv_decode_attend -- decode attention, with the beacons' denominators.
+ *
+ * Paper text §2.1 (scaled dot-product attention softmax(q k^T / sqrt(d)) V
+ * of the step's query over the cache); summary "未来方向" (beacon scoring
+ * folded into the attention kernel).  Per unit u and query head h of its
+ * group (qh = u * g + h):
+ *   qhat = q[qh] (pre-RoPE float32, [U*g, d]) rotated to t_q as bkv_score
+ *   rotates (fp64, then fp32, then bf16, both RNE);
+ *   s_j = qhat . K[u, j] * sm_scale for j in [0, L) (the step's own key is
+ *   already in slot L - 1, so every slot is visible);
+ *   out[qh] = sum_j softmax(s)_j V[u, j] (float32, [U*g, d]);
+ *   lse_q[qh] = log sum_j exp(s_j) (float32, [U*g]).
+ * With beacons non-NULL (rows 0..15 of each head, stride buf_cap rows, as
+ * for bkv_score), each beacon rotated to t_obs (the coming eviction's step)
+ * gets lse_obs[qh, b] = log sum_j exp(qhat_b . K[u, j] * sm_scale) over the
+ * same L slots (float32, [U*g, 16]); lse_obs may be NULL otherwise.
+ * Keys and values are read once for both.  Requires 1 <= L <= l_cap,
+ * t_q >= 0, t_obs >= 0 with beacons, n_beacon = 16 with beacons.
+ */
+int bkv_decode_attend(const bkv_dims* dims, const bkv_policy* pol, const uint16_t* K,
+                      const uint16_t* V, int64_t L, const float* q, int64_t t_q,
+                      const float* beacons, int64_t t_obs, float* out, float* lse_q,
+                      float* lse_obs, void* stream);
+
+/*
  * bkv_select -- keep set of every unit.
  *
  * Summary step (5); paper text §2.2 (retain the top-scoring pairs) and

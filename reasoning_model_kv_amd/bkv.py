@@ -23,7 +23,8 @@ BKV_FLAG_MEAN = 1      # policy flag: mean pooling (include/bkv.h)
 BKV_FLAG_UNSORTED = 2  # policy flag: bkv_evict fills holes instead of shifting
 
 EXPORTS = ("bkv_abi_version", "bkv_last_error", "bkv_workspace_bytes", "bkv_fps_update",
-           "bkv_score", "bkv_select", "bkv_compact", "bkv_compact_unsorted", "bkv_evict")
+           "bkv_score", "bkv_select", "bkv_compact", "bkv_compact_unsorted", "bkv_evict",
+           "bkv_score_lse", "bkv_decode_attend")
 
 
 class BkvError(RuntimeError):
@@ -116,6 +117,12 @@ def load_library(path=LIB_PATH):
     lib.bkv_evict.restype = ctypes.c_int
     lib.bkv_evict.argtypes = [_PD, _PP, _VP, _VP, _VP, _I64, _VP, _VP, _I64, _I64, _VP, _VP,
                               _VP, _VP, _VP, ctypes.c_size_t, _VP]
+    lib.bkv_score_lse.restype = ctypes.c_int
+    lib.bkv_score_lse.argtypes = [_PD, _PP, _VP, _VP, _I64, _VP, _VP, _I64, _VP, _I64, _VP,
+                                  _VP, ctypes.c_size_t, _VP]
+    lib.bkv_decode_attend.restype = ctypes.c_int
+    lib.bkv_decode_attend.argtypes = [_PD, _PP, _VP, _VP, _I64, _VP, _I64, _VP, _I64, _VP,
+                                      _VP, _VP, _VP]
     if lib.bkv_abi_version() != ABI_VERSION:
         raise ImportError(f"libbkv ABI {lib.bkv_abi_version()} != binding ABI {ABI_VERSION}")
     _lib = lib
@@ -214,6 +221,41 @@ def score(shape, K, kpos, L, beacons, recents, t, score_out, qobs_out=None, ws=N
         _ptr(recents, torch.float32, "recents"), int(t), _ptr(score_out, torch.float32, "score"),
         _bits(qobs_out, "qobs_out", True), _ptr(ws, torch.uint8, "ws"), ws.numel(),
         _stream(stream)))
+
+
+def score_lse(shape, K, kpos, L, beacons, recents, t, lse_in, lse_from, score_out, ws=None,
+              stream=None):
+    lib = load_library()
+    _need_score_inputs(shape, K, kpos, beacons, recents)
+    _need(score_out, shape.n_units * shape.l_cap, "score")
+    _need(lse_in, shape.n_units * shape.group * 32, "lse_in")
+    if ws is None:
+        ws = alloc_workspace(shape, L, 0, K.device)
+    _check(lib.bkv_score_lse(
+        ctypes.byref(shape.dims()), ctypes.byref(shape.policy()), _bits(K, "K"),
+        _ptr(kpos, torch.int32, "kpos"), int(L), _ptr(beacons, torch.float32, "beacons", shape.n_beacon == 0),
+        _ptr(recents, torch.float32, "recents"), int(t), _ptr(lse_in, torch.float32, "lse_in"),
+        int(lse_from), _ptr(score_out, torch.float32, "score"), _ptr(ws, torch.uint8, "ws"),
+        ws.numel(), _stream(stream)))
+
+
+def decode_attend(shape, K, V, L, q, t_q, out, lse_q, beacons=None, t_obs=0, lse_obs=None,
+                  stream=None):
+    lib = load_library()
+    U, d, cap, nq = shape.n_units, shape.d_head, shape.l_cap, shape.n_units * shape.group
+    _need(K, U * cap * d, "K")
+    _need(V, U * cap * d, "V")
+    _need(q, nq * d, "q")
+    _need(out, nq * d, "out")
+    _need(lse_q, nq, "lse_q")
+    _need(beacons, nq * shape.buf_cap * d, "beacons")
+    _need(lse_obs, nq * 16, "lse_obs")
+    _check(lib.bkv_decode_attend(
+        ctypes.byref(shape.dims()), ctypes.byref(shape.policy()), _bits(K, "K"), _bits(V, "V"),
+        int(L), _ptr(q, torch.float32, "q"), int(t_q),
+        _ptr(beacons, torch.float32, "beacons", True), int(t_obs),
+        _ptr(out, torch.float32, "out"), _ptr(lse_q, torch.float32, "lse_q"),
+        _ptr(lse_obs, torch.float32, "lse_obs", True), _stream(stream)))
 
 
 def select(shape, score_t, L, b_kv, kept, stream=None):

@@ -199,11 +199,10 @@ int bkv_fps_update(const bkv_dims* dims, const bkv_policy* pol, float* buf, int3
                       fn);
 }
 
-int bkv_score(const bkv_dims* dims, const bkv_policy* pol, const uint16_t* K,
-              const int32_t* kpos, int64_t L, const float* beacons, const float* recents,
-              int64_t t, float* score, uint16_t* qobs_out, void* ws, size_t ws_bytes,
-              void* stream) {
-    const char* fn = "bkv_score";
+static int score_impl(const char* fn, const bkv_dims* dims, const bkv_policy* pol,
+                      const uint16_t* K, const int32_t* kpos, int64_t L, const float* beacons,
+                      const float* recents, int64_t t, const float* lse_in, int64_t lse_from,
+                      float* score, uint16_t* qobs_out, void* ws, size_t ws_bytes, void* stream) {
     CHECK(check_dims(fn, dims));
     CHECK(check_policy(fn, pol));
     CHECK(check_score_args(fn, dims, pol, K, kpos, L, beacons, recents, t));
@@ -221,8 +220,58 @@ int bkv_score(const bkv_dims* dims, const bkv_policy* pol, const uint16_t* K,
         e = bkv::launch_score(K, kpos, dims->n_units, dims->group, dims->d_head, dims->l_cap,
                               L, beacons, pol->buf_cap, recents, pol->n_beacon,
                               pol->n_recent_q, t, pol->rope_theta, scale_of(dims, pol),
-                              (pol->flags & BKV_FLAG_MEAN) != 0, table, score, qobs_out, s);
+                              (pol->flags & BKV_FLAG_MEAN) != 0, table, score, qobs_out,
+                              lse_in, lse_from, s);
     return hip_result(e, fn);
+}
+
+int bkv_score(const bkv_dims* dims, const bkv_policy* pol, const uint16_t* K,
+              const int32_t* kpos, int64_t L, const float* beacons, const float* recents,
+              int64_t t, float* score, uint16_t* qobs_out, void* ws, size_t ws_bytes,
+              void* stream) {
+    return score_impl("bkv_score", dims, pol, K, kpos, L, beacons, recents, t, nullptr, 0,
+                      score, qobs_out, ws, ws_bytes, stream);
+}
+
+int bkv_score_lse(const bkv_dims* dims, const bkv_policy* pol, const uint16_t* K,
+                  const int32_t* kpos, int64_t L, const float* beacons, const float* recents,
+                  int64_t t, const float* lse_in, int64_t lse_from, float* score,
+                  void* ws, size_t ws_bytes, void* stream) {
+    const char* fn = "bkv_score_lse";
+    if (!lse_in) return fail(BKV_EINVAL, "%s: NULL lse_in", fn);
+    if (!(0 <= lse_from && lse_from <= L))
+        return fail(BKV_EINVAL, "%s: need 0 <= lse_from (%lld) <= L (%lld)", fn,
+                    (long long)lse_from, (long long)L);
+    return score_impl(fn, dims, pol, K, kpos, L, beacons, recents, t, lse_in, lse_from, score,
+                      nullptr, ws, ws_bytes, stream);
+}
+
+int bkv_decode_attend(const bkv_dims* dims, const bkv_policy* pol, const uint16_t* K,
+                      const uint16_t* V, int64_t L, const float* q, int64_t t_q,
+                      const float* beacons, int64_t t_obs, float* out, float* lse_q,
+                      float* lse_obs, void* stream) {
+    const char* fn = "bkv_decode_attend";
+    CHECK(check_dims(fn, dims));
+    CHECK(check_policy(fn, pol));
+    if (!K || !V || !q || !out || !lse_q) return fail(BKV_EINVAL, "%s: NULL tensor pointer", fn);
+    if (beacons && !lse_obs) return fail(BKV_EINVAL, "%s: beacons given without lse_obs", fn);
+    if (beacons && (pol->n_beacon != 16 || pol->buf_cap < 16))
+        return fail(BKV_EINVAL, "%s: beacons need n_beacon 16 and buf_cap >= 16", fn);
+    if (L < 1 || L > dims->l_cap)
+        return fail(BKV_EINVAL, "%s: L %lld not in [1, l_cap=%lld]", fn, (long long)L,
+                    (long long)dims->l_cap);
+    if (t_q < 0 || (beacons && t_obs < 0))
+        return fail(BKV_EINVAL, "%s: negative position", fn);
+    if (L * dims->d_head * 2 > INT32_MAX)
+        return fail(BKV_ENOTSUP, "%s: L %lld keys of d_head %d exceed 2^31 bytes per unit", fn,
+                    (long long)L, dims->d_head);
+    if (dims->n_units == 0) return ok();
+    if (fault_injected(fn)) return fail(BKV_EHIP, "%s: injected HIP failure", fn);
+    return hip_result(bkv::launch_decode(K, V, dims->n_units, dims->group, dims->d_head,
+                                         dims->l_cap, L, q, t_q, beacons, pol->buf_cap, t_obs,
+                                         pol->rope_theta, scale_of(dims, pol), out, lse_q,
+                                         beacons ? lse_obs : nullptr, (hipStream_t)stream),
+                      fn);
 }
 
 int bkv_select(const bkv_dims* dims, const bkv_policy* pol, const float* score, int64_t L,
@@ -317,7 +366,8 @@ int bkv_evict(const bkv_dims* dims, const bkv_policy* pol, uint16_t* K, uint16_t
         e = bkv::launch_score(K, kpos, dims->n_units, dims->group, dims->d_head, dims->l_cap,
                               L, beacons, pol->buf_cap, recents, pol->n_beacon,
                               pol->n_recent_q, t, pol->rope_theta, scale_of(dims, pol),
-                              (pol->flags & BKV_FLAG_MEAN) != 0, table, score, nullptr, s);
+                              (pol->flags & BKV_FLAG_MEAN) != 0, table, score, nullptr,
+                              nullptr, 0, s);
     if (e == hipSuccess)
         e = bkv::launch_select(score, dims->n_units, dims->l_cap, L, b_kv, pol->prefix,
                                pol->recent_tok, kept, s);

@@ -17,12 +17,24 @@ hipError_t launch_fps(float* buf, int32_t* count, const float* new_q,
 hipError_t launch_rope_table(double* table, int64_t t, int n_recent_q, int d,
                              double theta, hipStream_t s);
 
+// lse_in: known softmax denominators by observation row ([U, g, 32],
+// natural log) or NULL; see bkv_score_lse.
 hipError_t launch_score(const uint16_t* K, const int32_t* kpos, int64_t n_units,
                         int g, int d, int64_t l_cap, int64_t L,
                         const float* beacons, int buf_cap, const float* recents,
                         int n_beacon, int n_recent_q, int64_t t, double theta,
                         float sm_scale, bool mean, const double* table, float* score,
-                        uint16_t* qobs_out, hipStream_t s);
+                        uint16_t* qobs_out, const float* lse_in, int64_t lse_from,
+                        hipStream_t s);
+
+// Decode attention of each query head's new query (rotated to t_q) over
+// K, V [0, L), with the beacons' (rotated to t_obs) log-sum-exp when
+// beacons is non-NULL; see bkv_decode_attend.
+hipError_t launch_decode(const uint16_t* K, const uint16_t* V, int64_t n_units, int g, int d,
+                         int64_t l_cap, int64_t L, const float* q, int64_t t_q,
+                         const float* beacons, int buf_cap, int64_t t_obs, double theta,
+                         float sm_scale, float* out, float* lse_q, float* lse_obs,
+                         hipStream_t s);
 
 hipError_t launch_select(const float* score, int64_t n_units, int64_t l_cap,
                          int64_t L, int64_t b_kv, int prefix, int recent_tok,

@@ -82,6 +82,12 @@ struct ScoreArgs {
     int64_t n_units;
     int split;  // 1: each unit's heads are scored by two workgroups (scores pre-zeroed, combined atomically)
     float inv_rows;  // 1 / (g * 32): the mean pooling's divisor
+    // Known softmax denominators (natural-log LSE of the scaled logits),
+    // [U, g, 32] by observation row, or NULL.  Beacon rows' values cover
+    // slots [0, lse_from) and pass 1 adds [lse_from, L); recent rows' values
+    // are complete and pass 1 adds nothing to them.
+    const float* lse_in;
+    int64_t lse_from;
 };
 
 __device__ __forceinline__ int acc_row(int v, int lane) {
@@ -282,11 +288,11 @@ __device__ __forceinline__ void wait_vm() {
 // (the hardware range check, no memory access) and are masked later.  The
 // first NL wavefronts load, NPW direct-to-LDS instructions per lane and
 // tile; each lane's byte offsets within a tile are the same for every tile.
-template <int D, int NL>
+template <int D, int NL, int TK = KT>
 struct TileLoad {
     static constexpr int CPR = D / 8;
-    static constexpr int NPW = KT * CPR / (64 * NL);
-    static_assert(NPW * 64 * NL == KT * CPR, "tile split");
+    static constexpr int NPW = TK * CPR / (64 * NL);
+    static_assert(NPW * 64 * NL == TK * CPR, "tile split");
     // One load instruction fills 64 / CPR key rows (1 KB).  Load k of
     // wavefront w starts at row (k*NL + w) * 64/CPR; the swizzle term of a
     // lane repeats with period NP in k, so NP offsets serve all NPW loads
@@ -304,7 +310,7 @@ struct TileLoad {
         }
     }
 
-    // Issue the loads of keys [base, base + KT) of Ku (L keys) into lds_tile.
+    // Issue the loads of keys [base, base + TK) of Ku (L keys) into lds_tile.
     __device__ __forceinline__ void issue(const uint16_t* Ku, int64_t L, int64_t base,
                                           uint16_t* lds_tile, int wave) const {
         const int bytes = (int)((L - base) * D * 2);
@@ -394,6 +400,11 @@ void score_kernel(ScoreArgs a, int g, int hs) {
     const uint16_t* Ku = a.K + u * a.l_cap * D;
     const int ntiles = (int)((L + KT - 1) / KT);
     const int64_t mask_from = L - a.n_recent_q;  // tiles reaching past this need masks
+    // With known denominators pass 1 covers only the tiles from the one
+    // holding slot lse_from (at least the last tile): tiles t0 .. ntiles-1.
+    const bool lse_mode = a.lse_in != nullptr;
+    const int t0 = lse_mode ? (int)(a.lse_from / KT < ntiles - 1 ? a.lse_from / KT : ntiles - 1) : 0;
+    const int nt1 = ntiles - t0;
     const float c2 = a.c2;
 
     const TileLoad<D, NL> ld(h, lane);
@@ -436,9 +447,9 @@ void score_kernel(ScoreArgs a, int g, int hs) {
     ObsRows<D> obs;
     if (active) obs.load(src1, src2, lane);
     if (loader) {
-        ld.issue(Ku, L, 0, tile0, h);
-        if (!wide && 1 < ntiles) {
-            ld.issue(Ku, L, KT, tile1, h);
+        ld.issue(Ku, L, (int64_t)t0 * KT, tile0, h);
+        if (!wide && 1 < nt1) {
+            ld.issue(Ku, L, (int64_t)(t0 + 1) * KT, tile1, h);
             wait_vm<2 * NPW>();
         } else {
             wait_vm<NPW>();
@@ -501,7 +512,7 @@ void score_kernel(ScoreArgs a, int g, int hs) {
 
     // With 32 recent queries the second tile buffer held table rows: its key
     // tile is issued now.
-    if (loader && wide && 1 < ntiles) ld.issue(Ku, L, KT, tile1, h);
+    if (loader && wide && 1 < nt1) ld.issue(Ku, L, (int64_t)(t0 + 1) * KT, tile1, h);
 
     // Per-lane LDS offsets of the key tiles' B operands, formed after the
     // prologue (from a fresh copy of the lane index) so that they do not
@@ -517,17 +528,17 @@ void score_kernel(ScoreArgs a, int g, int hs) {
 #define BKV_TILE_ITER(it, NST, CUR, NXT2, ...)                                     \
     do {                                                                           \
         if (loader) {                                                              \
-            if ((it) + 1 >= ntiles) wait_vm<0>();                                  \
+            if ((it) + 1 >= nt1) wait_vm<0>();                                     \
             else if (NST) wait_vm<NPW + 1>();                                      \
             else wait_vm<NPW>();                                                   \
         }                                                                          \
         __syncthreads();                                                           \
-        if (loader && (it) + 2 < ntiles)                                           \
-            ld.issue(Ku, L, (int64_t)((it) + 2) * KT, NXT2, h);                    \
+        if (loader && (it) + 2 < nt1)                                              \
+            ld.issue(Ku, L, (int64_t)(t0 + (it) + 2) * KT, NXT2, h);               \
         f32x16 acc0, acc1;                                                         \
         if (SPLIT && !active) { acc0 = f32x16{}; acc1 = f32x16{}; }                \
         else tile_logits<D>(CUR, rd, frag, acc0, acc1);                            \
-        const int64_t base = (int64_t)(it) * KT;                                   \
+        const int64_t base = (int64_t)(t0 + (it)) * KT;                            \
         __VA_ARGS__;                                                               \
     } while (0)
 // Tiles rotate through tile0, tile1, tile2 (tiles 0 and 1 are issued by the
@@ -535,11 +546,11 @@ void score_kernel(ScoreArgs a, int g, int hs) {
 // iteration, which the wait of the next iteration must allow for.
 #define BKV_TILE_LOOP(SDEL, ...)                                                   \
     do {                                                                           \
-        for (int it = 0; it < ntiles; it += 3) {                                   \
+        for (int it = 0; it < nt1; it += 3) {                                      \
             BKV_TILE_ITER(it, (SDEL) && h == 0 && it > 0, tile0, tile2, __VA_ARGS__); \
-            if (it + 1 < ntiles)                                                   \
+            if (it + 1 < nt1)                                                      \
                 BKV_TILE_ITER(it + 1, (SDEL) && h == 0, tile1, tile0, __VA_ARGS__); \
-            if (it + 2 < ntiles)                                                   \
+            if (it + 2 < nt1)                                                      \
                 BKV_TILE_ITER(it + 2, (SDEL) && h == 0, tile2, tile1, __VA_ARGS__); \
         }                                                                          \
     } while (0)
@@ -551,12 +562,35 @@ void score_kernel(ScoreArgs a, int g, int hs) {
     // kRescaleBig (logits at most ~64 log2 units above mc) is summed against
     // the stale mc; otherwise (and for the first tile, where every term
     // overflows against the sentinel) the tile is redone with a rescale.
+    // With known denominators, column 0 of each row starts from the row's
+    // value (in log2 units: LSE * log2(e)) with a sum of 1; a value of -inf
+    // (no slots before lse_from) starts empty like the other columns.
     float mc[16], l[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) { mc[v] = kNegBig; l[v] = 0.f; }
+    if (lse_mode && active && (lane & 31) == 0) {
+        const float* li = a.lse_in + qh * 32;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const float x = li[acc_row(v, lane)] * 1.4426950408889634f;
+            if (x > kNegBig) { mc[v] = x; l[v] = 1.f; }
+        }
+    }
 #define BKV_PASS1                                                                  \
     if (active) {                                                                  \
-    if (base + KT > mask_from) {                                                   \
+    if (lse_mode) {                                                                \
+        /* Beacon rows add the slots in [lse_from, L); recent rows none. */       \
+        int ln = lane; /* fresh copy: the limits are not hoisted */                \
+        asm volatile("" : "+v"(ln));                                              \
+        const int64_t k0 = base + (ln & 31), k1 = k0 + 32;                         \
+        const bool in0 = k0 >= a.lse_from && k0 < L;                               \
+        const bool in1 = k1 >= a.lse_from && k1 < L;                               \
+        _Pragma("unroll") for (int v = 0; v < 16; ++v) {                           \
+            const bool brow = !wide && v < 8;                                      \
+            if (!(brow && in0)) acc0[v] = -__builtin_inff();                       \
+            if (!(brow && in1)) acc1[v] = -__builtin_inff();                       \
+        }                                                                          \
+    } else if (base + KT > mask_from) {                                            \
         int ln = lane; /* fresh copy: the limits are not hoisted */                \
         asm volatile("" : "+v"(ln));                                              \
         const int d0 = (int)(base - mask_from) + (ln & 31), d1 = d0 + 32;          \
@@ -611,6 +645,19 @@ void score_kernel(ScoreArgs a, int g, int hs) {
     for (int v = 0; v < 16; ++v) lse[v] = mc[v] + log2f(l[v]);
 
     // ---------------- pass 2: max over rows of (s - LSE) -------------------
+    // Tiles t_res .. ntiles-1 are still in LDS (tile T in buffer (T - t0) mod
+    // 3).  When pass 1 covered fewer than three tiles, the first two tiles
+    // the backward walk needs beyond those are issued here, into buffers
+    // pass 1 did not use.
+    const int t_res = t0 > ntiles - 3 ? t0 : ntiles - 3;
+    if (loader) {
+        // Tile T < t0 goes to buffer (T - t0) mod 3: 2 for T = t0 - 1, 1 for
+        // T = t0 - 2 (tile ntiles - 2 is issued first: it is used first).
+        if (ntiles - 2 >= 0 && ntiles - 2 < t0)
+            ld.issue(Ku, L, (int64_t)(ntiles - 2) * KT, t0 - (ntiles - 2) == 1 ? tile2 : tile1, h);
+        if (ntiles - 3 >= 0 && ntiles - 3 < t0)
+            ld.issue(Ku, L, (int64_t)(ntiles - 3) * KT, t0 - (ntiles - 3) == 1 ? tile2 : tile1, h);
+    }
     __syncthreads();
     float* score_u = a.score + u * a.l_cap;
 #define BKV_PASS2                                                                  \
@@ -710,7 +757,7 @@ void score_kernel(ScoreArgs a, int g, int hs) {
 #define BKV_REV_ITER(j, CUR, NXT, ...)                                             \
     do {                                                                           \
         const int T = ntiles - 1 - (j);                                            \
-        if (loader && T < ntiles - 3) {                                            \
+        if (loader && T < t_res) {                                                 \
             if (T == 0) wait_vm<0>();                                              \
             else if (h == 0) wait_vm<NPW + 1>();                                   \
             else wait_vm<NPW>();                                                   \
@@ -731,7 +778,7 @@ void score_kernel(ScoreArgs a, int g, int hs) {
         if (j + 2 < ntiles) BKV_REV_ITER(j + 2, B1, B2, __VA_ARGS__);              \
     }
     // Buffers visited from the last tile down: tile T lives in buffer T % 3.
-    switch ((ntiles - 1) % 3) {
+    switch ((ntiles - 1 - t0) % 3) {
         case 0: BKV_REV_LOOP(tile0, tile1, tile2, BKV_PASS2); break;
         case 1: BKV_REV_LOOP(tile1, tile2, tile0, BKV_PASS2); break;
         default: BKV_REV_LOOP(tile2, tile0, tile1, BKV_PASS2); break;
@@ -744,6 +791,265 @@ void score_kernel(ScoreArgs a, int g, int hs) {
 #undef BKV_TILE_LOOP
 #undef BKV_TILE_ITER
 }
+
+// ---------------------------------------------------------------------------
+// Decode attention with the beacons' softmax denominators.
+//
+// Paper text §2.1: the decode step's attention softmax(q k^T / sqrt(d)) V of
+// each query head's new query over its KV head's cache; summary "未来方向":
+// beacon scoring folded into the attention kernel.  While the keys stream
+// through, the same MFMA blocks give the logits of the head's 16 beacons
+// (rotated to the coming eviction's step t_obs), whose log-sum-exp over the
+// cache is the beacon rows' softmax denominator; the new query's own
+// log-sum-exp is a recent row's denominator at the next eviction.
+//
+// Mapping: one workgroup per unit, one wavefront per query head (g <= 8).
+// A fragments (rows of the 32 x 32 x 16 MFMA): rows 0..15 the beacons, row
+// 16 the new query, rows 17..31 zero; each lane rotates its own row's dims
+// (16 s + 8 (lane / 32) .. + 8 for step s pair with the same dims of step
+// s + D/32) in fp64 and rounds through fp32 to bf16.  Keys and values stream
+// through rings of three LDS tiles of 32 rows, two tiles ahead.  Per tile:
+// one 32 x 32 logit block; the beacon rows update a per-lane running (max,
+// sum of exp2) as the scoring's pass 1 does; the new query's 32 logits (row
+// 16: accumulator 8 of lanes 0..31) update a running max and sum, and the
+// lane owning dims 2 lane (D = 128) or lane (D = 64) of the output adds
+// p_j * V[j] for the tile's 32 rows (p_j read from lane j into a scalar).
+constexpr int DT = 32;  // keys per tile of the decode kernel
+
+struct DecodeArgs {
+    const uint16_t* K;
+    const uint16_t* V;
+    int64_t l_cap;
+    int64_t L;
+    const float* q;         // [U * g, D] pre-RoPE, rotated to t_q
+    int64_t t_q;
+    const float* beacons;   // [U * g, buf_cap, D] rows 0..15, rotated to t_obs; or NULL
+    int buf_cap;
+    int64_t t_obs;
+    double theta;
+    float c2;               // sm_scale * log2(e)
+    float* out;             // [U * g, D]
+    float* lse_q;           // [U * g]
+    float* lse_obs;         // [U * g, 16] (when beacons != NULL)
+};
+
+template <int D>
+__device__ __forceinline__ float2 v_pair(const uint16_t* vt, int j, int lane) {
+    constexpr int CPR = D / 8;
+    const char* b = reinterpret_cast<const char*>(vt);
+    if constexpr (D == 128) {
+        const int c = lane >> 2;
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(
+            b + (j * CPR + (c ^ (j % CPR))) * 16 + (lane & 3) * 4);
+        return float2{__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u)};
+    } else {
+        const int c = lane >> 3;
+        const uint16_t x = *reinterpret_cast<const uint16_t*>(
+            b + (j * CPR + (c ^ (j % CPR))) * 16 + (lane & 7) * 2);
+        return float2{__uint_as_float((uint32_t)x << 16), 0.f};
+    }
+}
+
+template <int D, int NL>
+__global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a, int g) {
+    __shared__ __attribute__((aligned(16))) uint16_t k0[DT * D];
+    __shared__ __attribute__((aligned(16))) uint16_t k1[DT * D];
+    __shared__ __attribute__((aligned(16))) uint16_t k2[DT * D];
+    __shared__ __attribute__((aligned(16))) uint16_t v0[DT * D];
+    __shared__ __attribute__((aligned(16))) uint16_t v1[DT * D];
+    __shared__ __attribute__((aligned(16))) uint16_t v2[DT * D];
+    __shared__ double2 tab[2][D / 2];  // cos/sin at t_obs (beacons), at t_q (new query)
+    constexpr int NPW = TileLoad<D, NL, DT>::NPW;
+    constexpr int NS = D / 16;
+
+    const int tid = threadIdx.x;
+    const int h = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const bool loader = h < NL;
+    const int64_t u = blockIdx.x;
+    const int64_t qh = u * g + h;
+    const int64_t L = a.L;
+    const uint16_t* Ku = a.K + u * a.l_cap * D;
+    const uint16_t* Vu = a.V + u * a.l_cap * D;
+    const int ntiles = (int)((L + DT - 1) / DT);
+    const bool obs = a.beacons != nullptr;
+    const TileLoad<D, NL, DT> ld(h, lane);
+
+    // The cos/sin pairs at t_obs and t_q (fp64), first, so that their
+    // registers are free before the rows arrive.
+    for (int e = tid; e < D; e += (int)blockDim.x) {
+        const int which = e / (D / 2), k = e % (D / 2);
+        double c, sn;
+        rope_cs((double)(which == 0 ? a.t_obs : a.t_q), k, D, a.theta, &c, &sn);
+        tab[which][k] = double2{c, sn};
+    }
+    // This lane's row (beacon r < 16, new query r == 16, zero beyond) is
+    // loaded before the first two tiles of keys and values are issued, so
+    // that waiting for it does not wait for the tiles.
+    const int r = lane & 31, hh = lane >> 5;
+    const float* src = nullptr;
+    if (r < 16 && obs) src = a.beacons + (qh * a.buf_cap + r) * (int64_t)D;
+    else if (r == 16) src = a.q + qh * (int64_t)D;
+    float4 x1[NS / 2][2], x2[NS / 2][2];
+#pragma unroll
+    for (int s = 0; s < NS / 2; ++s) {
+        const int k = 16 * s + 8 * hh;
+        x1[s][0] = x1[s][1] = x2[s][0] = x2[s][1] = float4{0.f, 0.f, 0.f, 0.f};
+        if (src) {
+            x1[s][0] = *reinterpret_cast<const float4*>(src + k);
+            x1[s][1] = *reinterpret_cast<const float4*>(src + k + 4);
+            x2[s][0] = *reinterpret_cast<const float4*>(src + k + D / 2);
+            x2[s][1] = *reinterpret_cast<const float4*>(src + k + D / 2 + 4);
+        }
+    }
+    if (loader) {
+        ld.issue(Ku, L, 0, k0, h);
+        ld.issue(Vu, L, 0, v0, h);
+        if (1 < ntiles) {
+            ld.issue(Ku, L, DT, k1, h);
+            ld.issue(Vu, L, DT, v1, h);
+        }
+    }
+    __syncthreads();  // the cos/sin table
+
+    // A fragments: rotate in fp64, round through fp32 to bf16 (zero rows
+    // rotate to zero).
+    bf16x8 frag[NS];
+    {
+        const double2* cs_tab = tab[r == 16 ? 1 : 0];
+#pragma unroll
+        for (int s = 0; s < NS / 2; ++s) {
+            const int k = 16 * s + 8 * hh;
+            double2 csa[4], csb[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) { csa[p] = cs_tab[k + p]; csb[p] = cs_tab[k + 4 + p]; }
+            const uint4 ra = rotate4(x1[s][0], x2[s][0], csa);
+            const uint4 rb = rotate4(x1[s][1], x2[s][1], csb);
+            frag[s] = __builtin_bit_cast(bf16x8, (uint4{ra.x, ra.y, rb.x, rb.y}));
+            frag[s + NS / 2] = __builtin_bit_cast(bf16x8, (uint4{ra.z, ra.w, rb.z, rb.w}));
+        }
+    }
+    const TileRead<D> rd(lane);
+    const float c2 = a.c2;
+
+    // Beacon rows (accumulators 0..7): running max and sum of exp2, lazily
+    // rescaled as in the scoring's pass 1.  New query: running max m (in
+    // log2 units, wave-uniform), per-lane partial sum ls and output o.
+    float mc[8], l[8];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) { mc[v] = kNegBig; l[v] = 0.f; }
+    float m = -__builtin_inff(), ls = 0.f;
+    float o0 = 0.f, o1 = 0.f;
+
+#define BKV_DEC_ITER(it, KC, VC, KN, VN)                                           \
+    do {                                                                           \
+        if (loader) {                                                              \
+            if ((it) + 1 >= ntiles) wait_vm<0>();                                  \
+            else wait_vm<2 * NPW>();                                               \
+        }                                                                          \
+        __syncthreads();                                                           \
+        if (loader && (it) + 2 < ntiles) {                                         \
+            ld.issue(Ku, L, (int64_t)((it) + 2) * DT, KN, h);                      \
+            ld.issue(Vu, L, (int64_t)((it) + 2) * DT, VN, h);                      \
+        }                                                                          \
+        f32x16 acc = f32x16{};                                                     \
+        {                                                                          \
+            const char* kt = reinterpret_cast<const char*>(KC);                    \
+            _Pragma("unroll") for (int s = 0; s < NS; ++s) {                       \
+                const uint4 w = *reinterpret_cast<const uint4*>(kt + rd.off[s]);   \
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                     \
+                    frag[s], __builtin_bit_cast(bf16x8, w), acc, 0, 0, 0);         \
+            }                                                                      \
+        }                                                                          \
+        const int64_t key = (int64_t)(it) * DT + (lane & 31);                      \
+        if (key >= L) {                                                            \
+            _Pragma("unroll") for (int v = 0; v < 16; ++v) acc[v] = -__builtin_inff(); \
+        }                                                                          \
+        if (obs) {                                                                 \
+            float tsum[8];                                                         \
+            float big = 0.f;                                                       \
+            _Pragma("unroll") for (int v = 0; v < 8; ++v) {                        \
+                tsum[v] = exp2_sum(fmaf(acc[v], c2, -mc[v]));                      \
+                big = vmax(big, tsum[v]);                                          \
+            }                                                                      \
+            if (__builtin_amdgcn_ballot_w64(!(big <= kRescaleBig)) == 0) {         \
+                _Pragma("unroll") for (int v = 0; v < 8; ++v) l[v] += tsum[v];     \
+            } else {                                                               \
+                _Pragma("unroll") for (int v = 0; v < 8; ++v) {                    \
+                    const float mn = vmax(mc[v], acc[v] * c2);                     \
+                    l[v] = l[v] * exp2_sum(mc[v] - mn) + exp2_sum(fmaf(acc[v], c2, -mn)); \
+                    mc[v] = mn;                                                    \
+                }                                                                  \
+            }                                                                      \
+        }                                                                          \
+        /* New query: logits in accumulator 8 of lanes 0..31. */                  \
+        const float x = lane < 32 ? acc[8] * c2 : -__builtin_inff();               \
+        float tm = x;                                                              \
+        _Pragma("unroll") for (int o = 1; o < 32; o <<= 1) tm = vmax(tm, __shfl_xor(tm, o)); \
+        const float mt = __builtin_bit_cast(float,                                 \
+            __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, tm)));          \
+        const float mn = vmax(m, mt);                                              \
+        const float alpha = exp2_sum(m - mn);                                      \
+        m = mn;                                                                    \
+        const float p = exp2_sum(x - mn);                                          \
+        ls = ls * alpha + p;                                                       \
+        o0 *= alpha;                                                               \
+        o1 *= alpha;                                                               \
+        _Pragma("unroll") for (int j = 0; j < DT; ++j) {                           \
+            const float pj = __builtin_bit_cast(float,                             \
+                __builtin_amdgcn_readlane(__builtin_bit_cast(int, p), j));         \
+            const float2 vv = v_pair<D>(VC, j, lane);                              \
+            o0 = fmaf(pj, vv.x, o0);                                               \
+            o1 = fmaf(pj, vv.y, o1);                                               \
+        }                                                                          \
+    } while (0)
+
+    for (int it = 0; it < ntiles; it += 3) {
+        BKV_DEC_ITER(it, k0, v0, k2, v2);
+        if (it + 1 < ntiles) BKV_DEC_ITER(it + 1, k1, v1, k0, v0);
+        if (it + 2 < ntiles) BKV_DEC_ITER(it + 2, k2, v2, k1, v1);
+    }
+#undef BKV_DEC_ITER
+
+    // New query: total sum over the 32 lanes, then the output and its LSE.
+    float lt = ls;
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) lt += __shfl_xor(lt, o);
+    lt = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, lt)));
+    const float inv = 1.0f / lt;
+    if constexpr (D == 128) {
+        *reinterpret_cast<float2*>(a.out + qh * (int64_t)D + 2 * lane) = float2{o0 * inv, o1 * inv};
+    } else {
+        a.out[qh * (int64_t)D + lane] = o0 * inv;
+    }
+    constexpr float kLn2 = 0.6931471805599453f;
+    if (lane == 0) a.lse_q[qh] = (m + log2f(lt)) * kLn2;
+    if (obs) {
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) {
+#pragma unroll
+            for (int v = 0; v < 8; ++v) {
+                const float m2 = __shfl_xor(mc[v], o);
+                const float l2 = __shfl_xor(l[v], o);
+                const float mm = fmaxf(mc[v], m2);
+                l[v] = l[v] * exp2_sum(mc[v] - mm) + l2 * exp2_sum(m2 - mm);
+                mc[v] = mm;
+            }
+        }
+        if ((lane & 31) == 0) {
+#pragma unroll
+            for (int v = 0; v < 8; ++v)
+                a.lse_obs[qh * 16 + acc_row(v, lane)] = (mc[v] + log2f(l[v])) * kLn2;
+        }
+    }
+}
+
+template __global__ void decode_kernel<128, 4>(DecodeArgs, int);
+template __global__ void decode_kernel<128, 2>(DecodeArgs, int);
+template __global__ void decode_kernel<128, 1>(DecodeArgs, int);
+template __global__ void decode_kernel<64, 4>(DecodeArgs, int);
+template __global__ void decode_kernel<64, 2>(DecodeArgs, int);
+template __global__ void decode_kernel<64, 1>(DecodeArgs, int);
 
 // Every variant is instantiated explicitly, so each gets its host launch stub
 // even though it is launched from one branch of a conditional.
@@ -786,7 +1092,8 @@ hipError_t launch_score(const uint16_t* K, const int32_t* kpos, int64_t n_units,
                         const float* beacons, int buf_cap, const float* recents,
                         int n_beacon, int n_recent_q, int64_t t, double theta,
                         float sm_scale, bool mean, const double* table, float* score,
-                        uint16_t* qobs_out, hipStream_t s) {
+                        uint16_t* qobs_out, const float* lse_in, int64_t lse_from,
+                        hipStream_t s) {
     (void)n_beacon;
     if (n_units <= 0) return hipSuccess;
     ScoreArgs a;
@@ -804,6 +1111,8 @@ hipError_t launch_score(const uint16_t* K, const int32_t* kpos, int64_t n_units,
     a.table = table;
     a.score = score;
     a.qobs = qobs_out;
+    a.lse_in = lse_in;
+    a.lse_from = lse_from;
     a.n_units = n_units;
     // Groups of more than 4 heads: two workgroups per unit (see score_kernel).
     a.split = g > 4 ? 1 : 0;
@@ -841,6 +1150,43 @@ hipError_t launch_score(const uint16_t* K, const int32_t* kpos, int64_t n_units,
     }
 #undef BKV_LAUNCH
 #undef BKV_LAUNCH_M
+    return hipGetLastError();
+}
+
+hipError_t launch_decode(const uint16_t* K, const uint16_t* V, int64_t n_units, int g, int d,
+                         int64_t l_cap, int64_t L, const float* q, int64_t t_q,
+                         const float* beacons, int buf_cap, int64_t t_obs, double theta,
+                         float sm_scale, float* out, float* lse_q, float* lse_obs,
+                         hipStream_t s) {
+    if (n_units <= 0) return hipSuccess;
+    DecodeArgs a;
+    a.K = K;
+    a.V = V;
+    a.l_cap = l_cap;
+    a.L = L;
+    a.q = q;
+    a.t_q = t_q;
+    a.beacons = beacons;
+    a.buf_cap = buf_cap;
+    a.t_obs = t_obs;
+    a.theta = theta;
+    a.c2 = sm_scale * 1.4426950408889634f;
+    a.out = out;
+    a.lse_q = lse_q;
+    a.lse_obs = lse_obs;
+    const dim3 grid((unsigned)n_units), block(64 * g);
+    const int nl = g >= 4 ? 4 : (g >= 2 ? 2 : 1);
+#define BKV_LAUNCH_DEC(DD, NN) decode_kernel<DD, NN><<<grid, block, 0, s>>>(a, g)
+    if (d == 128) {
+        if (nl == 4) BKV_LAUNCH_DEC(128, 4);
+        else if (nl == 2) BKV_LAUNCH_DEC(128, 2);
+        else BKV_LAUNCH_DEC(128, 1);
+    } else {
+        if (nl == 4) BKV_LAUNCH_DEC(64, 4);
+        else if (nl == 2) BKV_LAUNCH_DEC(64, 2);
+        else BKV_LAUNCH_DEC(64, 1);
+    }
+#undef BKV_LAUNCH_DEC
     return hipGetLastError();
 }
 

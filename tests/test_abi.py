@@ -184,3 +184,45 @@ def _load_missing(mod, tmp_path):
         mod.load_library(str(tmp_path / "nope.so"))
     finally:
         mod._lib = saved
+
+
+def _call_score_lse(lib, shape, L=300, lse_from=284, lse=FAKE):
+    return lib.bkv_score_lse(ctypes.byref(shape.dims()), ctypes.byref(shape.policy()), FAKE,
+                             FAKE, L, FAKE, FAKE, L, lse, lse_from, FAKE, FAKE, 1 << 20, None)
+
+
+def test_score_lse_validation(lib):
+    s = _shape()
+    assert _call_score_lse(lib, s, lse=None) == bkv.BKV_EINVAL
+    assert "lse_in" in bkv.last_error()
+    assert _call_score_lse(lib, s, lse_from=-1) == bkv.BKV_EINVAL
+    assert _call_score_lse(lib, s, lse_from=301) == bkv.BKV_EINVAL   # beyond L
+    assert _call_score_lse(lib, s, L=600) == bkv.BKV_EINVAL          # L > l_cap
+    assert _call_score_lse(lib, _shape(d_head=96)) == bkv.BKV_ENOTSUP
+    assert _call_score_lse(lib, _shape(n_units=0)) == bkv.BKV_OK
+    assert _call_score_lse(lib, _shape(n_units=0), lse_from=300) == bkv.BKV_OK
+
+
+def _call_decode(lib, shape, L=300, t_q=299, beacons=FAKE, t_obs=316, lse_obs=FAKE, out=FAKE,
+                 q=FAKE):
+    return lib.bkv_decode_attend(ctypes.byref(shape.dims()), ctypes.byref(shape.policy()), FAKE,
+                                 FAKE, L, q, t_q, beacons, t_obs, out, FAKE, lse_obs, None)
+
+
+def test_decode_attend_validation(lib, monkeypatch):
+    s = _shape()
+    assert _call_decode(lib, s, q=None) == bkv.BKV_EINVAL
+    assert _call_decode(lib, s, out=None) == bkv.BKV_EINVAL
+    assert _call_decode(lib, s, lse_obs=None) == bkv.BKV_EINVAL      # beacons need lse_obs
+    assert _call_decode(lib, s, L=0) == bkv.BKV_EINVAL
+    assert _call_decode(lib, s, L=513) == bkv.BKV_EINVAL             # L > l_cap
+    assert _call_decode(lib, s, t_q=-1) == bkv.BKV_EINVAL
+    assert _call_decode(lib, s, t_obs=-1) == bkv.BKV_EINVAL
+    assert _call_decode(lib, _shape(n_beacon=0, n_recent_q=32)) == bkv.BKV_EINVAL
+    assert _call_decode(lib, _shape(d_head=32)) == bkv.BKV_ENOTSUP
+    assert _call_decode(lib, _shape(group=9)) == bkv.BKV_ENOTSUP
+    big = _shape(n_units=1, l_cap=1 << 23)
+    assert _call_decode(lib, big, L=1 << 23) == bkv.BKV_ENOTSUP
+    assert _call_decode(lib, _shape(n_units=0), beacons=None, lse_obs=None) == bkv.BKV_OK
+    monkeypatch.setenv("BKV_FAULT_INJECT", "bkv_decode_attend")
+    assert _call_decode(lib, s) == bkv.BKV_EHIP

@@ -1,0 +1,186 @@
+"""Decode attention with beacon denominators (bkv_decode_attend) and scoring
+from known denominators (bkv_score_lse) against the float64 oracle.
+
+The decode kernel streams keys and values in tiles of 32 through rings of
+three LDS tiles; the cases cover one slot, a single partial tile, ragged
+tails with l_cap > L, several ring turns, groups of 2, 4, 5 and 7 and both
+head sizes.  The scoring cases place lse_from so that the tail pass covers
+one tile (the two tiles the backward walk needs next are then loaded
+separately), two tiles, every tile (lse_from = 0) and no slot at all
+(lse_from = L).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from parity_util import TOL, check_kept, check_scores, log
+from reasoning_model_kv_amd import bkv
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _workload(name):
+    if name == "tiny_g7":
+        return synth.shrink(synth.WORKLOADS["tiny"], group=7, d_head=128, theta=1e6)
+    if name == "tiny_g5":
+        return synth.shrink(synth.WORKLOADS["tiny"], group=5, d_head=128, theta=1e6, h_kv=3)
+    if name == "tiny_g1":
+        return synth.shrink(synth.WORKLOADS["tiny"], group=1)
+    return synth.WORKLOADS[name]
+
+
+def _setup(w, L, l_cap):
+    w2 = synth.shrink(w, L=L)
+    inp = synth.workload_inputs(w2)
+    dev = synth.to_device(inp, DEV, l_cap=l_cap)
+    shape = bkv.Shape(w.n_units, w.group, w.d_head, l_cap, w.prefix, w.theta,
+                      recent_tok=w.recent_tok)
+    return inp, dev, shape
+
+
+def _decode(shape, dev, L, q, t_q, beacons=None, t_obs=0):
+    nq, d = shape.n_units * shape.group, shape.d_head
+    out = torch.full((nq, d), float("nan"), device=DEV)
+    lse_q = torch.full((nq,), float("nan"), device=DEV)
+    lse_obs = torch.full((nq, 16), float("nan"), device=DEV) if beacons is not None else None
+    bkv.decode_attend(shape, dev["keys"], dev["values"], L, q, t_q, out, lse_q, beacons, t_obs,
+                      lse_obs)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), lse_q.cpu().numpy(), (None if lse_obs is None else
+                                                     lse_obs.cpu().numpy())
+
+
+DECODE_CASES = [
+    ("tiny", 256, 256),           # d 64, g 2: 8 tiles of 32, ring turns
+    ("tiny", 1, 64),              # one slot
+    ("tiny", 20, 64),             # one partial tile
+    ("tiny", 33, 64),             # one key in the second tile
+    ("tiny", 203, 256),           # ragged tail, l_cap > L
+    ("tiny_g1", 150, 160),        # one head per group (one loader wavefront)
+    ("tiny_g7", 300, 320),        # group 7, d 128
+    ("tiny_g5", 1000, 1000),      # group 5
+    ("qwen3_4b_layer", 2176, 2176),
+]
+
+
+@pytest.mark.parametrize("with_beacons", [True, False])
+@pytest.mark.parametrize("name,L,l_cap", DECODE_CASES)
+def test_decode_attend_matches_oracle(name, L, l_cap, with_beacons):
+    w = _workload(name)
+    log(f"decode {name} L={L} l_cap={l_cap} beacons={with_beacons}")
+    inp, dev, shape = _setup(w, max(L, 16), l_cap)
+    g, d = w.group, w.d_head
+    # The step's query: buffer row 20 of each head, at the newest slot's position.
+    q_host = inp["buf"][:, :, 20]                           # [U, g, d]
+    q = torch.from_numpy(np.ascontiguousarray(q_host.reshape(-1, d))).to(DEV)
+    t_q = int(inp["kpos"][0, L - 1])
+    t_obs = L + 16
+    beacons = dev["buf"] if with_beacons else None
+    out, lse_q, lse_obs = _decode(shape, dev, L, q, t_q, beacons, t_obs)
+    worst_o, worst_l = 0.0, 0.0
+    for u in range(w.n_units):
+        keys, vals = inp["keys"][u][:L], inp["values"][u][:L]
+        ref_o, ref_l = oracle.decode.decode_attention(keys, vals, q_host[u], t_q, w.theta)
+        # |out error| <= TOL * sum_j W_j |V_j|: the bound a relative error TOL
+        # in every softmax weight gives.
+        qhat = oracle.decode.rotated_queries(q_host[u], t_q, w.theta)
+        s = qhat @ np.asarray(keys, np.float64).T / np.sqrt(d)
+        wts = np.exp(s - ref_l[:, None])
+        bound = TOL * (wts @ np.abs(np.asarray(vals, np.float64))) + 1e-6
+        err = np.abs(out[u * g:(u + 1) * g] - ref_o)
+        assert np.all(err <= bound), f"unit {u}: output error {err.max():.3g}"
+        worst_o = max(worst_o, float((err / bound).max()))
+        dl = np.abs(lse_q[u * g:(u + 1) * g] - ref_l)
+        assert np.all(dl <= TOL), f"unit {u}: lse_q error {dl.max():.3g}"
+        worst_l = max(worst_l, float(dl.max()))
+        if with_beacons:
+            ref_b = oracle.decode.beacon_lse(keys, inp["buf"][u][:, :16], t_obs, w.theta)
+            db = np.abs(lse_obs[u * g:(u + 1) * g] - ref_b)
+            assert np.all(db <= TOL), f"unit {u}: lse_obs error {db.max():.3g}"
+            worst_l = max(worst_l, float(db.max()))
+    log(f"  output err / bound {worst_o:.3g}, max lse abs err {worst_l:.3g}")
+
+
+def _lse_from_decode(shape, dev, inp, L, lse_from, t):
+    """The denominators as decoding gathers them, all on the GPU: the beacons'
+    from the step whose cache held lse_from slots, recent query i's from its
+    own step (cache of L - 16 + i + 1 slots)."""
+    U, g, d = shape.n_units, shape.group, shape.d_head
+    lse = torch.empty((U, g, 32), device=DEV)
+    if lse_from > 0:
+        q = dev["recents"][:, 0].contiguous()
+        _, _, lo = _decode(shape, dev, lse_from, q, int(inp["kpos"][0, lse_from - 1]),
+                           dev["buf"], t)
+        lse[:, :, :16] = torch.from_numpy(lo.reshape(U, g, 16)).to(DEV)
+    else:
+        lse[:, :, :16] = -float("inf")
+    for i in range(16):
+        q = dev["recents"][:, i].contiguous()
+        _, lq, _ = _decode(shape, dev, L - 16 + i + 1, q, int(inp["kpos"][0, L - 16 + i]))
+        lse[:, :, 16 + i] = torch.from_numpy(lq.reshape(U, g)).to(DEV)
+    return lse.contiguous()
+
+
+SCORE_CASES = [
+    ("tiny", 256, 256, 240, "max"),        # tail pass: last tile only
+    ("tiny", 203, 256, 187, "max"),        # tail pass: last two tiles
+    ("tiny", 256, 256, 0, "max"),          # every tile (nothing known for the beacons)
+    ("tiny", 256, 256, 256, "max"),        # no slot added
+    ("tiny", 40, 64, 24, "max"),           # one tile in all
+    ("tiny", 517, 600, 501, "max"),        # 5-key last tile
+    ("tiny", 256, 256, 240, "mean"),
+    ("tiny_g7", 300, 320, 284, "max"),     # two workgroups per unit
+    ("tiny_g5", 1000, 1000, 984, "max"),
+    ("qwen3_4b_layer", 2176, 2176, 2160, "max"),
+]
+
+
+@pytest.mark.parametrize("name,L,l_cap,lse_from,aggregate", SCORE_CASES)
+def test_score_lse_matches_oracle(name, L, l_cap, lse_from, aggregate):
+    w = _workload(name)
+    log(f"score_lse {name} L={L} l_cap={l_cap} lse_from={lse_from} {aggregate}")
+    inp, dev, shape = _setup(w, L, l_cap)
+    shape.aggregate = aggregate
+    t = L
+    lse = _lse_from_decode(shape, dev, inp, L, lse_from, t)
+    score = torch.full((w.n_units, l_cap), -1.0, device=DEV)
+    bkv.score_lse(shape, dev["keys"], dev["kpos"], L, dev["buf"], dev["recents"], t, lse,
+                  lse_from, score)
+    torch.cuda.synchronize()
+    sc = score.cpu().numpy()
+    worst, n_diff = 0.0, 0
+    B = min(w.b_kv, L - 1)
+    for u in range(w.n_units):
+        beacons = inp["buf"][u][:, :16]
+        taus = inp["kpos"][u][L - 16:L]
+        ref = oracle.score.score_unit(inp["keys"][u], beacons, inp["recents"][u], t, taus,
+                                      w.theta, aggregate=aggregate)
+        worst = max(worst, check_scores(sc[u, :L], ref, f"{name} unit {u}"))
+        if l_cap > L:
+            assert np.all(sc[u, L:] == -1.0), "slots past L must be untouched"
+        if aggregate == "max" and B > w.prefix + w.recent_tok:
+            kept = oracle.select.select(sc[u, :L].astype(np.float64), L, B, w.prefix,
+                                        w.recent_tok)
+            n_diff += check_kept(kept, ref, L, B, w.prefix, w.recent_tok, f"unit {u}")
+    log(f"  max rel err {worst:.3g}, kept-set differences in the tie band {n_diff}")
+
+
+def test_score_lse_agrees_with_two_pass_kernel():
+    # Same unit, same kernel family: one read with known denominators vs the
+    # two-pass call; both within the tolerance of each other.
+    w = synth.WORKLOADS["qwen3_4b_layer"]
+    inp, dev, shape = _setup(w, w.L, w.L)
+    lse = _lse_from_decode(shape, dev, inp, w.L, w.L - 16, w.L)
+    s1 = torch.empty((w.n_units, w.L), device=DEV)
+    s2 = torch.empty((w.n_units, w.L), device=DEV)
+    bkv.score(shape, dev["keys"], dev["kpos"], w.L, dev["buf"], dev["recents"], w.L, s1)
+    bkv.score_lse(shape, dev["keys"], dev["kpos"], w.L, dev["buf"], dev["recents"], w.L, lse,
+                  w.L - 16, s2)
+    torch.cuda.synchronize()
+    a, b = s1.cpu().numpy().astype(np.float64), s2.cpu().numpy().astype(np.float64)
+    rel = np.abs(a - b) / b
+    log(f"score_lse vs score: max rel diff {rel.max():.3g}")
+    assert rel.max() <= 2 * TOL

@@ -71,6 +71,11 @@ def parse():
     p.add_argument("--prefill-fps", type=int, default=0, metavar="N",
                    help="time the prefill FPS instead: every query head of the workload "
                         "compresses an N-row prompt buffer to 16 (N up to 8192)")
+    p.add_argument("--fused-decode", action="store_true",
+                   help="the eviction with the softmax denominators gathered by decode "
+                        "attention (bkv_decode_attend at the beacon fix and at each recent "
+                        "query's step, then bkv_score_lse: one key read); the extra cost of the "
+                        "beacon rows in decode attention is timed and charged to the step")
     p.add_argument("--stream-steps", type=int, default=0,
                    help="decode steps of a streaming workload (0: the workload's own)")
     return p.parse_args()
@@ -225,6 +230,9 @@ def main():
         stream_main(args, w)
         return
     window = args.observe == "recent32"
+    if args.fused_decode:
+        fused_main(args, w)
+        return
     if window:
         w = synth.shrink(w, n_beacon=0, n_recent_q=32, recent_tok=32)
     cpu = None
@@ -437,6 +445,218 @@ def main():
     }
     print(json.dumps(out), flush=True)
 
+
+
+def fused_main(args, w):
+    """The eviction step with its softmax denominators taken from decode
+    attention.  Untimed set-up (work decoding does anyway): bkv_decode_attend
+    over each recent query's own cache gives the recent rows' denominators.
+    Timed: the decode attention of the step at the beacon fix (cache of L-16
+    slots) with and without the beacon rows (the difference is charged to the
+    eviction step), and the step itself: FPS compress, bkv_score_lse (one key
+    read), select, compact, merge FPS."""
+    import numpy as np
+    import torch
+
+    import synth
+    from reasoning_model_kv_amd import bkv
+
+    bkv.load_library()
+    if not torch.cuda.is_available():
+        eprint("no GPU visible")
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    U, g, d, L, B = w.n_units, w.group, w.d_head, w.L, w.b_kv
+    nq = U * g
+    L_fix = L - w.recent_tok
+    eprint(f"[bench] fused decode: workload {w.name}: U={U} g={g} d={d} L={L} B_KV={B}")
+    inp = synth.device_inputs(w, dev)
+    torch.cuda.synchronize()
+    K0, V0, P0 = inp["keys"], inp["values"], inp["kpos"]
+    buf0, rec = inp["buf"], inp["recents"]
+    newq = buf0[:, 31:32].clone()
+    K, V, kpos = torch.empty_like(K0), torch.empty_like(V0), torch.empty_like(P0)
+    buf = torch.empty_like(buf0)
+    count = torch.empty((nq,), dtype=torch.int32, device=dev)
+    score = torch.empty((U, L), dtype=torch.float32, device=dev)
+    kept = torch.empty((U, B), dtype=torch.int32, device=dev)
+    scrub = torch.empty(512 * 2**20 // 4, dtype=torch.float32, device=dev)
+    shape = bkv.Shape(U, g, d, L, w.prefix, w.theta, recent_tok=w.recent_tok)
+    ws = bkv.alloc_workspace(shape, L, 0, dev)
+    stream = torch.cuda.current_stream()
+    out = torch.empty((nq, d), dtype=torch.float32, device=dev)
+    lse_q = torch.empty((nq,), dtype=torch.float32, device=dev)
+    lse_obs = torch.empty((nq, 16), dtype=torch.float32, device=dev)
+    lse_in = torch.empty((U, g, 32), dtype=torch.float32, device=dev)
+    q_fix = buf0[:, 30].contiguous()     # the query of the step at the beacon fix
+
+    def restore():
+        K.copy_(K0)
+        V.copy_(V0)
+        kpos.copy_(P0)
+        buf.copy_(buf0)
+        count.fill_(31)
+        scrub.fill_(1.0)
+
+    # Denominators of the recent rows: each recent query's decode step.
+    K.copy_(K0)
+    V.copy_(V0)
+    for i in range(16):
+        qi = rec[:, i].contiguous()
+        bkv.decode_attend(shape, K, V, L - 16 + i + 1, qi, int(P0[0, L - 16 + i]), out, lse_q)
+        lse_in[:, :, 16 + i] = lse_q.view(U, g)
+
+    def decode_fix(with_beacons):
+        # The beacons are the compressed buffer's rows 0..15 (the state
+        # before this step's compress is the same up to the appended row).
+        if with_beacons:
+            bkv.decode_attend(shape, K, V, L_fix, q_fix, int(P0[0, L_fix - 1]), out, lse_q,
+                              buf, L, lse_obs)
+        else:
+            bkv.decode_attend(shape, K, V, L_fix, q_fix, int(P0[0, L_fix - 1]), out, lse_q)
+
+    names = ["fps_compress", "score", "select", "compact", "fps_merge"]
+    calls = {
+        "fps_compress": lambda: bkv.fps_update(shape, buf, count, newq, trigger=32, m=16),
+        "score": lambda: bkv.score_lse(shape, K, kpos, L, buf, rec, L, lse_in, L_fix, score,
+                                       ws=ws),
+        "select": lambda: bkv.select(shape, score, L, B, kept),
+        "compact": lambda: bkv.compact(shape, K, V, kpos, L, kept, B),
+        "fps_merge": lambda: bkv.fps_update(shape, buf, count, rec, trigger=32, m=16),
+    }
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+    evd = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+
+    def prepare():
+        # State before the step, plus the beacons' denominators as the fused
+        # decode step leaves them (from the compressed buffer of this state).
+        restore()
+        bkv.fps_update(shape, buf, count, newq, trigger=32, m=16)
+        decode_fix(True)
+        lse_in[:, :, :16] = lse_obs.view(U, g, 16)
+        buf.copy_(buf0)
+        count.fill_(31)
+        scrub.fill_(1.0)
+
+    def step():
+        ev[0].record(stream)
+        for j, n in enumerate(names):
+            calls[n]()
+            ev[j + 1].record(stream)
+
+    def decodes():
+        scrub.fill_(1.0)
+        evd[0].record(stream)
+        decode_fix(False)
+        evd[1].record(stream)
+        scrub.fill_(1.0)
+        torch.cuda.synchronize()
+        evd[2].record(stream)
+        decode_fix(True)
+        ev_end = torch.cuda.Event(enable_timing=True)
+        ev_end.record(stream)
+        torch.cuda.synchronize()
+        return evd[0].elapsed_time(evd[1]), evd[2].elapsed_time(ev_end)
+
+    for _ in range(args.warmup):
+        prepare()
+        torch.cuda.synchronize()
+        step()
+        torch.cuda.synchronize()
+        decodes()
+    stage_ms = {n: [] for n in names}
+    wall = []
+    dec_plain, dec_fused = [], []
+    for _ in range(args.steps):
+        prepare()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        step()
+        torch.cuda.synchronize()
+        wall.append(time.perf_counter() - t0)
+        for j, n in enumerate(names):
+            stage_ms[n].append(ev[j].elapsed_time(ev[j + 1]))
+        a, b = decodes()
+        dec_plain.append(a)
+        dec_fused.append(b)
+    eprint(f"[bench] {args.steps} timed steps done (fused-decode eviction)")
+
+    kept_host = kept.cpu().numpy()
+    n_mv = int(np.count_nonzero(kept_host != np.arange(B)[None, :]))
+    gpu_ms = {n: float(np.mean(v)) for n, v in stage_ms.items()}
+    sbytes = stage_bytes(w, n_mv)
+    sbytes["score"] += U * g * 32 * 4          # the known denominators read
+    extra_ms = max(0.0, float(np.mean(dec_fused)) - float(np.mean(dec_plain)))
+    step_ms = sum(gpu_ms.values()) + extra_ms
+    total_bytes = sum(sbytes.values())
+    stages = {}
+    for n in names:
+        gbs = sbytes[n] / (gpu_ms[n] * 1e-3) / 1e9
+        stages[n] = {"us": round(gpu_ms[n] * 1e3, 2), "alg_bytes": sbytes[n],
+                     "GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    flops = 2.0 * U * g * 32 * d * L
+    stages["score"]["TFLOPs"] = round(flops / (gpu_ms["score"] * 1e-3) / 1e12, 2)
+    dec_bytes = U * (2 * L_fix * d * 2) + nq * d * 4 * 2
+    dec = {"L": L_fix, "us_plain": round(float(np.mean(dec_plain)) * 1e3, 2),
+           "us_with_beacon_rows": round(float(np.mean(dec_fused)) * 1e3, 2),
+           "alg_bytes": dec_bytes,
+           "hbm_frac_plain": round(dec_bytes / (np.mean(dec_plain) * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                   4)}
+    dom = max(names, key=lambda n: gpu_ms[n])
+    achieved = sbytes[dom] / (gpu_ms[dom] * 1e-3) / 1e9
+
+    check = None
+    if not args.no_check:
+        import oracle
+        sample = [0, U // 3, U - 1]
+        prepare()
+        bkv.fps_update(shape, buf, count, newq, trigger=32, m=16)
+        beacons = buf[:, :16].cpu().numpy()
+        bkv.score_lse(shape, K, kpos, L, buf, rec, L, lse_in, L_fix, score, ws=ws)
+        torch.cuda.synchronize()
+        worst = 0.0
+        for u in sample:
+            taus = P0[u, L - 16:L].cpu().numpy()
+            ref = oracle.score.score_unit(K0[u, :L].float().cpu().numpy(),
+                                          beacons[u * g:(u + 1) * g],
+                                          rec[u * g:(u + 1) * g].cpu().numpy(), L, taus, w.theta)
+            s_gpu = score[u].cpu().numpy()
+            worst = max(worst, float(np.max(np.abs(s_gpu - ref) / (ref + 1e-30))))
+        check = {"units": sample, "max_score_rel_err": worst}
+        eprint(f"[bench] parity on units {sample}: {check}")
+
+    ms_wall = 1e3 * float(np.mean(wall)) + extra_ms
+    out_line = {
+        "metric": METRIC,
+        "value": round(U * L / (ms_wall * 1e-3), 1),
+        "unit": "KV-head·key-tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_wall, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "units": U, "layers": w.layers, "batch": w.batch,
+                   "kv_heads": w.h_kv, "group": g, "d_head": d, "L": L, "b_kv": B,
+                   "prefix": w.prefix, "recent": w.recent_tok, "rope_theta": w.theta,
+                   "pooling": "max", "compaction": "sorted",
+                   "observation": "beacons16+recent16",
+                   "denominators": "from decode attention (beacons at L-16, recents at their steps)"},
+        "unit_evictions_per_s": round(U / (ms_wall * 1e-3), 1),
+        "step": ("bkv_fps_update (compress) + bkv_score_lse + bkv_select + bkv_compact + "
+                 "bkv_fps_update (merge), plus the beacon rows' extra time in decode attention"),
+        "gpu_ms_per_step": round(step_ms, 4),
+        "gpu_ms_beacon_rows_in_decode": round(extra_ms, 4),
+        "alg_bytes_per_step": total_bytes,
+        "hbm_frac_step": round(total_bytes / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "moved_tokens": n_mv,
+        "stages": stages,
+        "decode_attention": dec,
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+        "cpu_baseline": None,
+        "parity": check,
+    }
+    print(json.dumps(out_line), flush=True)
 
 def stream_main(args, w):
     """Streaming decode run (the Qwen3-14B-shaped workload): the whole policy

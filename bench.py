@@ -38,7 +38,7 @@ METRIC = "KV-head·key-tokens scored/s + evictions/s at Qwen3-4B shape; % of HBM
 DEFAULT_WORKLOAD = "qwen3_4b_full_b2048"
 KERNEL_SOURCES = {
     "fps_compress": "fps.hip", "score": "score.hip", "select": "select.hip",
-    "compact": "compact.hip", "fps_merge": "fps.hip",
+    "compact": "compact.hip", "fps_merge": "fps.hip", "score_lse": "score.hip",
 }
 
 
@@ -652,7 +652,9 @@ def fused_main(args, w):
         "decode_attention": dec,
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_from_profile("score_lse" if dom == "score" else dom,
+                                                     w.name)},
         "cpu_baseline": None,
         "parity": check,
     }

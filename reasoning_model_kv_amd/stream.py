@@ -22,6 +22,15 @@ compact by filling the evicted slots (bkv_compact_unsorted): the cache is
 then not in position order, which scoring and the slot-based masks do not
 need (every slot below the recent window holds an older token).
 
+With fused_decode=True the steps' decode attention (bkv_decode_attend) also
+gathers the scores' softmax denominators: at the beacon fix it adds the
+beacon rows, rotated to the coming eviction's step, and at each recent step
+the new query's own log-sum-exp is kept; the eviction then scores with
+bkv_score_lse (one read of the keys) and runs select, compact and the merge
+as separate calls.  The attention output of those steps is left in
+`attn_out`; other steps' attention is the decoder's own business and is not
+run here.
+
 Writing the new token's key, value and position into the cache is the
 decoder's own work and is done here with plain tensor writes; every step of
 the policy runs in the library.  An optional observer is called with
@@ -37,12 +46,16 @@ from . import bkv
 
 class Stream:
     def __init__(self, n_units, group, d_head, b_max, b_kv, prefix, theta, recent_tok=16,
-                 device="cuda", observer=None, beacon_policy="fps", unsorted=False):
+                 device="cuda", observer=None, beacon_policy="fps", unsorted=False,
+                 fused_decode=False):
         if b_max - b_kv < recent_tok or b_kv < prefix + recent_tok:
             raise ValueError("need prefix + recent_tok <= b_kv <= b_max - recent_tok")
         if beacon_policy not in ("fps", "initial"):
             raise ValueError(f"beacon_policy must be 'fps' or 'initial', not {beacon_policy!r}")
         self.policy = beacon_policy
+        if fused_decode and beacon_policy != "fps":
+            raise ValueError("fused_decode needs the Continual-FPS beacons")
+        self.fused = fused_decode
         dev = torch.device(device)
         self.shape = bkv.Shape(n_units, group, d_head, b_max, prefix, theta,
                                recent_tok=recent_tok, unsorted=unsorted)
@@ -68,6 +81,13 @@ class Stream:
         self.events = []  # (kind, cache length)
         self.observer = observer
         self.n_evictions = 0
+        if fused_decode:
+            self.attn_out = torch.zeros((nq, d_head), dtype=torch.float32, device=dev)
+            self.lse_q = torch.zeros((nq,), dtype=torch.float32, device=dev)
+            self.lse_obs = torch.zeros((nq, 16), dtype=torch.float32, device=dev)
+            self.lse_in = torch.zeros((U, group, 32), dtype=torch.float32, device=dev)
+            self.lse_from = 0
+            self.t_obs = -1
 
     def _note(self, kind, stage):
         if self.observer is not None:
@@ -137,10 +157,25 @@ class Stream:
                     self.events.append(("beacon_fix_noop", L))
                 self.phase = "recent"
                 self.rcount.zero_()
+                if self.fused:
+                    # This step's attention, plus the fixed beacons rotated to
+                    # the eviction's step (recent_tok more tokens from here).
+                    self.t_obs = self.t + 1 + self.recent_tok
+                    bkv.decode_attend(self.shape, self.K, self.V, L, q, self.t, self.attn_out,
+                                      self.lse_q, self.buf, self.t_obs, self.lse_obs)
+                    self.lse_in[:, :, :16] = self.lse_obs.view(-1, self.shape.group, 16)
+                    self.lse_from = L
         else:
             # recent query: appended to the recents buffer, never compressed
             bkv.fps_update(self.rshape, self.recents, self.rcount, q[:, None],
                            trigger=self.rshape.buf_cap + 1, m=16)
+            if self.fused:
+                # The step's attention; its log-sum-exp is recent row i's
+                # denominator (this cache is exactly what that row sees).
+                i = L - 1 - (self.b_max - self.recent_tok)
+                bkv.decode_attend(self.shape, self.K, self.V, L, q, self.t, self.attn_out,
+                                  self.lse_q)
+                self.lse_in[:, :, 16 + i] = self.lse_q.view(-1, self.shape.group)
         self.t += 1
         if L == self.b_max:
             self._evict()
@@ -165,10 +200,23 @@ class Stream:
         L = self.L
         initial = self.policy == "initial"
         self._note("evict", "pre")
-        bkv.evict(self.shape, self.K, self.V, self.kpos, L, self.buf, self.recents, self.t,
-                  self.b_kv, buf=None if initial else self.buf,
-                  count=None if initial else self.count, score_out=self.score,
-                  kept_out=self.kept, ws=self.ws)
+        if self.fused:
+            if self.t != self.t_obs:
+                raise RuntimeError("eviction step differs from the beacons' rotation step")
+            sh = self.shape
+            bkv.score_lse(sh, self.K, self.kpos, L, self.buf, self.recents, self.t,
+                          self.lse_in, self.lse_from, self.score, ws=self.ws)
+            bkv.select(sh, self.score, L, self.b_kv, self.kept)
+            if sh.unsorted:
+                bkv.compact_unsorted(sh, self.K, self.V, self.kpos, L, self.kept, self.b_kv)
+            else:
+                bkv.compact(sh, self.K, self.V, self.kpos, L, self.kept, self.b_kv)
+            bkv.fps_update(sh, self.buf, self.count, self.recents, trigger=32, m=16)
+        else:
+            bkv.evict(self.shape, self.K, self.V, self.kpos, L, self.buf, self.recents,
+                      self.t, self.b_kv, buf=None if initial else self.buf,
+                      count=None if initial else self.count, score_out=self.score,
+                      kept_out=self.kept, ws=self.ws)
         self.L = self.b_kv
         if not initial:
             self.rows = 16

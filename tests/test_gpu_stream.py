@@ -112,10 +112,11 @@ def _oracle_events(w, n_steps, policy="fps"):
     return st.events
 
 
-def _run(w, n_steps, units, chunk=128, policy="fps", unsorted=False):
+def _run(w, n_steps, units, chunk=128, policy="fps", unsorted=False, fused=False):
     chk = Checker(w, units, policy, unsorted)
     st = bstream.Stream(w.n_units, w.group, w.d_head, w.L, w.b_kv, w.prefix, w.theta,
-                        device=DEV, observer=chk, beacon_policy=policy, unsorted=unsorted)
+                        device=DEV, observer=chk, beacon_policy=policy, unsorted=unsorted,
+                        fused_decode=fused)
     gen = synth.StreamInputs(w, DEV)
     st.prefill(*gen.prompt())
     done = 0
@@ -197,3 +198,28 @@ def test_stream_long_prompt_prefill():
     assert st.n_evictions == 1 and chk.n["evict"] == 1 and chk.n["fps"] > 5
     log(f"  FPS events {chk.n['fps']}, exact FPS sets {chk.n['exact_fps']}, "
         f"max score rel err {chk.worst:.3g}")
+
+
+@pytest.mark.parametrize("unsorted", [False, True])
+def test_stream_small_fused_decode_all_units(unsorted):
+    """Denominators gathered by decode attention (beacon rows at the beacon
+    fix, each recent query's own step), one key read at each eviction: same
+    cadence, and every eviction checked against the two-pass definition."""
+    w = synth.WORKLOADS["stream_small"]
+    n = w.stream_steps
+    log(f"stream {w.name} (fused decode, unsorted={unsorted}): U={w.n_units} steps={n}")
+    st, chk = _run(w, n, range(w.n_units), unsorted=unsorted, fused=True)
+    assert st.events == _oracle_events(w, n)
+    assert chk.n["evict"] == st.n_evictions >= 2 and chk.n["fps"] > 10
+    log(f"  evictions {st.n_evictions}, max score rel err {chk.worst:.3g}")
+
+
+def test_stream_qwen3_14b_fused_decode_sampled():
+    w = synth.WORKLOADS["qwen3_14b_stream"]
+    n = (w.L - w.prefix) + 128 + 40
+    units = [0, 2047, w.n_units - 1]
+    log(f"stream {w.name} (fused decode): steps={n} sampled units {units}")
+    st, chk = _run(w, n, units, fused=True)
+    assert st.events == _oracle_events(w, n)
+    assert st.n_evictions == 2 and chk.n["evict"] == 2
+    log(f"  max score rel err {chk.worst:.3g}")

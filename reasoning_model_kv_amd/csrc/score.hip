@@ -996,6 +996,7 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a, int g) {
         o0 *= alpha;                                                               \
         o1 *= alpha;                                                               \
         _Pragma("unroll") for (int j = 0; j < DT; ++j) {                           \
+            if (j % 8 == 0) __builtin_amdgcn_sched_barrier(0);                     \
             const float pj = __builtin_bit_cast(float,                             \
                 __builtin_amdgcn_readlane(__builtin_bit_cast(int, p), j));         \
             const float2 vv = v_pair<D>(VC, j, lane);                              \

@@ -405,6 +405,12 @@ void score_kernel(ScoreArgs a, int g, int hs) {
     const bool lse_mode = a.lse_in != nullptr;
     const int t0 = lse_mode ? (int)(a.lse_from / KT < ntiles - 1 ? a.lse_from / KT : ntiles - 1) : 0;
     const int nt1 = ntiles - t0;
+    // The prologue's second tile: the next one of pass 1, or, when pass 1
+    // has a single tile, the first one pass 2 needs beyond it (tile
+    // ntiles-2, into buffer 1; pass 2 then visits the buffers in the
+    // reflected order 0, 1, 2).
+    const bool reflect = lse_mode && nt1 == 1 && ntiles >= 2;
+    const int second = nt1 >= 2 ? t0 + 1 : (reflect ? ntiles - 2 : -1);
     const float c2 = a.c2;
 
     const TileLoad<D, NL> ld(h, lane);
@@ -448,8 +454,8 @@ void score_kernel(ScoreArgs a, int g, int hs) {
     if (active) obs.load(src1, src2, lane);
     if (loader) {
         ld.issue(Ku, L, (int64_t)t0 * KT, tile0, h);
-        if (!wide && 1 < nt1) {
-            ld.issue(Ku, L, (int64_t)(t0 + 1) * KT, tile1, h);
+        if (!wide && second >= 0) {
+            ld.issue(Ku, L, (int64_t)second * KT, tile1, h);
             wait_vm<2 * NPW>();
         } else {
             wait_vm<NPW>();
@@ -512,7 +518,7 @@ void score_kernel(ScoreArgs a, int g, int hs) {
 
     // With 32 recent queries the second tile buffer held table rows: its key
     // tile is issued now.
-    if (loader && wide && 1 < nt1) ld.issue(Ku, L, (int64_t)(t0 + 1) * KT, tile1, h);
+    if (loader && wide && second >= 0) ld.issue(Ku, L, (int64_t)second * KT, tile1, h);
 
     // Per-lane LDS offsets of the key tiles' B operands, formed after the
     // prologue (from a fresh copy of the lane index) so that they do not
@@ -645,19 +651,11 @@ void score_kernel(ScoreArgs a, int g, int hs) {
     for (int v = 0; v < 16; ++v) lse[v] = mc[v] + log2f(l[v]);
 
     // ---------------- pass 2: max over rows of (s - LSE) -------------------
-    // Tiles t_res .. ntiles-1 are still in LDS (tile T in buffer (T - t0) mod
-    // 3).  When pass 1 covered fewer than three tiles, the first two tiles
-    // the backward walk needs beyond those are issued here, into buffers
-    // pass 1 did not use.
-    const int t_res = t0 > ntiles - 3 ? t0 : ntiles - 3;
-    if (loader) {
-        // Tile T < t0 goes to buffer (T - t0) mod 3: 2 for T = t0 - 1, 1 for
-        // T = t0 - 2 (tile ntiles - 2 is issued first: it is used first).
-        if (ntiles - 2 >= 0 && ntiles - 2 < t0)
-            ld.issue(Ku, L, (int64_t)(ntiles - 2) * KT, t0 - (ntiles - 2) == 1 ? tile2 : tile1, h);
-        if (ntiles - 3 >= 0 && ntiles - 3 < t0)
-            ld.issue(Ku, L, (int64_t)(ntiles - 3) * KT, t0 - (ntiles - 3) == 1 ? tile2 : tile1, h);
-    }
+    // Tiles t_res .. ntiles-1 are in LDS and complete (tile T in buffer
+    // (T - t0) mod 3, or (ntiles - 1 - T) mod 3 when reflected); every other
+    // tile is loaded by the walk two iterations ahead, the first of them at
+    // iteration 0 when fewer than three tiles are resident.
+    const int t_res = reflect ? ntiles - 2 : (t0 > ntiles - 3 ? t0 : ntiles - 3);
     __syncthreads();
     float* score_u = a.score + u * a.l_cap;
 #define BKV_PASS2                                                                  \
@@ -749,11 +747,12 @@ void score_kernel(ScoreArgs a, int g, int hs) {
                 score_u[key] = tot * a.inv_rows;                                   \
         }                                                                          \
     }
-// Pass 2 walks the tiles backwards: at the end of pass 1 the last three
-// tiles are still in LDS (tile T in buffer T % 3), so they are scored
-// without being read again, and the rest stream in from the end with the
-// same ring, two tiles ahead.  Iteration j scores tile T = ntiles - 1 - j
-// from CUR and loads tile T - 2 into NXT (the buffer tile T + 1 used).
+// Pass 2 walks the tiles backwards: at the end of pass 1 the last tiles
+// (three, or the ones pass 1 covered plus the prologue's second tile) are
+// still in LDS, so they are scored without being read again, and the rest
+// stream in from the end with the same ring, two tiles ahead.  Iteration j
+// scores tile T = ntiles - 1 - j from CUR and loads tile T - 2 into NXT
+// (the buffer tile T + 1 used, or an unused one at j = 0).
 #define BKV_REV_ITER(j, CUR, NXT, ...)                                             \
     do {                                                                           \
         const int T = ntiles - 1 - (j);                                            \
@@ -763,7 +762,7 @@ void score_kernel(ScoreArgs a, int g, int hs) {
             else wait_vm<NPW>();                                                   \
         }                                                                          \
         __syncthreads();                                                           \
-        if (loader && T - 2 >= 0 && T - 2 < ntiles - 3)                            \
+        if (loader && T - 2 >= 0 && T - 2 < t_res)                                 \
             ld.issue(Ku, L, (int64_t)(T - 2) * KT, NXT, h);                        \
         f32x16 acc0, acc1;                                                         \
         if (SPLIT && !active) { acc0 = f32x16{}; acc1 = f32x16{}; }                \
@@ -777,11 +776,15 @@ void score_kernel(ScoreArgs a, int g, int hs) {
         if (j + 1 < ntiles) BKV_REV_ITER(j + 1, B2, B0, __VA_ARGS__);              \
         if (j + 2 < ntiles) BKV_REV_ITER(j + 2, B1, B2, __VA_ARGS__);              \
     }
-    // Buffers visited from the last tile down: tile T lives in buffer T % 3.
-    switch ((ntiles - 1 - t0) % 3) {
-        case 0: BKV_REV_LOOP(tile0, tile1, tile2, BKV_PASS2); break;
-        case 1: BKV_REV_LOOP(tile1, tile2, tile0, BKV_PASS2); break;
-        default: BKV_REV_LOOP(tile2, tile0, tile1, BKV_PASS2); break;
+    // Buffers visited from the last tile down.
+    if (reflect) {
+        BKV_REV_LOOP(tile0, tile2, tile1, BKV_PASS2);
+    } else {
+        switch ((ntiles - 1 - t0) % 3) {
+            case 0: BKV_REV_LOOP(tile0, tile1, tile2, BKV_PASS2); break;
+            case 1: BKV_REV_LOOP(tile1, tile2, tile0, BKV_PASS2); break;
+            default: BKV_REV_LOOP(tile2, tile0, tile1, BKV_PASS2); break;
+        }
     }
 #undef BKV_REV_LOOP
 #undef BKV_REV_ITER

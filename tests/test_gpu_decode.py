@@ -130,6 +130,8 @@ SCORE_CASES = [
     ("tiny", 256, 256, 0, "max"),          # every tile (nothing known for the beacons)
     ("tiny", 256, 256, 256, "max"),        # no slot added
     ("tiny", 40, 64, 24, "max"),           # one tile in all
+    ("tiny", 100, 128, 84, "max"),         # two tiles: pass 1 on one, the other from the prologue
+    ("tiny", 150, 192, 100, "max"),        # three tiles, pass 1 on two: the third at pass 2's start
     ("tiny", 517, 600, 501, "max"),        # 5-key last tile
     ("tiny", 256, 256, 240, "mean"),
     ("tiny_g7", 300, 320, 284, "max"),     # two workgroups per unit

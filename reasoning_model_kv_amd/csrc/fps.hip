@@ -51,6 +51,26 @@ __device__ __forceinline__ void wave_sync_lds() {
 }
 
 typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+
+// Eight fp32 values split into bf16 high parts (the top 16 bits, exact) and
+// low parts (the remainder, exact in fp32, rounded to bf16): hi + lo equals
+// each value to within 2^-16 of it.  Packed in dimension order.
+__device__ __forceinline__ void split_bf16(const float* v, uint4& hi, uint4& lo) {
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t b0 = __float_as_uint(v[2 * i]), b1 = __float_as_uint(v[2 * i + 1]);
+        h[i] = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
+        const f32x2 r = {v[2 * i] - __uint_as_float(b0 & 0xFFFF0000u),
+                         v[2 * i + 1] - __uint_as_float(b1 & 0xFFFF0000u)};
+        l[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2));
+    }
+    hi = uint4{h[0], h[1], h[2], h[3]};
+    lo = uint4{l[0], l[1], l[2], l[3]};
+}
 
 // A candidate as one 32-bit key that orders like (value, row): the float's
 // bits made monotone (larger value, larger key), the low 5 mantissa bits
@@ -80,19 +100,24 @@ __device__ __forceinline__ int half_argmin_key(uint32_t k) {
 // Buffers of up to 32 rows: one wavefront per query head.
 //  * Lane pair (2r, 2r+1) loads row r (half of its d fp32 values each) into
 //    registers, where the rows stay until the kept ones are written back.
-//  * The unit-normalised rows go to LDS transposed (dim-major), one half of
-//    the dims at a time, and the 32 x 32 cosine matrix C = Qn Qn^T is formed
-//    with d/2 fp32 MFMAs (v_mfma_f32_32x32x2_f32; lane l supplies row
-//    l % 32, dim 2t + l / 32 of the half in LDS).
+//  * The unit-normalised rows go to LDS row-major, one half of the dims at a
+//    time, each value split into bf16 high and low parts (hi + lo within
+//    2^-16 of it), and the 32 x 32 cosine matrix C = Qn Qn^T is formed as
+//    Hi Hi^T + Hi Lo^T + Lo Hi^T on bf16 MFMAs (v_mfma_f32_32x32x16_bf16,
+//    fp32 accumulate; lane l supplies row l % 32, dims 16 s + 8 (l / 32) ..
+//    + 8 of step s, which serve as both operands since C = Qn Qn^T): 3 d/16
+//    MFMAs instead of the d/2 of 32x32x2 fp32 ones.  The dropped Lo Lo^T
+//    term and the rounding leave each cosine within about 2^-15 of fp32.
 //  * Lane l then stands for row l % 32.  The average cosine of row j is the
 //    sum of column j of C (C is symmetric) over N; the seed is its argmin.
 //    Each further pick p adds column p of C (one LDS read per lane) to the
 //    running max S, and the next pick is the argmin of S over the rows not
 //    yet picked.
 //  * The kept rows leave through LDS, eight at a time, as contiguous stores.
-//  LDS stays at about 8 KB (d = 128), so some 18 wavefronts share a CU.
+//  LDS stays at about 8 KB (d = 128) and registers at 128 or fewer, so 16
+//  wavefronts share a CU.
 template <int D>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(5))) void fps_wave_kernel(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void fps_wave_kernel(
     float* __restrict__ buf, int32_t* __restrict__ count,
     const float* __restrict__ new_q, int n_new, int cap, int trigger, int m,
     int32_t* __restrict__ sel_order, int32_t* __restrict__ n_overflow) {
@@ -155,25 +180,43 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(5))) void fp
     nn += dpp_f<0xB1>(nn);  // the lane pair's other half (quad_perm [1,0,3,2])
     const float inv = 1.0f / fmaxf(sqrtf(nn), kNormFloor);
 
-    // C = Qn Qn^T over two rounds, one per half of the dims: the lanes holding
-    // that half store it transposed to LDS (padding rows are zero rows), then
-    // d/4 MFMAs add it.  Lane l ends with C[i][l % 32] for
+    // C over two rounds, one per half of the dims: the lanes holding that half
+    // store it (hi and lo parts, rows of HD bf16 each, 16-byte chunks
+    // XOR-swizzled by row so the fragment reads spread over the banks), then
+    // 3 * HD / 16 MFMAs add it.  Lane l ends with C[i][l % 32] for
     // i = 8 (v / 4) + 4 (l / 32) + v % 4.
     const int r32 = lane & 31;
     const int kk = lane >> 5;
+    constexpr int CH = HD / 8;  // 16-byte chunks per half row
+    uint4* qh4 = reinterpret_cast<uint4*>(qt);           // hi parts: [32][CH]
+    uint4* ql4 = reinterpret_cast<uint4*>(qt) + 32 * CH;  // lo parts: [32][CH]
+    static_assert(2 * 32 * CH * 16 <= LDSF * 4, "hi/lo halves fit the LDS buffer");
     f32x16 acc = f32x16{};
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
         if (hf) wave_sync_lds();  // the first round's operand reads are done
         if (half == hf) {
 #pragma unroll
-            for (int k = 0; k < HD; ++k) qt[k * TS + row] = x[k] * inv;
+            for (int c = 0; c < CH; ++c) {
+                float v[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = x[8 * c + e] * inv;
+                uint4 h4, l4;
+                split_bf16(v, h4, l4);
+                const int pc = row * CH + (c ^ (row % CH));
+                qh4[pc] = h4;
+                ql4[pc] = l4;
+            }
         }
         wave_sync_lds();
-#pragma unroll 8
-        for (int t = 0; t < HD / 2; ++t) {
-            const float a = qt[(2 * t + kk) * TS + r32];
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, a, acc, 0, 0, 0);
+#pragma unroll
+        for (int st = 0; st < HD / 16; ++st) {
+            const int pc = r32 * CH + ((2 * st + kk) ^ (r32 % CH));
+            const bf16x8 a = __builtin_bit_cast(bf16x8, qh4[pc]);
+            const bf16x8 b = __builtin_bit_cast(bf16x8, ql4[pc]);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, a, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, acc, 0, 0, 0);
         }
     }
     float colsum = 0.f;
@@ -187,7 +230,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(5))) void fp
 
     // Lane l stands for row l % 32 from here on.
     const bool valid32 = r32 < N;
-    const float inf = __builtin_inff();
     int pick = half_argmin_key(valid32 ? pick_key(colsum / (float)N, r32) : kNoCandidate);
     uint32_t sel = 1u << pick;
     int my_pick = (lane == 0) ? pick : -1;

@@ -29,6 +29,10 @@ def _workload(name):
         return synth.shrink(synth.WORKLOADS["tiny"], group=5, d_head=128, theta=1e6, h_kv=3)
     if name == "tiny_g1":
         return synth.shrink(synth.WORKLOADS["tiny"], group=1)
+    if name == "tiny_g3":
+        return synth.shrink(synth.WORKLOADS["tiny"], group=3, d_head=128, theta=1e6)
+    if name == "tiny_g8":
+        return synth.shrink(synth.WORKLOADS["tiny"], group=8, d_head=64)
     return synth.WORKLOADS[name]
 
 
@@ -60,6 +64,8 @@ DECODE_CASES = [
     ("tiny", 33, 64),             # one key in the second tile
     ("tiny", 203, 256),           # ragged tail, l_cap > L
     ("tiny_g1", 150, 160),        # one head per group (one loader wavefront)
+    ("tiny_g3", 97, 128),         # three wavefronts, two of them loaders
+    ("tiny_g8", 129, 160),        # eight wavefronts (512 threads), d 64
     ("tiny_g7", 300, 320),        # group 7, d 128
     ("tiny_g5", 1000, 1000),      # group 5
     ("qwen3_4b_layer", 2176, 2176),
@@ -136,6 +142,8 @@ SCORE_CASES = [
     ("tiny", 256, 256, 240, "mean"),
     ("tiny_g7", 300, 320, 284, "max"),     # two workgroups per unit
     ("tiny_g5", 1000, 1000, 984, "max"),
+    ("tiny_g8", 300, 300, 284, "mean"),    # split group of eight, mean pooling
+    ("tiny_g3", 129, 160, 113, "max"),     # three heads, a 1-key last tile
     ("qwen3_4b_layer", 2176, 2176, 2160, "max"),
 ]
 

@@ -76,6 +76,8 @@ def parse():
                         "attention (bkv_decode_attend at the beacon fix and at each recent "
                         "query's step, then bkv_score_lse: one key read); the extra cost of the "
                         "beacon rows in decode attention is timed and charged to the step")
+    p.add_argument("--no-variants", dest="variants", action="store_false",
+                   help="skip the fused-decode variant that the default run appends to its line")
     p.add_argument("--stream-steps", type=int, default=0,
                    help="decode steps of a streaming workload (0: the workload's own)")
     return p.parse_args()
@@ -231,7 +233,7 @@ def main():
         return
     window = args.observe == "recent32"
     if args.fused_decode:
-        fused_main(args, w)
+        print(json.dumps(fused_main(args, w)), flush=True)
         return
     if window:
         w = synth.shrink(w, n_beacon=0, n_recent_q=32, recent_tok=32)
@@ -447,6 +449,18 @@ def main():
         "cpu_baseline": cpu,
         "parity": check,
     }
+    if (args.variants and not window and args.aggregate == "max"
+            and args.compaction == "sorted"):
+        # The same step with its denominators from decode attention, in the
+        # same run (the standalone measurement's buffers released first).
+        del K, V, kpos, K0, V0, P0, buf, buf0, rec, scrub, inp
+        torch.cuda.empty_cache()
+        f = fused_main(args, w)
+        fv = {k: f[k] for k in ("value", "ms_per_step", "gpu_ms_per_step",
+                                "gpu_ms_beacon_rows_in_decode", "hbm_frac_step", "step")}
+        fv["score_us"] = f["stages"]["score"]["us"]
+        fv["parity"] = f["parity"]
+        out["variants"] = {"fused_decode": fv}
     print(json.dumps(out), flush=True)
 
 
@@ -666,7 +680,7 @@ def fused_main(args, w):
         "cpu_baseline": None,
         "parity": check,
     }
-    print(json.dumps(out_line), flush=True)
+    return out_line
 
 def stream_main(args, w):
     """Streaming decode run (the Qwen3-14B-shaped workload): the whole policy

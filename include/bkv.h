@@ -128,8 +128,9 @@ size_t bkv_workspace_bytes(const bkv_dims* dims, const bkv_policy* pol,
  * n_new = 16 recents with trigger 32 after an eviction (merge);
  * trigger = buf_cap + 1 (append only, never compress: collecting the recent
  * queries, summary step (3), in a buffer of n_recent_q rows).
- * The cosine matrix of a buffer of up to 32 rows is formed on fp32 MFMA
- * (v_mfma_f32_32x32x2_f32); other arithmetic is fp32.  Requires
+ * The cosine matrix of a buffer of up to 32 rows is formed on bf16 MFMA
+ * from a high/low split of the fp32 rows (each cosine within about 2^-15 of
+ * fp32); other arithmetic is fp32.  Requires
  * 0 <= n_new <= buf_cap, new_q NULL iff n_new == 0,
  * 1 <= m < trigger <= buf_cap + 1, buf_cap <= 8192 (and m <= 64 when
  * buf_cap > 256 and heads can compress), every count in

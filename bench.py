@@ -39,6 +39,7 @@ DEFAULT_WORKLOAD = "qwen3_4b_full_b2048"
 KERNEL_SOURCES = {
     "fps_compress": "fps.hip", "score": "score.hip", "select": "select.hip",
     "compact": "compact.hip", "fps_merge": "fps.hip", "score_lse": "score.hip",
+    "select_compact": ("compact.hip", "select_wave.h"),
 }
 
 
@@ -99,13 +100,19 @@ def stage_bytes(w, n_mv_total):
         "compact": n_mv_total * (4 * d * 2 + 8) + U * B * 4,
         # 16 beacons + 16 recents in, 16 rows out, count
         "fps_merge": nq * ((16 + 16 + 16) * d * 4 + 8),
+        # the two in one launch
+        "select_compact": (U * ((L - P - R) * 4 + B * 4) +
+                           n_mv_total * (4 * d * 2 + 8) + U * B * 4),
     }
 
 
-def source_digest(name):
-    path = os.path.join(ROOT, "reasoning_model_kv_amd", "csrc", name)
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_digest(names):
+    """First 16 hex digits of the SHA-256 of the named source(s), concatenated."""
+    h = hashlib.sha256()
+    for name in ([names] if isinstance(names, str) else names):
+        with open(os.path.join(ROOT, "reasoning_model_kv_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_from_profile(kernel, workload):
@@ -306,9 +313,11 @@ def main():
         eva[2].record(stream)
 
     # The same work as separate calls, with events between them, for the
-    # per-stage breakdown and the roofline of the dominant kernel.
-    names = (["score", "select", "compact"] if window else
-             ["fps_compress", "score", "select", "compact", "fps_merge"])
+    # per-stage breakdown and the roofline of the dominant kernel: the
+    # kernels bkv_evict runs (selection and in-place compaction in one
+    # launch, except for the unsorted compaction).
+    sel = ["select", "compact"] if shape.unsorted else ["select_compact"]
+    names = (["score"] + sel if window else ["fps_compress", "score"] + sel + ["fps_merge"])
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
 
     def step():
@@ -319,6 +328,7 @@ def main():
             "select": lambda: bkv.select(shape, score, L, B, kept),
             "compact": lambda: (bkv.compact_unsorted(shape, K, V, kpos, L, kept, B)
                                 if shape.unsorted else bkv.compact(shape, K, V, kpos, L, kept, B)),
+            "select_compact": lambda: bkv.select_compact(shape, score, L, B, K, V, kpos, kept),
             "fps_merge": lambda: bkv.fps_update(shape, buf, count, rec, trigger=32, m=16),
         }
         ev[0].record(stream)
@@ -537,13 +547,12 @@ def fused_main(args, w):
         else:
             bkv.decode_attend(shape, K, V, L_fix, q_fix, int(P0[0, L_fix - 1]), out, lse_q)
 
-    names = ["fps_compress", "score", "select", "compact", "fps_merge"]
+    names = ["fps_compress", "score", "select_compact", "fps_merge"]
     calls = {
         "fps_compress": lambda: bkv.fps_update(shape, buf, count, newq, trigger=32, m=16),
         "score": lambda: bkv.score_lse(shape, K, kpos, L, buf, rec, L, lse_in, L_fix, score,
                                        ws=ws),
-        "select": lambda: bkv.select(shape, score, L, B, kept),
-        "compact": lambda: bkv.compact(shape, K, V, kpos, L, kept, B),
+        "select_compact": lambda: bkv.select_compact(shape, score, L, B, K, V, kpos, kept),
         "fps_merge": lambda: bkv.fps_update(shape, buf, count, rec, trigger=32, m=16),
     }
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
@@ -606,7 +615,7 @@ def fused_main(args, w):
     kept_host = kept.cpu().numpy()
     n_mv = int(np.count_nonzero(kept_host != np.arange(B)[None, :]))
     gpu_ms = {n: float(np.mean(v)) for n, v in stage_ms.items()}
-    sbytes = stage_bytes(w, n_mv)
+    sbytes = {n: b for n, b in stage_bytes(w, n_mv).items() if n in names}
     sbytes["score"] += U * g * 32 * 4          # the known denominators read
     extra_ms = max(0.0, float(np.mean(dec_fused)) - float(np.mean(dec_plain)))
     step_ms = sum(gpu_ms.values()) + extra_ms
@@ -663,7 +672,7 @@ def fused_main(args, w):
                    "observation": "beacons16+recent16",
                    "denominators": "from decode attention (beacons at L-16, recents at their steps)"},
         "unit_evictions_per_s": round(U / (ms_wall * 1e-3), 1),
-        "step": ("bkv_fps_update (compress) + bkv_score_lse + bkv_select + bkv_compact + "
+        "step": ("bkv_fps_update (compress) + bkv_score_lse + bkv_select_compact + "
                  "bkv_fps_update (merge), plus the beacon rows' extra time in decode attention"),
         "gpu_ms_per_step": round(step_ms, 4),
         "gpu_ms_beacon_rows_in_decode": round(extra_ms, 4),

@@ -254,6 +254,20 @@ int bkv_compact(const bkv_dims* dims, uint16_t* K, uint16_t* V, int32_t* kpos,
                 void* stream);
 
 /*
+ * bkv_select_compact -- bkv_select, then an in-place bkv_compact, in one
+ * launch where the unit fits (L <= 4608 slots; beyond, the two kernels).
+ *
+ * Summary step (5) (keep prefix, recent and Top-K; write back in position
+ * order); paper text §2.2.  The same kept sets and the same compacted K, V
+ * and kpos as the two calls: one wavefront per unit selects its keep set
+ * (written to kept, [U, b_kv], ascending) and then moves the kept tokens.
+ * Requires what bkv_select requires.
+ */
+int bkv_select_compact(const bkv_dims* dims, const bkv_policy* pol, const float* score,
+                       int64_t L, int64_t b_kv, uint16_t* K, uint16_t* V, int32_t* kpos,
+                       int32_t* kept, void* stream);
+
+/*
  * bkv_compact_unsorted -- fill the evicted slots instead of shifting.
  *
  * Unsorted variant of bkv_compact, in place.  The ThinKV pages note that
@@ -273,8 +287,8 @@ int bkv_compact_unsorted(const bkv_dims* dims, uint16_t* K, uint16_t* V, int32_t
 /*
  * bkv_evict -- one full eviction event (summary steps (4)-(6)).
  *
- * Runs bkv_score, bkv_select and an in-place bkv_compact (bkv_compact_unsorted
- * with BKV_FLAG_UNSORTED) on K, V, kpos; then,
+ * Runs bkv_score, then bkv_select_compact (or bkv_select and
+ * bkv_compact_unsorted with BKV_FLAG_UNSORTED) on K, V, kpos; then,
  * if buf is non-NULL, the rolling update of summary step (6): the recent
  * queries are appended to each head's buffer (which must hold exactly the
  * n_beacon beacons, count == n_beacon) and the buffer is compressed back to

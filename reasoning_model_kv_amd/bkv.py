@@ -24,7 +24,7 @@ BKV_FLAG_UNSORTED = 2  # policy flag: bkv_evict fills holes instead of shifting
 
 EXPORTS = ("bkv_abi_version", "bkv_last_error", "bkv_workspace_bytes", "bkv_fps_update",
            "bkv_score", "bkv_select", "bkv_compact", "bkv_compact_unsorted", "bkv_evict",
-           "bkv_score_lse", "bkv_decode_attend")
+           "bkv_score_lse", "bkv_decode_attend", "bkv_select_compact")
 
 
 class BkvError(RuntimeError):
@@ -120,6 +120,8 @@ def load_library(path=LIB_PATH):
     lib.bkv_score_lse.restype = ctypes.c_int
     lib.bkv_score_lse.argtypes = [_PD, _PP, _VP, _VP, _I64, _VP, _VP, _I64, _VP, _I64, _VP,
                                   _VP, ctypes.c_size_t, _VP]
+    lib.bkv_select_compact.restype = ctypes.c_int
+    lib.bkv_select_compact.argtypes = [_PD, _PP, _VP, _I64, _I64, _VP, _VP, _VP, _VP, _VP]
     lib.bkv_decode_attend.restype = ctypes.c_int
     lib.bkv_decode_attend.argtypes = [_PD, _PP, _VP, _VP, _I64, _VP, _I64, _VP, _I64, _VP,
                                       _VP, _VP, _VP]
@@ -266,6 +268,20 @@ def select(shape, score_t, L, b_kv, kept, stream=None):
         ctypes.byref(shape.dims()), ctypes.byref(shape.policy()),
         _ptr(score_t, torch.float32, "score"), int(L), int(b_kv),
         _ptr(kept, torch.int32, "kept"), _stream(stream)))
+
+
+def select_compact(shape, score_t, L, b_kv, K, V, kpos, kept, stream=None):
+    lib = load_library()
+    U, d, cap = shape.n_units, shape.d_head, shape.l_cap
+    _need(score_t, U * cap, "score")
+    _need(kept, U * int(b_kv), "kept")
+    _need(K, U * cap * d, "K")
+    _need(V, U * cap * d, "V")
+    _need(kpos, U * cap, "kpos")
+    _check(lib.bkv_select_compact(
+        ctypes.byref(shape.dims()), ctypes.byref(shape.policy()),
+        _ptr(score_t, torch.float32, "score"), int(L), int(b_kv), _bits(K, "K"), _bits(V, "V"),
+        _ptr(kpos, torch.int32, "kpos"), _ptr(kept, torch.int32, "kept"), _stream(stream)))
 
 
 def compact(shape, K, V, kpos, L, kept, b_kv, K_out=None, V_out=None, kpos_out=None,

@@ -15,6 +15,7 @@
 // before the store that needs its data is issued.
 
 #include "common.h"
+#include "select_wave.h"
 
 namespace bkv {
 namespace {
@@ -41,18 +42,16 @@ constexpr int TPI = 16;  // tokens per iteration
 // the store may be missing and wait for loads still in flight).  Never read.
 __device__ uint4 g_sink[64];
 
+// The walk of one unit u by one wavefront (lane = its lane).
 template <int D>
-__global__ __launch_bounds__(64 * WAVES) void compact_kernel(
+__device__ __forceinline__ void compact_wave(
     uint16_t* K, uint16_t* V, int32_t* kpos, int64_t l_cap, const int32_t* __restrict__ kept,
     int64_t L, int64_t b_kv, uint16_t* Ko, uint16_t* Vo, int32_t* kposo, int64_t out_cap,
-    int64_t n_units) {
+    int64_t u, int lane) {
     constexpr int LPT = D / 8;        // lanes per token row (16-byte chunks)
     constexpr int TPW = 64 / LPT;     // tokens per wave instruction
     constexpr int NI = TPI / TPW;     // instructions per tensor per iteration (<= 4)
     static_assert(NI >= 1 && NI <= 4, "tokens per iteration");
-    const int lane = threadIdx.x & 63;
-    const int64_t u = (int64_t)blockIdx.x * WAVES + (threadIdx.x >> 6);
-    if (u >= n_units) return;
     const bool inplace = (Ko == nullptr);
     const int32_t* ku = kept + u * b_kv;
     const uint16_t* Ks = K + u * l_cap * D;
@@ -144,6 +143,64 @@ __global__ __launch_bounds__(64 * WAVES) void compact_kernel(
         base += TPI;
         if (base >= b_kv) break;
     }
+}
+
+template <int D>
+__global__ __launch_bounds__(64 * WAVES) void compact_kernel(
+    uint16_t* K, uint16_t* V, int32_t* kpos, int64_t l_cap, const int32_t* __restrict__ kept,
+    int64_t L, int64_t b_kv, uint16_t* Ko, uint16_t* Vo, int32_t* kposo, int64_t out_cap,
+    int64_t n_units) {
+    const int64_t u = (int64_t)blockIdx.x * WAVES + (threadIdx.x >> 6);
+    if (u >= n_units) return;
+    compact_wave<D>(K, V, kpos, l_cap, kept, L, b_kv, Ko, Vo, kposo, out_cap, u, threadIdx.x & 63);
+}
+
+// Selection and in-place compaction of a unit by one wavefront (summary
+// step (5) as one launch): the wavefront selects the unit's keep set from its
+// scores (select_wave_reg, units of up to 64 * NR slots), writes it to kept,
+// and then walks it as compact_kernel does.  The keep set is read back from
+// memory after a workgroup-scope release/acquire, so the walk sees every
+// lane's writes.  A unit's selection is latency-bound and its walk
+// bandwidth-bound: the wavefronts of other units keep HBM busy meanwhile.
+template <int D, int NR>
+__device__ __forceinline__ void select_compact_wave(
+    uint16_t* K, uint16_t* V, int32_t* kpos, int64_t l_cap, const float* __restrict__ score,
+    int32_t* kept, int64_t L, int64_t b_kv, int prefix, int recent_tok, int64_t u, int lane,
+    uint32_t* hist) {
+    select_wave_reg<NR>(score + u * l_cap, L, b_kv, prefix, recent_tok, kept + u * b_kv, hist,
+                        lane);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    compact_wave<D>(K, V, kpos, l_cap, kept, L, b_kv, nullptr, nullptr, nullptr, 0, u, lane);
+}
+
+// Units of up to 64 * 36 slots: held to 128 VGPRs, four wavefronts per SIMD
+// as in compact_kernel.
+template <int D, int NR>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4)))
+void select_compact_kernel(uint16_t* K, uint16_t* V, int32_t* kpos, int64_t l_cap,
+                           const float* __restrict__ score, int32_t* kept, int64_t L,
+                           int64_t b_kv, int prefix, int recent_tok, int64_t n_units) {
+    __shared__ uint32_t hist[WAVES][256];
+    const int w = threadIdx.x >> 6;
+    const int64_t u = (int64_t)blockIdx.x * WAVES + w;
+    if (u >= n_units) return;
+    select_compact_wave<D, NR>(K, V, kpos, l_cap, score, kept, L, b_kv, prefix, recent_tok, u,
+                               threadIdx.x & 63, hist[w]);
+}
+
+// Up to 64 * 72 slots: the 72 score registers per lane need more than 128
+// VGPRs (held to 128 they spill), so three wavefronts per SIMD.
+template <int D>
+__global__ __launch_bounds__(64 * WAVES) void select_compact_kernel_wide(
+    uint16_t* K, uint16_t* V, int32_t* kpos, int64_t l_cap, const float* __restrict__ score,
+    int32_t* kept, int64_t L, int64_t b_kv, int prefix, int recent_tok, int64_t n_units) {
+    __shared__ uint32_t hist[WAVES][256];
+    const int w = threadIdx.x >> 6;
+    const int64_t u = (int64_t)blockIdx.x * WAVES + w;
+    if (u >= n_units) return;
+    select_compact_wave<D, 72>(K, V, kpos, l_cap, score, kept, L, b_kv, prefix, recent_tok, u,
+                               threadIdx.x & 63, hist[w]);
 }
 
 // Wavefront-wide synchronisation of LDS between the lanes of one wavefront.
@@ -284,6 +341,35 @@ hipError_t launch_compact(uint16_t* K, uint16_t* V, int32_t* kpos,
     else
         compact_kernel<64><<<grid, 64 * WAVES, 0, s>>>(K, V, kpos, l_cap, kept, L, b_kv, K_out,
                                                        V_out, kpos_out, out_cap, n_units);
+    return hipGetLastError();
+}
+
+bool select_compact_fits(int64_t L) { return L <= 64 * 72; }
+
+hipError_t launch_select_compact(uint16_t* K, uint16_t* V, int32_t* kpos, int64_t n_units,
+                                 int d, int64_t l_cap, int64_t L, const float* score,
+                                 int32_t* kept, int64_t b_kv, int prefix, int recent_tok,
+                                 hipStream_t s) {
+    if (n_units <= 0) return hipSuccess;
+    if (!select_compact_fits(L)) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)((n_units + WAVES - 1) / WAVES));
+#define BKV_SC(DD, NR)                                                                    \
+    select_compact_kernel<DD, NR><<<grid, 64 * WAVES, 0, s>>>(K, V, kpos, l_cap, score, kept, \
+                                                              L, b_kv, prefix, recent_tok, n_units)
+#define BKV_SC_D(NR)                                                                      \
+    if (d == 128) BKV_SC(128, NR); else BKV_SC(64, NR)
+    if (L <= 64 * 8) { BKV_SC_D(8); }
+    else if (L <= 64 * 16) { BKV_SC_D(16); }
+    else if (L <= 64 * 36) { BKV_SC_D(36); }
+    else if (d == 128) {
+        select_compact_kernel_wide<128><<<grid, 64 * WAVES, 0, s>>>(
+            K, V, kpos, l_cap, score, kept, L, b_kv, prefix, recent_tok, n_units);
+    } else {
+        select_compact_kernel_wide<64><<<grid, 64 * WAVES, 0, s>>>(
+            K, V, kpos, l_cap, score, kept, L, b_kv, prefix, recent_tok, n_units);
+    }
+#undef BKV_SC_D
+#undef BKV_SC
     return hipGetLastError();
 }
 

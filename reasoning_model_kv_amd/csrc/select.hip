@@ -16,6 +16,7 @@
 // ascending; entries equal to T are taken lowest slot first.
 
 #include "common.h"
+#include "select_wave.h"
 
 namespace bkv {
 namespace {
@@ -235,134 +236,19 @@ __global__ __launch_bounds__(64) void select_wave_kernel(const float* __restrict
     }
 }
 
-// Register-resident variant (units of up to 64 * NR slots): lane l holds
-// the score bits of slots l + 64 r, r < NR, in registers, so only the
-// 256-bin histogram lives in LDS and every unit of a large launch is
-// resident at once (the LDS-staged kernel keeps (256 + L) words per
-// wavefront, which at L = 2176 caps a CU at 16 wavefronts).  The passes are
-// those of select_wave_kernel; register r of every lane is the chunk of
-// slots [64 r, 64 r + 64) for the final ballots.
+// Register-resident variant (units of up to 64 * NR slots): the scores stay
+// in registers, so only the 256-bin histogram lives in LDS and every unit of
+// a large launch is resident at once (the LDS-staged kernel keeps (256 + L)
+// words per wavefront, which at L = 2176 caps a CU at 16 wavefronts).
 template <int NR>
 __global__ __launch_bounds__(64) void select_reg_kernel(const float* __restrict__ score,
                                                         int64_t l_cap, int64_t L, int64_t b_kv,
                                                         int prefix, int recent_tok,
                                                         int32_t* __restrict__ kept) {
     __shared__ uint32_t hist[256];
-    const int lane = threadIdx.x;
     const int64_t u = blockIdx.x;
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(score + u * l_cap);
-    int32_t* out = kept + u * b_kv;
-    const int n = (int)L;
-    const int lo = prefix, hi = n - recent_tok;  // middle slots [lo, hi)
-    const int64_t want = b_kv - prefix - recent_tok;
-
-    // Unconditional loads (slots past the end read slot n - 1 and are never
-    // used): no branch per chunk, all loads in flight together.
-    uint32_t bits[NR];
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-        const int j = lane + 64 * r;
-        bits[r] = src[j < n ? j : n - 1];
-    }
-    // Bit r of midm[r / 32]: slot lane + 64 r is a middle slot.
-    constexpr int NW = (NR + 31) / 32;
-    uint32_t midm[NW];
-#pragma unroll
-    for (int w = 0; w < NW; ++w) midm[w] = 0;
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-        const int j = lane + 64 * r;
-        if (j >= lo && j < hi) midm[r / 32] |= 1u << (r % 32);
-    }
-
-    uint32_t thr = 0, pmask = 0;
-    uint32_t krem = (uint32_t)want;
-    if (want > 0) {
-        for (int pass = 0; pass < 4; ++pass) {
-            const int shift = 24 - 8 * pass;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) hist[lane + 64 * k] = 0;
-            wave_sync_lds();
-            // Fresh copies of the masks per pass: the per-slot conditions
-            // are not hoisted out of the pass loop (as 64-bit exec masks,
-            // one per slot chunk, they would not fit in scalar registers).
-            uint32_t mm[NW];
-#pragma unroll
-            for (int w = 0; w < NW; ++w) {
-                mm[w] = midm[w];
-                asm volatile("" : "+v"(mm[w]));
-            }
-#pragma unroll
-            for (int r = 0; r < NR; ++r) {
-                const uint32_t b = bits[r];
-                if (((mm[r / 32] >> (r % 32)) & 1u) && (b & pmask) == thr)
-                    atomicAdd(&hist[(b >> shift) & 255u], 1u);
-            }
-            wave_sync_lds();
-            // Lane l takes digits 255 - 4l .. 252 - 4l (descending).
-            uint32_t c[4], cs = 0;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                c[k] = hist[255 - 4 * lane - k];
-                cs += c[k];
-            }
-            uint32_t inc = cs;
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const uint32_t t = __shfl_up(inc, o);
-                if (lane >= o) inc += t;
-            }
-            const uint32_t exc = inc - cs;
-            const bool here = exc < krem && inc >= krem;  // exactly one lane
-            uint32_t digit = 0, kr = 0;
-            if (here) {
-                uint32_t e = exc;
-                bool found = false;
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    if (!found) {
-                        if (e + c[k] >= krem) {
-                            digit = 255u - 4u * (uint32_t)lane - (uint32_t)k;
-                            kr = krem - e;
-                            found = true;
-                        } else {
-                            e += c[k];
-                        }
-                    }
-                }
-            }
-            const uint64_t who = __ballot(here);
-            const int srcl = who ? (int)__builtin_ctzll(who) : 0;
-            thr |= (uint32_t)__builtin_amdgcn_readlane((int)digit, srcl) << shift;
-            pmask |= 0xFFu << shift;
-            krem = (uint32_t)__builtin_amdgcn_readlane((int)kr, srcl);
-            wave_sync_lds();  // every lane has read the histogram
-        }
-    }
-
-    uint32_t written = 0, eq_seen = 0;
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-        // One chunk at a time: unfenced, the scheduler hoists every chunk's
-        // ballot masks and runs out of scalar registers.
-        __builtin_amdgcn_sched_barrier(0);
-        const int j = lane + 64 * r;
-        const bool in = j < n;
-        const bool forced = in && (j < lo || j >= hi);
-        const bool mid = in && !forced && want > 0;
-        const uint32_t b = mid ? bits[r] : 0u;
-        const bool eq = mid && b == thr;
-        const uint64_t eqm = __ballot(eq);
-        const uint32_t below = __builtin_amdgcn_mbcnt_hi(
-            (uint32_t)(eqm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)eqm, 0u));
-        const bool take = forced || (mid && b > thr) || (eq && eq_seen + below < krem);
-        const uint64_t tm = __ballot(take);
-        const uint32_t pos = written + __builtin_amdgcn_mbcnt_hi(
-            (uint32_t)(tm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)tm, 0u));
-        if (take && pos < (uint32_t)b_kv) out[pos] = j;
-        written += (uint32_t)__builtin_popcountll(tm);
-        eq_seen += (uint32_t)__builtin_popcountll(eqm);
-    }
+    select_wave_reg<NR>(score + u * l_cap, L, b_kv, prefix, recent_tok, kept + u * b_kv, hist,
+                        threadIdx.x);
 }
 
 // Largest unit handled by one wavefront (beyond it a workgroup shares the

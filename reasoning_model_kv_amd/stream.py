@@ -26,8 +26,8 @@ With fused_decode=True the steps' decode attention (bkv_decode_attend) also
 gathers the scores' softmax denominators: at the beacon fix it adds the
 beacon rows, rotated to the coming eviction's step, and at each recent step
 the new query's own log-sum-exp is kept; the eviction then scores with
-bkv_score_lse (one read of the keys) and runs select, compact and the merge
-as separate calls.  The attention output of those steps is left in
+bkv_score_lse (one read of the keys) and runs select and compact (one
+launch, bkv_select_compact) and the merge as separate calls.  The attention output of those steps is left in
 `attn_out`; other steps' attention is the decoder's own business and is not
 run here.
 
@@ -206,11 +206,12 @@ class Stream:
             sh = self.shape
             bkv.score_lse(sh, self.K, self.kpos, L, self.buf, self.recents, self.t,
                           self.lse_in, self.lse_from, self.score, ws=self.ws)
-            bkv.select(sh, self.score, L, self.b_kv, self.kept)
             if sh.unsorted:
+                bkv.select(sh, self.score, L, self.b_kv, self.kept)
                 bkv.compact_unsorted(sh, self.K, self.V, self.kpos, L, self.kept, self.b_kv)
             else:
-                bkv.compact(sh, self.K, self.V, self.kpos, L, self.kept, self.b_kv)
+                bkv.select_compact(sh, self.score, L, self.b_kv, self.K, self.V, self.kpos,
+                                   self.kept)
             bkv.fps_update(sh, self.buf, self.count, self.recents, trigger=32, m=16)
         else:
             bkv.evict(self.shape, self.K, self.V, self.kpos, L, self.buf, self.recents,

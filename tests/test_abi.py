@@ -226,3 +226,18 @@ def test_decode_attend_validation(lib, monkeypatch):
     assert _call_decode(lib, _shape(n_units=0), beacons=None, lse_obs=None) == bkv.BKV_OK
     monkeypatch.setenv("BKV_FAULT_INJECT", "bkv_decode_attend")
     assert _call_decode(lib, s) == bkv.BKV_EHIP
+
+
+def test_select_compact_validation(lib, monkeypatch):
+    s = _shape(prefix=8)
+    call = lambda L, b, K=FAKE: lib.bkv_select_compact(
+        ctypes.byref(s.dims()), ctypes.byref(s.policy()), FAKE, L, b, K, FAKE, FAKE, FAKE, None)
+    assert call(300, 100, K=None) == bkv.BKV_EINVAL
+    assert call(300, 300) == bkv.BKV_EINVAL        # b_kv must be < L
+    assert call(300, 20) == bkv.BKV_EINVAL         # below prefix + recent
+    assert call(600, 100) == bkv.BKV_EINVAL        # L > l_cap
+    s0 = _shape(n_units=0, prefix=8)
+    assert lib.bkv_select_compact(ctypes.byref(s0.dims()), ctypes.byref(s0.policy()), FAKE, 300,
+                                  100, FAKE, FAKE, FAKE, FAKE, None) == bkv.BKV_OK
+    monkeypatch.setenv("BKV_FAULT_INJECT", "bkv_select_compact")
+    assert call(300, 100) == bkv.BKV_EHIP

@@ -128,3 +128,48 @@ def test_compact_unsorted_bit_exact(d, L, b_kv):
         assert np.array_equal(Pg[u, :b_kv].numpy(), ep), f"unit {u} kpos"
         # slots at and past b_kv are read, never written
         assert np.array_equal(Kg[u, b_kv:], Kh[u, b_kv:]), f"unit {u} tail"
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("L,b_kv,P,kind", [
+    (256, 128, 8, "cont"),      # 4 score registers per lane
+    (1000, 24, 8, "cont"),      # only the forced slots kept
+    (777, 300, 33, "ties"),     # many equal scores around the cut
+    (2176, 2048, 8, "cont"),    # the Qwen3-4B step's shape
+    (4224, 4096, 512, "ties"),  # the wide kernel (72 score registers per lane)
+    (5000, 1000, 8, "cont"),    # beyond one launch: select, then compact
+])
+def test_select_compact_matches_the_two_calls(d, L, b_kv, P, kind):
+    """Selection and compaction in one launch: the oracle's kept set exactly,
+    and K, V, positions equal to the oracle's compaction of the inputs."""
+    U, R = 21, 16
+    log(f"select_compact d={d} L={L} b_kv={b_kv} P={P} {kind}")
+    r = np.random.default_rng(L + d)
+    if kind == "cont":
+        s = r.random((U, L)).astype(np.float32) * 1e-3
+    else:
+        s = r.choice(np.array([1e-6, 2e-6, 2e-6, 5e-4, 0.25, 0.0], np.float32), size=(U, L))
+    l_cap = L + 7
+    sc = torch.zeros((U, l_cap), dtype=torch.float32, device=DEV)
+    sc[:, :L] = torch.from_numpy(s).to(DEV)
+    K = torch.from_numpy(r.standard_normal((U, l_cap, d)).astype(np.float32)).to(
+        torch.bfloat16).to(DEV)
+    V = torch.from_numpy(r.standard_normal((U, l_cap, d)).astype(np.float32)).to(
+        torch.bfloat16).to(DEV)
+    kpos = torch.from_numpy((np.arange(l_cap)[None].repeat(U, 0) * 3 + 5).astype(np.int32)).to(DEV)
+    Kh, Vh, Ph = K.cpu(), V.cpu(), kpos.cpu().numpy()
+    kept = torch.full((U, b_kv), -1, dtype=torch.int32, device=DEV)
+    shape = bkv.Shape(U, 1, d, l_cap, P, 1e4, recent_tok=R)
+    bkv.select_compact(shape, sc, L, b_kv, K, V, kpos, kept)
+    torch.cuda.synchronize()
+    k = kept.cpu().numpy()
+    for u in range(U):
+        ref = oracle.select.select(s[u].astype(np.float64), L, b_kv, P, R)
+        assert np.array_equal(k[u], ref), f"unit {u} kept"
+        ek, ev, ep = oracle.compact.compact(Kh[u].view(torch.int16).numpy(),
+                                            Vh[u].view(torch.int16).numpy(), Ph[u], ref)
+        assert np.array_equal(K[u, :b_kv].cpu().view(torch.int16).numpy(), ek), f"unit {u} K"
+        assert np.array_equal(V[u, :b_kv].cpu().view(torch.int16).numpy(), ev), f"unit {u} V"
+        assert np.array_equal(kpos[u, :b_kv].cpu().numpy(), ep), f"unit {u} kpos"
+    # Slots past b_kv are left as they were.
+    assert torch.equal(K[:, b_kv:].cpu().view(torch.int16), Kh[:, b_kv:].view(torch.int16))

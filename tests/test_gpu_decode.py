@@ -194,3 +194,42 @@ def test_score_lse_agrees_with_two_pass_kernel():
     rel = np.abs(a - b) / b
     log(f"score_lse vs score: max rel diff {rel.max():.3g}")
     assert rel.max() <= 2 * TOL
+
+
+def test_fused_path_full_size_sampled():
+    """Qwen3-4B shape, all 4608 units, in the launch configuration the bench
+    times: beacon denominators from decode attention at L - 16, the recent
+    rows' from their own steps, then bkv_score_lse.  Sampled units against the
+    oracle; every unit against the two-pass kernel within twice the tolerance."""
+    w = synth.WORKLOADS["qwen3_4b_full_b2048"]
+    U, g, d, L = w.n_units, w.group, w.d_head, w.L
+    log(f"fused path full size: U={U} g={g} L={L}")
+    dev = synth.device_inputs(w, DEV)
+    shape = bkv.Shape(U, g, d, L, w.prefix, w.theta, recent_tok=w.recent_tok)
+    K, V, P = dev["keys"], dev["values"], dev["kpos"]
+    lse = torch.empty((U, g, 32), device=DEV)
+    out = torch.empty((U * g, d), device=DEV)
+    lq = torch.empty((U * g,), device=DEV)
+    lo = torch.empty((U * g, 16), device=DEV)
+    bkv.decode_attend(shape, K, V, L - 16, dev["buf"][:, 30].contiguous(), int(P[0, L - 17]),
+                      out, lq, dev["buf"], L, lo)
+    lse[:, :, :16] = lo.view(U, g, 16)
+    for i in range(16):
+        bkv.decode_attend(shape, K, V, L - 16 + i + 1, dev["recents"][:, i].contiguous(),
+                          int(P[0, L - 16 + i]), out, lq)
+        lse[:, :, 16 + i] = lq.view(U, g)
+    s1 = torch.empty((U, L), device=DEV)
+    s2 = torch.empty((U, L), device=DEV)
+    bkv.score_lse(shape, K, P, L, dev["buf"], dev["recents"], L, lse, L - 16, s1)
+    bkv.score(shape, K, P, L, dev["buf"], dev["recents"], L, s2)
+    torch.cuda.synchronize()
+    rel = ((s1 - s2).abs() / s2).max().item()
+    assert rel <= 2 * TOL, rel
+    worst = 0.0
+    for u in (0, 1777, U - 1):
+        ref = oracle.score.score_unit(K[u].float().cpu().numpy(),
+                                      dev["buf"][u * g:(u + 1) * g, :16].cpu().numpy(),
+                                      dev["recents"][u * g:(u + 1) * g].cpu().numpy(), L,
+                                      P[u, L - 16:L].cpu().numpy(), w.theta)
+        worst = max(worst, check_scores(s1[u].cpu().numpy(), ref, f"unit {u}"))
+    log(f"  one-read vs two-pass max rel diff {rel:.3g}; sampled max rel err {worst:.3g}")

@@ -173,3 +173,31 @@ def test_select_compact_matches_the_two_calls(d, L, b_kv, P, kind):
         assert np.array_equal(kpos[u, :b_kv].cpu().numpy(), ep), f"unit {u} kpos"
     # Slots past b_kv are left as they were.
     assert torch.equal(K[:, b_kv:].cpu().view(torch.int16), Kh[:, b_kv:].view(torch.int16))
+
+
+def test_select_compact_full_size_equals_two_calls():
+    """Qwen3-4B shape, all 4608 units: the one-launch kernel against select
+    followed by an out-of-place compaction, bit for bit."""
+    import synth
+    w = synth.WORKLOADS["qwen3_4b_full_b2048"]
+    log(f"select_compact full size: U={w.n_units} L={w.L} B={w.b_kv}")
+    dev = synth.device_inputs(w, DEV)
+    shape = bkv.Shape(w.n_units, w.group, w.d_head, w.L, w.prefix, w.theta,
+                      recent_tok=w.recent_tok)
+    score = torch.zeros((w.n_units, w.L), device=DEV)
+    bkv.score(shape, dev["keys"], dev["kpos"], w.L, dev["buf"], dev["recents"], w.L, score)
+    kept_a = torch.zeros((w.n_units, w.b_kv), dtype=torch.int32, device=DEV)
+    kept_b = torch.zeros_like(kept_a)
+    bkv.select(shape, score, w.L, w.b_kv, kept_a)
+    Ko = torch.empty((w.n_units, w.b_kv, w.d_head), dtype=torch.bfloat16, device=DEV)
+    Vo, Po = torch.empty_like(Ko), torch.empty((w.n_units, w.b_kv), dtype=torch.int32,
+                                                device=DEV)
+    bkv.compact(shape, dev["keys"], dev["values"], dev["kpos"], w.L, kept_a, w.b_kv, Ko, Vo, Po,
+                out_cap=w.b_kv)
+    bkv.select_compact(shape, score, w.L, w.b_kv, dev["keys"], dev["values"], dev["kpos"],
+                       kept_b)
+    torch.cuda.synchronize()
+    assert torch.equal(kept_a, kept_b)
+    assert torch.equal(dev["keys"][:, :w.b_kv].view(torch.int16), Ko.view(torch.int16))
+    assert torch.equal(dev["values"][:, :w.b_kv].view(torch.int16), Vo.view(torch.int16))
+    assert torch.equal(dev["kpos"][:, :w.b_kv], Po)

@@ -434,6 +434,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "ms_per_step_p10_p50_p90": [round(1e3 * float(np.percentile(wall, q)), 4)
+                                    for q in (10, 50, 90)],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -707,6 +707,13 @@ def stream_main(args, w):
     from reasoning_model_kv_amd import bkv
     from reasoning_model_kv_amd import stream as bstream
 
+    cpu = None
+    if args.cpu_seconds > 0:
+        # The oracle's eviction event per unit (the GPU is not touched yet).
+        eprint(f"[bench] oracle CPU baseline (~{args.cpu_seconds:.0f} s of CPU work per core)")
+        c = cpu_baseline(w, args.cpu_seconds)
+        cpu = dict(c, value=round(c["value"] / w.L, 2), unit="unit-evictions/s")
+        eprint(f"[bench] cpu baseline: {cpu}")
     bkv.load_library()
     if not torch.cuda.is_available():
         eprint("no GPU visible")
@@ -795,6 +802,14 @@ def stream_main(args, w):
         "full_cache_bytes_at_end": 2 * U * (w.prefix + n_steps) * d * 2,
         "torch_max_memory_allocated": torch.cuda.max_memory_allocated(),
         "moved_tokens_per_eviction": n_mv,
+        # The eviction events dominate the bytes; their algorithmic bytes over
+        # their event-timed duration.
+        "roofline": {"kernel": "eviction event (bkv_evict)", "bound": "hbm",
+                     "achieved": round(ev_bytes / (mean_ev * 1e-3) / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(ev_bytes / (mean_ev * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": None},
+        "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
 

@@ -233,3 +233,34 @@ def test_fused_path_full_size_sampled():
                                       P[u, L - 16:L].cpu().numpy(), w.theta)
         worst = max(worst, check_scores(s1[u].cpu().numpy(), ref, f"unit {u}"))
     log(f"  one-read vs two-pass max rel diff {rel:.3g}; sampled max rel err {worst:.3g}")
+
+
+@pytest.mark.parametrize("L,l_cap", [(256, 256), (203, 256)])
+def test_score_lse_recent_window(L, l_cap):
+    """The baselines' window of 32 recent queries (no beacons): every row's
+    denominator comes from that query's own decode step, and the one-read
+    scores equal the oracle's two-pass definition."""
+    w = synth.shrink(synth.WORKLOADS["tiny"], n_beacon=0, n_recent_q=32, recent_tok=32)
+    log(f"score_lse 32-query window L={L} l_cap={l_cap}")
+    inp, dev, _ = _setup(w, L, l_cap)
+    shape = bkv.Shape(w.n_units, w.group, w.d_head, l_cap, w.prefix, w.theta, recent_tok=32,
+                      n_beacon=0, n_recent_q=32)
+    U, g = w.n_units, w.group
+    lse = torch.empty((U, g, 32), device=DEV)
+    for i in range(32):
+        q = dev["recents"][:, i].contiguous()
+        _, lq, _ = _decode(shape, dev, L - 32 + i + 1, q, int(inp["kpos"][0, L - 32 + i]))
+        lse[:, :, i] = torch.from_numpy(lq.reshape(U, g)).to(DEV)
+    score = torch.full((U, l_cap), -1.0, device=DEV)
+    bkv.score_lse(shape, dev["keys"], dev["kpos"], L, None, dev["recents"], L, lse, L, score)
+    torch.cuda.synchronize()
+    sc = score.cpu().numpy()
+    worst = 0.0
+    for u in range(U):
+        none = np.zeros((g, 0, w.d_head))
+        ref = oracle.score.score_unit(inp["keys"][u], none, inp["recents"][u], L,
+                                      inp["kpos"][u][L - 32:L], w.theta)
+        worst = max(worst, check_scores(sc[u, :L], ref, f"unit {u}"))
+        if l_cap > L:
+            assert np.all(sc[u, L:] == -1.0)
+    log(f"  max rel err {worst:.3g}")

@@ -89,6 +89,42 @@ class Stream:
             self.lse_from = 0
             self.t_obs = -1
 
+    # Checkpoint and resume: every piece of the policy's state is either a
+    # tensor the caller could save or one of these host fields.
+    _TENSORS = ("K", "V", "kpos", "buf", "count", "recents", "rcount", "score", "kept", "sel")
+    _FUSED_TENSORS = ("attn_out", "lse_q", "lse_obs", "lse_in")
+    _HOST = ("L", "t", "rows", "phase", "events", "n_evictions")
+    _FUSED_HOST = ("lse_from", "t_obs")
+
+    def state_dict(self):
+        """The whole state as a dict of tensors (copies on the host) and plain
+        values, loadable with torch.load(weights_only=True)."""
+        names_t = self._TENSORS + (self._FUSED_TENSORS if self.fused else ())
+        names_h = self._HOST + (self._FUSED_HOST if self.fused else ())
+        sd = {n: getattr(self, n).detach().cpu().clone() for n in names_t}
+        sd.update({n: getattr(self, n) for n in names_h if n != "events"})
+        sd["events"] = [list(e) for e in self.events]
+        sd["prompt_queries"] = (self.prompt_queries.detach().cpu().clone()
+                                if hasattr(self, "prompt_queries") else None)
+        return sd
+
+    def load_state_dict(self, sd):
+        """Restore a state_dict() of a Stream built with the same arguments."""
+        names_t = self._TENSORS + (self._FUSED_TENSORS if self.fused else ())
+        names_h = self._HOST + (self._FUSED_HOST if self.fused else ())
+        for n in names_t:
+            dst = getattr(self, n)
+            if tuple(sd[n].shape) != tuple(dst.shape) or sd[n].dtype != dst.dtype:
+                raise ValueError(f"state {n}: {tuple(sd[n].shape)} {sd[n].dtype} does not match "
+                                 f"{tuple(dst.shape)} {dst.dtype}")
+            dst.copy_(sd[n])
+        for n in names_h:
+            if n != "events":
+                setattr(self, n, sd[n])
+        self.events = [tuple(e) for e in sd["events"]]
+        if sd.get("prompt_queries") is not None:
+            self.prompt_queries = sd["prompt_queries"].to(self.K.device)
+
     def _note(self, kind, stage):
         if self.observer is not None:
             self.observer(kind, stage, self)

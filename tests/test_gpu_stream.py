@@ -223,3 +223,48 @@ def test_stream_qwen3_14b_fused_decode_sampled():
     assert st.events == _oracle_events(w, n)
     assert st.n_evictions == 2 and chk.n["evict"] == 2
     log(f"  max score rel err {chk.worst:.3g}")
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_stream_checkpoint_resume_bit_identical(fused):
+    """A run snapshotted in its recent-query phase (state_dict through
+    torch.save / torch.load(weights_only=True)) and resumed in a new driver
+    continues bit for bit like the original, through two more evictions."""
+    import io
+    w = synth.WORKLOADS["stream_small"]
+    n1, n2 = 340, 300
+    log(f"stream checkpoint/resume (fused={fused}): {n1} steps, snapshot, {n2} more")
+    gen = synth.StreamInputs(w, DEV)
+    prompt = gen.prompt()
+    chunks = [gen.chunk(c, 128) for c in range((n1 + n2 + 127) // 128)]
+
+    def step(st, i):
+        k, v, q = chunks[i // 128]
+        st.step(k[i % 128], v[i % 128], q[i % 128])
+
+    def make():
+        return bstream.Stream(w.n_units, w.group, w.d_head, w.L, w.b_kv, w.prefix, w.theta,
+                              device=DEV, fused_decode=fused)
+
+    a = make()
+    a.prefill(*prompt)
+    for i in range(n1):
+        step(a, i)
+    assert a.phase == "recent"
+    blob = io.BytesIO()
+    torch.save(a.state_dict(), blob)
+    for i in range(n1, n1 + n2):
+        step(a, i)
+    blob.seek(0)
+    b = make()
+    b.load_state_dict(torch.load(blob, weights_only=True))
+    for i in range(n1, n1 + n2):
+        step(b, i)
+    torch.cuda.synchronize()
+    assert a.n_evictions == b.n_evictions >= 3
+    assert a.events == b.events and (a.L, a.t, a.rows, a.phase) == (b.L, b.t, b.rows, b.phase)
+    for n in ("K", "V"):
+        assert torch.equal(getattr(a, n).view(torch.int16), getattr(b, n).view(torch.int16)), n
+    for n in ("kpos", "buf", "count", "recents", "rcount", "kept", "score"):
+        assert torch.equal(getattr(a, n), getattr(b, n)), n
+    log(f"  evictions {a.n_evictions}, events {len(a.events)}")

@@ -53,6 +53,10 @@ def parse():
     p.add_argument("--steps", type=int, default=30)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    p.add_argument("--bkv", type=int, choices=(128, 512, 1024, 2048, 4096), default=0,
+                   help="the Qwen3-4B 36-layer x batch-16 step at this B_KV (sets --workload)")
+    p.add_argument("--seed", type=int, default=0,
+                   help="master seed of the synthetic inputs (0: the workloads' own)")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle baseline sample (0 disables)")
     p.add_argument("--no-check", action="store_true", help="skip the sampled parity check")
@@ -231,7 +235,14 @@ def main():
 
     import synth
 
+    if args.bkv:
+        args.workload = f"qwen3_4b_full_b{args.bkv}"
+    if args.workload not in synth.WORKLOADS:
+        eprint(f"unknown workload {args.workload!r}; known: {', '.join(synth.WORKLOADS)}")
+        sys.exit(2)
     w = synth.WORKLOADS[args.workload]
+    if args.seed:
+        w = synth.shrink(w, seed=args.seed)
     if args.prefill_fps:
         prefill_fps_main(args, w)
         return

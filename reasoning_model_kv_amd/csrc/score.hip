@@ -834,6 +834,7 @@ struct DecodeArgs {
     float* out;             // [U * g, D]
     float* lse_q;           // [U * g]
     float* lse_obs;         // [U * g, 16] (when beacons != NULL)
+    int64_t n_units;
 };
 
 template <int D>
@@ -853,8 +854,14 @@ __device__ __forceinline__ float2 v_pair(const uint16_t* vt, int j, int lane) {
     }
 }
 
-template <int D, int NL>
-__global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a, int g) {
+// Groups of more than four heads (SPLIT) are shared by two workgroups of hs
+// wavefronts on one XCD (blocks b and b + 8; the second may have an idle
+// wavefront, which loads and keeps the barriers but writes nothing), so
+// that more than one group fits on a CU; each reads the unit's keys and
+// values, the second mostly from L2.  Their heads are disjoint, so nothing
+// is combined.
+template <int D, int NL, bool SPLIT>
+__global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a, int g, int hs) {
     __shared__ __attribute__((aligned(16))) uint16_t k0[DT * D];
     __shared__ __attribute__((aligned(16))) uint16_t k1[DT * D];
     __shared__ __attribute__((aligned(16))) uint16_t k2[DT * D];
@@ -869,8 +876,16 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a, int g) {
     const int h = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const bool loader = h < NL;
-    const int64_t u = blockIdx.x;
-    const int64_t qh = u * g + h;
+    int64_t u = blockIdx.x;
+    int hg = h;  // query head of the group this wavefront attends for
+    if (SPLIT) {
+        const int64_t b = blockIdx.x;
+        u = (b / 16) * 8 + (b % 8);
+        hg = (int)((b / 8) & 1) * hs + h;
+        if (u >= a.n_units) return;  // whole workgroup, before any barrier
+    }
+    const bool active = !SPLIT || hg < g;
+    const int64_t qh = u * g + hg;
     const int64_t L = a.L;
     const uint16_t* Ku = a.K + u * a.l_cap * D;
     const uint16_t* Vu = a.V + u * a.l_cap * D;
@@ -891,8 +906,8 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a, int g) {
     // that waiting for it does not wait for the tiles.
     const int r = lane & 31, hh = lane >> 5;
     const float* src = nullptr;
-    if (r < 16 && obs) src = a.beacons + (qh * a.buf_cap + r) * (int64_t)D;
-    else if (r == 16) src = a.q + qh * (int64_t)D;
+    if (active && r < 16 && obs) src = a.beacons + (qh * a.buf_cap + r) * (int64_t)D;
+    else if (active && r == 16) src = a.q + qh * (int64_t)D;
     float4 x1[NS / 2][2], x2[NS / 2][2];
 #pragma unroll
     for (int s = 0; s < NS / 2; ++s) {
@@ -1021,6 +1036,7 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a, int g) {
     for (int o = 1; o < 32; o <<= 1) lt += __shfl_xor(lt, o);
     lt = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, lt)));
     const float inv = 1.0f / lt;
+    if (!active) return;  // an idle wavefront of a split group (no barrier follows)
     if constexpr (D == 128) {
         *reinterpret_cast<float2*>(a.out + qh * (int64_t)D + 2 * lane) = float2{o0 * inv, o1 * inv};
     } else {
@@ -1048,12 +1064,18 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a, int g) {
     }
 }
 
-template __global__ void decode_kernel<128, 4>(DecodeArgs, int);
-template __global__ void decode_kernel<128, 2>(DecodeArgs, int);
-template __global__ void decode_kernel<128, 1>(DecodeArgs, int);
-template __global__ void decode_kernel<64, 4>(DecodeArgs, int);
-template __global__ void decode_kernel<64, 2>(DecodeArgs, int);
-template __global__ void decode_kernel<64, 1>(DecodeArgs, int);
+template __global__ void decode_kernel<128, 4, false>(DecodeArgs, int, int);
+template __global__ void decode_kernel<128, 2, false>(DecodeArgs, int, int);
+template __global__ void decode_kernel<128, 1, false>(DecodeArgs, int, int);
+template __global__ void decode_kernel<64, 4, false>(DecodeArgs, int, int);
+template __global__ void decode_kernel<64, 2, false>(DecodeArgs, int, int);
+template __global__ void decode_kernel<64, 1, false>(DecodeArgs, int, int);
+template __global__ void decode_kernel<128, 4, true>(DecodeArgs, int, int);
+template __global__ void decode_kernel<128, 2, true>(DecodeArgs, int, int);
+template __global__ void decode_kernel<64, 4, true>(DecodeArgs, int, int);
+template __global__ void decode_kernel<64, 2, true>(DecodeArgs, int, int);
+template __global__ void decode_kernel<128, 1, true>(DecodeArgs, int, int);
+template __global__ void decode_kernel<64, 1, true>(DecodeArgs, int, int);
 
 // Every variant is instantiated explicitly, so each gets its host launch stub
 // even though it is launched from one branch of a conditional.
@@ -1178,9 +1200,18 @@ hipError_t launch_decode(const uint16_t* K, const uint16_t* V, int64_t n_units, 
     a.out = out;
     a.lse_q = lse_q;
     a.lse_obs = lse_obs;
-    const dim3 grid((unsigned)n_units), block(64 * g);
-    const int nl = g >= 4 ? 4 : (g >= 2 ? 2 : 1);
-#define BKV_LAUNCH_DEC(DD, NN) decode_kernel<DD, NN><<<grid, block, 0, s>>>(a, g)
+    a.n_units = n_units;
+    // Groups of more than four heads: two workgroups per unit (see decode_kernel).
+    const bool split = g > 4;
+    const int hs = split ? (g + 1) / 2 : g;
+    const dim3 grid(split ? (unsigned)((n_units + 7) / 8 * 16) : (unsigned)n_units);
+    const dim3 block(64 * hs);
+    const int nl = hs >= 4 ? 4 : (hs >= 2 ? 2 : 1);
+#define BKV_LAUNCH_DEC(DD, NN)                                                     \
+    do {                                                                           \
+        if (split) decode_kernel<DD, NN, true><<<grid, block, 0, s>>>(a, g, hs);   \
+        else decode_kernel<DD, NN, false><<<grid, block, 0, s>>>(a, g, hs);        \
+    } while (0)
     if (d == 128) {
         if (nl == 4) BKV_LAUNCH_DEC(128, 4);
         else if (nl == 2) BKV_LAUNCH_DEC(128, 2);

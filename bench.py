@@ -247,6 +247,10 @@ def main():
         prefill_fps_main(args, w)
         return
     if w.stream_steps:
+        if args.fused_decode:
+            eprint("--fused-decode times single eviction events; the streaming run's decode-time "
+                   "denominators are exercised by the tests (Stream(fused_decode=True))")
+            sys.exit(2)
         stream_main(args, w)
         return
     window = args.observe == "recent32"

@@ -44,6 +44,9 @@ constexpr float kNegBig = -1.0e30f;  // finite "no key seen yet" running max
 // Buffer-resource flags word (gfx9 family: raw 32-bit data, no swizzle).
 constexpr int kBufferFlags = 0x00020000;
 constexpr float kRescaleBig = 0x1p64f; // lazy rescale: largest tile term sum kept
+// Cache-policy word of a load whose data is not read again (non-temporal:
+// it does not displace lines that other loads will reuse).
+constexpr int kLoadStreaming = 2;
 
 __device__ __forceinline__ void rope_cs(double pos, int i, int d, double theta,
                                         double* c, double* s) {
@@ -310,7 +313,9 @@ struct TileLoad {
         }
     }
 
-    // Issue the loads of keys [base, base + TK) of Ku (L keys) into lds_tile.
+    // Issue the loads of keys [base, base + TK) of Ku (L keys) into lds_tile,
+    // with cache policy AUX (0, or kLoadStreaming for a last read).
+    template <int AUX = 0>
     __device__ __forceinline__ void issue(const uint16_t* Ku, int64_t L, int64_t base,
                                           uint16_t* lds_tile, int wave) const {
         const int bytes = (int)((L - base) * D * 2);
@@ -323,7 +328,7 @@ struct TileLoad {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rsrc,
                 (__attribute__((address_space(3))) void*)(lds_tile + (k * NL + wave) * 64 * 8),
-                16, voff[k % NP], 0, 0, 0);
+                16, voff[k % NP], 0, 0, AUX);
         }
     }
 };
@@ -750,9 +755,13 @@ void score_kernel(ScoreArgs a, int g, int hs) {
 // Pass 2 walks the tiles backwards: at the end of pass 1 the last tiles
 // (three, or the ones pass 1 covered plus the prologue's second tile) are
 // still in LDS, so they are scored without being read again, and the rest
-// stream in from the end with the same ring, two tiles ahead.  Iteration j
-// scores tile T = ntiles - 1 - j from CUR and loads tile T - 2 into NXT
-// (the buffer tile T + 1 used, or an unused one at j = 0).
+// stream in from the end with the same ring, two tiles ahead, as streaming
+// (non-temporal) loads: it is their last read, and left out of the caches
+// they do not push out the tiles pass 1 of other workgroups will read again
+// (6% faster than plain loads; pass 1's loads stay plain, as pass 2 reads
+// its last tiles from L2).  Iteration j scores tile T = ntiles - 1 - j from
+// CUR and loads tile T - 2 into NXT (the buffer tile T + 1 used, or an unused
+// one at j = 0).
 #define BKV_REV_ITER(j, CUR, NXT, ...)                                             \
     do {                                                                           \
         const int T = ntiles - 1 - (j);                                            \
@@ -763,7 +772,7 @@ void score_kernel(ScoreArgs a, int g, int hs) {
         }                                                                          \
         __syncthreads();                                                           \
         if (loader && T - 2 >= 0 && T - 2 < t_res)                                 \
-            ld.issue(Ku, L, (int64_t)(T - 2) * KT, NXT, h);                        \
+            ld.template issue<kLoadStreaming>(Ku, L, (int64_t)(T - 2) * KT, NXT, h); \
         f32x16 acc0, acc1;                                                         \
         if (SPLIT && !active) { acc0 = f32x16{}; acc1 = f32x16{}; }                \
         else tile_logits<D>(CUR, rd, frag, acc0, acc1);                            \
@@ -903,7 +912,9 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a, int g, int hs
     }
     // This lane's row (beacon r < 16, new query r == 16, zero beyond) is
     // loaded before the first two tiles of keys and values are issued, so
-    // that waiting for it does not wait for the tiles.
+    // that waiting for it does not wait for the tiles.  Keys and values are
+    // read once here: streaming (non-temporal) loads, 8% faster than plain
+    // ones without the beacon rows.
     const int r = lane & 31, hh = lane >> 5;
     const float* src = nullptr;
     if (active && r < 16 && obs) src = a.beacons + (qh * a.buf_cap + r) * (int64_t)D;
@@ -921,11 +932,11 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a, int g, int hs
         }
     }
     if (loader) {
-        ld.issue(Ku, L, 0, k0, h);
-        ld.issue(Vu, L, 0, v0, h);
+        ld.template issue<kLoadStreaming>(Ku, L, 0, k0, h);
+        ld.template issue<kLoadStreaming>(Vu, L, 0, v0, h);
         if (1 < ntiles) {
-            ld.issue(Ku, L, DT, k1, h);
-            ld.issue(Vu, L, DT, v1, h);
+            ld.template issue<kLoadStreaming>(Ku, L, DT, k1, h);
+            ld.template issue<kLoadStreaming>(Vu, L, DT, v1, h);
         }
     }
     __syncthreads();  // the cos/sin table
@@ -967,8 +978,8 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a, int g, int hs
         }                                                                          \
         __syncthreads();                                                           \
         if (loader && (it) + 2 < ntiles) {                                         \
-            ld.issue(Ku, L, (int64_t)((it) + 2) * DT, KN, h);                      \
-            ld.issue(Vu, L, (int64_t)((it) + 2) * DT, VN, h);                      \
+            ld.template issue<kLoadStreaming>(Ku, L, (int64_t)((it) + 2) * DT, KN, h);                   \
+            ld.template issue<kLoadStreaming>(Vu, L, (int64_t)((it) + 2) * DT, VN, h);                   \
         }                                                                          \
         f32x16 acc = f32x16{};                                                     \
         {                                                                          \

@@ -33,6 +33,8 @@ def _workload(name):
         return synth.shrink(synth.WORKLOADS["tiny"], group=3, d_head=128, theta=1e6)
     if name == "tiny_g8":
         return synth.shrink(synth.WORKLOADS["tiny"], group=8, d_head=64)
+    if name == "long_g4":
+        return synth.shrink(synth.WORKLOADS["tiny"], group=4, d_head=128, theta=1e6, h_kv=1)
     return synth.WORKLOADS[name]
 
 
@@ -69,6 +71,7 @@ DECODE_CASES = [
     ("tiny_g7", 300, 320),        # group 7, d 128
     ("tiny_g5", 1000, 1000),      # group 5
     ("qwen3_4b_layer", 2176, 2176),
+    ("long_g4", 9000, 9001),      # a long cache: 282 tiles of 32 keys
 ]
 
 

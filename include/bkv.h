@@ -305,6 +305,22 @@ int bkv_evict(const bkv_dims* dims, const bkv_policy* pol, uint16_t* K,
               int32_t* count, float* score_out, int32_t* kept_out, void* ws,
               size_t ws_bytes, void* stream);
 
+/*
+ * bkv_evict_lse -- bkv_evict with the softmax denominators already known.
+ *
+ * Summary "未来方向" (beacon scoring folded into attention); summary steps
+ * (4)-(6).  The eviction event of bkv_evict, its scores formed as
+ * bkv_score_lse forms them from lse_in ([U, g, 32] natural-log LSE; beacon
+ * rows over slots [0, lse_from), recent rows complete) with one read of the
+ * keys.  Requires what bkv_evict and bkv_score_lse require.
+ */
+int bkv_evict_lse(const bkv_dims* dims, const bkv_policy* pol, uint16_t* K,
+                  uint16_t* V, int32_t* kpos, int64_t L, const float* beacons,
+                  const float* recents, int64_t t, const float* lse_in,
+                  int64_t lse_from, int64_t b_kv, float* buf, int32_t* count,
+                  float* score_out, int32_t* kept_out, void* ws, size_t ws_bytes,
+                  void* stream);
+
 #ifdef __cplusplus
 }
 #endif

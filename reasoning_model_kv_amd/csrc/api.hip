@@ -360,11 +360,11 @@ int bkv_compact(const bkv_dims* dims, uint16_t* K, uint16_t* V, int32_t* kpos, i
                       fn);
 }
 
-int bkv_evict(const bkv_dims* dims, const bkv_policy* pol, uint16_t* K, uint16_t* V,
-              int32_t* kpos, int64_t L, const float* beacons, const float* recents, int64_t t,
-              int64_t b_kv, float* buf, int32_t* count, float* score_out, int32_t* kept_out,
-              void* ws, size_t ws_bytes, void* stream) {
-    const char* fn = "bkv_evict";
+static int evict_impl(const char* fn, const bkv_dims* dims, const bkv_policy* pol, uint16_t* K,
+                      uint16_t* V, int32_t* kpos, int64_t L, const float* beacons,
+                      const float* recents, int64_t t, const float* lse_in, int64_t lse_from,
+                      int64_t b_kv, float* buf, int32_t* count, float* score_out,
+                      int32_t* kept_out, void* ws, size_t ws_bytes, void* stream) {
     CHECK(check_dims(fn, dims));
     CHECK(check_policy(fn, pol));
     CHECK(check_score_args(fn, dims, pol, K, kpos, L, beacons, recents, t));
@@ -393,7 +393,7 @@ int bkv_evict(const bkv_dims* dims, const bkv_policy* pol, uint16_t* K, uint16_t
                               L, beacons, pol->buf_cap, recents, pol->n_beacon,
                               pol->n_recent_q, t, pol->rope_theta, scale_of(dims, pol),
                               (pol->flags & BKV_FLAG_MEAN) != 0, table, score, nullptr,
-                              nullptr, 0, s);
+                              lse_in, lse_from, s);
     const bool sorted = (pol->flags & BKV_FLAG_UNSORTED) == 0;
     if (e == hipSuccess && sorted && bkv::select_compact_fits(L)) {
         // Selection and in-place compaction in one launch.
@@ -415,6 +415,28 @@ int bkv_evict(const bkv_dims* dims, const bkv_policy* pol, uint16_t* K, uint16_t
                             dims->n_units * dims->group, dims->d_head, pol->buf_cap,
                             pol->n_beacon + pol->n_recent_q, pol->n_beacon, nullptr, nullptr, s);
     return hip_result(e, fn);
+}
+
+int bkv_evict(const bkv_dims* dims, const bkv_policy* pol, uint16_t* K, uint16_t* V,
+              int32_t* kpos, int64_t L, const float* beacons, const float* recents, int64_t t,
+              int64_t b_kv, float* buf, int32_t* count, float* score_out, int32_t* kept_out,
+              void* ws, size_t ws_bytes, void* stream) {
+    return evict_impl("bkv_evict", dims, pol, K, V, kpos, L, beacons, recents, t, nullptr, 0,
+                      b_kv, buf, count, score_out, kept_out, ws, ws_bytes, stream);
+}
+
+int bkv_evict_lse(const bkv_dims* dims, const bkv_policy* pol, uint16_t* K, uint16_t* V,
+                  int32_t* kpos, int64_t L, const float* beacons, const float* recents,
+                  int64_t t, const float* lse_in, int64_t lse_from, int64_t b_kv, float* buf,
+                  int32_t* count, float* score_out, int32_t* kept_out, void* ws,
+                  size_t ws_bytes, void* stream) {
+    const char* fn = "bkv_evict_lse";
+    if (!lse_in) return fail(BKV_EINVAL, "%s: NULL lse_in", fn);
+    if (!(0 <= lse_from && lse_from <= L))
+        return fail(BKV_EINVAL, "%s: need 0 <= lse_from (%lld) <= L (%lld)", fn,
+                    (long long)lse_from, (long long)L);
+    return evict_impl(fn, dims, pol, K, V, kpos, L, beacons, recents, t, lse_in, lse_from, b_kv,
+                      buf, count, score_out, kept_out, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

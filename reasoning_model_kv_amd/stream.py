@@ -26,8 +26,8 @@ With fused_decode=True the steps' decode attention (bkv_decode_attend) also
 gathers the scores' softmax denominators: at the beacon fix it adds the
 beacon rows, rotated to the coming eviction's step, and at each recent step
 the new query's own log-sum-exp is kept; the eviction then scores with
-bkv_score_lse (one read of the keys) and runs select and compact (one
-launch, bkv_select_compact) and the merge as separate calls.  The attention output of those steps is left in
+bkv_evict_lse (bkv_evict with the scores from those denominators: one read
+of the keys).  The attention output of those steps is left in
 `attn_out`; other steps' attention is the decoder's own business and is not
 run here.
 
@@ -239,16 +239,10 @@ class Stream:
         if self.fused:
             if self.t != self.t_obs:
                 raise RuntimeError("eviction step differs from the beacons' rotation step")
-            sh = self.shape
-            bkv.score_lse(sh, self.K, self.kpos, L, self.buf, self.recents, self.t,
-                          self.lse_in, self.lse_from, self.score, ws=self.ws)
-            if sh.unsorted:
-                bkv.select(sh, self.score, L, self.b_kv, self.kept)
-                bkv.compact_unsorted(sh, self.K, self.V, self.kpos, L, self.kept, self.b_kv)
-            else:
-                bkv.select_compact(sh, self.score, L, self.b_kv, self.K, self.V, self.kpos,
-                                   self.kept)
-            bkv.fps_update(sh, self.buf, self.count, self.recents, trigger=32, m=16)
+            bkv.evict_lse(self.shape, self.K, self.V, self.kpos, L, self.buf, self.recents,
+                          self.t, self.lse_in, self.lse_from, self.b_kv, buf=self.buf,
+                          count=self.count, score_out=self.score, kept_out=self.kept,
+                          ws=self.ws)
         else:
             bkv.evict(self.shape, self.K, self.V, self.kpos, L, self.buf, self.recents,
                       self.t, self.b_kv, buf=None if initial else self.buf,

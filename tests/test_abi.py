@@ -241,3 +241,18 @@ def test_select_compact_validation(lib, monkeypatch):
                                   100, FAKE, FAKE, FAKE, FAKE, None) == bkv.BKV_OK
     monkeypatch.setenv("BKV_FAULT_INJECT", "bkv_select_compact")
     assert call(300, 100) == bkv.BKV_EHIP
+
+
+def test_evict_lse_validation(lib):
+    s = _shape(prefix=8)
+    need = bkv.workspace_bytes(s, 300, 200)
+    call = lambda lse=FAKE, lse_from=284, L=300: lib.bkv_evict_lse(
+        ctypes.byref(s.dims()), ctypes.byref(s.policy()), FAKE, FAKE, FAKE, L, FAKE, FAKE, L,
+        lse, lse_from, 200, None, None, None, None, FAKE, need, None)
+    assert call(lse=None) == bkv.BKV_EINVAL
+    assert call(lse_from=-1) == bkv.BKV_EINVAL
+    assert call(lse_from=301) == bkv.BKV_EINVAL
+    s0 = _shape(n_units=0, prefix=8)
+    assert lib.bkv_evict_lse(ctypes.byref(s0.dims()), ctypes.byref(s0.policy()), FAKE, FAKE, FAKE,
+                             300, FAKE, FAKE, 300, FAKE, 284, 200, None, None, None, None, FAKE,
+                             need, None) == bkv.BKV_OK

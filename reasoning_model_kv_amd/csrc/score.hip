@@ -815,7 +815,8 @@ void score_kernel(ScoreArgs a, int g, int hs) {
 // cache is the beacon rows' softmax denominator; the new query's own
 // log-sum-exp is a recent row's denominator at the next eviction.
 //
-// Mapping: one workgroup per unit, one wavefront per query head (g <= 8).
+// Mapping: one workgroup per unit, one wavefront per query head (g <= 4;
+// larger groups are split over two workgroups, see decode_kernel).
 // A fragments (rows of the 32 x 32 x 16 MFMA): rows 0..15 the beacons, row
 // 16 the new query, rows 17..31 zero; each lane rotates its own row's dims
 // (16 s + 8 (lane / 32) .. + 8 for step s pair with the same dims of step
@@ -826,6 +827,7 @@ void score_kernel(ScoreArgs a, int g, int hs) {
 // 16: accumulator 8 of lanes 0..31) update a running max and sum, and the
 // lane owning dims 2 lane (D = 128) or lane (D = 64) of the output adds
 // p_j * V[j] for the tile's 32 rows (p_j read from lane j into a scalar).
+// Keys and values are read once, with streaming (non-temporal) loads.
 constexpr int DT = 32;  // keys per tile of the decode kernel
 
 struct DecodeArgs {

@@ -4,20 +4,26 @@
 One step is one pass of the whole hot path over one batch of synthetic
 input, every stage through the C ABI on one stream:
 
-  1. bkv_fps_update  append this step's pre-RoPE query and Continual-FPS
-                     compress every head's buffer 32 -> 16        (a1, a2)
-  2. bkv_score       RoPE-align beacons/recents, Q_obs . K^T on bf16 MFMA,
-                     row softmax, max over the GQA group          (a4-a7)
-  3. bkv_select      forced prefix/recent slots + Top-K, ascending (a8)
-  4. bkv_compact     in-place gather of K, V, positions            (a9)
-  5. bkv_fps_update  merge the recent queries and compress 32 -> 16 (a10)
+  1. bkv_fps_update      append this step's pre-RoPE query and Continual-FPS
+                         compress every head's buffer 32 -> 16     (a1, a2)
+  2. bkv_score           RoPE-align beacons/recents, Q_obs . K^T on bf16
+                         MFMA, row softmax, max over the GQA group (a4-a7)
+  3. bkv_select_compact  forced prefix/recent slots + Top-K, then the
+                         in-place gather of K, V, positions, in one
+                         launch                                    (a8, a9)
+  4. bkv_fps_update      merge the recent queries and compress 32 -> 16 (a10)
 
-bkv_evict launches exactly stages 2-5; the bench calls them one by one so
-that HIP events on the launch stream time every kernel inside the timed
-region.  Before each step the cache, positions and buffers are restored
-from pristine copies and a scratch buffer is overwritten to flush caches;
-both happen outside the timed step.  Each timed step is bracketed by
-torch.cuda.synchronize() on both sides.
+The timed step is stage 1 plus one bkv_evict (stages 2-4); a second loop
+runs the stages as separate calls with HIP events between them on the
+launch stream, for the per-stage breakdown and the roofline of the dominant
+kernel.  Before each step the cache, positions and buffers are restored from
+pristine copies and a 512 MB buffer is read to leave the caches cold and
+clean; both happen outside the timed step.  Each timed step is bracketed by
+torch.cuda.synchronize() on both sides.  The default line also carries, under
+"variants", the same step with its softmax denominators taken from decode
+attention (--fused-decode alone prints that line); --workload
+qwen3_14b_stream runs the decode-time streaming policy and --prefill-fps N
+the prefill FPS over N-row prompts.
 
 Prints ONE JSON line (stdout).  Diagnostics go to stderr.
 """

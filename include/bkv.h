@@ -32,6 +32,10 @@
  *        buf       fp32  [Uq, buf_cap, d] pre-RoPE query buffer per head
  *        count     int32 [Uq]            rows in use in buf
  *        recents   fp32  [Uq, n_recent_q, d] pre-RoPE recent queries
+ *        lse_in    fp32  [U, g, 32]      softmax denominators by observation
+ *                                        row (natural-log log-sum-exp)
+ *        q, out    fp32  [Uq, d]         decode-step query, attention output
+ *        lse_q     fp32  [Uq]; lse_obs fp32 [Uq, 16]
  *    Unit u is (layer * batch + b) * h_kv + kv_head; query head j of unit u
  *    is u * g + j.
  */

@@ -4,10 +4,12 @@ from known denominators (bkv_score_lse) against the float64 oracle.
 The decode kernel streams keys and values in tiles of 32 through rings of
 three LDS tiles; the cases cover one slot, a single partial tile, ragged
 tails with l_cap > L, several ring turns, groups of 2, 4, 5 and 7 and both
-head sizes.  The scoring cases place lse_from so that the tail pass covers
-one tile (the two tiles the backward walk needs next are then loaded
-separately), two tiles, every tile (lse_from = 0) and no slot at all
-(lse_from = L).
+head sizes, a long cache, and the two-workgroup split of groups larger than
+four.  The scoring cases place lse_from so that the tail pass covers one
+tile (the prologue then loads the first tile the backward walk needs beyond
+it, and the walk visits the buffers in the reflected order), two tiles,
+every tile (lse_from = 0) and no slot at all (lse_from = L); the 32-query
+window and the full-size path are covered too.
 """
 import numpy as np
 import pytest

@@ -94,6 +94,20 @@ def parse():
     return p.parse_args()
 
 
+def moved_token_count(kept, b_kv, unsorted):
+    """Tokens a compaction moves, from the ascending keep sets [U, b_kv].
+
+    In position order the k-th kept slot moves unless it already is slot k;
+    filling the holes instead moves only the kept slots at or past b_kv.
+    """
+    import numpy as np
+
+    kept = np.asarray(kept).reshape(-1, b_kv)
+    if unsorted:
+        return int(np.count_nonzero(kept >= b_kv))
+    return int(np.count_nonzero(kept != np.arange(b_kv)[None, :]))
+
+
 def stage_bytes(w, n_mv_total):
     """Algorithmic HBM bytes per launch of each stage (what the method must move)."""
     U, g, d, L, B = w.n_units, w.group, w.d_head, w.L, w.b_kv
@@ -366,11 +380,7 @@ def main():
     eprint(f"[bench] {args.warmup} warmup steps done")
 
     # Moved tokens of this (deterministic) eviction, for the compaction bytes.
-    kept_host = kept.cpu().numpy()
-    if shape.unsorted:  # only the kept tokens past B_KV move
-        n_mv = int(np.count_nonzero(kept_host >= B))
-    else:
-        n_mv = int(np.count_nonzero(kept_host != np.arange(B)[None, :]))
+    n_mv = moved_token_count(kept.cpu().numpy(), B, shape.unsorted)
 
     wall, gpu_evict, gpu_fps_c = [], [], []
     for i in range(args.steps):
@@ -635,8 +645,7 @@ def fused_main(args, w):
         dec_fused.append(b)
     eprint(f"[bench] {args.steps} timed steps done (fused-decode eviction)")
 
-    kept_host = kept.cpu().numpy()
-    n_mv = int(np.count_nonzero(kept_host != np.arange(B)[None, :]))
+    n_mv = moved_token_count(kept.cpu().numpy(), B, False)
     gpu_ms = {n: float(np.mean(v)) for n, v in stage_ms.items()}
     sbytes = {n: b for n, b in stage_bytes(w, n_mv).items() if n in names}
     sbytes["score"] += U * g * 32 * 4          # the known denominators read

@@ -55,8 +55,3 @@ def evict_unit(keys, values, kpos, L, beacons, recents, t, b_kv, prefix,
         out["fps_order"] = orders
     return out
 
-
-def moved_tokens(kept):
-    """Number of kept entries whose slot changes when compacting in place."""
-    kept = np.asarray(kept)
-    return int(np.count_nonzero(kept != np.arange(kept.shape[0])))

@@ -2,6 +2,8 @@
 import subprocess
 import sys
 
+import numpy as np
+
 import bench
 import synth
 
@@ -38,3 +40,23 @@ def test_unknown_workload_is_refused():
     r = subprocess.run([sys.executable, bench.__file__, "--workload", "nope"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "unknown workload" in r.stderr
+
+
+def test_moved_token_count():
+    # Hand cases: nothing evicted below the last kept slot moves nothing; a
+    # gap at slot 2 moves every later kept slot; unsorted moves only the
+    # kept slots at or past b_kv.
+    assert bench.moved_token_count([[0, 1, 2, 3]], 4, False) == 0
+    assert bench.moved_token_count([[0, 1, 3, 4]], 4, False) == 2
+    assert bench.moved_token_count([[1, 2, 3, 4]], 4, False) == 4
+    assert bench.moved_token_count([[0, 1, 3, 4]], 4, True) == 1
+    assert bench.moved_token_count([[0, 5, 6, 7]], 4, True) == 3
+    # Random keep sets against an explicit loop.
+    r = np.random.default_rng(0)
+    for _ in range(20):
+        L, b = int(r.integers(10, 60)), int(r.integers(2, 9))
+        kept = np.array([np.sort(r.choice(L, size=b, replace=False)) for _ in range(3)])
+        want_sorted = sum(1 for row in kept for k, slot in enumerate(row) if slot != k)
+        want_fill = sum(1 for row in kept for slot in row if slot >= b)
+        assert bench.moved_token_count(kept, b, False) == want_sorted
+        assert bench.moved_token_count(kept, b, True) == want_fill

@@ -3,16 +3,20 @@
 // Paper text §2.2: the compressed cache indexes the sequence dimension with
 // the retained set; summary step (5): written back in position order.
 //
-// Mapping: one wavefront per KV group walks its kept list in ascending
-// order, 16 tokens per iteration (a bf16 row of d = 128 is 16 lanes x 16
-// bytes, so one load instruction moves 4 rows), with the next iteration's
-// rows in flight while this one's are stored.  In place, tokens before the
-// first evicted slot do not move and are skipped.  The walk is safe in
-// place without any barrier: kept is strictly ascending, so the source of
-// token k is at a slot >= k and every destination written by an iteration
-// lies below every source read by later iterations; a destination can only
-// be the source of the same or an earlier token, whose load has completed
-// before the store that needs its data is issued.
+// Mapping: two wavefronts per KV group, one moving the key rows and the
+// positions, the other the value rows.  Each walks the kept list in
+// ascending order, 32 tokens per iteration (a bf16 row of d = 128 is 16
+// lanes x 16 bytes, so one load instruction moves 4 rows), with the next
+// iteration's rows in flight while this one's are stored.  In place, tokens
+// before the first evicted slot do not move and are skipped.  The walk is
+// safe in place without any barrier: kept is strictly ascending, so the
+// source of token k is at a slot >= k and every destination written by an
+// iteration lies below every source read by later iterations; a destination
+// can only be the source of the same or an earlier token, whose load has
+// completed before the store that needs its data is issued; and the two
+// wavefronts of a group touch disjoint tensors.  Splitting a group's moves
+// over two wavefronts (rather than one wavefront moving both tensors) keeps
+// twice as many groups' streams in flight: 5.1 against 4.9 TB/s.
 
 #include "common.h"
 #include "select_wave.h"
@@ -34,7 +38,7 @@ __device__ __forceinline__ uint4 ld_nt(const uint16_t* p) {
     return __builtin_bit_cast(uint4,
                               __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
 }
-constexpr int TPI = 16;  // tokens per iteration
+constexpr int TPI = 32;  // tokens per iteration
 
 // Write-only sink for the stores of tokens past the end of the kept list (or
 // of malformed entries): every store is issued unconditionally, so that the
@@ -42,40 +46,30 @@ constexpr int TPI = 16;  // tokens per iteration
 // the store may be missing and wait for loads still in flight).  Never read.
 __device__ uint4 g_sink[64];
 
-// The walk of one unit u by one wavefront (lane = its lane).
-template <int D>
-__device__ __forceinline__ void compact_wave(
-    uint16_t* K, uint16_t* V, int32_t* kpos, int64_t l_cap, const int32_t* __restrict__ kept,
-    int64_t L, int64_t b_kv, uint16_t* Ko, uint16_t* Vo, int32_t* kposo, int64_t out_cap,
-    int64_t u, int lane) {
+// First index k whose kept slot is not k (kept[k] - k never decreases), or
+// b_kv if nothing moves.
+__device__ __forceinline__ int64_t first_moved(const int32_t* __restrict__ ku, int64_t b_kv,
+                                               int lane) {
+    for (int64_t k0 = 0; k0 < b_kv; k0 += 64) {
+        const int64_t k = k0 + lane;
+        const bool moved = k < b_kv && ku[k] != (int32_t)k;
+        const uint64_t bal = __builtin_amdgcn_ballot_w64(moved);
+        if (bal) return k0 + __builtin_ctzll(bal);
+    }
+    return b_kv;
+}
+
+// The walk of one tensor of unit u by one wavefront: rows Ts[kept[k]] go to
+// Td[k] (Ts == Td in place), and with POS the positions ps[kept[k]] to
+// pd[k].  Tokens before k0 are not moved.
+template <int D, bool POS>
+__device__ __forceinline__ void compact_walk(const uint16_t* Ts, uint16_t* Td, const int32_t* ps,
+                                             int32_t* pd, const int32_t* __restrict__ ku,
+                                             int64_t L, int64_t b_kv, int64_t k0, int lane) {
     constexpr int LPT = D / 8;        // lanes per token row (16-byte chunks)
     constexpr int TPW = 64 / LPT;     // tokens per wave instruction
-    constexpr int NI = TPI / TPW;     // instructions per tensor per iteration (<= 4)
-    static_assert(NI >= 1 && NI <= 4, "tokens per iteration");
-    const bool inplace = (Ko == nullptr);
-    const int32_t* ku = kept + u * b_kv;
-    const uint16_t* Ks = K + u * l_cap * D;
-    const uint16_t* Vs = V + u * l_cap * D;
-    const int32_t* ps = kpos + u * l_cap;
-    uint16_t* Kd = inplace ? K + u * l_cap * D : Ko + u * out_cap * D;
-    uint16_t* Vd = inplace ? V + u * l_cap * D : Vo + u * out_cap * D;
-    int32_t* pd = inplace ? kpos + u * l_cap : kposo + u * out_cap;
-
-    int64_t k0 = 0;
-    if (inplace) {
-        // First index whose slot changes (kept[k] - k never decreases).
-        for (k0 = 0; k0 < b_kv; k0 += 64) {
-            const int64_t k = k0 + lane;
-            const bool moved = k < b_kv && ku[k] != (int32_t)k;
-            const uint64_t bal = __builtin_amdgcn_ballot_w64(moved);
-            if (bal) {
-                k0 += __builtin_ctzll(bal);
-                break;
-            }
-        }
-        if (k0 >= b_kv) return;
-    }
-
+    constexpr int NI = TPI / TPW;     // instructions per iteration (<= 8)
+    static_assert(NI >= 1 && NI <= 8, "tokens per iteration");
     const int st = lane / LPT;  // token within an instruction
     const int ch = lane % LPT;  // 16-byte chunk within the row
     const int64_t off = 8 * ch;
@@ -87,11 +81,11 @@ __device__ __forceinline__ void compact_wave(
         const int32_t v = ku[k < b_kv ? k : b_kv - 1];
         return (k < b_kv && v >= 0 && v < L) ? v : -1;
     };
-    // One iteration's rows and positions.  Invalid tokens load slot 0 (the
+    // One iteration's rows (and positions).  Invalid tokens load slot 0 (the
     // loads stay unconditional, so the compiler's waits count exactly) and
     // are stored into the sink.
     struct Batch {
-        uint4 k[NI], v[NI];
+        uint4 r[NI];
         int32_t s[NI];
         int32_t p;
         bool pv;
@@ -101,11 +95,12 @@ __device__ __forceinline__ void compact_wave(
         for (int i = 0; i < NI; ++i) {
             b.s[i] = __shfl(kv, st + i * TPW);
             const int64_t r = b.s[i] >= 0 ? b.s[i] : 0;
-            b.k[i] = ld_nt(Ks + r * D + off);
-            b.v[i] = ld_nt(Vs + r * D + off);
+            b.r[i] = ld_nt(Ts + r * D + off);
         }
-        b.pv = kv >= 0;
-        b.p = ps[kv >= 0 ? kv : 0];
+        if (POS) {
+            b.pv = kv >= 0;
+            b.p = ps[kv >= 0 ? kv : 0];
+        }
     };
     // Every lane stores: invalid tokens into the sink; lanes TPI.. repeat the
     // position stores of lanes 0..TPI-1 (same address, same value).
@@ -114,19 +109,20 @@ __device__ __forceinline__ void compact_wave(
         for (int i = 0; i < NI; ++i) {
             const int64_t kb = base + st + i * TPW;
             const bool ok = b.s[i] >= 0;
-            st_nt(ok ? Kd + kb * D + off : reinterpret_cast<uint16_t*>(&g_sink[lane]), b.k[i]);
-            st_nt(ok ? Vd + kb * D + off : reinterpret_cast<uint16_t*>(&g_sink[lane]), b.v[i]);
+            st_nt(ok ? Td + kb * D + off : reinterpret_cast<uint16_t*>(&g_sink[lane]), b.r[i]);
         }
-        *(b.pv ? pd + base + (lane & (TPI - 1)) : reinterpret_cast<int32_t*>(&g_sink[lane])) = b.p;
+        if (POS)
+            *(b.pv ? pd + base + (lane & (TPI - 1)) : reinterpret_cast<int32_t*>(&g_sink[lane])) =
+                b.p;
     };
 
     // Software pipeline: the kept entries of the iteration after next and
     // the rows of the next iteration are loaded before this iteration's rows
-    // are stored.  Unrolled by two
-    // over two buffers, so that no register with a load in flight is ever
-    // copied (a copy would wait for the load).  Safe in place: every
-    // destination written by an iteration lies below every source read by
-    // the later ones (kept is strictly ascending and kept[k] >= k).
+    // are stored.  Unrolled by two over two buffers, so that no register
+    // with a load in flight is ever copied (a copy would wait for the load).
+    // Safe in place: every destination written by an iteration lies below
+    // every source read by the later ones (kept is strictly ascending and
+    // kept[k] >= k).
     Batch A, B;
     int32_t kvA = load_kept(k0);
     load_rows(kvA, A);
@@ -145,33 +141,65 @@ __device__ __forceinline__ void compact_wave(
     }
 }
 
+// Wavefront `part` (0: keys and positions, 1: values) of unit u's
+// compaction; Ko == nullptr means in place.
+template <int D>
+__device__ __forceinline__ void compact_part(uint16_t* K, uint16_t* V, int32_t* kpos,
+                                             int64_t l_cap, const int32_t* __restrict__ kept,
+                                             int64_t L, int64_t b_kv, uint16_t* Ko,
+                                             uint16_t* Vo, int32_t* kposo, int64_t out_cap,
+                                             int64_t u, int part, int lane) {
+    const bool inplace = (Ko == nullptr);
+    const int32_t* ku = kept + u * b_kv;
+    const int64_t k0 = inplace ? first_moved(ku, b_kv, lane) : 0;
+    if (k0 >= b_kv) return;
+    const int64_t so = u * l_cap * D, dof = inplace ? so : u * out_cap * D;
+    if (part == 0) {
+        compact_walk<D, true>(K + so, (inplace ? K : Ko) + dof, kpos + u * l_cap,
+                              inplace ? kpos + u * l_cap : kposo + u * out_cap, ku, L, b_kv, k0,
+                              lane);
+    } else {
+        compact_walk<D, false>(V + so, (inplace ? V : Vo) + dof, nullptr, nullptr, ku, L, b_kv,
+                               k0, lane);
+    }
+}
+
+// Wavefront w of workgroup b: unit (4 b + w) / 2, part w % 2.
 template <int D>
 __global__ __launch_bounds__(64 * WAVES) void compact_kernel(
     uint16_t* K, uint16_t* V, int32_t* kpos, int64_t l_cap, const int32_t* __restrict__ kept,
     int64_t L, int64_t b_kv, uint16_t* Ko, uint16_t* Vo, int32_t* kposo, int64_t out_cap,
     int64_t n_units) {
-    const int64_t u = (int64_t)blockIdx.x * WAVES + (threadIdx.x >> 6);
+    const int64_t gw = (int64_t)blockIdx.x * WAVES + (threadIdx.x >> 6);
+    const int64_t u = gw >> 1;
     if (u >= n_units) return;
-    compact_wave<D>(K, V, kpos, l_cap, kept, L, b_kv, Ko, Vo, kposo, out_cap, u, threadIdx.x & 63);
+    compact_part<D>(K, V, kpos, l_cap, kept, L, b_kv, Ko, Vo, kposo, out_cap, u, (int)(gw & 1),
+                    threadIdx.x & 63);
 }
 
-// Selection and in-place compaction of a unit by one wavefront (summary
-// step (5) as one launch): the wavefront selects the unit's keep set from its
-// scores (select_wave_reg, units of up to 64 * NR slots), writes it to kept,
-// and then walks it as compact_kernel does.  The keep set is read back from
-// memory after a workgroup-scope release/acquire, so the walk sees every
-// lane's writes.  A unit's selection is latency-bound and its walk
-// bandwidth-bound: the wavefronts of other units keep HBM busy meanwhile.
+// Selection and in-place compaction in one launch (summary step (5)): a
+// workgroup of four wavefronts takes two units.  Wavefronts 0 and 1 select
+// the keep sets of the two units (select_wave_reg, units of up to 64 * NR
+// slots) and write them to kept; after a workgroup barrier, which makes
+// those writes visible to the whole workgroup, wavefronts 2u' and 2u' + 1
+// move unit u''s keys and positions and its values.  A unit's selection is
+// latency-bound and its walk bandwidth-bound: the wavefronts of other
+// workgroups keep HBM busy meanwhile.
 template <int D, int NR>
-__device__ __forceinline__ void select_compact_wave(
+__device__ __forceinline__ void select_compact_group(
     uint16_t* K, uint16_t* V, int32_t* kpos, int64_t l_cap, const float* __restrict__ score,
-    int32_t* kept, int64_t L, int64_t b_kv, int prefix, int recent_tok, int64_t u, int lane,
-    uint32_t* hist) {
-    select_wave_reg<NR>(score + u * l_cap, L, b_kv, prefix, recent_tok, kept + u * b_kv, hist,
+    int32_t* kept, int64_t L, int64_t b_kv, int prefix, int recent_tok, int64_t n_units,
+    uint32_t (*hist)[256]) {
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t u0 = (int64_t)blockIdx.x * 2;
+    if (w < 2 && u0 + w < n_units)
+        select_wave_reg<NR>(score + (u0 + w) * l_cap, L, b_kv, prefix, recent_tok,
+                            kept + (u0 + w) * b_kv, hist[w], lane);
+    __syncthreads();
+    const int64_t u = u0 + (w >> 1);
+    if (u < n_units)
+        compact_part<D>(K, V, kpos, l_cap, kept, L, b_kv, nullptr, nullptr, nullptr, 0, u, w & 1,
                         lane);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    compact_wave<D>(K, V, kpos, l_cap, kept, L, b_kv, nullptr, nullptr, nullptr, 0, u, lane);
 }
 
 // Units of up to 64 * 36 slots: held to 128 VGPRs, four wavefronts per SIMD
@@ -181,12 +209,9 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4)))
 void select_compact_kernel(uint16_t* K, uint16_t* V, int32_t* kpos, int64_t l_cap,
                            const float* __restrict__ score, int32_t* kept, int64_t L,
                            int64_t b_kv, int prefix, int recent_tok, int64_t n_units) {
-    __shared__ uint32_t hist[WAVES][256];
-    const int w = threadIdx.x >> 6;
-    const int64_t u = (int64_t)blockIdx.x * WAVES + w;
-    if (u >= n_units) return;
-    select_compact_wave<D, NR>(K, V, kpos, l_cap, score, kept, L, b_kv, prefix, recent_tok, u,
-                               threadIdx.x & 63, hist[w]);
+    __shared__ uint32_t hist[2][256];
+    select_compact_group<D, NR>(K, V, kpos, l_cap, score, kept, L, b_kv, prefix, recent_tok,
+                                n_units, hist);
 }
 
 // Up to 64 * 72 slots: the 72 score registers per lane need more than 128
@@ -195,12 +220,9 @@ template <int D>
 __global__ __launch_bounds__(64 * WAVES) void select_compact_kernel_wide(
     uint16_t* K, uint16_t* V, int32_t* kpos, int64_t l_cap, const float* __restrict__ score,
     int32_t* kept, int64_t L, int64_t b_kv, int prefix, int recent_tok, int64_t n_units) {
-    __shared__ uint32_t hist[WAVES][256];
-    const int w = threadIdx.x >> 6;
-    const int64_t u = (int64_t)blockIdx.x * WAVES + w;
-    if (u >= n_units) return;
-    select_compact_wave<D, 72>(K, V, kpos, l_cap, score, kept, L, b_kv, prefix, recent_tok, u,
-                               threadIdx.x & 63, hist[w]);
+    __shared__ uint32_t hist[2][256];
+    select_compact_group<D, 72>(K, V, kpos, l_cap, score, kept, L, b_kv, prefix, recent_tok,
+                                n_units, hist);
 }
 
 // Wavefront-wide synchronisation of LDS between the lanes of one wavefront.
@@ -334,7 +356,8 @@ hipError_t launch_compact(uint16_t* K, uint16_t* V, int32_t* kpos,
                           uint16_t* V_out, int32_t* kpos_out, int64_t out_cap,
                           hipStream_t s) {
     if (n_units <= 0) return hipSuccess;
-    const dim3 grid((unsigned)((n_units + WAVES - 1) / WAVES));
+    // Two wavefronts per unit.
+    const dim3 grid((unsigned)((2 * n_units + WAVES - 1) / WAVES));
     if (d == 128)
         compact_kernel<128><<<grid, 64 * WAVES, 0, s>>>(K, V, kpos, l_cap, kept, L, b_kv, K_out,
                                                         V_out, kpos_out, out_cap, n_units);
@@ -352,7 +375,8 @@ hipError_t launch_select_compact(uint16_t* K, uint16_t* V, int32_t* kpos, int64_
                                  hipStream_t s) {
     if (n_units <= 0) return hipSuccess;
     if (!select_compact_fits(L)) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)((n_units + WAVES - 1) / WAVES));
+    // Two units per workgroup.
+    const dim3 grid((unsigned)((n_units + 1) / 2));
 #define BKV_SC(DD, NR)                                                                    \
     select_compact_kernel<DD, NR><<<grid, 64 * WAVES, 0, s>>>(K, V, kpos, l_cap, score, kept, \
                                                               L, b_kv, prefix, recent_tok, n_units)

@@ -48,8 +48,15 @@ class Stream:
     def __init__(self, n_units, group, d_head, b_max, b_kv, prefix, theta, recent_tok=16,
                  device="cuda", observer=None, beacon_policy="fps", unsorted=False,
                  fused_decode=False):
-        if b_max - b_kv < recent_tok or b_kv < prefix + recent_tok:
-            raise ValueError("need prefix + recent_tok <= b_kv <= b_max - recent_tok")
+        # The recent phase starts when the cache reaches b_max - n_recent_q, so
+        # that n_recent_q queries are collected before the eviction at b_max;
+        # after an eviction the cache holds b_kv slots and must lie below that
+        # point again, or the next interval would never switch phase.
+        n_recent_q = 16
+        if not (b_kv < b_max - n_recent_q and prefix + recent_tok <= b_kv):
+            raise ValueError(f"need prefix + recent_tok <= b_kv < b_max - n_recent_q "
+                             f"({n_recent_q}); got prefix {prefix}, recent_tok {recent_tok}, "
+                             f"b_kv {b_kv}, b_max {b_max}")
         if beacon_policy not in ("fps", "initial"):
             raise ValueError(f"beacon_policy must be 'fps' or 'initial', not {beacon_policy!r}")
         self.policy = beacon_policy
@@ -62,6 +69,8 @@ class Stream:
         self.rshape = replace(self.shape, buf_cap=self.shape.n_recent_q)
         U, nq = n_units, n_units * group
         self.b_max, self.b_kv, self.recent_tok = b_max, b_kv, recent_tok
+        self.n_recent_q = self.shape.n_recent_q
+        assert self.n_recent_q == n_recent_q
         self.K = torch.zeros((U, b_max, d_head), dtype=torch.bfloat16, device=dev)
         self.V = torch.zeros_like(self.K)
         self.kpos = torch.zeros((U, b_max), dtype=torch.int32, device=dev)
@@ -132,14 +141,14 @@ class Stream:
     def prefill(self, keys, values, queries):
         """keys, values: bf16 [U, P, d]; queries: fp32 [U*g, P, d] (P <= 8192)."""
         P = keys.shape[1]
-        if P < 17 or P > 8192 or P >= self.b_max - self.recent_tok:
+        if P < 17 or P > 8192 or P >= self.b_max - self.n_recent_q:
             raise ValueError(f"prompt length {P} not supported")
         self.K[:, :P] = keys
         self.V[:, :P] = values
         self.kpos[:, :P] = torch.arange(P, dtype=torch.int32, device=self.K.device)
         self.L = self.t = P
         if self.policy == "initial":  # the references come from the generation
-            if self.b_max - self.recent_tok - P < 16:
+            if self.b_max - self.n_recent_q - P < 16:
                 raise ValueError("prompt too long: 16 generated queries must precede the "
                                  "recent window")
             self.count.zero_()
@@ -181,7 +190,7 @@ class Stream:
             if compress:
                 self.events.append(("collect_fps", L))
                 self._note("collect_fps", "post")
-            if L == self.b_max - self.recent_tok:
+            if L == self.b_max - self.n_recent_q:
                 if self.rows > 16:
                     self._note("beacon_fix_fps", "pre")
                     bkv.fps_update(self.shape, self.buf, self.count, None, trigger=17, m=16,
@@ -195,8 +204,8 @@ class Stream:
                 self.rcount.zero_()
                 if self.fused:
                     # This step's attention, plus the fixed beacons rotated to
-                    # the eviction's step (recent_tok more tokens from here).
-                    self.t_obs = self.t + 1 + self.recent_tok
+                    # the eviction's step (n_recent_q more tokens from here).
+                    self.t_obs = self.t + 1 + self.n_recent_q
                     bkv.decode_attend(self.shape, self.K, self.V, L, q, self.t, self.attn_out,
                                       self.lse_q, self.buf, self.t_obs, self.lse_obs)
                     self.lse_in[:, :, :16] = self.lse_obs.view(-1, self.shape.group, 16)
@@ -208,7 +217,7 @@ class Stream:
             if self.fused:
                 # The step's attention; its log-sum-exp is recent row i's
                 # denominator (this cache is exactly what that row sees).
-                i = L - 1 - (self.b_max - self.recent_tok)
+                i = L - 1 - (self.b_max - self.n_recent_q)
                 bkv.decode_attend(self.shape, self.K, self.V, L, q, self.t, self.attn_out,
                                   self.lse_q)
                 self.lse_in[:, :, 16 + i] = self.lse_q.view(-1, self.shape.group)
@@ -224,7 +233,7 @@ class Stream:
                 self.rows += 1
                 if self.rows == 16:
                     self.events.append(("initial_set", L))
-            if L == self.b_max - self.recent_tok:
+            if L == self.b_max - self.n_recent_q:
                 self.events.append(("recent_start", L))
                 self.phase = "recent"
                 self.rcount.zero_()
@@ -235,6 +244,12 @@ class Stream:
     def _evict(self):
         L = self.L
         initial = self.policy == "initial"
+        # The merge appends the recents to buffers that must hold exactly the
+        # beacons (the library leaves a head whose rows would not fit
+        # unchanged); every head holds self.rows rows.
+        if not initial and self.rows != self.shape.n_beacon:
+            raise RuntimeError(f"eviction with {self.rows} buffer rows per head; the merge "
+                               f"needs exactly {self.shape.n_beacon}")
         self._note("evict", "pre")
         if self.fused:
             if self.t != self.t_obs:

@@ -60,3 +60,56 @@ def test_moved_token_count():
         want_fill = sum(1 for row in kept for slot in row if slot >= b)
         assert bench.moved_token_count(kept, b, False) == want_sorted
         assert bench.moved_token_count(kept, b, True) == want_fill
+
+
+def test_parity_sample_accepts_the_oracle_and_rejects_mistakes():
+    """The bench's parity leg, fed outputs built by the oracle itself (CPU
+    tensors), passes; a wrong keep set or a wrong compacted row fails it."""
+    import torch
+
+    import oracle
+    w = synth.WORKLOADS["tiny"]
+    inp = synth.workload_inputs(w)
+    U, g, d, L, B = w.n_units, w.group, w.d_head, w.L, w.b_kv
+    K0 = torch.from_numpy(inp["keys"]).to(torch.bfloat16)
+    V0 = torch.from_numpy(inp["values"]).to(torch.bfloat16)
+    P0 = torch.from_numpy(inp["kpos"])
+    buf0 = torch.from_numpy(inp["buf"].reshape(U * g, 32, d))
+    rec = torch.from_numpy(inp["recents"].reshape(U * g, 16, d))
+    newq = buf0[:, 31:32].clone()
+    beacons = np.stack([buf0[q].numpy()[oracle.fps.fps(buf0[q].numpy(), 16)[1]]
+                        for q in range(U * g)])
+    K, V, kpos = K0.clone(), V0.clone(), P0.clone()
+    buf, score = buf0.clone(), torch.zeros(U, L)
+    kept = torch.zeros(U, B, dtype=torch.int64)
+    for u in range(U):
+        ref = oracle.evict.evict_unit(K0[u].float().numpy(), V0[u].float().numpy(), P0[u].numpy(),
+                                      L, beacons[u * g:(u + 1) * g], rec[u * g:(u + 1) * g].numpy(),
+                                      L, B, w.prefix, w.recent_tok, w.theta)
+        score[u] = torch.from_numpy(ref["score"].astype(np.float32))
+        kept[u] = torch.from_numpy(ref["kept"])
+        K[u, :B], V[u, :B], kpos[u, :B] = K0[u, kept[u]], V0[u, kept[u]], P0[u, kept[u]]
+        for h in range(g):
+            buf[u * g + h, :16] = torch.from_numpy(ref["buf"][h])
+    args = (w, [0, U - 1], K0, V0, P0, buf0, newq, rec, beacons)
+    good = bench.parity_sample(*args, K, V, kpos, buf, score, kept, False, "max", False)
+    assert good["ok"] and good["kept_diff_outside_tie_band"] == 0 and good["compaction_exact"]
+    assert good["fps_rows_are_distinct_inputs"] and good["max_score_rel_err"] < 1e-6
+    # Swap the best kept middle slot for the worst evicted one.
+    s = score[0].numpy()
+    k0 = set(kept[0].tolist())
+    mid = [j for j in range(w.prefix, L - w.recent_tok)]
+    best = max((j for j in mid if j in k0), key=lambda j: s[j])
+    worst = min((j for j in mid if j not in k0), key=lambda j: s[j])
+    bad = kept.clone()
+    bad[0] = torch.tensor(sorted((k0 - {best}) | {worst}))
+    r = bench.parity_sample(*args, K, V, kpos, buf, score, bad, False, "max", False)
+    assert not r["ok"] and r["kept_diff_outside_tie_band"] == 2
+    K2 = K.clone()
+    K2[U - 1, 5] = K2[U - 1, 5] + 1
+    r = bench.parity_sample(*args, K2, V, kpos, buf, score, kept, False, "max", False)
+    assert not r["ok"] and not r["compaction_exact"]
+    buf2 = buf.clone()
+    buf2[1, 3] = buf2[1, 3] * 1.5    # a merged row that is no input row
+    r = bench.parity_sample(*args, K, V, kpos, buf2, score, kept, False, "max", False)
+    assert not r["ok"] and not r["fps_rows_are_distinct_inputs"]

@@ -360,11 +360,12 @@ int bkv_compact(const bkv_dims* dims, uint16_t* K, uint16_t* V, int32_t* kpos, i
                       fn);
 }
 
-static int evict_impl(const char* fn, const bkv_dims* dims, const bkv_policy* pol, uint16_t* K,
-                      uint16_t* V, int32_t* kpos, int64_t L, const float* beacons,
-                      const float* recents, int64_t t, const float* lse_in, int64_t lse_from,
-                      int64_t b_kv, float* buf, int32_t* count, float* score_out,
-                      int32_t* kept_out, void* ws, size_t ws_bytes, void* stream) {
+// Argument checks of bkv_evict and its variants (everything but the
+// workspace).
+static int evict_checks(const char* fn, const bkv_dims* dims, const bkv_policy* pol,
+                        const uint16_t* K, const uint16_t* V, const int32_t* kpos, int64_t L,
+                        const float* beacons, const float* recents, int64_t t, int64_t b_kv,
+                        const float* buf, const int32_t* count) {
     CHECK(check_dims(fn, dims));
     CHECK(check_policy(fn, pol));
     CHECK(check_score_args(fn, dims, pol, K, kpos, L, beacons, recents, t));
@@ -377,15 +378,16 @@ static int evict_impl(const char* fn, const bkv_dims* dims, const bkv_policy* po
     if (buf && pol->buf_cap < pol->n_beacon + pol->n_recent_q)
         return fail(BKV_EINVAL, "%s: buf_cap %d cannot hold beacons + recents", fn,
                     pol->buf_cap);
-    const WsLayout w = ws_layout(dims, pol, b_kv);
-    if (!ws || ws_bytes < w.total)
-        return fail(BKV_ENOSPC, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, w.total);
-    if (dims->n_units == 0) return ok();
-    if (fault_injected(fn)) return fail(BKV_EHIP, "%s: injected HIP failure", fn);
-    hipStream_t s = (hipStream_t)stream;
-    double* table = (double*)((char*)ws + w.table);
-    float* score = score_out ? score_out : (float*)((char*)ws + w.score);
-    int32_t* kept = kept_out ? kept_out : (int32_t*)((char*)ws + w.kept);
+    return BKV_OK;
+}
+
+// The launch sequence of one eviction event: RoPE table, scores, selection
+// and compaction, then the merge.  table, score and kept are device memory.
+static hipError_t evict_launch(const bkv_dims* dims, const bkv_policy* pol, uint16_t* K,
+                               uint16_t* V, int32_t* kpos, int64_t L, const float* beacons,
+                               const float* recents, int64_t t, const float* lse_in,
+                               int64_t lse_from, int64_t b_kv, float* buf, int32_t* count,
+                               double* table, float* score, int32_t* kept, hipStream_t s) {
     hipError_t e = bkv::launch_rope_table(table, t, pol->n_recent_q, dims->d_head,
                                           pol->rope_theta, s);
     if (e == hipSuccess)
@@ -414,7 +416,27 @@ static int evict_impl(const char* fn, const bkv_dims* dims, const bkv_policy* po
         e = bkv::launch_fps(buf, count, recents, pol->n_recent_q,
                             dims->n_units * dims->group, dims->d_head, pol->buf_cap,
                             pol->n_beacon + pol->n_recent_q, pol->n_beacon, nullptr, nullptr, s);
-    return hip_result(e, fn);
+    return e;
+}
+
+static int evict_impl(const char* fn, const bkv_dims* dims, const bkv_policy* pol, uint16_t* K,
+                      uint16_t* V, int32_t* kpos, int64_t L, const float* beacons,
+                      const float* recents, int64_t t, const float* lse_in, int64_t lse_from,
+                      int64_t b_kv, float* buf, int32_t* count, float* score_out,
+                      int32_t* kept_out, void* ws, size_t ws_bytes, void* stream) {
+    CHECK(evict_checks(fn, dims, pol, K, V, kpos, L, beacons, recents, t, b_kv, buf, count));
+    const WsLayout w = ws_layout(dims, pol, b_kv);
+    if (!ws || ws_bytes < w.total)
+        return fail(BKV_ENOSPC, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, w.total);
+    if (dims->n_units == 0) return ok();
+    if (fault_injected(fn)) return fail(BKV_EHIP, "%s: injected HIP failure", fn);
+    double* table = (double*)((char*)ws + w.table);
+    float* score = score_out ? score_out : (float*)((char*)ws + w.score);
+    int32_t* kept = kept_out ? kept_out : (int32_t*)((char*)ws + w.kept);
+    return hip_result(evict_launch(dims, pol, K, V, kpos, L, beacons, recents, t, lse_in,
+                                   lse_from, b_kv, buf, count, table, score, kept,
+                                   (hipStream_t)stream),
+                      fn);
 }
 
 int bkv_evict(const bkv_dims* dims, const bkv_policy* pol, uint16_t* K, uint16_t* V,

@@ -12,7 +12,8 @@
  * ---------------------------------------
  *  - Tensor pointers are DEVICE pointers allocated and owned by the caller.
  *    The library allocates no device memory in these calls and keeps no
- *    state between calls; scratch memory comes from the caller's workspace.
+ *    state between calls; scratch memory comes from the caller's workspace
+ *    (bkv_evict_noalloc alone uses a fixed array of the library instead).
  *  - bfloat16 tensors are passed as uint16_t bit patterns.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Every call only enqueues work on `stream`; none synchronises the host.
@@ -308,6 +309,29 @@ int bkv_evict(const bkv_dims* dims, const bkv_policy* pol, uint16_t* K,
               const float* recents, int64_t t, int64_t b_kv, float* buf,
               int32_t* count, float* score_out, int32_t* kept_out, void* ws,
               size_t ws_bytes, void* stream);
+
+/*
+ * bkv_evict_noalloc -- bkv_evict without a workspace, allocating nothing.
+ *
+ * For callers that cannot allocate device memory or pass a workspace: code
+ * under stream capture, tight serving loops, harnesses that forbid
+ * allocation.  The same eviction event as bkv_evict (same kernels, same
+ * results), with its scratch -- the RoPE angle table and, when score_out /
+ * kept_out are NULL, the score and kept arrays -- in a fixed 16 MiB array
+ * compiled into the library: one copy per GPU, held until the process ends.
+ * A call whose scratch would exceed 16 MiB returns BKV_ENOSPC before
+ * anything is enqueued (for U units, l_cap slots and b_kv kept, about
+ * U * (l_cap + b_kv) * 4 bytes when neither output is passed; pass score_out
+ * and kept_out for large caches).  Calls that overlap on one GPU (two
+ * streams, or two host threads) share that scratch and race; serialise them.
+ * The first call on a device looks up that device's copy (no allocation).
+ * Requires what bkv_evict requires, except ws.
+ */
+int bkv_evict_noalloc(const bkv_dims* dims, const bkv_policy* pol, uint16_t* K,
+                      uint16_t* V, int32_t* kpos, int64_t L, const float* beacons,
+                      const float* recents, int64_t t, int64_t b_kv, float* buf,
+                      int32_t* count, float* score_out, int32_t* kept_out,
+                      void* stream);
 
 /*
  * bkv_evict_lse -- bkv_evict with the softmax denominators already known.

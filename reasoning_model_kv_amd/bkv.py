@@ -24,7 +24,8 @@ BKV_FLAG_UNSORTED = 2  # policy flag: bkv_evict fills holes instead of shifting
 
 EXPORTS = ("bkv_abi_version", "bkv_last_error", "bkv_workspace_bytes", "bkv_fps_update",
            "bkv_score", "bkv_select", "bkv_compact", "bkv_compact_unsorted", "bkv_evict",
-           "bkv_score_lse", "bkv_decode_attend", "bkv_select_compact", "bkv_evict_lse")
+           "bkv_score_lse", "bkv_decode_attend", "bkv_select_compact", "bkv_evict_lse",
+           "bkv_evict_noalloc")
 
 
 class BkvError(RuntimeError):
@@ -117,6 +118,9 @@ def load_library(path=LIB_PATH):
     lib.bkv_evict.restype = ctypes.c_int
     lib.bkv_evict.argtypes = [_PD, _PP, _VP, _VP, _VP, _I64, _VP, _VP, _I64, _I64, _VP, _VP,
                               _VP, _VP, _VP, ctypes.c_size_t, _VP]
+    lib.bkv_evict_noalloc.restype = ctypes.c_int
+    lib.bkv_evict_noalloc.argtypes = [_PD, _PP, _VP, _VP, _VP, _I64, _VP, _VP, _I64, _I64, _VP,
+                                      _VP, _VP, _VP, _VP]
     lib.bkv_score_lse.restype = ctypes.c_int
     lib.bkv_score_lse.argtypes = [_PD, _PP, _VP, _VP, _I64, _VP, _VP, _I64, _VP, _I64, _VP,
                                   _VP, ctypes.c_size_t, _VP]
@@ -337,6 +341,24 @@ def evict(shape, K, V, kpos, L, beacons, recents, t, b_kv, buf=None, count=None,
         _ptr(score_out, torch.float32, "score_out", True),
         _ptr(kept_out, torch.int32, "kept_out", True), _ptr(ws, torch.uint8, "ws"), ws.numel(),
         _stream(stream)))
+
+
+def evict_noalloc(shape, K, V, kpos, L, beacons, recents, t, b_kv, buf=None, count=None,
+                  score_out=None, kept_out=None, stream=None):
+    lib = load_library()
+    _need_score_inputs(shape, K, kpos, beacons, recents)
+    _need(V, shape.n_units * shape.l_cap * shape.d_head, "V")
+    _need(buf, shape.n_units * shape.group * shape.buf_cap * shape.d_head, "buf")
+    _need(count, shape.n_units * shape.group, "count")
+    _need(score_out, shape.n_units * shape.l_cap, "score_out")
+    _need(kept_out, shape.n_units * int(b_kv), "kept_out")
+    _check(lib.bkv_evict_noalloc(
+        ctypes.byref(shape.dims()), ctypes.byref(shape.policy()), _bits(K, "K"), _bits(V, "V"),
+        _ptr(kpos, torch.int32, "kpos"), int(L), _ptr(beacons, torch.float32, "beacons", shape.n_beacon == 0),
+        _ptr(recents, torch.float32, "recents"), int(t), int(b_kv),
+        _ptr(buf, torch.float32, "buf", True), _ptr(count, torch.int32, "count", True),
+        _ptr(score_out, torch.float32, "score_out", True),
+        _ptr(kept_out, torch.int32, "kept_out", True), _stream(stream)))
 
 
 def evict_lse(shape, K, V, kpos, L, beacons, recents, t, lse_in, lse_from, b_kv, buf=None,

@@ -8,6 +8,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "common.h"
@@ -152,6 +153,42 @@ int check_select_args(const char* fn, const bkv_dims* d, const bkv_policy* p, in
         int rc_ = (x);               \
         if (rc_ != BKV_OK) return rc_; \
     } while (0)
+
+// Scratch memory of bkv_evict_noalloc, for callers that cannot allocate:
+// a fixed array in the library's device code, one copy on every GPU the
+// library runs on, held until the process ends.  It holds the RoPE angle
+// table and, when the caller passes no score or kept output, those arrays.
+// Nothing in it needs to start at zero: each call writes every byte it
+// reads.  Calls on one GPU share it, so calls that overlap on one GPU race.
+constexpr size_t kScratchBytes = 16u << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Device address of each GPU's copy of `scratch` (host code never passes the
+// array's own name, which on the host is only a stand-in): looked up once per
+// device, on the first bkv_evict_noalloc call with that device current.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+int scratch_of_current_device(const char* fn, void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_result(e, fn);
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(BKV_ENOTSUP, "%s: device %d beyond the %d the library tracks", fn, dev,
+                    kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(BKV_EHIP, "%s: scratch address on device %d: HIP error %d (%s)", fn, dev,
+                        (int)e, hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return BKV_OK;
+}
 
 }  // namespace
 
@@ -445,6 +482,42 @@ int bkv_evict(const bkv_dims* dims, const bkv_policy* pol, uint16_t* K, uint16_t
               void* ws, size_t ws_bytes, void* stream) {
     return evict_impl("bkv_evict", dims, pol, K, V, kpos, L, beacons, recents, t, nullptr, 0,
                       b_kv, buf, count, score_out, kept_out, ws, ws_bytes, stream);
+}
+
+int bkv_evict_noalloc(const bkv_dims* dims, const bkv_policy* pol, uint16_t* K, uint16_t* V,
+                      int32_t* kpos, int64_t L, const float* beacons, const float* recents,
+                      int64_t t, int64_t b_kv, float* buf, int32_t* count, float* score_out,
+                      int32_t* kept_out, void* stream) {
+    const char* fn = "bkv_evict_noalloc";
+    CHECK(evict_checks(fn, dims, pol, K, V, kpos, L, beacons, recents, t, b_kv, buf, count));
+    // Scratch layout: the table, then score and kept where the caller passes
+    // no output for them.  Checked before any HIP call.
+    size_t off = align_up(bkv::rope_table_bytes(pol->n_recent_q, dims->d_head));
+    size_t score_off = 0, kept_off = 0;
+    if (!score_out) {
+        score_off = off;
+        off = align_up(off + (size_t)dims->n_units * (size_t)dims->l_cap * sizeof(float));
+    }
+    if (!kept_out) {
+        kept_off = off;
+        off = align_up(off + (size_t)dims->n_units * (size_t)b_kv * sizeof(int32_t));
+    }
+    if (off > kScratchBytes)
+        return fail(BKV_ENOSPC,
+                    "%s: needs %zu bytes of scratch, the library's fixed scratch holds %zu; "
+                    "pass score_out and kept_out, or use bkv_evict with a workspace",
+                    fn, off, kScratchBytes);
+    if (dims->n_units == 0) return ok();
+    if (fault_injected(fn)) return fail(BKV_EHIP, "%s: injected HIP failure", fn);
+    void* base = nullptr;
+    CHECK(scratch_of_current_device(fn, &base));
+    char* ws = (char*)base;
+    float* score = score_out ? score_out : (float*)(ws + score_off);
+    int32_t* kept = kept_out ? kept_out : (int32_t*)(ws + kept_off);
+    return hip_result(evict_launch(dims, pol, K, V, kpos, L, beacons, recents, t, nullptr, 0,
+                                   b_kv, buf, count, (double*)ws, score, kept,
+                                   (hipStream_t)stream),
+                      fn);
 }
 
 int bkv_evict_lse(const bkv_dims* dims, const bkv_policy* pol, uint16_t* K, uint16_t* V,

@@ -256,3 +256,23 @@ def test_evict_lse_validation(lib):
     assert lib.bkv_evict_lse(ctypes.byref(s0.dims()), ctypes.byref(s0.policy()), FAKE, FAKE, FAKE,
                              300, FAKE, FAKE, 300, FAKE, 284, 200, None, None, None, None, FAKE,
                              need, None) == bkv.BKV_OK
+
+
+def test_evict_noalloc_scratch_limit(lib, monkeypatch):
+    """The fixed scratch (16 MiB) must hold the RoPE table plus the score and
+    kept arrays the caller does not pass; beyond it the call is refused before
+    anything reaches the HIP runtime."""
+    big = _shape(n_units=4608, l_cap=2176)
+    call = lambda s, score=None, kept=None, L=2176, b=2048: lib.bkv_evict_noalloc(
+        ctypes.byref(s.dims()), ctypes.byref(s.policy()), FAKE, FAKE, FAKE, L, FAKE, FAKE, L, b,
+        FAKE, FAKE, score, kept, None)
+    assert call(big) == bkv.BKV_ENOSPC
+    assert "16777216" in bkv.last_error() and "score_out" in bkv.last_error()
+    assert call(big, score=FAKE) == bkv.BKV_ENOSPC        # kept alone: 37.7 MB
+    monkeypatch.setenv("BKV_FAULT_INJECT", "bkv_evict_noalloc")
+    assert call(big, score=FAKE, kept=FAKE) == bkv.BKV_EHIP   # table only: fits
+    small = _shape(n_units=8, l_cap=2176)
+    assert call(small) == bkv.BKV_EHIP                      # 8 units: 135 KB fits
+    assert "injected" in bkv.last_error()
+    assert call(_shape(n_units=0, l_cap=2176)) == bkv.BKV_OK
+    assert call(small, b=2176) == bkv.BKV_EINVAL            # b_kv must be < L

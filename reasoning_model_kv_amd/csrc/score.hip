@@ -40,6 +40,13 @@ typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 constexpr int KT = 64;               // keys per tile
+// Key tiles in the scoring kernel's LDS ring: loads run two tiles ahead, so
+// the ring's last kRing tiles of pass 1 are still resident when pass 2
+// starts from the end.  With four 16 KB tiles (d = 128) two workgroups share
+// a CU: fewer units stream at once than with three tiles at three
+// workgroups, and more of each unit's keys are still on chip for pass 2.
+constexpr int kRing = 3;
+static_assert(kRing == 3 || kRing == 4, "ring depth");
 constexpr float kNegBig = -1.0e30f;  // finite "no key seen yet" running max
 // Buffer-resource flags word (gfx9 family: raw 32-bit data, no swizzle).
 constexpr int kBufferFlags = 0x00020000;
@@ -281,6 +288,22 @@ __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// Workgroup barrier of the scoring kernel.  HIP's __syncthreads() carries a
+// workgroup-scope release fence, which on this target waits for every
+// outstanding vector memory operation -- including the direct-to-LDS loads
+// of the key tiles still ahead -- and so would drain the prefetch at every
+// tile.  Here each wavefront has already waited (vmcnt) for its share of
+// every tile read after the barrier; the barrier drains only LDS traffic
+// (lgkmcnt: earlier reads of a buffer about to be refilled, writes of the
+// reduction buffer), and wavefront-scope fences keep the compiler from
+// moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt unbounded
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Key tiles in LDS: chunk p (16 bytes) of a tile holds global chunk (row j,
 // column c) of the tile's keys with p = j*CPR + (c ^ (j % CPR)), CPR = D/8
 // chunks per row; the XOR swizzle by row makes the 32 lanes that read one
@@ -384,6 +407,7 @@ void score_kernel(ScoreArgs a, int g, int hs) {
     __shared__ __attribute__((aligned(16))) uint16_t tile0[KT * D];
     __shared__ __attribute__((aligned(16))) uint16_t tile1[KT * D];
     __shared__ __attribute__((aligned(16))) uint16_t tile2[KT * D];
+    __shared__ __attribute__((aligned(16))) uint16_t tile3[kRing == 4 ? KT * D : 8];
     __shared__ float red[8][KT];
     constexpr int NPW = TileLoad<D, NL>::NPW;  // loads per loader lane per tile
 
@@ -468,7 +492,7 @@ void score_kernel(ScoreArgs a, int g, int hs) {
     } else {
         wait_vm<0>();
     }
-    __syncthreads();  // the cos/sin rows have landed
+    lds_barrier();  // the cos/sin rows have landed
     double2* rtab_lo = reinterpret_cast<double2*>(tile2);
     double2* rtab_hi = reinterpret_cast<double2*>(tile1);
     if (fix_recent_table<D>(a, u, rpos, lane, tid, 64 * nw, rtab_lo, rtab_hi)) {
@@ -491,7 +515,7 @@ void score_kernel(ScoreArgs a, int g, int hs) {
 #pragma unroll
         for (int i = 0; i < 2 * ObsRows<D>::NB; ++i)
             asm volatile("" : "+v"(rows[i].x), "+v"(rows[i].y), "+v"(rows[i].z), "+v"(rows[i].w));
-        __syncthreads();  // the cos/sin rows are no longer needed
+        lds_barrier();  // the cos/sin rows are no longer needed
         uint16_t* stage = tile2 + (h & 1) * 32 * D;
         for (int rnd = 0; 2 * rnd < nw; ++rnd) {
             const bool mine = active && (h >> 1) == rnd;
@@ -500,7 +524,7 @@ void score_kernel(ScoreArgs a, int g, int hs) {
             int ln = lane;
             asm volatile("" : "+v"(ln));
             if (mine) put_rows<D>(rows, ln, stage);
-            __syncthreads();
+            lds_barrier();
             if (mine) {
                 const TileRead<D> rs(ln);
                 const char* st = reinterpret_cast<const char*>(stage);
@@ -517,7 +541,7 @@ void score_kernel(ScoreArgs a, int g, int hs) {
                         *reinterpret_cast<uint4*>(q + 16 * s) = __builtin_bit_cast(uint4, frag[s]);
                 }
             }
-            __syncthreads();
+            lds_barrier();
         }
     }
 
@@ -543,7 +567,7 @@ void score_kernel(ScoreArgs a, int g, int hs) {
             else if (NST) wait_vm<NPW + 1>();                                      \
             else wait_vm<NPW>();                                                   \
         }                                                                          \
-        __syncthreads();                                                           \
+        lds_barrier();                                                           \
         if (loader && (it) + 2 < nt1)                                              \
             ld.issue(Ku, L, (int64_t)(t0 + (it) + 2) * KT, NXT2, h);               \
         f32x16 acc0, acc1;                                                         \
@@ -552,43 +576,46 @@ void score_kernel(ScoreArgs a, int g, int hs) {
         const int64_t base = (int64_t)(t0 + (it)) * KT;                            \
         __VA_ARGS__;                                                               \
     } while (0)
-// Tiles rotate through tile0, tile1, tile2 (tiles 0 and 1 are issued by the
+// Tiles rotate through tile0 .. tile(kRing-1) (tiles 0 and 1 are issued by the
 // prologue); SDEL is 1 when wavefront 0 issues a score store in each
 // iteration, which the wait of the next iteration must allow for.
 #define BKV_TILE_LOOP(SDEL, ...)                                                   \
     do {                                                                           \
-        for (int it = 0; it < nt1; it += 3) {                                      \
-            BKV_TILE_ITER(it, (SDEL) && h == 0 && it > 0, tile0, tile2, __VA_ARGS__); \
-            if (it + 1 < nt1)                                                      \
-                BKV_TILE_ITER(it + 1, (SDEL) && h == 0, tile1, tile0, __VA_ARGS__); \
-            if (it + 2 < nt1)                                                      \
-                BKV_TILE_ITER(it + 2, (SDEL) && h == 0, tile2, tile1, __VA_ARGS__); \
+        if constexpr (kRing == 3) {                                                \
+            for (int it = 0; it < nt1; it += 3) {                                  \
+                BKV_TILE_ITER(it, (SDEL) && h == 0 && it > 0, tile0, tile2, __VA_ARGS__); \
+                if (it + 1 < nt1)                                                  \
+                    BKV_TILE_ITER(it + 1, (SDEL) && h == 0, tile1, tile0, __VA_ARGS__); \
+                if (it + 2 < nt1)                                                  \
+                    BKV_TILE_ITER(it + 2, (SDEL) && h == 0, tile2, tile1, __VA_ARGS__); \
+            }                                                                      \
+        } else {                                                                   \
+            for (int it = 0; it < nt1; it += 4) {                                  \
+                BKV_TILE_ITER(it, (SDEL) && h == 0 && it > 0, tile0, tile2, __VA_ARGS__); \
+                if (it + 1 < nt1)                                                  \
+                    BKV_TILE_ITER(it + 1, (SDEL) && h == 0, tile1, tile3, __VA_ARGS__); \
+                if (it + 2 < nt1)                                                  \
+                    BKV_TILE_ITER(it + 2, (SDEL) && h == 0, tile2, tile0, __VA_ARGS__); \
+                if (it + 3 < nt1)                                                  \
+                    BKV_TILE_ITER(it + 3, (SDEL) && h == 0, tile3, tile1, __VA_ARGS__); \
+            }                                                                      \
         }                                                                          \
     } while (0)
 
-    // ---------------- pass 1: per-row running max and sum of exp2 ----------
-    // mc[v]: running maximum of row v's logits in log2 units (logit * c2),
-    // starting at a finite sentinel; l[v]: sum of exp2(logit * c2 - mc[v]).
-    // The maximum is updated lazily: a tile whose terms stay below
-    // kRescaleBig (logits at most ~64 log2 units above mc) is summed against
-    // the stale mc; otherwise (and for the first tile, where every term
-    // overflows against the sentinel) the tile is redone with a rescale.
+    // ---------------- pass 1: the rows' log-sum-exp --------------------------
+    // Fast path: ls[v] sums exp2(logit * c2) for row v over the lane's
+    // columns against a fixed reference of 0 (log2 units): one multiply, one
+    // exp2 and one add per logit, no running maximum and no branch.  In fp32
+    // this is as exact as the running-maximum form while every row's total
+    // lies in [2^-60, 2^100]: no partial sum overflows, and terms flushed to
+    // zero (below 2^-126) are under 2^-53 of the row's largest term.  That
+    // covers row log-sum-exps from about -41 to 69 (natural log).  A
+    // workgroup with any row outside redoes pass 1 with the running maximum
+    // (exact for any logits), so the range only decides the speed.
     // With known denominators, column 0 of each row starts from the row's
-    // value (in log2 units: LSE * log2(e)) with a sum of 1; a value of -inf
-    // (no slots before lse_from) starts empty like the other columns.
-    float mc[16], l[16];
-#pragma unroll
-    for (int v = 0; v < 16; ++v) { mc[v] = kNegBig; l[v] = 0.f; }
-    if (lse_mode && active && (lane & 31) == 0) {
-        const float* li = a.lse_in + qh * 32;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const float x = li[acc_row(v, lane)] * 1.4426950408889634f;
-            if (x > kNegBig) { mc[v] = x; l[v] = 1.f; }
-        }
-    }
-#define BKV_PASS1                                                                  \
-    if (active) {                                                                  \
+    // value (in log2 units: LSE * log2(e)); -inf (no slots before lse_from)
+    // starts empty.
+#define BKV_PASS1_MASKS                                                            \
     if (lse_mode) {                                                                \
         /* Beacon rows add the slots in [lse_from, L); recent rows none. */       \
         int ln = lane; /* fresh copy: the limits are not hoisted */                \
@@ -610,9 +637,70 @@ void score_kernel(ScoreArgs a, int g, int hs) {
             if (d0 > lim) acc0[v] = -__builtin_inff();                             \
             if (d1 > lim) acc1[v] = -__builtin_inff();                             \
         }                                                                          \
-    }                                                                              \
-    BKV_PASS1_HALF(0);                                                             \
-    BKV_PASS1_HALF(8);                                                             \
+    }
+    float ls[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) ls[v] = 0.f;
+    if (lse_mode && active && (lane & 31) == 0) {
+        const float* li = a.lse_in + qh * 32;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) ls[v] = exp2_sum(li[acc_row(v, lane)] * 1.4426950408889634f);
+    }
+#define BKV_PASS1_FAST                                                             \
+    if (active) {                                                                  \
+        BKV_PASS1_MASKS                                                            \
+        _Pragma("unroll") for (int v = 0; v < 16; ++v)                             \
+            ls[v] += exp2_sum(acc0[v] * c2) + exp2_sum(acc1[v] * c2);              \
+    }
+    BKV_TILE_LOOP(0, BKV_PASS1_FAST);
+#undef BKV_PASS1_FAST
+    // Totals over the 32 lanes of each half.
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) ls[v] += __shfl_xor(ls[v], o);
+    }
+    int out_of_range = 0;
+    if (active) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) out_of_range |= !(ls[v] >= 0x1p-60f && ls[v] <= 0x1p100f);
+    }
+    float lse[16];  // log2-domain LSE in units of (logit * c2)
+    if (!__syncthreads_or(out_of_range)) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) lse[v] = log2f(ls[v]);
+    } else {
+        // Pass 1 again with a running maximum.  Every wavefront is past the
+        // barrier, so no tile buffer is still being read; the loads start
+        // over as the prologue issued them.
+        if (loader) {
+            ld.issue(Ku, L, (int64_t)t0 * KT, tile0, h);
+            if (second >= 0) ld.issue(Ku, L, (int64_t)second * KT, tile1, h);
+        }
+        // mc[v]: running maximum of row v's logits in log2 units (logit * c2),
+        // starting at a finite sentinel; l[v]: sum of exp2(logit * c2 - mc[v]).
+        // The maximum is updated lazily: a tile whose terms stay below
+        // kRescaleBig (logits at most ~64 log2 units above mc) is summed
+        // against the stale mc; otherwise (and for the first tile, where every
+        // term overflows against the sentinel) the tile is redone with a
+        // rescale.  Known denominators start column 0 at their value with a
+        // sum of 1.
+        float mc[16], l[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) { mc[v] = kNegBig; l[v] = 0.f; }
+        if (lse_mode && active && (lane & 31) == 0) {
+            const float* li = a.lse_in + qh * 32;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const float x = li[acc_row(v, lane)] * 1.4426950408889634f;
+                if (x > kNegBig) { mc[v] = x; l[v] = 1.f; }
+            }
+        }
+#define BKV_PASS1                                                                  \
+    if (active) {                                                                  \
+        BKV_PASS1_MASKS                                                            \
+        BKV_PASS1_HALF(0);                                                         \
+        BKV_PASS1_HALF(8);                                                         \
     }
 // Rows v0..v0+7 of one tile: sum against the stale maxima if every term
 // stays below kRescaleBig, else rescale those rows.
@@ -636,32 +724,33 @@ void score_kernel(ScoreArgs a, int g, int hs) {
             }                                                                      \
         }                                                                          \
     } while (0)
-    BKV_TILE_LOOP(0, BKV_PASS1);
+        BKV_TILE_LOOP(0, BKV_PASS1);
 #undef BKV_PASS1
 #undef BKV_PASS1_HALF
-    // Merge the 32 lanes of each half: every lane ends with its rows' LSE.
+        // Merge the 32 lanes of each half: every lane ends with its rows' LSE.
 #pragma unroll
-    for (int o = 1; o < 32; o <<= 1) {
+        for (int o = 1; o < 32; o <<= 1) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const float m2 = __shfl_xor(mc[v], o);
-            const float l2 = __shfl_xor(l[v], o);
-            const float mn = fmaxf(mc[v], m2);
-            l[v] = l[v] * exp2_sum(mc[v] - mn) + l2 * exp2_sum(m2 - mn);
-            mc[v] = mn;
+            for (int v = 0; v < 16; ++v) {
+                const float m2 = __shfl_xor(mc[v], o);
+                const float l2 = __shfl_xor(l[v], o);
+                const float mn = fmaxf(mc[v], m2);
+                l[v] = l[v] * exp2_sum(mc[v] - mn) + l2 * exp2_sum(m2 - mn);
+                mc[v] = mn;
+            }
         }
-    }
-    float lse[16];  // log2-domain LSE in units of (logit * c2)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) lse[v] = mc[v] + log2f(l[v]);
+        for (int v = 0; v < 16; ++v) lse[v] = mc[v] + log2f(l[v]);
+    }
+#undef BKV_PASS1_MASKS
 
     // ---------------- pass 2: max over rows of (s - LSE) -------------------
     // Tiles t_res .. ntiles-1 are in LDS and complete (tile T in buffer
     // (T - t0) mod 3, or (ntiles - 1 - T) mod 3 when reflected); every other
     // tile is loaded by the walk two iterations ahead, the first of them at
     // iteration 0 when fewer than three tiles are resident.
-    const int t_res = reflect ? ntiles - 2 : (t0 > ntiles - 3 ? t0 : ntiles - 3);
-    __syncthreads();
+    const int t_res = reflect ? ntiles - 2 : (t0 > ntiles - kRing ? t0 : ntiles - kRing);
+    lds_barrier();
     float* score_u = a.score + u * a.l_cap;
 #define BKV_PASS2                                                                  \
     if constexpr (MEAN) {                                                          \
@@ -697,7 +786,7 @@ void score_kernel(ScoreArgs a, int g, int hs) {
         red[h][lane] = active ? c0 : -__builtin_inff();                            \
         red[h][32 + lane] = active ? c1 : -__builtin_inff();                       \
     }                                                                              \
-    __syncthreads();                                                               \
+    lds_barrier();                                                               \
     if (tid < KT) {                                                                \
         float best = red[0][tid];                                                  \
         for (int w = 1; w < nw; ++w) best = vmax(best, red[w][tid]);               \
@@ -740,7 +829,7 @@ void score_kernel(ScoreArgs a, int g, int hs) {
         red[h][lane] = active ? c0 : 0.f;                                          \
         red[h][32 + lane] = active ? c1 : 0.f;                                     \
     }                                                                              \
-    __syncthreads();                                                               \
+    lds_barrier();                                                               \
     if (tid < KT) {                                                                \
         float tot = red[0][tid];                                                   \
         for (int w = 1; w < nw; ++w) tot += red[w][tid];                           \
@@ -770,7 +859,7 @@ void score_kernel(ScoreArgs a, int g, int hs) {
             else if (h == 0) wait_vm<NPW + 1>();                                   \
             else wait_vm<NPW>();                                                   \
         }                                                                          \
-        __syncthreads();                                                           \
+        lds_barrier();                                                           \
         if (loader && T - 2 >= 0 && T - 2 < t_res)                                 \
             ld.template issue<kLoadStreaming>(Ku, L, (int64_t)(T - 2) * KT, NXT, h); \
         f32x16 acc0, acc1;                                                         \
@@ -785,16 +874,41 @@ void score_kernel(ScoreArgs a, int g, int hs) {
         if (j + 1 < ntiles) BKV_REV_ITER(j + 1, B2, B0, __VA_ARGS__);              \
         if (j + 2 < ntiles) BKV_REV_ITER(j + 2, B1, B2, __VA_ARGS__);              \
     }
+// Four buffers: B0..B3 hold (or will hold) tiles ntiles-1 .. ntiles-4, and
+// tile T - 2 goes into the buffer of tile T + 2.
+#define BKV_REV_LOOP4(B0, B1, B2, B3, ...)                                         \
+    for (int j = 0; j < ntiles; j += 4) {                                          \
+        BKV_REV_ITER(j, B0, B2, __VA_ARGS__);                                      \
+        if (j + 1 < ntiles) BKV_REV_ITER(j + 1, B1, B3, __VA_ARGS__);              \
+        if (j + 2 < ntiles) BKV_REV_ITER(j + 2, B2, B0, __VA_ARGS__);              \
+        if (j + 3 < ntiles) BKV_REV_ITER(j + 3, B3, B1, __VA_ARGS__);              \
+    }
     // Buffers visited from the last tile down.
-    if (reflect) {
-        BKV_REV_LOOP(tile0, tile2, tile1, BKV_PASS2);
+    if constexpr (kRing == 3) {
+        if (reflect) {
+            BKV_REV_LOOP(tile0, tile2, tile1, BKV_PASS2);
+        } else {
+            switch ((ntiles - 1 - t0) % 3) {
+                case 0: BKV_REV_LOOP(tile0, tile1, tile2, BKV_PASS2); break;
+                case 1: BKV_REV_LOOP(tile1, tile2, tile0, BKV_PASS2); break;
+                default: BKV_REV_LOOP(tile2, tile0, tile1, BKV_PASS2); break;
+            }
+        }
     } else {
-        switch ((ntiles - 1 - t0) % 3) {
-            case 0: BKV_REV_LOOP(tile0, tile1, tile2, BKV_PASS2); break;
-            case 1: BKV_REV_LOOP(tile1, tile2, tile0, BKV_PASS2); break;
-            default: BKV_REV_LOOP(tile2, tile0, tile1, BKV_PASS2); break;
+        // Tile T sits in buffer (T - t0) mod 4, or (ntiles - 1 - T) mod 4 when
+        // reflected.
+        if (reflect) {
+            BKV_REV_LOOP4(tile0, tile1, tile2, tile3, BKV_PASS2);
+        } else {
+            switch ((ntiles - 1 - t0) % 4) {
+                case 0: BKV_REV_LOOP4(tile0, tile3, tile2, tile1, BKV_PASS2); break;
+                case 1: BKV_REV_LOOP4(tile1, tile0, tile3, tile2, BKV_PASS2); break;
+                case 2: BKV_REV_LOOP4(tile2, tile1, tile0, tile3, BKV_PASS2); break;
+                default: BKV_REV_LOOP4(tile3, tile2, tile1, tile0, BKV_PASS2); break;
+            }
         }
     }
+#undef BKV_REV_LOOP4
 #undef BKV_REV_LOOP
 #undef BKV_REV_ITER
 #undef BKV_PASS2

@@ -269,3 +269,30 @@ def test_score_lse_recent_window(L, l_cap):
         if l_cap > L:
             assert np.all(sc[u, L:] == -1.0)
     log(f"  max rel err {worst:.3g}")
+
+
+# Known denominators outside the fast pass-1 range: a beacon row starting at
+# 150 (its total overflows 2^100) or, with no slot added, at -50 (its total
+# falls below 2^-60).  The workgroup then redoes pass 1 with a running
+# maximum; the scores must still follow the given denominators.
+@pytest.mark.parametrize("lse_from,special", [(240, 150.0), (256, -50.0)])
+def test_score_lse_out_of_range_denominators(lse_from, special):
+    w = _workload("tiny")
+    L = 256
+    log(f"score_lse with a beacon denominator of {special}, lse_from={lse_from}")
+    inp, dev, shape = _setup(w, L, L)
+    r = np.random.default_rng(5)
+    lse_np = r.uniform(-5.0, 5.0, size=(w.n_units, w.group, 32)).astype(np.float32)
+    lse_np[0, 0, 3] = special
+    lse = torch.from_numpy(lse_np).to(DEV)
+    score = torch.full((w.n_units, L), -1.0, device=DEV)
+    bkv.score_lse(shape, dev["keys"], dev["kpos"], L, dev["buf"], dev["recents"], L, lse,
+                  lse_from, score)
+    torch.cuda.synchronize()
+    sc = score.cpu().numpy()
+    for u in range(w.n_units):
+        taus = inp["kpos"][u][L - 16:L]
+        ref = oracle.decode.score_from_lse(inp["keys"][u], inp["buf"][u][:, :16],
+                                           inp["recents"][u], L, taus, w.theta,
+                                           lse_np[u].astype(np.float64), lse_from)
+        check_scores(sc[u], ref, f"unit {u}")

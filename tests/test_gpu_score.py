@@ -171,3 +171,40 @@ def test_score_recent_window_matches_oracle(name, L, l_cap, t_shift, aggregate):
             assert np.all(np.abs(got_q[neq] - qhat[neq]) <= ulp)
     assert flips <= 1e-4 * qobs.numel()
     log(f"  max rel err {worst:.3g}, bf16 rounding flips {flips}")
+
+
+# Pass 1 sums exp2(logit * scale * log2 e) against a fixed reference; a
+# workgroup with a row total outside [2^-60, 2^100] redoes pass 1 with a
+# running maximum.  These cases put rows outside that range, so the scores
+# come from the second path; they must still match the oracle.
+RESCUE_SCALES = [
+    (40.0, "logits up to several hundred: row totals overflow the fast range"),
+    (6.0, "some rows above 2^100, most inside"),
+]
+
+
+@pytest.mark.parametrize("sm_scale,why", RESCUE_SCALES)
+def test_score_large_logits_take_the_running_max_path(sm_scale, why):
+    w = synth.WORKLOADS["tiny"]
+    L = 300
+    w2 = synth.shrink(w, L=L)
+    inp = synth.workload_inputs(w2)
+    dev = synth.to_device(inp, DEV)
+    shape = bkv.Shape(w.n_units, w.group, w.d_head, L, w.prefix, w.theta,
+                      recent_tok=w.recent_tok, sm_scale=sm_scale)
+    log(f"score with sm_scale {sm_scale}: {why}")
+    score = torch.full((w.n_units, L), -1.0, device=DEV)
+    bkv.score(shape, dev["keys"], dev["kpos"], L, dev["buf"], dev["recents"], L, score)
+    torch.cuda.synchronize()
+    sc = score.cpu().numpy()
+    top = 0.0
+    for u in range(w.n_units):
+        taus = inp["kpos"][u][L - 16:L]
+        ref, _, logits, _ = oracle.score.score_unit(inp["keys"][u], inp["buf"][u][:, :16],
+                                                    inp["recents"][u], L, taus, w.theta,
+                                                    scale=sm_scale, return_all=True)
+        top = max(top, float(np.max(logits[:, :16])))  # beacon rows see every slot
+        check_scores(sc[u], ref, f"sm_scale {sm_scale} unit {u}")
+    # The case really leaves the fast range: some beacon row's log-sum-exp (at
+    # least its largest logit) exceeds 100 log2 units.
+    assert top * 1.4426950408889634 > 100, top

@@ -398,8 +398,8 @@ __device__ __forceinline__ void tile_logits(const uint16_t* lds_tile, const Tile
 // (blocks b and b + 8), where the second read of each key tile is likely to
 // hit L2, and combines its column maxima with an atomic maximum on the
 // score bits (non-negative floats order like their bit patterns).
-template <int D, int NL, bool SPLIT, bool MEAN>
-__global__ __launch_bounds__(512)
+template <int D, int NL, bool SPLIT, bool MEAN, int OCC = 0>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1, 8)))
 void score_kernel(ScoreArgs a, int g, int hs) {
     // Three separately declared tiles (not one array) so that the compiler
     // can tell the tiles being loaded by the direct-to-LDS loads from the tile
@@ -1232,6 +1232,10 @@ template __global__ void score_kernel<128, 1, true, true>(ScoreArgs, int, int);
 template __global__ void score_kernel<64, 4, true, true>(ScoreArgs, int, int);
 template __global__ void score_kernel<64, 2, true, true>(ScoreArgs, int, int);
 template __global__ void score_kernel<64, 1, true, true>(ScoreArgs, int, int);
+template __global__ void score_kernel<128, 4, false, false, 4>(ScoreArgs, int, int);
+template __global__ void score_kernel<128, 4, false, true, 4>(ScoreArgs, int, int);
+template __global__ void score_kernel<64, 4, false, false, 4>(ScoreArgs, int, int);
+template __global__ void score_kernel<64, 4, false, true, 4>(ScoreArgs, int, int);
 
 }  // namespace
 
@@ -1269,10 +1273,16 @@ hipError_t launch_score(const uint16_t* K, const int32_t* kpos, int64_t n_units,
     a.lse_in = lse_in;
     a.lse_from = lse_from;
     a.n_units = n_units;
-    // Groups of more than 4 heads: two workgroups per unit (see score_kernel).
-    a.split = g > 4 ? 1 : 0;
+    // One workgroup per unit, one wavefront per query head.  Groups of 5 to 8
+    // heads take the variant held to 128 VGPRs (four wavefronts per SIMD, its
+    // spills confined to the rare running-maximum pass 1), so that two or
+    // three workgroups share a CU: R1-Distill-Qwen-7B shape (g = 7) 2.50 ->
+    // 2.05 ms and Qwen3-14B shape (g = 5) 2.94 -> 2.50 ms against splitting a
+    // group over two workgroups, each of which read every key.
+    a.split = 0;
     a.inv_rows = 1.0f / (float)(g * 32);
     const int hs = a.split ? (g + 1) / 2 : g;
+    const bool capped = !a.split && g >= 5;
     if (a.split) {
         const int64_t n = n_units * L;
         const unsigned zb = (unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
@@ -1287,6 +1297,7 @@ hipError_t launch_score(const uint16_t* K, const int32_t* kpos, int64_t n_units,
 #define BKV_LAUNCH_M(DD, NN, MM)                                                   \
     do {                                                                           \
         if (a.split) score_kernel<DD, NN, true, MM><<<grid, block, 0, s>>>(a, g, hs); \
+        else if (capped) score_kernel<DD, 4, false, MM, 4><<<grid, block, 0, s>>>(a, g, hs); \
         else score_kernel<DD, NN, false, MM><<<grid, block, 0, s>>>(a, g, hs);     \
     } while (0)
 #define BKV_LAUNCH(DD, NN)                                                         \

@@ -250,6 +250,8 @@ def _all_unit_properties(w, kept):
 @pytest.mark.parametrize("name,samples", [
     ("qwen3_4b_full_b2048", [0, 1, 777, 2303, 4095, 4607]),
     ("qwen3_4b_full_b128", [0, 2304, 4607]),    # L = 256: a unit of four key tiles
+    ("qwen3_4b_full_b512", [0, 1500, 4607]),    # L = 640: the 16-register select
+    ("qwen3_4b_full_b1024", [0, 3100, 4607]),   # L = 1152: the 36-register select
     ("qwen3_4b_full_b4096", [0, 3001, 4607]),   # L = 4224
     ("r1_qwen_7b", [0, 1791, 3583]),
 ])

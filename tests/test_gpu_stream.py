@@ -8,7 +8,8 @@ oracle's scores and kept set on the pre-eviction cache, exact compaction
 with the GPU's kept set, and the merged buffer.  Small run: every unit and
 head, under the method's Continual FPS and under the Initial+Recent
 comparison (the first 16 generated queries as fixed references).  Qwen3-14B shape (40 layers x batch 16 x 8 KV heads, group 5): the
-first two eviction intervals on sampled units and heads.
+first two eviction intervals on sampled units and heads, and the whole
+32,768-step run with every 16th eviction checked.
 """
 import numpy as np
 import pytest
@@ -26,14 +27,26 @@ DEV = "cuda"
 class Checker:
     """Observer: snapshots sampled state before each event, checks after."""
 
-    def __init__(self, w, units, policy="fps", unsorted=False):
+    def __init__(self, w, units, policy="fps", unsorted=False, every_evict=1, every_fps=1):
         self.w, self.units, self.policy, self.unsorted = w, list(units), policy, unsorted
         self.heads = [u * w.group + h for u in self.units for h in range(w.group)]
         self.pre = None
         self.n = {"fps": 0, "evict": 0, "exact_fps": 0}
         self.worst = 0.0
+        # Check every every_evict-th eviction and every every_fps-th FPS event
+        # (counting from the first); the others run unobserved.
+        self.every = {"evict": every_evict, "fps": every_fps}
+        self.seen = {"evict": 0, "fps": 0}
+        self.checking = True
+        self.checked_evictions = []
 
     def __call__(self, kind, stage, st):
+        cls = "evict" if kind == "evict" else "fps"
+        if stage == "pre":
+            self.checking = self.seen[cls] % self.every[cls] == 0
+            self.seen[cls] += 1
+        if not self.checking:
+            return
         hi = torch.tensor(self.heads, device=st.buf.device)
         if stage == "pre":
             if kind == "prefill_fps":
@@ -99,6 +112,7 @@ class Checker:
                     order, _ = oracle.fps.fps(merged, 16)
                     assert sorted(order) == idx, where + " merged FPS set"
         self.n["evict"] += 1
+        self.checked_evictions.append(self.seen["evict"] - 1)
 
 
 def _oracle_events(w, n_steps, policy="fps"):
@@ -112,8 +126,9 @@ def _oracle_events(w, n_steps, policy="fps"):
     return st.events
 
 
-def _run(w, n_steps, units, chunk=128, policy="fps", unsorted=False, fused=False):
-    chk = Checker(w, units, policy, unsorted)
+def _run(w, n_steps, units, chunk=128, policy="fps", unsorted=False, fused=False,
+         every_evict=1, every_fps=1):
+    chk = Checker(w, units, policy, unsorted, every_evict, every_fps)
     st = bstream.Stream(w.n_units, w.group, w.d_head, w.L, w.b_kv, w.prefix, w.theta,
                         device=DEV, observer=chk, beacon_policy=policy, unsorted=unsorted,
                         fused_decode=fused)
@@ -155,6 +170,31 @@ def test_stream_qwen3_14b_two_intervals_sampled():
     assert st.L == w.b_kv + 40
     assert torch.all(st.count == 16 + 40 % 16)
     log(f"  FPS events {chk.n['fps']}, exact FPS sets {chk.n['exact_fps']}, "
+        f"max score rel err {chk.worst:.3g}")
+
+
+def test_stream_qwen3_14b_full_run_sampled():
+    """All 32,768 decode steps of the Qwen3-14B shape (5120 units, 226
+    evictions per unit): the cadence equals the oracle's over the whole run,
+    every 16th eviction and every 64th FPS event is checked in lockstep on
+    three units spread over the cache, and at the end every unit's positions
+    are strictly ascending and every head holds the rows the cadence says."""
+    w = synth.WORKLOADS["qwen3_14b_stream"]
+    n = w.stream_steps
+    units = [0, 2047, w.n_units - 1]
+    log(f"stream {w.name}: all {n} steps, units {units}, every 16th eviction checked")
+    st, chk = _run(w, n, units, every_evict=16, every_fps=64)
+    assert st.events == _oracle_events(w, n)
+    first = w.L - w.prefix
+    assert st.n_evictions == 1 + (n - first) // 128 == 226
+    assert chk.checked_evictions == list(range(0, st.n_evictions, 16))
+    assert chk.checked_evictions[-1] >= 208  # checks reach the end of the run
+    L = st.L
+    assert torch.all(st.kpos[:, 1:L] > st.kpos[:, :L - 1])
+    assert torch.all(st.kpos[:, L - 1] == st.t - 1)
+    assert torch.all(st.count == st.rows)
+    log(f"  evictions {st.n_evictions} ({len(chk.checked_evictions)} checked), FPS events "
+        f"checked {chk.n['fps']}, exact FPS sets {chk.n['exact_fps']}, "
         f"max score rel err {chk.worst:.3g}")
 
 

@@ -8,12 +8,11 @@ input, every stage through the C ABI on one stream:
                          compress every head's buffer 32 -> 16     (a1, a2)
   2. bkv_score           RoPE-align beacons/recents, Q_obs . K^T on bf16
                          MFMA, row softmax, max over the GQA group (a4-a7)
-  3. bkv_select_compact  forced prefix/recent slots + Top-K, then the
-                         in-place gather of K, V, positions, in one
-                         launch                                    (a8, a9)
-  4. bkv_fps_update      merge the recent queries and compress 32 -> 16 (a10)
+  3. bkv_select          forced prefix/recent slots + Top-K      (a8)
+  4. bkv_compact         in-place gather of K, V, positions      (a9)
+  5. bkv_fps_update      merge the recent queries and compress 32 -> 16 (a10)
 
-The timed step is stage 1 plus one bkv_evict (stages 2-4); a second loop
+The timed step is stage 1 plus one bkv_evict (stages 2-5); a second loop
 runs the stages as separate calls with HIP events between them on the
 launch stream, for the per-stage breakdown and the roofline of the dominant
 kernel.  Before each step the cache, positions and buffers are restored from
@@ -49,7 +48,7 @@ DEFAULT_WORKLOAD = "qwen3_4b_full_b2048"
 KERNEL_SOURCES = {
     "fps_compress": "fps.hip", "score": "score.hip", "select": "select.hip",
     "compact": "compact.hip", "fps_merge": "fps.hip", "score_lse": "score.hip",
-    "select_compact": ("compact.hip", "select_wave.h"),
+    "select_compact": ("select.hip", "select_wave.h", "compact.hip"),
 }
 
 
@@ -434,9 +433,8 @@ def main():
 
     # The same work as separate calls, with events between them, for the
     # per-stage breakdown and the roofline of the dominant kernel: the
-    # kernels bkv_evict runs (selection and in-place compaction in one
-    # launch, except for the unsorted compaction).
-    sel = ["select", "compact"] if shape.unsorted else ["select_compact"]
+    # kernels bkv_evict runs, one call each.
+    sel = ["select", "compact"]
     names = (["score"] + sel if window else ["fps_compress", "score"] + sel + ["fps_merge"])
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
 
@@ -448,7 +446,6 @@ def main():
             "select": lambda: bkv.select(shape, score, L, B, kept),
             "compact": lambda: (bkv.compact_unsorted(shape, K, V, kpos, L, kept, B)
                                 if shape.unsorted else bkv.compact(shape, K, V, kpos, L, kept, B)),
-            "select_compact": lambda: bkv.select_compact(shape, score, L, B, K, V, kpos, kept),
             "fps_merge": lambda: bkv.fps_update(shape, buf, count, rec, trigger=32, m=16),
         }
         ev[0].record(stream)
@@ -661,12 +658,13 @@ def fused_main(args, w):
         else:
             bkv.decode_attend(shape, K, V, L_fix, q_fix, int(P0[0, L_fix - 1]), out, lse_q)
 
-    names = ["fps_compress", "score", "select_compact", "fps_merge"]
+    names = ["fps_compress", "score", "select", "compact", "fps_merge"]
     calls = {
         "fps_compress": lambda: bkv.fps_update(shape, buf, count, newq, trigger=32, m=16),
         "score": lambda: bkv.score_lse(shape, K, kpos, L, buf, rec, L, lse_in, L_fix, score,
                                        ws=ws),
-        "select_compact": lambda: bkv.select_compact(shape, score, L, B, K, V, kpos, kept),
+        "select": lambda: bkv.select(shape, score, L, B, kept),
+        "compact": lambda: bkv.compact(shape, K, V, kpos, L, kept, B),
         "fps_merge": lambda: bkv.fps_update(shape, buf, count, rec, trigger=32, m=16),
     }
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
@@ -785,7 +783,7 @@ def fused_main(args, w):
                    "observation": "beacons16+recent16",
                    "denominators": "from decode attention (beacons at L-16, recents at their steps)"},
         "unit_evictions_per_s": round(U / (ms_wall * 1e-3), 1),
-        "step": ("bkv_fps_update (compress) + bkv_score_lse + bkv_select_compact + "
+        "step": ("bkv_fps_update (compress) + bkv_score_lse + bkv_select + bkv_compact + "
                  "bkv_fps_update (merge), plus the beacon rows' extra time in decode attention"),
         "gpu_ms_per_step": round(step_ms, 4),
         "gpu_ms_beacon_rows_in_decode": round(extra_ms, 4),

@@ -260,13 +260,12 @@ int bkv_compact(const bkv_dims* dims, uint16_t* K, uint16_t* V, int32_t* kpos,
 
 /*
  * bkv_select_compact -- bkv_select, then an in-place bkv_compact, in one
- * launch where the unit fits (L <= 4608 slots; beyond, the two kernels).
+ * call.
  *
  * Summary step (5) (keep prefix, recent and Top-K; write back in position
- * order); paper text §2.2.  The same kept sets and the same compacted K, V
- * and kpos as the two calls: one wavefront per unit selects its keep set
- * (written to kept, [U, b_kv], ascending) and then moves the kept tokens.
- * Requires what bkv_select requires.
+ * order); paper text §2.2.  The same kept sets (written to kept, [U, b_kv],
+ * ascending) and the same compacted K, V and kpos as the two calls, which
+ * it makes on the same stream.  Requires what bkv_select requires.
  */
 int bkv_select_compact(const bkv_dims* dims, const bkv_policy* pol, const float* score,
                        int64_t L, int64_t b_kv, uint16_t* K, uint16_t* V, int32_t* kpos,

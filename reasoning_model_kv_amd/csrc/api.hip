@@ -338,18 +338,10 @@ int bkv_select_compact(const bkv_dims* dims, const bkv_policy* pol, const float*
     if (dims->n_units == 0) return ok();
     if (fault_injected(fn)) return fail(BKV_EHIP, "%s: injected HIP failure", fn);
     hipStream_t s = (hipStream_t)stream;
-    hipError_t e;
-    if (bkv::select_compact_fits(L)) {
-        e = bkv::launch_select_compact(K, V, kpos, dims->n_units, dims->d_head, dims->l_cap, L,
-                                       score, kept, b_kv, pol->prefix, pol->recent_tok, s);
-    } else {
-        e = bkv::launch_select(score, dims->n_units, dims->l_cap, L, b_kv, pol->prefix,
-                               pol->recent_tok, kept, s);
-        if (e == hipSuccess)
-            e = bkv::launch_compact(K, V, kpos, dims->n_units, dims->d_head, dims->l_cap, L,
-                                    kept, b_kv, nullptr, nullptr, nullptr, dims->l_cap, s);
-    }
-    return hip_result(e, fn);
+    return hip_result(bkv::launch_select_compact(K, V, kpos, dims->n_units, dims->d_head,
+                                                 dims->l_cap, L, score, kept, b_kv, pol->prefix,
+                                                 pol->recent_tok, s),
+                      fn);
 }
 
 int bkv_compact_unsorted(const bkv_dims* dims, uint16_t* K, uint16_t* V, int32_t* kpos,
@@ -434,21 +426,15 @@ static hipError_t evict_launch(const bkv_dims* dims, const bkv_policy* pol, uint
                               (pol->flags & BKV_FLAG_MEAN) != 0, table, score, nullptr,
                               lse_in, lse_from, s);
     const bool sorted = (pol->flags & BKV_FLAG_UNSORTED) == 0;
-    if (e == hipSuccess && sorted && bkv::select_compact_fits(L)) {
-        // Selection and in-place compaction in one launch.
-        e = bkv::launch_select_compact(K, V, kpos, dims->n_units, dims->d_head, dims->l_cap, L,
-                                       score, kept, b_kv, pol->prefix, pol->recent_tok, s);
-    } else {
-        if (e == hipSuccess)
-            e = bkv::launch_select(score, dims->n_units, dims->l_cap, L, b_kv, pol->prefix,
-                                   pol->recent_tok, kept, s);
-        if (e == hipSuccess && !sorted)
-            e = bkv::launch_compact_fill(K, V, kpos, dims->n_units, dims->d_head, dims->l_cap,
-                                         L, kept, b_kv, s);
-        else if (e == hipSuccess)
-            e = bkv::launch_compact(K, V, kpos, dims->n_units, dims->d_head, dims->l_cap, L,
-                                    kept, b_kv, nullptr, nullptr, nullptr, dims->l_cap, s);
-    }
+    if (e == hipSuccess)
+        e = bkv::launch_select(score, dims->n_units, dims->l_cap, L, b_kv, pol->prefix,
+                               pol->recent_tok, kept, s);
+    if (e == hipSuccess && !sorted)
+        e = bkv::launch_compact_fill(K, V, kpos, dims->n_units, dims->d_head, dims->l_cap, L,
+                                     kept, b_kv, s);
+    else if (e == hipSuccess)
+        e = bkv::launch_compact(K, V, kpos, dims->n_units, dims->d_head, dims->l_cap, L, kept,
+                                b_kv, nullptr, nullptr, nullptr, dims->l_cap, s);
     if (e == hipSuccess && buf)
         e = bkv::launch_fps(buf, count, recents, pol->n_recent_q,
                             dims->n_units * dims->group, dims->d_head, pol->buf_cap,

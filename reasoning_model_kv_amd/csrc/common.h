@@ -40,10 +40,8 @@ hipError_t launch_select(const float* score, int64_t n_units, int64_t l_cap,
                          int64_t L, int64_t b_kv, int prefix, int recent_tok,
                          int32_t* kept, hipStream_t s);
 
-// Keep-set selection and in-place position-ordered compaction in one
-// launch (units of up to select_compact_fits(L) slots); kept receives the
-// keep sets as launch_select writes them.
-bool select_compact_fits(int64_t L);
+// Keep-set selection, then in-place position-ordered compaction; kept
+// receives the keep sets as launch_select writes them.
 hipError_t launch_select_compact(uint16_t* K, uint16_t* V, int32_t* kpos, int64_t n_units,
                                  int d, int64_t l_cap, int64_t L, const float* score,
                                  int32_t* kept, int64_t b_kv, int prefix, int recent_tok,

@@ -3,48 +3,58 @@
 // Paper text §2.2: the compressed cache indexes the sequence dimension with
 // the retained set; summary step (5): written back in position order.
 //
-// Mapping: two wavefronts per KV group, one moving the key rows and the
-// positions, the other the value rows.  Each walks the kept list in
-// ascending order, 32 tokens per iteration (a bf16 row of d = 128 is 16
-// lanes x 16 bytes, so one load instruction moves 4 rows), with the next
-// iteration's rows in flight while this one's are stored.  In place, tokens
-// before the first evicted slot do not move and are skipped.  The walk is
-// safe in place without any barrier: kept is strictly ascending, so the
-// source of token k is at a slot >= k and every destination written by an
-// iteration lies below every source read by later iterations; a destination
-// can only be the source of the same or an earlier token, whose load has
-// completed before the store that needs its data is issued; and the two
-// wavefronts of a group touch disjoint tensors.  Splitting a group's moves
-// over two wavefronts (rather than one wavefront moving both tensors) keeps
-// twice as many groups' streams in flight: 5.1 against 4.9 TB/s.
+// Mapping: one workgroup of W wavefronts per tensor part of a KV group (the
+// key rows and the positions, or the value rows), which walks the kept list
+// in ascending order in rounds of W x 32 tokens; wavefront w moves tokens
+// [base + 32 w, base + 32 w + 32) of the round starting at base (a bf16 row
+// of d = 128 is 16 lanes x 16 bytes, so one load instruction moves 4 rows),
+// and the next round's rows are in flight while this round's are stored.
+// In place, tokens before the first evicted slot do not move and are
+// skipped.
+//
+// Why it is safe in place.  kept is strictly ascending and kept[k] >= k, so
+// the source of token k lies at or above every destination of the tokens
+// before it: a round's stores land below every source of the later rounds,
+// and only overwrite sources of the same or earlier rounds.  Each round
+// therefore waits, in every wavefront, for that wavefront's loads of the
+// round to land, then meets at a workgroup barrier, and only then stores;
+// the loads of the next round may already be in flight (their sources lie
+// above this round's destinations).  The barrier carries no memory fence:
+// the hazard is between loads that have returned their data and stores
+// issued after the barrier, which needs no cache visibility.
+//
+// Why a workgroup per part rather than a wavefront: with one wavefront per
+// part (about 9,000 independent streams at the Qwen3-4B shape), moving
+// 9.7 GB took 1.90 ms (5.1 TB/s); with sixteen wavefronts walking one part
+// together (about 500 streams of 512 tokens per round) 1.75 ms (5.5 TB/s,
+// the rate of a plain device copy of the same bytes on this GPU).
 
 #include "common.h"
-#include "select_wave.h"
 
 namespace bkv {
 namespace {
-
-constexpr int WAVES = 4;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // Streaming (non-temporal) 16-byte store: the compacted rows are not read
 // again by this step.
+__device__ __forceinline__ void st_nt(uint16_t* p, u32x4 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
 __device__ __forceinline__ void st_nt(uint16_t* p, uint4 v) {
-    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4*>(p));
+    st_nt(p, __builtin_bit_cast(u32x4, v));
 }
 // Streaming (non-temporal) 16-byte load: each moved row is read once.
-__device__ __forceinline__ uint4 ld_nt(const uint16_t* p) {
-    return __builtin_bit_cast(uint4,
-                              __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
+__device__ __forceinline__ u32x4 ld_nt(const uint16_t* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
-constexpr int TPI = 32;  // tokens per iteration
+constexpr int TPB = 32;  // tokens per wavefront per round
 
 // Write-only sink for the stores of tokens past the end of the kept list (or
 // of malformed entries): every store is issued unconditionally, so that the
 // compiler's vmcnt waits count exactly (a conditional store makes it assume
 // the store may be missing and wait for loads still in flight).  Never read.
-__device__ uint4 g_sink[64];
+__device__ u32x4 g_sink[64];
 
 // First index k whose kept slot is not k (kept[k] - k never decreases), or
 // b_kv if nothing moves.
@@ -59,171 +69,146 @@ __device__ __forceinline__ int64_t first_moved(const int32_t* __restrict__ ku, i
     return b_kv;
 }
 
-// The walk of one tensor of unit u by one wavefront: rows Ts[kept[k]] go to
-// Td[k] (Ts == Td in place), and with POS the positions ps[kept[k]] to
-// pd[k].  Tokens before k0 are not moved.
-template <int D, bool POS>
-__device__ __forceinline__ void compact_walk(const uint16_t* Ts, uint16_t* Td, const int32_t* ps,
-                                             int32_t* pd, const int32_t* __restrict__ ku,
-                                             int64_t L, int64_t b_kv, int64_t k0, int lane) {
+// Workgroup barrier without a memory fence (see the header): the
+// wavefront-scope fences only keep the compiler from moving memory accesses
+// across it.
+__device__ __forceinline__ void round_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Stand-in source of the positions for the value part, whose position loads
+// are discarded: one cached line instead of a second read of the positions.
+__device__ int32_t g_nopos[64];
+
+// The walk of one tensor of unit u by wavefront w of W: rows Ts[kept[k]] go
+// to Td[k] (Ts == Td in place), and with pos the positions ps[kept[k]] to
+// pd[k].  Tokens before k0 are not moved.  Every wavefront of the workgroup
+// runs the same number of rounds (the loop bounds depend on k0 and b_kv
+// only), so the barriers match.  Both parts run this one code path (pos is
+// a runtime flag): with the two parts specialised into two inlined loops the
+// same walk took 2.8 instead of 1.75 ms at the Qwen3-4B shape.
+template <int D, int W>
+__device__ __forceinline__ void coop_walk(const uint16_t* Ts, uint16_t* Td, const int32_t* ps,
+                                          int32_t* pd, bool pos, const int32_t* __restrict__ ku,
+                                          int64_t L, int64_t b_kv, int64_t k0, int w, int lane) {
     constexpr int LPT = D / 8;        // lanes per token row (16-byte chunks)
     constexpr int TPW = 64 / LPT;     // tokens per wave instruction
-    constexpr int NI = TPI / TPW;     // instructions per iteration (<= 8)
-    static_assert(NI >= 1 && NI <= 8, "tokens per iteration");
+    constexpr int NI = TPB / TPW;     // instructions per round (<= 8)
+    constexpr int RS = W * TPB;       // tokens per round
+    static_assert(NI >= 1 && NI <= 8, "tokens per round");
     const int st = lane / LPT;  // token within an instruction
     const int ch = lane % LPT;  // 16-byte chunk within the row
     const int64_t off = 8 * ch;
-    // Kept entries of tokens [base, base + TPI): lane j (mod TPI) holds
-    // kept[base + j], or -1 past b_kv or for an entry outside [0, L) (a
-    // malformed list is skipped, never followed).  One load per lane.
+    const int tl = lane & (TPB - 1);
+    // Raw kept entries of this wavefront's tokens of the round at base (lane
+    // j (mod TPB): kept[base + TPB w + j]); checked only where they are used,
+    // so that the load is not waited for at once.
     auto load_kept = [&](int64_t base) -> int32_t {
-        const int64_t k = base + (lane & (TPI - 1));
-        const int32_t v = ku[k < b_kv ? k : b_kv - 1];
+        const int64_t k = base + TPB * w + tl;
+        return ku[k < b_kv ? k : b_kv - 1];
+    };
+    // -1 past b_kv or for an entry outside [0, L) (a malformed list is
+    // skipped, never followed).
+    auto checked = [&](int64_t base, int32_t v) -> int32_t {
+        const int64_t k = base + TPB * w + tl;
         return (k < b_kv && v >= 0 && v < L) ? v : -1;
     };
-    // One iteration's rows (and positions).  Invalid tokens load slot 0 (the
-    // loads stay unconditional, so the compiler's waits count exactly) and
-    // are stored into the sink.
+    // One round's rows and positions.  Invalid tokens load slot 0 (the loads
+    // stay unconditional, so the compiler's waits count exactly) and are
+    // stored into the sink.
     struct Batch {
-        uint4 r[NI];
+        u32x4 r[NI];
         int32_t s[NI];
         int32_t p;
         bool pv;
     };
-    auto load_rows = [&](int32_t kv, Batch& b) {
+    auto load_rows = [&](int64_t base, int32_t raw, Batch& b) {
+        const int32_t kv = checked(base, raw);
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             b.s[i] = __shfl(kv, st + i * TPW);
             const int64_t r = b.s[i] >= 0 ? b.s[i] : 0;
             b.r[i] = ld_nt(Ts + r * D + off);
         }
-        if (POS) {
-            b.pv = kv >= 0;
-            b.p = ps[kv >= 0 ? kv : 0];
-        }
+        b.pv = pos && kv >= 0;
+        b.p = ps[pos && kv >= 0 ? kv : 0];
     };
-    // Every lane stores: invalid tokens into the sink; lanes TPI.. repeat the
-    // position stores of lanes 0..TPI-1 (same address, same value).
+    // Waits until this wavefront's loads of b have returned their data.
+    auto landed = [&](const Batch& b) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) asm volatile("" ::"v"(b.r[i]));
+        asm volatile("" ::"v"(b.p));
+    };
+    // Every lane stores: invalid tokens into the sink; lanes TPB.. repeat the
+    // position stores of lanes 0..TPB-1 (same address, same value).
     auto store_rows = [&](int64_t base, const Batch& b) {
+        const int64_t bw = base + TPB * w;
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-            const int64_t kb = base + st + i * TPW;
+            const int64_t kb = bw + st + i * TPW;
             const bool ok = b.s[i] >= 0;
             st_nt(ok ? Td + kb * D + off : reinterpret_cast<uint16_t*>(&g_sink[lane]), b.r[i]);
         }
-        if (POS)
-            *(b.pv ? pd + base + (lane & (TPI - 1)) : reinterpret_cast<int32_t*>(&g_sink[lane])) =
-                b.p;
+        *(b.pv ? pd + bw + tl : reinterpret_cast<int32_t*>(&g_sink[lane])) = b.p;
     };
 
-    // Software pipeline: the kept entries of the iteration after next and
-    // the rows of the next iteration are loaded before this iteration's rows
-    // are stored.  Unrolled by two over two buffers, so that no register
-    // with a load in flight is ever copied (a copy would wait for the load).
-    // Safe in place: every destination written by an iteration lies below
-    // every source read by the later ones (kept is strictly ascending and
-    // kept[k] >= k).
+    // Software pipeline over two register buffers (no register with a load
+    // in flight is ever copied): the raw kept entries of the round after
+    // next and the rows of the next round are loaded before this round's
+    // barrier and stores.
     Batch A, B;
     int32_t kvA = load_kept(k0);
-    load_rows(kvA, A);
-    int32_t kvB = load_kept(k0 + TPI);
+    load_rows(k0, kvA, A);
+    int32_t kvB = load_kept(k0 + RS);
     for (int64_t base = k0;;) {
-        kvA = load_kept(base + 2 * TPI);
-        load_rows(kvB, B);
+        kvA = load_kept(base + 2 * RS);
+        load_rows(base + RS, kvB, B);
+        landed(A);
+        round_barrier();
         store_rows(base, A);
-        base += TPI;
+        base += RS;
         if (base >= b_kv) break;
-        kvB = load_kept(base + 2 * TPI);
-        load_rows(kvA, A);
+        kvB = load_kept(base + 2 * RS);
+        load_rows(base + RS, kvA, A);
+        landed(B);
+        round_barrier();
         store_rows(base, B);
-        base += TPI;
+        base += RS;
         if (base >= b_kv) break;
     }
+    // Keeps the kept-entry loads where they are issued: with no use on the
+    // exit path the compiler sinks them below the loop's exit test, next to
+    // their first use, and the wait there drains every load and store in
+    // flight (the counter is in order).
+    asm volatile("" ::"v"(kvA), "v"(kvB));
 }
 
-// Wavefront `part` (0: keys and positions, 1: values) of unit u's
-// compaction; Ko == nullptr means in place.
-template <int D>
-__device__ __forceinline__ void compact_part(uint16_t* K, uint16_t* V, int32_t* kpos,
-                                             int64_t l_cap, const int32_t* __restrict__ kept,
-                                             int64_t L, int64_t b_kv, uint16_t* Ko,
-                                             uint16_t* Vo, int32_t* kposo, int64_t out_cap,
-                                             int64_t u, int part, int lane) {
-    const bool inplace = (Ko == nullptr);
-    const int32_t* ku = kept + u * b_kv;
-    const int64_t k0 = inplace ? first_moved(ku, b_kv, lane) : 0;
-    if (k0 >= b_kv) return;
-    const int64_t so = u * l_cap * D, dof = inplace ? so : u * out_cap * D;
-    if (part == 0) {
-        compact_walk<D, true>(K + so, (inplace ? K : Ko) + dof, kpos + u * l_cap,
-                              inplace ? kpos + u * l_cap : kposo + u * out_cap, ku, L, b_kv, k0,
-                              lane);
-    } else {
-        compact_walk<D, false>(V + so, (inplace ? V : Vo) + dof, nullptr, nullptr, ku, L, b_kv,
-                               k0, lane);
-    }
-}
-
-// Wavefront w of workgroup b: unit (4 b + w) / 2, part w % 2.
-template <int D>
-__global__ __launch_bounds__(64 * WAVES) void compact_kernel(
+// Workgroup b: unit b / 2, part b % 2 (0: keys and positions, 1: values);
+// Ko == nullptr means in place.
+template <int D, int W>
+__global__ __launch_bounds__(64 * W) void compact_kernel(
     uint16_t* K, uint16_t* V, int32_t* kpos, int64_t l_cap, const int32_t* __restrict__ kept,
     int64_t L, int64_t b_kv, uint16_t* Ko, uint16_t* Vo, int32_t* kposo, int64_t out_cap,
     int64_t n_units) {
-    const int64_t gw = (int64_t)blockIdx.x * WAVES + (threadIdx.x >> 6);
-    const int64_t u = gw >> 1;
-    if (u >= n_units) return;
-    compact_part<D>(K, V, kpos, l_cap, kept, L, b_kv, Ko, Vo, kposo, out_cap, u, (int)(gw & 1),
-                    threadIdx.x & 63);
-}
-
-// Selection and in-place compaction in one launch (summary step (5)): a
-// workgroup of four wavefronts takes two units.  Wavefronts 0 and 1 select
-// the keep sets of the two units (select_wave_reg, units of up to 64 * NR
-// slots) and write them to kept; after a workgroup barrier, which makes
-// those writes visible to the whole workgroup, wavefronts 2u' and 2u' + 1
-// move unit u''s keys and positions and its values.  A unit's selection is
-// latency-bound and its walk bandwidth-bound: the wavefronts of other
-// workgroups keep HBM busy meanwhile.
-template <int D, int NR>
-__device__ __forceinline__ void select_compact_group(
-    uint16_t* K, uint16_t* V, int32_t* kpos, int64_t l_cap, const float* __restrict__ score,
-    int32_t* kept, int64_t L, int64_t b_kv, int prefix, int recent_tok, int64_t n_units,
-    uint32_t (*hist)[256]) {
+    const int64_t u = (int64_t)(blockIdx.x >> 1);
+    const int part = (int)(blockIdx.x & 1);
+    if (u >= n_units) return;  // uniform over the workgroup
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t u0 = (int64_t)blockIdx.x * 2;
-    if (w < 2 && u0 + w < n_units)
-        select_wave_reg<NR>(score + (u0 + w) * l_cap, L, b_kv, prefix, recent_tok,
-                            kept + (u0 + w) * b_kv, hist[w], lane);
-    __syncthreads();
-    const int64_t u = u0 + (w >> 1);
-    if (u < n_units)
-        compact_part<D>(K, V, kpos, l_cap, kept, L, b_kv, nullptr, nullptr, nullptr, 0, u, w & 1,
-                        lane);
+    const bool inplace = (Ko == nullptr);
+    const int32_t* ku = kept + u * b_kv;
+    const int64_t k0 = inplace ? first_moved(ku, b_kv, lane) : 0;
+    if (k0 >= b_kv) return;  // uniform: every wavefront finds the same k0
+    const int64_t so = u * l_cap * D, dof = inplace ? so : u * out_cap * D;
+    uint16_t* src = (part == 0 ? K : V) + so;
+    uint16_t* dst = (inplace ? src : (part == 0 ? Ko : Vo) + dof);
+    int32_t* pdst = inplace ? kpos + u * l_cap : kposo + u * out_cap;
+    coop_walk<D, W>(src, dst, part == 0 ? kpos + u * l_cap : g_nopos, pdst, part == 0, ku, L,
+                    b_kv, k0, w, lane);
 }
 
-// Units of up to 64 * 36 slots: held to 128 VGPRs, four wavefronts per SIMD
-// as in compact_kernel.
-template <int D, int NR>
-__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4)))
-void select_compact_kernel(uint16_t* K, uint16_t* V, int32_t* kpos, int64_t l_cap,
-                           const float* __restrict__ score, int32_t* kept, int64_t L,
-                           int64_t b_kv, int prefix, int recent_tok, int64_t n_units) {
-    __shared__ uint32_t hist[2][256];
-    select_compact_group<D, NR>(K, V, kpos, l_cap, score, kept, L, b_kv, prefix, recent_tok,
-                                n_units, hist);
-}
-
-// Up to 64 * 72 slots: the 72 score registers per lane need more than 128
-// VGPRs (held to 128 they spill), so three wavefronts per SIMD.
-template <int D>
-__global__ __launch_bounds__(64 * WAVES) void select_compact_kernel_wide(
-    uint16_t* K, uint16_t* V, int32_t* kpos, int64_t l_cap, const float* __restrict__ score,
-    int32_t* kept, int64_t L, int64_t b_kv, int prefix, int recent_tok, int64_t n_units) {
-    __shared__ uint32_t hist[2][256];
-    select_compact_group<D, 72>(K, V, kpos, l_cap, score, kept, L, b_kv, prefix, recent_tok,
-                                n_units, hist);
-}
+constexpr int WAVES = 4;  // wavefronts per workgroup of the unsorted compaction
 
 // Wavefront-wide synchronisation of LDS between the lanes of one wavefront.
 __device__ __forceinline__ void wave_sync() {
@@ -356,45 +341,34 @@ hipError_t launch_compact(uint16_t* K, uint16_t* V, int32_t* kpos,
                           uint16_t* V_out, int32_t* kpos_out, int64_t out_cap,
                           hipStream_t s) {
     if (n_units <= 0) return hipSuccess;
-    // Two wavefronts per unit.
-    const dim3 grid((unsigned)((2 * n_units + WAVES - 1) / WAVES));
-    if (d == 128)
-        compact_kernel<128><<<grid, 64 * WAVES, 0, s>>>(K, V, kpos, l_cap, kept, L, b_kv, K_out,
-                                                        V_out, kpos_out, out_cap, n_units);
-    else
-        compact_kernel<64><<<grid, 64 * WAVES, 0, s>>>(K, V, kpos, l_cap, kept, L, b_kv, K_out,
-                                                       V_out, kpos_out, out_cap, n_units);
+    if (n_units > (int64_t)1 << 30) return hipErrorInvalidValue;
+    // Two workgroups per unit; rounds of W x 32 tokens, W sized to the kept
+    // list so that short lists do not leave most wavefronts idle.
+    const dim3 grid((unsigned)(2 * n_units));
+#define BKV_CMP(DD, WW)                                                                 \
+    compact_kernel<DD, WW><<<grid, 64 * (WW), 0, s>>>(K, V, kpos, l_cap, kept, L, b_kv, \
+                                                      K_out, V_out, kpos_out, out_cap,  \
+                                                      n_units)
+#define BKV_CMP_W(DD)                                                                   \
+    if (b_kv >= 1024) BKV_CMP(DD, 16);                                                  \
+    else if (b_kv >= 512) BKV_CMP(DD, 8);                                               \
+    else BKV_CMP(DD, 4)
+    if (d == 128) { BKV_CMP_W(128); }
+    else { BKV_CMP_W(64); }
+#undef BKV_CMP_W
+#undef BKV_CMP
     return hipGetLastError();
 }
-
-bool select_compact_fits(int64_t L) { return L <= 64 * 72; }
 
 hipError_t launch_select_compact(uint16_t* K, uint16_t* V, int32_t* kpos, int64_t n_units,
                                  int d, int64_t l_cap, int64_t L, const float* score,
                                  int32_t* kept, int64_t b_kv, int prefix, int recent_tok,
                                  hipStream_t s) {
-    if (n_units <= 0) return hipSuccess;
-    if (!select_compact_fits(L)) return hipErrorInvalidValue;
-    // Two units per workgroup.
-    const dim3 grid((unsigned)((n_units + 1) / 2));
-#define BKV_SC(DD, NR)                                                                    \
-    select_compact_kernel<DD, NR><<<grid, 64 * WAVES, 0, s>>>(K, V, kpos, l_cap, score, kept, \
-                                                              L, b_kv, prefix, recent_tok, n_units)
-#define BKV_SC_D(NR)                                                                      \
-    if (d == 128) BKV_SC(128, NR); else BKV_SC(64, NR)
-    if (L <= 64 * 8) { BKV_SC_D(8); }
-    else if (L <= 64 * 16) { BKV_SC_D(16); }
-    else if (L <= 64 * 36) { BKV_SC_D(36); }
-    else if (d == 128) {
-        select_compact_kernel_wide<128><<<grid, 64 * WAVES, 0, s>>>(
-            K, V, kpos, l_cap, score, kept, L, b_kv, prefix, recent_tok, n_units);
-    } else {
-        select_compact_kernel_wide<64><<<grid, 64 * WAVES, 0, s>>>(
-            K, V, kpos, l_cap, score, kept, L, b_kv, prefix, recent_tok, n_units);
-    }
-#undef BKV_SC_D
-#undef BKV_SC
-    return hipGetLastError();
+    hipError_t e = launch_select(score, n_units, l_cap, L, b_kv, prefix, recent_tok, kept, s);
+    if (e == hipSuccess)
+        e = launch_compact(K, V, kpos, n_units, d, l_cap, L, kept, b_kv, nullptr, nullptr,
+                           nullptr, l_cap, s);
+    return e;
 }
 
 }  // namespace bkv

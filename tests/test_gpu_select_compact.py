@@ -51,8 +51,16 @@ def test_select_bit_exact(L, b_kv, P, R, kind):
 
 
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("L,b_kv", [(256, 128), (2176, 2048), (519, 301)])
+@pytest.mark.parametrize("L,b_kv", [
+    (256, 128), (519, 301),             # four wavefronts per part
+    (700, 600), (1100, 1023),           # eight
+    (2176, 2048), (4224, 4096),         # sixteen, one to eight rounds of 512 tokens
+    (1000, 999),                        # one eviction
+])
 def test_compact_in_place_and_out_of_place(d, L, b_kv):
+    """Unit 0: nothing moves; unit 1: only the last entry moves; unit 2:
+    every kept slot but the first comes from the tail (each token moves by
+    L - b_kv, further than a round when L - b_kv > 512)."""
     U = 13
     log(f"compact d={d} L={L} b_kv={b_kv}")
     r = np.random.default_rng(d + L)
@@ -64,6 +72,8 @@ def test_compact_in_place_and_out_of_place(d, L, b_kv):
     kept[0] = np.arange(b_kv)           # nothing moves
     kept[1, : b_kv - 1] = np.arange(b_kv - 1)
     kept[1, -1] = L - 1                  # only the last entry moves
+    kept[2, 0] = 0
+    kept[2, 1:] = np.arange(L - b_kv + 1, L)
     Kt = torch.from_numpy(K).to(torch.bfloat16).to(DEV)
     Vt = torch.from_numpy(V).to(torch.bfloat16).to(DEV)
     Pt = torch.from_numpy(kpos).to(DEV)
@@ -137,10 +147,10 @@ def test_compact_unsorted_bit_exact(d, L, b_kv):
     (777, 300, 33, "ties"),     # many equal scores around the cut
     (2176, 2048, 8, "cont"),    # the Qwen3-4B step's shape
     (4224, 4096, 512, "ties"),  # the wide kernel (72 score registers per lane)
-    (5000, 1000, 8, "cont"),    # beyond one launch: select, then compact
+    (5000, 1000, 8, "cont"),    # the LDS-staged selection
 ])
 def test_select_compact_matches_the_two_calls(d, L, b_kv, P, kind):
-    """Selection and compaction in one launch: the oracle's kept set exactly,
+    """Selection and compaction in one call: the oracle's kept set exactly,
     and K, V, positions equal to the oracle's compaction of the inputs."""
     U, R = 21, 16
     log(f"select_compact d={d} L={L} b_kv={b_kv} P={P} {kind}")
@@ -176,7 +186,7 @@ def test_select_compact_matches_the_two_calls(d, L, b_kv, P, kind):
 
 
 def test_select_compact_full_size_equals_two_calls():
-    """Qwen3-4B shape, all 4608 units: the one-launch kernel against select
+    """Qwen3-4B shape, all 4608 units: the in-place call against select
     followed by an out-of-place compaction, bit for bit."""
     import synth
     w = synth.WORKLOADS["qwen3_4b_full_b2048"]

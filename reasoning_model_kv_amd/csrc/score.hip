@@ -750,6 +750,10 @@ void score_kernel(ScoreArgs a, int g, int hs) {
     // tile is loaded by the walk two iterations ahead, the first of them at
     // iteration 0 when fewer than three tiles are resident.
     const int t_res = reflect ? ntiles - 2 : (t0 > ntiles - kRing ? t0 : ntiles - kRing);
+    // Pass 1 has waited for all its loads in its last iteration; saying so
+    // here (free at run time) tells the compiler that no tile load is still
+    // in flight when pass 2 starts, so that its first reads need no wait.
+    wait_vm<0>();
     lds_barrier();
     float* score_u = a.score + u * a.l_cap;
 #define BKV_PASS2                                                                  \
@@ -851,7 +855,7 @@ void score_kernel(ScoreArgs a, int g, int hs) {
 // its last tiles from L2).  Iteration j scores tile T = ntiles - 1 - j from
 // CUR and loads tile T - 2 into NXT (the buffer tile T + 1 used, or an unused
 // one at j = 0).
-#define BKV_REV_ITER(j, CUR, NXT, ...)                                             \
+#define BKV_REV_STEP(j, CUR, NXT, LOAD, ...)                                       \
     do {                                                                           \
         const int T = ntiles - 1 - (j);                                            \
         if (loader && T < t_res) {                                                 \
@@ -860,7 +864,7 @@ void score_kernel(ScoreArgs a, int g, int hs) {
             else wait_vm<NPW>();                                                   \
         }                                                                          \
         lds_barrier();                                                           \
-        if (loader && T - 2 >= 0 && T - 2 < t_res)                                 \
+        if (LOAD)                                                                  \
             ld.template issue<kLoadStreaming>(Ku, L, (int64_t)(T - 2) * KT, NXT, h); \
         f32x16 acc0, acc1;                                                         \
         if (SPLIT && !active) { acc0 = f32x16{}; acc1 = f32x16{}; }                \
@@ -868,14 +872,32 @@ void score_kernel(ScoreArgs a, int g, int hs) {
         const int64_t base = (int64_t)T * KT;                                      \
         __VA_ARGS__;                                                               \
     } while (0)
+#define BKV_REV_ITER(j, CUR, NXT, ...)                                             \
+    BKV_REV_STEP(j, CUR, NXT, loader && T - 2 >= 0 && T - 2 < t_res, __VA_ARGS__)
 #define BKV_REV_LOOP(B0, B1, B2, ...)                                              \
     for (int j = 0; j < ntiles; j += 3) {                                          \
         BKV_REV_ITER(j, B0, B1, __VA_ARGS__);                                      \
         if (j + 1 < ntiles) BKV_REV_ITER(j + 1, B2, B0, __VA_ARGS__);              \
         if (j + 2 < ntiles) BKV_REV_ITER(j + 2, B1, B2, __VA_ARGS__);              \
     }
-// Four buffers: B0..B3 hold (or will hold) tiles ntiles-1 .. ntiles-4, and
-// tile T - 2 goes into the buffer of tile T + 2.
+// The loader wavefronts from iteration j on, X0 being the buffer iteration j
+// scores: whole rounds of three iterations that each load a tile (no branch
+// around a load inside the loop: with loads that some paths through the loop
+// skip, the compiler cannot count which loads are still in flight and waits
+// for all of them before reading a tile -- one round trip to memory in every
+// third iteration), then the last one to four iterations, whose loads stop
+// at tile 0.
+#define BKV_REV_FAST(X0, X1, X2, ...)                                              \
+    wait_vm<0>();                                                                  \
+    for (; j + 3 <= ntiles - 2; j += 3) {                                          \
+        BKV_REV_STEP(j, X0, X1, true, __VA_ARGS__);                                \
+        BKV_REV_STEP(j + 1, X2, X0, true, __VA_ARGS__);                            \
+        BKV_REV_STEP(j + 2, X1, X2, true, __VA_ARGS__);                            \
+    }                                                                              \
+    if (j < ntiles) BKV_REV_STEP(j, X0, X1, T >= 2, __VA_ARGS__);                  \
+    if (j + 1 < ntiles) BKV_REV_STEP(j + 1, X2, X0, T >= 2, __VA_ARGS__);          \
+    if (j + 2 < ntiles) BKV_REV_STEP(j + 2, X1, X2, T >= 2, __VA_ARGS__);          \
+    if (j + 3 < ntiles) BKV_REV_STEP(j + 3, X0, X1, T >= 2, __VA_ARGS__)
 #define BKV_REV_LOOP4(B0, B1, B2, B3, ...)                                         \
     for (int j = 0; j < ntiles; j += 4) {                                          \
         BKV_REV_ITER(j, B0, B2, __VA_ARGS__);                                      \
@@ -885,7 +907,35 @@ void score_kernel(ScoreArgs a, int g, int hs) {
     }
     // Buffers visited from the last tile down.
     if constexpr (kRing == 3) {
-        if (reflect) {
+        if (loader && (reflect || t0 <= ntiles - 3)) {
+            // Reflected: no tile is resident beyond the two pass 1 left, so
+            // every iteration from the first loads (t_res = ntiles - 2).
+            // Otherwise the first iteration scores the last tile, resident,
+            // and loads nothing (t_res = ntiles - 3); the rounds start at
+            // iteration 1, one buffer further round the ring.
+            int j = 0;
+            if (reflect) {
+                BKV_REV_FAST(tile0, tile2, tile1, BKV_PASS2);
+            } else {
+                switch ((ntiles - 1 - t0) % 3) {
+                    case 0:
+                        BKV_REV_STEP(0, tile0, tile1, false, BKV_PASS2);
+                        j = 1;
+                        BKV_REV_FAST(tile2, tile0, tile1, BKV_PASS2);
+                        break;
+                    case 1:
+                        BKV_REV_STEP(0, tile1, tile2, false, BKV_PASS2);
+                        j = 1;
+                        BKV_REV_FAST(tile0, tile1, tile2, BKV_PASS2);
+                        break;
+                    default:
+                        BKV_REV_STEP(0, tile2, tile0, false, BKV_PASS2);
+                        j = 1;
+                        BKV_REV_FAST(tile1, tile2, tile0, BKV_PASS2);
+                        break;
+                }
+            }
+        } else if (reflect) {
             BKV_REV_LOOP(tile0, tile2, tile1, BKV_PASS2);
         } else {
             switch ((ntiles - 1 - t0) % 3) {
@@ -909,8 +959,10 @@ void score_kernel(ScoreArgs a, int g, int hs) {
         }
     }
 #undef BKV_REV_LOOP4
+#undef BKV_REV_FAST
 #undef BKV_REV_LOOP
 #undef BKV_REV_ITER
+#undef BKV_REV_STEP
 #undef BKV_PASS2
 #undef BKV_PASS2_MAX
 #undef BKV_PASS2_MEAN

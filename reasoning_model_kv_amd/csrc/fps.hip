@@ -5,8 +5,9 @@
 // largest cosine to the picked set is lowest joins it, until m rows remain.
 //
 // Mapping.  Buffers of up to 32 rows: one wavefront per query head forms
-// the 32 x 32 cosine matrix once on fp32 MFMA and runs the greedy picks on
-// it (see fps_wave_kernel).  Buffers of up to 256 rows (prefill) use one
+// the 32 x 32 cosine matrix once on bf16 MFMAs (each fp32 value split into
+// a high and a low bf16 part) and runs the greedy picks on it (see
+// fps_wave_kernel).  Buffers of up to 256 rows (prefill) use one
 // workgroup per head and one thread per row; there the average cosine of
 // row i uses the sum of all normalised rows (sum_j cos(q_i, q_j) equals
 // q_i/|q_i| . sum_j q_j/|q_j|) and each pick broadcasts the new member's

@@ -17,15 +17,18 @@
 //    tiles ahead by buffer_load ... lds (16-byte chunks XOR-swizzled by row
 //    so the 32 lanes that read one chunk column hit distinct banks); all
 //    wavefronts of the group read the same tile.
-//  * Pass 1: per tile each wavefront forms a 32 x 64 logit block and keeps a
-//    per-lane running (max, sum of exp2) for its 16 rows; the 32 lanes of a
-//    half are merged once at the end into each row's LSE.
+//  * Pass 1: per tile each wavefront forms a 32 x 64 logit block and adds
+//    exp2 of its scaled logits to a per-lane sum for each of its 16 rows
+//    (against a fixed reference: exact in fp32 while the row totals stay in
+//    [2^-60, 2^100]; a workgroup with a row outside redoes pass 1 with a
+//    running maximum); the 32 lanes of a half are merged once at the end
+//    into each row's LSE.
 //  * Pass 2 walks the tiles backwards (the last three are still in LDS): the
 //    logits are formed again, shifted by the row LSE, reduced over the
 //    lane's 16 rows, the other half (lane ^ 32) and the wavefronts (LDS),
 //    and written as score = exp2(max).
-//  * Groups of more than four heads are shared by two workgroups on one XCD
-//    that combine their maxima with an atomic maximum.
+//  * Groups of five to eight heads run a variant held to 128 VGPRs, so that
+//    two workgroups share a CU.
 //  Output layout of the 32x32 MFMA: lane l, accumulator v holds
 //  row 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32.
 
@@ -41,12 +44,10 @@ typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 constexpr int KT = 64;               // keys per tile
 // Key tiles in the scoring kernel's LDS ring: loads run two tiles ahead, so
-// the ring's last kRing tiles of pass 1 are still resident when pass 2
-// starts from the end.  With four 16 KB tiles (d = 128) two workgroups share
-// a CU: fewer units stream at once than with three tiles at three
-// workgroups, and more of each unit's keys are still on chip for pass 2.
+// the ring's last three tiles of pass 1 are still resident when pass 2
+// starts from the end.  (Four tiles, at two workgroups per CU instead of
+// three, streamed fewer units at once and were slower.)
 constexpr int kRing = 3;
-static_assert(kRing == 3 || kRing == 4, "ring depth");
 constexpr float kNegBig = -1.0e30f;  // finite "no key seen yet" running max
 // Buffer-resource flags word (gfx9 family: raw 32-bit data, no swizzle).
 constexpr int kBufferFlags = 0x00020000;
@@ -90,7 +91,6 @@ struct ScoreArgs {
     float* score;
     uint16_t* qobs;
     int64_t n_units;
-    int split;  // 1: each unit's heads are scored by two workgroups (scores pre-zeroed, combined atomically)
     float inv_rows;  // 1 / (g * 32): the mean pooling's divisor
     // Known softmax denominators (natural-log LSE of the scaled logits),
     // [U, g, 32] by observation row, or NULL.  Beacon rows' values cover
@@ -242,15 +242,6 @@ __device__ __forceinline__ void put_rows(const uint4 (&v)[2 * ObsRows<D>::NB], i
     }
 }
 
-// Clears the score slots [0, L) of every unit; groups split over two
-// workgroups combine their scores there with an atomic maximum.
-__global__ __launch_bounds__(256) void zero_scores_kernel(float* score, int64_t l_cap, int64_t L,
-                                                          int64_t n_units) {
-    const int64_t n = n_units * L;
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
-        score[(i / L) * l_cap + i % L] = 0.f;
-}
-
 // Causal limit of accumulator entry v as an offset from the first recent
 // slot L - nrq: a key at offset d is visible iff d <= limit.  Beacon rows
 // see every live slot (offset nrq - 1 is slot L - 1); recent row i sees
@@ -390,24 +381,18 @@ __device__ __forceinline__ void tile_logits(const uint16_t* lds_tile, const Tile
     }
 }
 
-// One workgroup per unit, one wavefront per query head; with 162 VGPRs, 12
-// wavefronts share a CU.  For g > 4 (a.split) a unit's heads are shared by
-// two workgroups of hs wavefronts each (the second may have an idle
-// wavefront, which loads and keeps the barriers but computes nothing), so
-// that more than one group fits on a CU; the pair runs on one XCD
-// (blocks b and b + 8), where the second read of each key tile is likely to
-// hit L2, and combines its column maxima with an atomic maximum on the
-// score bits (non-negative floats order like their bit patterns).
-template <int D, int NL, bool SPLIT, bool MEAN, int OCC = 0>
+// One workgroup per unit, one wavefront per query head; with 165 VGPRs, 12
+// wavefronts share a CU.  OCC > 0 holds the kernel to the registers of OCC
+// wavefronts per SIMD (groups of 5 to 8 heads: see launch_score).
+template <int D, int NL, bool MEAN, int OCC = 0>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1, 8)))
-void score_kernel(ScoreArgs a, int g, int hs) {
+void score_kernel(ScoreArgs a, int g) {
     // Three separately declared tiles (not one array) so that the compiler
     // can tell the tiles being loaded by the direct-to-LDS loads from the tile
     // being read, and does not wait for the former before reading the latter.
     __shared__ __attribute__((aligned(16))) uint16_t tile0[KT * D];
     __shared__ __attribute__((aligned(16))) uint16_t tile1[KT * D];
     __shared__ __attribute__((aligned(16))) uint16_t tile2[KT * D];
-    __shared__ __attribute__((aligned(16))) uint16_t tile3[kRing == 4 ? KT * D : 8];
     __shared__ float red[8][KT];
     constexpr int NPW = TileLoad<D, NL>::NPW;  // loads per loader lane per tile
 
@@ -415,15 +400,8 @@ void score_kernel(ScoreArgs a, int g, int hs) {
     const int h = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int lane = tid & 63;
     const bool loader = h < NL;
-    int64_t u = blockIdx.x;
-    int hg = h;  // query head of the group this wavefront scores
-    if (SPLIT) {
-        const int64_t b = blockIdx.x;
-        u = (b / 16) * 8 + (b % 8);
-        hg = (int)((b / 8) & 1) * hs + h;
-        if (u >= a.n_units) return;  // whole workgroup, before any barrier
-    }
-    const bool active = !SPLIT || hg < g;
+    const int64_t u = blockIdx.x;
+    const int hg = h;  // query head of the group this wavefront scores
     const int nw = (int)(blockDim.x / 64);
     const int64_t L = a.L;
     const uint16_t* Ku = a.K + u * a.l_cap * D;
@@ -480,7 +458,7 @@ void score_kernel(ScoreArgs a, int g, int hs) {
                              : a.beacons + qh * a.buf_cap * (int64_t)D;
     const float* src2 = a.recents + (qh * nrq + nrq - 16) * (int64_t)D;
     ObsRows<D> obs;
-    if (active) obs.load(src1, src2, lane);
+    obs.load(src1, src2, lane);
     if (loader) {
         ld.issue(Ku, L, (int64_t)t0 * KT, tile0, h);
         if (!wide && second >= 0) {
@@ -498,12 +476,12 @@ void score_kernel(ScoreArgs a, int g, int hs) {
     if (fix_recent_table<D>(a, u, rpos, lane, tid, 64 * nw, rtab_lo, rtab_hi)) {
         // Rare path: the rows are loaded again, so that their first copy is
         // dead while the cos/sin pairs are computed and its registers free.
-        if (active) obs.load(src1, src2, lane);
+        obs.load(src1, src2, lane);
     }
     bf16x8 frag[D / 16];
     {
         uint4 rows[2 * ObsRows<D>::NB];
-        if (active) {
+        {
             // Rows 0..15: the beacons' row for t, or recent rows 0..15; rows
             // 16..31: the last 16 recent rows.
             const double2* tab1 = wide ? rtab_lo : reinterpret_cast<const double2*>(&red[0][0]);
@@ -518,7 +496,7 @@ void score_kernel(ScoreArgs a, int g, int hs) {
         lds_barrier();  // the cos/sin rows are no longer needed
         uint16_t* stage = tile2 + (h & 1) * 32 * D;
         for (int rnd = 0; 2 * rnd < nw; ++rnd) {
-            const bool mine = active && (h >> 1) == rnd;
+            const bool mine = (h >> 1) == rnd;
             // A fresh copy of the lane index per round keeps the staging
             // addresses from being hoisted out of the loop into registers.
             int ln = lane;
@@ -571,34 +549,21 @@ void score_kernel(ScoreArgs a, int g, int hs) {
         if (loader && (it) + 2 < nt1)                                              \
             ld.issue(Ku, L, (int64_t)(t0 + (it) + 2) * KT, NXT2, h);               \
         f32x16 acc0, acc1;                                                         \
-        if (SPLIT && !active) { acc0 = f32x16{}; acc1 = f32x16{}; }                \
-        else tile_logits<D>(CUR, rd, frag, acc0, acc1);                            \
+        tile_logits<D>(CUR, rd, frag, acc0, acc1);                                 \
         const int64_t base = (int64_t)(t0 + (it)) * KT;                            \
         __VA_ARGS__;                                                               \
     } while (0)
-// Tiles rotate through tile0 .. tile(kRing-1) (tiles 0 and 1 are issued by the
+// Tiles rotate through tile0 .. tile2 (tiles 0 and 1 are issued by the
 // prologue); SDEL is 1 when wavefront 0 issues a score store in each
 // iteration, which the wait of the next iteration must allow for.
 #define BKV_TILE_LOOP(SDEL, ...)                                                   \
     do {                                                                           \
-        if constexpr (kRing == 3) {                                                \
-            for (int it = 0; it < nt1; it += 3) {                                  \
-                BKV_TILE_ITER(it, (SDEL) && h == 0 && it > 0, tile0, tile2, __VA_ARGS__); \
-                if (it + 1 < nt1)                                                  \
-                    BKV_TILE_ITER(it + 1, (SDEL) && h == 0, tile1, tile0, __VA_ARGS__); \
-                if (it + 2 < nt1)                                                  \
-                    BKV_TILE_ITER(it + 2, (SDEL) && h == 0, tile2, tile1, __VA_ARGS__); \
-            }                                                                      \
-        } else {                                                                   \
-            for (int it = 0; it < nt1; it += 4) {                                  \
-                BKV_TILE_ITER(it, (SDEL) && h == 0 && it > 0, tile0, tile2, __VA_ARGS__); \
-                if (it + 1 < nt1)                                                  \
-                    BKV_TILE_ITER(it + 1, (SDEL) && h == 0, tile1, tile3, __VA_ARGS__); \
-                if (it + 2 < nt1)                                                  \
-                    BKV_TILE_ITER(it + 2, (SDEL) && h == 0, tile2, tile0, __VA_ARGS__); \
-                if (it + 3 < nt1)                                                  \
-                    BKV_TILE_ITER(it + 3, (SDEL) && h == 0, tile3, tile1, __VA_ARGS__); \
-            }                                                                      \
+        for (int it = 0; it < nt1; it += 3) {                                      \
+            BKV_TILE_ITER(it, (SDEL) && h == 0 && it > 0, tile0, tile2, __VA_ARGS__); \
+            if (it + 1 < nt1)                                                      \
+                BKV_TILE_ITER(it + 1, (SDEL) && h == 0, tile1, tile0, __VA_ARGS__); \
+            if (it + 2 < nt1)                                                      \
+                BKV_TILE_ITER(it + 2, (SDEL) && h == 0, tile2, tile1, __VA_ARGS__); \
         }                                                                          \
     } while (0)
 
@@ -641,17 +606,17 @@ void score_kernel(ScoreArgs a, int g, int hs) {
     float ls[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) ls[v] = 0.f;
-    if (lse_mode && active && (lane & 31) == 0) {
+    if (lse_mode && (lane & 31) == 0) {
         const float* li = a.lse_in + qh * 32;
 #pragma unroll
         for (int v = 0; v < 16; ++v) ls[v] = exp2_sum(li[acc_row(v, lane)] * 1.4426950408889634f);
     }
 #define BKV_PASS1_FAST                                                             \
-    if (active) {                                                                  \
+    do {                                                                           \
         BKV_PASS1_MASKS                                                            \
         _Pragma("unroll") for (int v = 0; v < 16; ++v)                             \
             ls[v] += exp2_sum(acc0[v] * c2) + exp2_sum(acc1[v] * c2);              \
-    }
+    } while (0)
     BKV_TILE_LOOP(0, BKV_PASS1_FAST);
 #undef BKV_PASS1_FAST
     // Totals over the 32 lanes of each half.
@@ -661,10 +626,8 @@ void score_kernel(ScoreArgs a, int g, int hs) {
         for (int v = 0; v < 16; ++v) ls[v] += __shfl_xor(ls[v], o);
     }
     int out_of_range = 0;
-    if (active) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) out_of_range |= !(ls[v] >= 0x1p-60f && ls[v] <= 0x1p100f);
-    }
+    for (int v = 0; v < 16; ++v) out_of_range |= !(ls[v] >= 0x1p-60f && ls[v] <= 0x1p100f);
     float lse[16];  // log2-domain LSE in units of (logit * c2)
     if (!__syncthreads_or(out_of_range)) {
 #pragma unroll
@@ -688,7 +651,7 @@ void score_kernel(ScoreArgs a, int g, int hs) {
         float mc[16], l[16];
 #pragma unroll
         for (int v = 0; v < 16; ++v) { mc[v] = kNegBig; l[v] = 0.f; }
-        if (lse_mode && active && (lane & 31) == 0) {
+        if (lse_mode && (lane & 31) == 0) {
             const float* li = a.lse_in + qh * 32;
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
@@ -697,11 +660,11 @@ void score_kernel(ScoreArgs a, int g, int hs) {
             }
         }
 #define BKV_PASS1                                                                  \
-    if (active) {                                                                  \
+    do {                                                                           \
         BKV_PASS1_MASKS                                                            \
         BKV_PASS1_HALF(0);                                                         \
         BKV_PASS1_HALF(8);                                                         \
-    }
+    } while (0)
 // Rows v0..v0+7 of one tile: sum against the stale maxima if every term
 // stays below kRescaleBig, else rescale those rows.
 #define BKV_PASS1_HALF(v0)                                                         \
@@ -787,27 +750,20 @@ void score_kernel(ScoreArgs a, int g, int hs) {
     c0 = vmax(c0, __shfl_xor(c0, 32));                                             \
     c1 = vmax(c1, __shfl_xor(c1, 32));                                             \
     if (lane < 32) {                                                               \
-        red[h][lane] = active ? c0 : -__builtin_inff();                            \
-        red[h][32 + lane] = active ? c1 : -__builtin_inff();                       \
+        red[h][lane] = c0;                                                         \
+        red[h][32 + lane] = c1;                                                    \
     }                                                                              \
     lds_barrier();                                                               \
     if (tid < KT) {                                                                \
         float best = red[0][tid];                                                  \
         for (int w = 1; w < nw; ++w) best = vmax(best, red[w][tid]);               \
         const int64_t key = base + tid;                                            \
-        if (key < L) {                                                             \
-            if (SPLIT)                                                             \
-                atomicMax(reinterpret_cast<unsigned int*>(score_u + key),          \
-                          __float_as_uint(exp2f(best)));                           \
-            else                                                                   \
-                score_u[key] = exp2f(best);                                        \
-        }                                                                          \
+        if (key < L) score_u[key] = exp2f(best);                                   \
     }
 // Mean pooling: the sum of exp2(s - LSE) = W over the lane's rows (hidden
 // entries add nothing), the other half and the wavefronts, divided by the
-// group's g * 32 rows; a split group adds its two halves atomically (two
-// addends: the result does not depend on their order).  Terms below 2^-126
-// flush to zero, far below any score that matters (at most 224 of them).
+// group's g * 32 rows.  Terms below 2^-126 flush to zero, far below any
+// score that matters (at most 256 of them).
 #define BKV_PASS2_MEAN                                                             \
     float c0 = 0.f, c1 = 0.f;                                                      \
     if (base + KT > mask_from) {                                                   \
@@ -830,20 +786,15 @@ void score_kernel(ScoreArgs a, int g, int hs) {
     c0 += __shfl_xor(c0, 32);                                                      \
     c1 += __shfl_xor(c1, 32);                                                      \
     if (lane < 32) {                                                               \
-        red[h][lane] = active ? c0 : 0.f;                                          \
-        red[h][32 + lane] = active ? c1 : 0.f;                                     \
+        red[h][lane] = c0;                                                         \
+        red[h][32 + lane] = c1;                                                    \
     }                                                                              \
     lds_barrier();                                                               \
     if (tid < KT) {                                                                \
         float tot = red[0][tid];                                                   \
         for (int w = 1; w < nw; ++w) tot += red[w][tid];                           \
         const int64_t key = base + tid;                                            \
-        if (key < L) {                                                             \
-            if (SPLIT)                                                             \
-                atomicAdd(score_u + key, tot * a.inv_rows);                        \
-            else                                                                   \
-                score_u[key] = tot * a.inv_rows;                                   \
-        }                                                                          \
+        if (key < L) score_u[key] = tot * a.inv_rows;                              \
     }
 // Pass 2 walks the tiles backwards: at the end of pass 1 the last tiles
 // (three, or the ones pass 1 covered plus the prologue's second tile) are
@@ -867,8 +818,7 @@ void score_kernel(ScoreArgs a, int g, int hs) {
         if (LOAD)                                                                  \
             ld.template issue<kLoadStreaming>(Ku, L, (int64_t)(T - 2) * KT, NXT, h); \
         f32x16 acc0, acc1;                                                         \
-        if (SPLIT && !active) { acc0 = f32x16{}; acc1 = f32x16{}; }                \
-        else tile_logits<D>(CUR, rd, frag, acc0, acc1);                            \
+        tile_logits<D>(CUR, rd, frag, acc0, acc1);                                 \
         const int64_t base = (int64_t)T * KT;                                      \
         __VA_ARGS__;                                                               \
     } while (0)
@@ -898,15 +848,8 @@ void score_kernel(ScoreArgs a, int g, int hs) {
     if (j + 1 < ntiles) BKV_REV_STEP(j + 1, X2, X0, T >= 2, __VA_ARGS__);          \
     if (j + 2 < ntiles) BKV_REV_STEP(j + 2, X1, X2, T >= 2, __VA_ARGS__);          \
     if (j + 3 < ntiles) BKV_REV_STEP(j + 3, X0, X1, T >= 2, __VA_ARGS__)
-#define BKV_REV_LOOP4(B0, B1, B2, B3, ...)                                         \
-    for (int j = 0; j < ntiles; j += 4) {                                          \
-        BKV_REV_ITER(j, B0, B2, __VA_ARGS__);                                      \
-        if (j + 1 < ntiles) BKV_REV_ITER(j + 1, B1, B3, __VA_ARGS__);              \
-        if (j + 2 < ntiles) BKV_REV_ITER(j + 2, B2, B0, __VA_ARGS__);              \
-        if (j + 3 < ntiles) BKV_REV_ITER(j + 3, B3, B1, __VA_ARGS__);              \
-    }
     // Buffers visited from the last tile down.
-    if constexpr (kRing == 3) {
+    {
         if (loader && (reflect || t0 <= ntiles - 3)) {
             // Reflected: no tile is resident beyond the two pass 1 left, so
             // every iteration from the first loads (t_res = ntiles - 2).
@@ -944,21 +887,7 @@ void score_kernel(ScoreArgs a, int g, int hs) {
                 default: BKV_REV_LOOP(tile2, tile0, tile1, BKV_PASS2); break;
             }
         }
-    } else {
-        // Tile T sits in buffer (T - t0) mod 4, or (ntiles - 1 - T) mod 4 when
-        // reflected.
-        if (reflect) {
-            BKV_REV_LOOP4(tile0, tile1, tile2, tile3, BKV_PASS2);
-        } else {
-            switch ((ntiles - 1 - t0) % 4) {
-                case 0: BKV_REV_LOOP4(tile0, tile3, tile2, tile1, BKV_PASS2); break;
-                case 1: BKV_REV_LOOP4(tile1, tile0, tile3, tile2, BKV_PASS2); break;
-                case 2: BKV_REV_LOOP4(tile2, tile1, tile0, tile3, BKV_PASS2); break;
-                default: BKV_REV_LOOP4(tile3, tile2, tile1, tile0, BKV_PASS2); break;
-            }
-        }
     }
-#undef BKV_REV_LOOP4
 #undef BKV_REV_FAST
 #undef BKV_REV_LOOP
 #undef BKV_REV_ITER
@@ -1260,34 +1189,22 @@ template __global__ void decode_kernel<64, 1, true>(DecodeArgs, int, int);
 
 // Every variant is instantiated explicitly, so each gets its host launch stub
 // even though it is launched from one branch of a conditional.
-template __global__ void score_kernel<128, 4, false, false>(ScoreArgs, int, int);
-template __global__ void score_kernel<128, 2, false, false>(ScoreArgs, int, int);
-template __global__ void score_kernel<128, 1, false, false>(ScoreArgs, int, int);
-template __global__ void score_kernel<64, 4, false, false>(ScoreArgs, int, int);
-template __global__ void score_kernel<64, 2, false, false>(ScoreArgs, int, int);
-template __global__ void score_kernel<64, 1, false, false>(ScoreArgs, int, int);
-template __global__ void score_kernel<128, 4, true, false>(ScoreArgs, int, int);
-template __global__ void score_kernel<128, 2, true, false>(ScoreArgs, int, int);
-template __global__ void score_kernel<128, 1, true, false>(ScoreArgs, int, int);
-template __global__ void score_kernel<64, 4, true, false>(ScoreArgs, int, int);
-template __global__ void score_kernel<64, 2, true, false>(ScoreArgs, int, int);
-template __global__ void score_kernel<64, 1, true, false>(ScoreArgs, int, int);
-template __global__ void score_kernel<128, 4, false, true>(ScoreArgs, int, int);
-template __global__ void score_kernel<128, 2, false, true>(ScoreArgs, int, int);
-template __global__ void score_kernel<128, 1, false, true>(ScoreArgs, int, int);
-template __global__ void score_kernel<64, 4, false, true>(ScoreArgs, int, int);
-template __global__ void score_kernel<64, 2, false, true>(ScoreArgs, int, int);
-template __global__ void score_kernel<64, 1, false, true>(ScoreArgs, int, int);
-template __global__ void score_kernel<128, 4, true, true>(ScoreArgs, int, int);
-template __global__ void score_kernel<128, 2, true, true>(ScoreArgs, int, int);
-template __global__ void score_kernel<128, 1, true, true>(ScoreArgs, int, int);
-template __global__ void score_kernel<64, 4, true, true>(ScoreArgs, int, int);
-template __global__ void score_kernel<64, 2, true, true>(ScoreArgs, int, int);
-template __global__ void score_kernel<64, 1, true, true>(ScoreArgs, int, int);
-template __global__ void score_kernel<128, 4, false, false, 4>(ScoreArgs, int, int);
-template __global__ void score_kernel<128, 4, false, true, 4>(ScoreArgs, int, int);
-template __global__ void score_kernel<64, 4, false, false, 4>(ScoreArgs, int, int);
-template __global__ void score_kernel<64, 4, false, true, 4>(ScoreArgs, int, int);
+template __global__ void score_kernel<128, 4, false>(ScoreArgs, int);
+template __global__ void score_kernel<128, 2, false>(ScoreArgs, int);
+template __global__ void score_kernel<128, 1, false>(ScoreArgs, int);
+template __global__ void score_kernel<64, 4, false>(ScoreArgs, int);
+template __global__ void score_kernel<64, 2, false>(ScoreArgs, int);
+template __global__ void score_kernel<64, 1, false>(ScoreArgs, int);
+template __global__ void score_kernel<128, 4, true>(ScoreArgs, int);
+template __global__ void score_kernel<128, 2, true>(ScoreArgs, int);
+template __global__ void score_kernel<128, 1, true>(ScoreArgs, int);
+template __global__ void score_kernel<64, 4, true>(ScoreArgs, int);
+template __global__ void score_kernel<64, 2, true>(ScoreArgs, int);
+template __global__ void score_kernel<64, 1, true>(ScoreArgs, int);
+template __global__ void score_kernel<128, 4, false, 4>(ScoreArgs, int);
+template __global__ void score_kernel<128, 4, true, 4>(ScoreArgs, int);
+template __global__ void score_kernel<64, 4, false, 4>(ScoreArgs, int);
+template __global__ void score_kernel<64, 4, true, 4>(ScoreArgs, int);
 
 }  // namespace
 
@@ -1331,26 +1248,16 @@ hipError_t launch_score(const uint16_t* K, const int32_t* kpos, int64_t n_units,
     // three workgroups share a CU: R1-Distill-Qwen-7B shape (g = 7) 2.50 ->
     // 2.05 ms and Qwen3-14B shape (g = 5) 2.94 -> 2.50 ms against splitting a
     // group over two workgroups, each of which read every key.
-    a.split = 0;
     a.inv_rows = 1.0f / (float)(g * 32);
-    const int hs = a.split ? (g + 1) / 2 : g;
-    const bool capped = !a.split && g >= 5;
-    if (a.split) {
-        const int64_t n = n_units * L;
-        const unsigned zb = (unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
-        zero_scores_kernel<<<zb, 256, 0, s>>>(score, l_cap, L, n_units);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    const dim3 grid(a.split ? (unsigned)((n_units + 7) / 8 * 16) : (unsigned)n_units);
-    const dim3 block(64 * hs);
-    // Loader wavefronts: the largest power of two <= hs, at most 4.
-    const int nl = hs >= 4 ? 4 : (hs >= 2 ? 2 : 1);
+    const bool capped = g >= 5;
+    const dim3 grid((unsigned)n_units);
+    const dim3 block(64 * g);
+    // Loader wavefronts: the largest power of two <= g, at most 4.
+    const int nl = g >= 4 ? 4 : (g >= 2 ? 2 : 1);
 #define BKV_LAUNCH_M(DD, NN, MM)                                                   \
     do {                                                                           \
-        if (a.split) score_kernel<DD, NN, true, MM><<<grid, block, 0, s>>>(a, g, hs); \
-        else if (capped) score_kernel<DD, 4, false, MM, 4><<<grid, block, 0, s>>>(a, g, hs); \
-        else score_kernel<DD, NN, false, MM><<<grid, block, 0, s>>>(a, g, hs);     \
+        if (capped) score_kernel<DD, 4, MM, 4><<<grid, block, 0, s>>>(a, g);       \
+        else score_kernel<DD, NN, MM><<<grid, block, 0, s>>>(a, g);                \
     } while (0)
 #define BKV_LAUNCH(DD, NN)                                                         \
     do {                                                                           \

@@ -11,10 +11,13 @@
 // workgroup per head and one thread per row; there the average cosine of
 // row i uses the sum of all normalised rows (sum_j cos(q_i, q_j) equals
 // q_i/|q_i| . sum_j q_j/|q_j|) and each pick broadcasts the new member's
-// row through LDS.  Longer buffers (up to 8192 rows) stream their rows on
-// every pass (fps_long_kernel).
+// row through LDS.  Longer buffers (up to 8192 rows) are read in three full
+// passes, after which the greedy runs lazily on a shortlist of rows gathered
+// from memory (fps_long_kernel).
 //
 // Arithmetic is fp32; ties go to the lower slot.
+
+#include <algorithm>
 
 #include "common.h"
 
@@ -401,38 +404,136 @@ __global__ __launch_bounds__(256) void fps_block_kernel(
 }
 
 // Buffers of more than 256 rows (up to kLongCap; the prefill FPS over a
-// long prompt, or FPS over a whole query history): one workgroup per head,
-// with the rows left in memory and streamed on every pass.  A wavefront
+// long prompt, or FPS over a whole query history): one workgroup of
+// kLongThreads per head, with the rows left in memory.  A wavefront
 // instruction reads RPI = 64 / (D/4) whole rows, one float4 per lane, and a
-// row's dot products reduce over its D/4 lanes with xor shuffles; the row's
-// norm is re-formed from the same loads on every pass, so LDS holds only
-// the running maxima S (4 bytes per row).
+// row's dot products reduce over its D/4 lanes with xor shuffles; a row's
+// norm is re-formed from the same loads wherever the row is read.
 //  * pass 1: the sum of the normalised rows (then the average cosine of row
 //    i is q_i/|q_i| . sum / N, as in fps_block_kernel);
 //  * pass 2: the average cosines; the seed is their argmin;
-//  * each further pass: the cosine of every row with the last pick (the
-//    pick's column of the Gram matrix), S = max(S, it), and the argmin of S
-//    over the rows not yet picked (a picked row holds S = +inf).
-// m + 1 passes over the N rows in all.  The picked rows are staged in
-// registers before they are written back to rows 0..m-1 (a destination row
-// can be another pick's source).
+//  * pass 3: every row's cosine with the seed.
+// From then on each row keeps in LDS a lower bound lb of its S (its largest
+// cosine to the picked set): the largest cosine over the ep picks applied
+// to it so far.  The greedy's next pick, the row of least (S, slot), is
+// found lazily.  The kShort rows of least (lb, slot) form a shortlist whose
+// bound T is the least (lb, slot) outside it; their rows are gathered into
+// registers and take the cosines with the picks they lack, so their S are
+// exact.  Every row outside has S >= lb and (lb, slot) >= T, so while the
+// least (S, slot) of the shortlist is below T it is the greedy's pick; the
+// shortlist rows then take the new pick's cosine and the test repeats.
+// Once it fails, the bounds go back to LDS and a new shortlist is formed.
+// Each (row, pick) cosine is formed once, in the same fp32 arithmetic as a
+// pass over all rows would form it, so the picks are those of the plain
+// greedy over these cosines.  The shortlist's bound comes from a radix
+// select over (lb, slot) keys in LDS, stopped as soon as at least
+// kShort / 2 rows fall below a digit boundary.  The picked rows' normalised
+// rows stay in LDS (pick rows [m][D]) for the gathers.
 constexpr int kLongCap = 8192;
 constexpr int kLongM = 64;
+constexpr int kLongThreads = 512;
+constexpr int kLongWaves = kLongThreads / 64;
+constexpr int kShort = 128;        // shortlist rows
+constexpr uint32_t kPicked = 0xff;  // ep of a picked row
 
+// (value, slot) as one 45-bit key that orders like the pair: the float's
+// bits made monotone (-0 folded onto +0), then the slot (below 2^13).
+__device__ __forceinline__ uint64_t order_key(float v, int j) {
+    uint32_t u = __float_as_uint(v);
+    if (u == 0x80000000u) u = 0;
+    u ^= (u >> 31) ? 0xffffffffu : 0x80000000u;
+    return ((uint64_t)u << 13) | (uint32_t)j;
+}
+
+// The value of the lane that differs from this one in bit b of its index
+// within 32.  The DPP mirror pairings differ in bits 2 and 3 (and in the
+// bits below), so every step pairs lanes by XOR with a constant and a
+// reduction over steps 0..4 leaves the same result in all 32 lanes.
+__device__ __forceinline__ int lane_xchg_i(int x, int b) {
+    switch (b) {
+        case 0: return dpp_i<0xB1>(x);   // quad_perm [1,0,3,2]
+        case 1: return dpp_i<0x4E>(x);   // quad_perm [2,3,0,1]
+        case 2: return dpp_i<0x141>(x);  // row_half_mirror
+        case 3: return dpp_i<0x140>(x);  // row_mirror
+        default: return swap16_i(x);
+    }
+}
+__device__ __forceinline__ float lane_xchg(float x, int b) {
+    return __builtin_bit_cast(float, lane_xchg_i(__builtin_bit_cast(int, x), b));
+}
+
+// Least value over the wavefront, returned as a wavefront-uniform value.
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+#pragma unroll
+    for (int b = 0; b < 5; ++b) x = min(x, (uint32_t)lane_xchg_i((int)x, b));
+    return min((uint32_t)__builtin_amdgcn_readlane((int)x, 0),
+               (uint32_t)__builtin_amdgcn_readlane((int)x, 32));
+}
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t x) {
+#pragma unroll
+    for (int b = 0; b < 5; ++b) {
+        const uint64_t y = ((uint64_t)(uint32_t)lane_xchg_i((int)(x >> 32), b) << 32) |
+                           (uint32_t)lane_xchg_i((int)x, b);
+        x = y < x ? y : x;
+    }
+    const uint64_t a = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(x >> 32), 0) << 32) |
+                       (uint32_t)__builtin_amdgcn_readlane((int)x, 0);
+    const uint64_t c = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(x >> 32), 32) << 32) |
+                       (uint32_t)__builtin_amdgcn_readlane((int)x, 32);
+    return c < a ? c : a;
+}
+
+// Sums of NI rows' partial sums over the C4 lanes that hold each row: a
+// reduce-scatter (each step trades half of the values with the partner lane
+// and adds) leaves row i's total in the C4/NI lanes with c4 / (C4/NI) == i.
+template <int C4, int NI>
+__device__ __forceinline__ float rows_sum_scatter(float (&v)[NI], int c4) {
+    constexpr int LC4 = __builtin_ctz(C4), LNI = __builtin_ctz(NI);
+#pragma unroll
+    for (int s = 0; s < LNI; ++s) {
+        const int b = LC4 - 1 - s, h = NI >> (s + 1);
+        const bool hi = (c4 >> b) & 1;
+#pragma unroll
+        for (int k = 0; k < h; ++k) {
+            float lo_v = v[k], hi_v = v[k + h];
+            // Values, not array slots: keeps the choice below a register
+            // select instead of a run-time index into v.
+            asm volatile("" : "+v"(lo_v), "+v"(hi_v));
+            const float send = hi ? lo_v : hi_v;
+            const float keep = hi ? hi_v : lo_v;
+            v[k] = keep + lane_xchg(send, b);
+        }
+    }
+    float x = v[0];
+#pragma unroll
+    for (int b = LC4 - LNI - 1; b >= 0; --b) x += lane_xchg(x, b);
+    return x;
+}
+
+// At most 80 VGPRs (six wavefronts per SIMD): three workgroups per CU, so
+// that one workgroup's shortlist work overlaps the others' passes.
 template <int D>
-__global__ __launch_bounds__(256) void fps_long_kernel(
+__global__ __launch_bounds__(kLongThreads, 6) void fps_long_kernel(
     float* __restrict__ buf, int32_t* __restrict__ count, const float* __restrict__ new_q,
     int n_new, int cap, int trigger, int m, int32_t* __restrict__ sel_order,
     int32_t* __restrict__ n_overflow) {
-    extern __shared__ float S[];  // [cap]
+    extern __shared__ float dyn[];  // pick rows [m][D], then lb [cap], then ep [cap] bytes
     __shared__ float bc[D];
-    __shared__ float part[4][D];
-    __shared__ float red_v[4];
-    __shared__ int red_i[4];
+    __shared__ float part[kLongWaves][D];
+    __shared__ uint32_t hist[256];
+    __shared__ int eidx[kShort];
+    __shared__ uint64_t red_k[kLongWaves];
+    __shared__ float red_v[kLongWaves];
+    __shared__ int red_i[kLongWaves];
     __shared__ int picks[kLongM];
-    constexpr int C4 = D / 4;       // float4 chunks per row
-    constexpr int RPI = 64 / C4;    // rows per wavefront instruction
-    constexpr int STEP = 4 * RPI;   // rows per pass iteration of the workgroup
+    __shared__ int sh_n;
+    __shared__ uint32_t sh_digit, sh_below;
+    constexpr int NT = kLongThreads, NW = kLongWaves;
+    constexpr int C4 = D / 4;                // float4 chunks per row
+    constexpr int RPI = 64 / C4;             // rows per wavefront instruction
+    constexpr int STEP = NW * RPI;           // rows per pass iteration of the workgroup
+    constexpr int NI = kShort / NW / RPI;    // shortlist rows per lane group
+    constexpr int U = 4;                     // row loads in flight per lane in a pass
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int sub = lane / C4, c4 = lane % C4;
     const int64_t head = blockIdx.x;
@@ -443,34 +544,47 @@ __global__ __launch_bounds__(256) void fps_long_kernel(
     const int N = cnt + n_new;
     const bool compress = (cnt >= 0 && N <= cap && N >= trigger && N > m);
     if (sel_order && !compress)
-        for (int i = tid; i < m; i += 256) sel_order[head * m + i] = -1;
+        for (int i = tid; i < m; i += NT) sel_order[head * m + i] = -1;
     if (cnt < 0 || N > cap) {
         if (tid == 0 && n_overflow) atomicAdd(n_overflow, 1);
         return;
     }
     if (!compress) {
-        for (int e = tid * 4; e < n_new * D; e += 256 * 4)
+        for (int e = tid * 4; e < n_new * D; e += NT * 4)
             *reinterpret_cast<float4*>(hb + (int64_t)cnt * D + e) =
                 *reinterpret_cast<const float4*>(nq + e);
         if (tid == 0) count[head] = N;
         return;
     }
+    float* P = dyn;
+    float* lb = dyn + min(m, kLongM) * D;
+    uint8_t* ep = reinterpret_cast<uint8_t*>(lb + cap);
 
     auto row_ptr = [&](int j) -> const float* {
         return j < cnt ? hb + (int64_t)j * D : nq + (int64_t)(j - cnt) * D;
     };
     auto load4 = [&](int j) -> float4 {
-        return j < N ? *reinterpret_cast<const float4*>(row_ptr(j) + 4 * c4)
-                     : make_float4(0.f, 0.f, 0.f, 0.f);
+        return (j >= 0 && j < N) ? *reinterpret_cast<const float4*>(row_ptr(j) + 4 * c4)
+                                 : make_float4(0.f, 0.f, 0.f, 0.f);
     };
-    auto row_sum = [&](float x) {  // over the C4 lanes of a row
+    auto row_sum = [&](float x) {  // over the C4 lanes of a row, the same in each
 #pragma unroll
-        for (int o = 1; o < C4; o <<= 1) x += __shfl_xor(x, o);
+        for (int b = 0; (1 << b) < C4; ++b) x += lane_xchg(x, b);
         return x;
     };
     auto dot4 = [](float4 a, float4 b) { return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w; };
     auto inv_norm = [&](float4 v) {
         return 1.0f / fmaxf(sqrtf(row_sum(dot4(v, v))), kNormFloor);
+    };
+    // A pass over all rows, U row loads in flight per lane.
+    auto stream = [&](auto&& body) {
+        for (int j0 = wave * RPI + sub; j0 < N + sub; j0 += U * STEP) {
+            float4 v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) v[u] = load4(j0 + u * STEP);
+#pragma unroll
+            for (int u = 0; u < U; ++u) body(j0 + u * STEP, v[u]);
+        }
     };
     // (value, index) argmin where index kNone means "no candidate": any
     // candidate beats none, so the result is a real row even if every value
@@ -484,19 +598,19 @@ __global__ __launch_bounds__(256) void fps_long_kernel(
     };
     auto block_argmin = [&](float v, int i) -> int {
 #pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const float ov = __shfl_xor(v, o);
-            const int oi = __shfl_xor(i, o);
-            take(v, i, ov, oi);
-        }
+        for (int b = 0; b < 5; ++b) take(v, i, lane_xchg(v, b), lane_xchg_i(i, b));
+        const float v32 = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+        const int i32 = __builtin_amdgcn_readlane(i, 32);
         if (lane == 0) {
+            take(v, i, v32, i32);
             red_v[wave] = v;
             red_i[wave] = i;
         }
         __syncthreads();
         float bv = red_v[0];
         int bi = red_i[0];
-        for (int w = 1; w < 4; ++w) take(bv, bi, red_v[w], red_i[w]);
+        for (int w = 1; w < NW; ++w) take(bv, bi, red_v[w], red_i[w]);
         __syncthreads();  // red_* are free again
         return bi;
     };
@@ -504,9 +618,7 @@ __global__ __launch_bounds__(256) void fps_long_kernel(
 
     // Pass 1: sum of the normalised rows.
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j0 = wave * RPI; j0 < N; j0 += STEP) {
-        const int j = j0 + sub;
-        const float4 v = load4(j);
+    stream([&](int j, float4 v) {
         const float inv = inv_norm(v);
         if (j < N) {
             acc.x = fmaf(v.x, inv, acc.x);
@@ -514,7 +626,7 @@ __global__ __launch_bounds__(256) void fps_long_kernel(
             acc.z = fmaf(v.z, inv, acc.z);
             acc.w = fmaf(v.w, inv, acc.w);
         }
-    }
+    });
 #pragma unroll
     for (int o = C4; o < 64; o <<= 1) {
         acc.x += __shfl_xor(acc.x, o);
@@ -524,67 +636,235 @@ __global__ __launch_bounds__(256) void fps_long_kernel(
     }
     if (sub == 0) *reinterpret_cast<float4*>(&part[wave][4 * c4]) = acc;
     __syncthreads();
-    if (tid < D) bc[tid] = part[0][tid] + part[1][tid] + part[2][tid] + part[3][tid];
+    if (tid < D) {
+        float s = part[0][tid];
+        for (int w = 1; w < NW; ++w) s += part[w][tid];
+        bc[tid] = s;
+    }
     __syncthreads();
 
-    // Pass 2: average cosines; S starts at -inf.
+    // Pass 2: average cosines; the seed is their argmin.
     const float invN = 1.0f / (float)N;
     float bv = inf;
     int bi = kNone;
     {
         const float4 sv = *reinterpret_cast<const float4*>(&bc[4 * c4]);
-        for (int j0 = wave * RPI; j0 < N; j0 += STEP) {
-            const int j = j0 + sub;
-            const float4 v = load4(j);
+        stream([&](int j, float4 v) {
             const float inv = inv_norm(v);
             const float a = row_sum(dot4(v, sv)) * inv * invN;
-            if (j < N) {
-                take(bv, bi, a, j);
-                if (c4 == 0) S[j] = -inf;
-            }
-        }
+            if (j < N) take(bv, bi, a, j);
+        });
     }
-    int p = block_argmin(bv, bi);
+    const int seed = block_argmin(bv, bi);
+    if (tid == 0) {
+        picks[0] = seed;
+        if (sel_order) sel_order[head * m] = seed;
+    }
+    if (wave == 0) {  // the seed's normalised row
+        const float4 v = sub == 0 ? *reinterpret_cast<const float4*>(row_ptr(seed) + 4 * c4)
+                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float inv = inv_norm(v);
+        if (sub == 0)
+            *reinterpret_cast<float4*>(&P[4 * c4]) =
+                make_float4(v.x * inv, v.y * inv, v.z * inv, v.w * inv);
+    }
+    __syncthreads();
 
-    // Greedy picks: each pass adds the last pick's cosines to S.
-    for (int it = 0;; ++it) {
-        if (tid == 0) {
-            picks[it] = p;
-            S[p] = inf;
-            if (sel_order) sel_order[head * m + it] = p;
-        }
-        if (it + 1 == m) break;
-        if (wave == 0) {  // the pick's normalised row
-            const float4 v = sub == 0 ? *reinterpret_cast<const float4*>(row_ptr(p) + 4 * c4)
-                                      : make_float4(0.f, 0.f, 0.f, 0.f);
-            const float inv = inv_norm(v);
-            if (sub == 0)
-                *reinterpret_cast<float4*>(&bc[4 * c4]) =
-                    make_float4(v.x * inv, v.y * inv, v.z * inv, v.w * inv);
-        }
-        __syncthreads();
-        const float4 b4 = *reinterpret_cast<const float4*>(&bc[4 * c4]);
-        bv = inf;
-        bi = kNone;
-        for (int j0 = wave * RPI; j0 < N; j0 += STEP) {
-            const int j = j0 + sub;
-            const float4 v = load4(j);
+    // Pass 3: every row's cosine with the seed.
+    {
+        const float4 b4 = *reinterpret_cast<const float4*>(&P[4 * c4]);
+        stream([&](int j, float4 v) {
             const float inv = inv_norm(v);
             const float c = row_sum(dot4(v, b4)) * inv;
-            if (j < N) {
-                const float so = S[j];
-                if (so != inf) {
-                    const float sn = fmaxf(so, c);
-                    if (c4 == 0) S[j] = sn;
-                    take(bv, bi, sn, j);
+            if (j < N && c4 == 0) {
+                lb[j] = fmaxf(-inf, c);  // a NaN cosine leaves -inf
+                ep[j] = j == seed ? kPicked : 1;
+            }
+        });
+    }
+    __syncthreads();
+
+    // A refill that makes no pick brings at least one stale row up to date
+    // (were every shortlist row current, its least key would be below T), so
+    // there are at most N + 1 refills per pick; the cap only guarantees that
+    // the workgroup finishes whatever its input.
+    int npk = 1;
+    const int64_t refill_cap = (int64_t)m * (N + 1);
+    for (int64_t refills = 0; npk < m && refills < refill_cap; ++refills) {
+        // The shortlist bound T (exclusive) over the keys of the unpicked
+        // rows: the kShort-th least key, or an earlier digit boundary with at
+        // least kShort / 2 keys below it.  8-bit digits from the top.
+        uint64_t T = ~0ull;
+        if (N - npk > kShort) {
+            uint64_t prefix = 0;
+            uint32_t rank = kShort, below = 0;
+            int sh = 45;
+            while (sh > 0) {
+                const int width = sh >= 8 ? 8 : sh;
+                sh -= width;
+                if (tid < 256) hist[tid] = 0;
+                __syncthreads();
+                for (int j = tid; j < N; j += NT) {
+                    if (ep[j] == kPicked) continue;
+                    const uint64_t k = order_key(lb[j], j);
+                    if ((k >> (sh + width)) == prefix)
+                        atomicAdd(&hist[(uint32_t)(k >> sh) & ((1u << width) - 1)], 1u);
                 }
+                __syncthreads();
+                if (wave == 0) {  // the bin that holds rank `rank`
+                    uint32_t h[4], s = 0;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        h[q] = hist[4 * lane + q];
+                        s += h[q];
+                    }
+                    // Inclusive scan: within rows of 16 lanes by DPP row
+                    // shifts (lanes shifted in from outside the row read 0),
+                    // then the totals of the rows below.
+                    uint32_t incl = s;
+                    incl += (uint32_t)dpp_i<0x111>((int)incl);  // row_shr:1
+                    incl += (uint32_t)dpp_i<0x112>((int)incl);  // row_shr:2
+                    incl += (uint32_t)dpp_i<0x114>((int)incl);  // row_shr:4
+                    incl += (uint32_t)dpp_i<0x118>((int)incl);  // row_shr:8
+                    const uint32_t r0 = __builtin_amdgcn_readlane((int)incl, 15);
+                    const uint32_t r1 = __builtin_amdgcn_readlane((int)incl, 31);
+                    const uint32_t r2 = __builtin_amdgcn_readlane((int)incl, 47);
+                    const int row16 = lane >> 4;
+                    incl += (row16 >= 1 ? r0 : 0u) + (row16 >= 2 ? r1 : 0u) + (row16 >= 3 ? r2 : 0u);
+                    uint32_t c = incl - s;
+                    if (c <= rank && rank < incl) {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            if (rank < c + h[q]) {
+                                sh_digit = 4 * lane + q;
+                                sh_below = c;
+                                break;
+                            }
+                            c += h[q];
+                        }
+                    }
+                }
+                __syncthreads();
+                const uint32_t dg = __builtin_amdgcn_readfirstlane(sh_digit);
+                const uint32_t cb = __builtin_amdgcn_readfirstlane(sh_below);
+                prefix = (prefix << width) | dg;
+                below += cb;
+                rank -= cb;
+                if (below >= kShort / 2) break;
+            }
+            T = prefix << sh;
+        }
+        if (tid == 0) sh_n = 0;
+        __syncthreads();
+        for (int j = tid; j < N; j += NT) {
+            if (ep[j] != kPicked && order_key(lb[j], j) < T) {
+                const int s = atomicAdd(&sh_n, 1);
+                if (s < kShort) eidx[s] = j;
             }
         }
-        p = block_argmin(bv, bi);  // its barriers also order the bc reads before the next write
+        __syncthreads();
+        const int ne = __builtin_amdgcn_readfirstlane(min(sh_n, kShort));
+
+        // Gather the shortlist rows and apply the picks each one lacks.  Lane
+        // group `sub` holds rows i = 0..NI-1 of its share in er[i]; the
+        // bookkeeping of row i (slot, S, 1/|q|, picks applied) sits in the G
+        // lanes with c4 / G == i, where rows_sum_scatter leaves its sums.
+        constexpr int G = C4 / NI;
+        const int my_row = c4 / G;
+        float4 er[NI];
+        int my_j = -1, my_ep = npk;
+        float my_s = inf, my_inv;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int s = (wave * NI + i) * RPI + sub;
+            const int j = s < ne ? eidx[s] : -1;
+            er[i] = load4(j);
+            if (my_row == i) my_j = j;
+        }
+        if (my_j >= 0) {
+            my_ep = ep[my_j];
+            my_s = lb[my_j];
+        }
+        const int emin = (int)wave_min_u32((uint32_t)my_ep);
+        {
+            float t[NI];
+#pragma unroll
+            for (int i = 0; i < NI; ++i) t[i] = dot4(er[i], er[i]);
+            my_inv = 1.0f / fmaxf(sqrtf(rows_sum_scatter<C4, NI>(t, c4)), kNormFloor);
+        }
+        for (int k = emin; k < npk; ++k) {
+            const float4 b4 = *reinterpret_cast<const float4*>(&P[k * D + 4 * c4]);
+            float t[NI];
+#pragma unroll
+            for (int i = 0; i < NI; ++i) t[i] = dot4(er[i], b4);
+            const float d = rows_sum_scatter<C4, NI>(t, c4);
+            if (k >= my_ep) my_s = fmaxf(my_s, d * my_inv);
+        }
+
+        // Greedy picks while the shortlist's least key is below T.
+        for (;;) {
+            uint64_t kb = my_j >= 0 ? order_key(my_s, my_j) : ~0ull;
+            kb = wave_min_u64(kb);
+            if (lane == 0) red_k[wave] = kb;
+            __syncthreads();
+            uint64_t best = red_k[0];
+            for (int w = 1; w < NW; ++w) best = red_k[w] < best ? red_k[w] : best;
+            // (readfirstlane returns int: each half goes through uint32_t so
+            // that the low half is not sign-extended into the high one.)
+            best = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(best >> 32)) << 32) |
+                   (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)best);
+            if (best >= T) break;
+            const int pj = (int)(best & 0x1fff);
+            const unsigned long long hold = __ballot(my_j == pj);
+            if (hold) {  // this wavefront holds the pick: row (L % C4) / G of group L / C4
+                const int L = __builtin_ctzll(hold);
+                const int ri = (L % C4) / G;
+                const float inv = __shfl(my_inv, L);
+                if (sub == L / C4) {
+                    float4 v = er[0];
+#pragma unroll
+                    for (int i = 1; i < NI; ++i)
+                        if (ri == i) v = er[i];
+                    *reinterpret_cast<float4*>(&P[npk * D + 4 * c4]) =
+                        make_float4(v.x * inv, v.y * inv, v.z * inv, v.w * inv);
+                    if (c4 == ri * G) ep[pj] = kPicked;
+                }
+                if (my_j == pj) my_j = -1;
+            }
+            if (tid == 0) {
+                picks[npk] = pj;
+                if (sel_order) sel_order[head * m + npk] = pj;
+            }
+            ++npk;
+            __syncthreads();  // the pick row is in LDS; red_k is free again
+            if (npk == m) break;
+            const float4 b4 = *reinterpret_cast<const float4*>(&P[(npk - 1) * D + 4 * c4]);
+            float t[NI];
+#pragma unroll
+            for (int i = 0; i < NI; ++i) t[i] = dot4(er[i], b4);
+            const float d = rows_sum_scatter<C4, NI>(t, c4);
+            my_s = fmaxf(my_s, d * my_inv);
+        }
+        if (my_j >= 0 && c4 % G == 0) {
+            lb[my_j] = my_s;
+            ep[my_j] = (uint8_t)npk;
+        }
+        __syncthreads();
+    }
+
+    if (npk < m) {  // past the cap (not reached): the lowest unpicked slots
+        if (tid == 0)
+            for (int j = 0; j < N && npk < m; ++j)
+                if (ep[j] != kPicked) {
+                    ep[j] = kPicked;
+                    picks[npk] = j;
+                    if (sel_order) sel_order[head * m + npk] = j;
+                    ++npk;
+                }
+        __syncthreads();
     }
 
     // Write back the picks in ascending slot order.
-    __syncthreads();
     if (tid == 0) {
         for (int a = 1; a < m; ++a) {
             const int x = picks[a];
@@ -599,11 +879,11 @@ __global__ __launch_bounds__(256) void fps_long_kernel(
     __syncthreads();
     // (Native vector type: an array of the float4 struct would live in scratch.)
     typedef float v4f __attribute__((ext_vector_type(4)));
-    constexpr int KS = kLongM * C4 / 256;  // staged chunks per thread
+    constexpr int KS = kLongM * C4 / NT;  // staged chunks per thread
     v4f stg[KS];
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
-        const int e = tid + 256 * k;
+        const int e = tid + NT * k;
         stg[k] = e < m * C4
                      ? *reinterpret_cast<const v4f*>(row_ptr(picks[e / C4]) + 4 * (e % C4))
                      : v4f{0.f, 0.f, 0.f, 0.f};
@@ -611,7 +891,7 @@ __global__ __launch_bounds__(256) void fps_long_kernel(
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
-        const int e = tid + 256 * k;
+        const int e = tid + NT * k;
         if (e < m * C4)
             *reinterpret_cast<v4f*>(hb + (int64_t)(e / C4) * D + 4 * (e % C4)) = stg[k];
     }
@@ -681,13 +961,22 @@ hipError_t launch_fps(float* buf, int32_t* count, const float* new_q,
                                                       trigger, m, sel_order, n_overflow);
     } else {
         if (buf_cap > kLongCap || (m > kLongM && trigger <= buf_cap)) return hipErrorInvalidValue;
-        const size_t lds = (size_t)buf_cap * sizeof(float);
-        if (d == 128)
-            fps_long_kernel<128><<<grid, 256, lds, s>>>(buf, count, new_q, n_new, buf_cap,
-                                                        trigger, m, sel_order, n_overflow);
-        else
-            fps_long_kernel<64><<<grid, 256, lds, s>>>(buf, count, new_q, n_new, buf_cap,
-                                                       trigger, m, sel_order, n_overflow);
+        // Pick rows [min(m, kLongM)][d] floats, lb [buf_cap] floats, ep [buf_cap] bytes.
+        const size_t lds = ((size_t)std::min(m, kLongM) * d * 4 + (size_t)buf_cap * 5 + 15) &
+                           ~(size_t)15;
+        if (d == 128) {
+            if (lds > 65536) {
+                const hipError_t e = hipFuncSetAttribute(
+                    reinterpret_cast<const void*>(&fps_long_kernel<128>),
+                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+                if (e != hipSuccess) return e;
+            }
+            fps_long_kernel<128><<<grid, kLongThreads, lds, s>>>(
+                buf, count, new_q, n_new, buf_cap, trigger, m, sel_order, n_overflow);
+        } else {
+            fps_long_kernel<64><<<grid, kLongThreads, lds, s>>>(
+                buf, count, new_q, n_new, buf_cap, trigger, m, sel_order, n_overflow);
+        }
     }
     return hipGetLastError();
 }

@@ -165,10 +165,13 @@ def test_prefill_block_path(d, n):
 
 @pytest.mark.parametrize("d,n,cap,nq,m,n_new", [
     (128, 257, 300, 8, 16, 0),     # just past the workgroup-per-row path
+    (64, 100, 300, 3, 16, 2),      # every unpicked row fits the shortlist from the start
+    (128, 150, 300, 2, 64, 0),     # the unpicked rows come to fit the shortlist midway
     (64, 1000, 1000, 6, 16, 1),    # the last row arrives as a new query
     (128, 2000, 2048, 4, 64, 0),   # the largest kept set of the long path
     (128, 4096, 4096, 3, 16, 5),
     (64, 8192, 8192, 1, 16, 0),    # the largest buffer
+    (128, 8192, 8192, 1, 64, 0),   # the largest buffer and kept set: 72 KB of LDS
 ])
 def test_long_buffer_fps(d, n, cap, nq, m, n_new):
     """Buffers of more than 256 rows (prefill FPS over a long prompt): rows
@@ -193,6 +196,29 @@ def test_long_buffer_fps(d, n, cap, nq, m, n_new):
         exact += check_fps(host[q, :n], sel[q], m, f"long head {q}")
         assert np.array_equal(out[q, :m], host[q, :n][np.sort(sel[q])]), f"head {q} rows"
     log(f"  {exact}/{nq} heads outside near-ties matched exactly")
+
+
+@pytest.mark.parametrize("d,n,m", [(128, 1500, 32), (64, 700, 16)])
+def test_long_buffer_fps_duplicate_rows(d, n, m):
+    """Rows drawn from 40 distinct vectors: equal cosines everywhere, so the
+    slot breaks every tie, inside the shortlist and at its bound."""
+    nq = 2
+    log(f"fps long buffer, duplicated rows d={d} N={n} m={m}")
+    r = np.random.default_rng(d + n)
+    base = r.standard_normal((nq, 40, d)).astype(np.float32)
+    host = np.ascontiguousarray(base[:, r.integers(0, 40, n)])
+    shape = bkv.Shape(n_units=nq, group=1, d_head=d, l_cap=64, prefix=0, rope_theta=1e6,
+                      buf_cap=n)
+    buf = torch.from_numpy(host.copy()).to(DEV)
+    count = torch.full((nq,), n, dtype=torch.int32, device=DEV)
+    sel = torch.full((nq, m), -7, dtype=torch.int32, device=DEV)
+    bkv.fps_update(shape, buf, count, trigger=n, m=m, sel_order=sel)
+    torch.cuda.synchronize()
+    assert torch.all(count == m)
+    out, sel = buf.cpu().numpy(), sel.cpu().numpy()
+    for q in range(nq):
+        check_fps(host[q], sel[q], m, f"duplicated head {q}")
+        assert np.array_equal(out[q, :m], host[q][np.sort(sel[q])]), f"head {q} rows"
 
 
 def test_long_buffer_append_only():

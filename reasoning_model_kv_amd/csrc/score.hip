@@ -25,8 +25,9 @@
 //    into each row's LSE.
 //  * Pass 2 walks the tiles backwards (the last three are still in LDS): the
 //    logits are formed again, shifted by the row LSE, reduced over the
-//    lane's 16 rows, the other half (lane ^ 32) and the wavefronts (LDS),
-//    and written as score = exp2(max).
+//    lane's 16 rows, the other half (lane ^ 32) and the wavefronts (LDS,
+//    two buffers: a tile's last step runs after the next tile's barrier, one
+//    barrier per tile), and written as score = exp2(max).
 //  * Groups of five to eight heads run a variant held to 128 VGPRs, so that
 //    two workgroups share a CU.
 //  Output layout of the 32x32 MFMA: lane l, accumulator v holds
@@ -393,7 +394,7 @@ void score_kernel(ScoreArgs a, int g) {
     __shared__ __attribute__((aligned(16))) uint16_t tile0[KT * D];
     __shared__ __attribute__((aligned(16))) uint16_t tile1[KT * D];
     __shared__ __attribute__((aligned(16))) uint16_t tile2[KT * D];
-    __shared__ float red[8][KT];
+    __shared__ float red[2][8][KT];  // pass 2: one buffer per tile parity
     constexpr int NPW = TileLoad<D, NL>::NPW;  // loads per loader lane per tile
 
     const int tid = threadIdx.x;
@@ -449,7 +450,7 @@ void score_kernel(ScoreArgs a, int g) {
             uint16_t* dst = (i < NIT ? tile2 : tile1) + (i % NIT) * 512;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rsrc,
-                (__attribute__((address_space(3))) void*)(row0 ? (void*)&red[0][0] : (void*)dst),
+                (__attribute__((address_space(3))) void*)(row0 ? (void*)&red[0][0][0] : (void*)dst),
                 16, lane * 16, 0, 0, 0);
         }
     }
@@ -484,7 +485,7 @@ void score_kernel(ScoreArgs a, int g) {
         {
             // Rows 0..15: the beacons' row for t, or recent rows 0..15; rows
             // 16..31: the last 16 recent rows.
-            const double2* tab1 = wide ? rtab_lo : reinterpret_cast<const double2*>(&red[0][0]);
+            const double2* tab1 = wide ? rtab_lo : reinterpret_cast<const double2*>(&red[0][0][0]);
             obs.rotate(lane, tab1, wide ? D / 2 : 0, wide ? rtab_hi : rtab_lo, rows);
         }
         // The rotated words pass through an empty asm before the barrier, so
@@ -719,6 +720,23 @@ void score_kernel(ScoreArgs a, int g) {
     wait_vm<0>();
     lds_barrier();
     float* score_u = a.score + u * a.l_cap;
+    // The cross-wavefront step of a tile's reduction (wavefront 0), run
+    // after the next tile's barrier: the tiles alternate between the two
+    // halves of red, so pass 2 needs one barrier per tile.
+    auto p2_reduce = [&](int64_t kb, int b) {
+        if (tid < KT) {
+            const int64_t key = kb + tid;
+            if constexpr (MEAN) {
+                float tot = red[b][0][tid];
+                for (int w = 1; w < nw; ++w) tot += red[b][w][tid];
+                if (key < L) score_u[key] = tot * a.inv_rows;
+            } else {
+                float best = red[b][0][tid];
+                for (int w = 1; w < nw; ++w) best = vmax(best, red[b][w][tid]);
+                if (key < L) score_u[key] = exp2f(best);
+            }
+        }
+    };
 #define BKV_PASS2                                                                  \
     if constexpr (MEAN) {                                                          \
         BKV_PASS2_MEAN;                                                            \
@@ -750,15 +768,8 @@ void score_kernel(ScoreArgs a, int g) {
     c0 = vmax(c0, __shfl_xor(c0, 32));                                             \
     c1 = vmax(c1, __shfl_xor(c1, 32));                                             \
     if (lane < 32) {                                                               \
-        red[h][lane] = c0;                                                         \
-        red[h][32 + lane] = c1;                                                    \
-    }                                                                              \
-    lds_barrier();                                                               \
-    if (tid < KT) {                                                                \
-        float best = red[0][tid];                                                  \
-        for (int w = 1; w < nw; ++w) best = vmax(best, red[w][tid]);               \
-        const int64_t key = base + tid;                                            \
-        if (key < L) score_u[key] = exp2f(best);                                   \
+        red[rb][h][lane] = c0;                                                     \
+        red[rb][h][32 + lane] = c1;                                                \
     }
 // Mean pooling: the sum of exp2(s - LSE) = W over the lane's rows (hidden
 // entries add nothing), the other half and the wavefronts, divided by the
@@ -786,15 +797,8 @@ void score_kernel(ScoreArgs a, int g) {
     c0 += __shfl_xor(c0, 32);                                                      \
     c1 += __shfl_xor(c1, 32);                                                      \
     if (lane < 32) {                                                               \
-        red[h][lane] = c0;                                                         \
-        red[h][32 + lane] = c1;                                                    \
-    }                                                                              \
-    lds_barrier();                                                               \
-    if (tid < KT) {                                                                \
-        float tot = red[0][tid];                                                   \
-        for (int w = 1; w < nw; ++w) tot += red[w][tid];                           \
-        const int64_t key = base + tid;                                            \
-        if (key < L) score_u[key] = tot * a.inv_rows;                              \
+        red[rb][h][lane] = c0;                                                     \
+        red[rb][h][32 + lane] = c1;                                                \
     }
 // Pass 2 walks the tiles backwards: at the end of pass 1 the last tiles
 // (three, or the ones pass 1 covered plus the prologue's second tile) are
@@ -805,7 +809,8 @@ void score_kernel(ScoreArgs a, int g) {
 // (6% faster than plain loads; pass 1's loads stay plain, as pass 2 reads
 // its last tiles from L2).  Iteration j scores tile T = ntiles - 1 - j from
 // CUR and loads tile T - 2 into NXT (the buffer tile T + 1 used, or an unused
-// one at j = 0).
+// one at j = 0); from j = 1 on, wavefront 0 then stores tile T + 1's scores,
+// one store younger than those loads, which its wait allows for.
 #define BKV_REV_STEP(j, CUR, NXT, LOAD, ...)                                       \
     do {                                                                           \
         const int T = ntiles - 1 - (j);                                            \
@@ -817,9 +822,11 @@ void score_kernel(ScoreArgs a, int g) {
         lds_barrier();                                                           \
         if (LOAD)                                                                  \
             ld.template issue<kLoadStreaming>(Ku, L, (int64_t)(T - 2) * KT, NXT, h); \
+        if ((j) > 0) p2_reduce((int64_t)(T + 1) * KT, ((j) - 1) & 1);            \
         f32x16 acc0, acc1;                                                         \
         tile_logits<D>(CUR, rd, frag, acc0, acc1);                                 \
         const int64_t base = (int64_t)T * KT;                                      \
+        const int rb = (j) & 1;                                                    \
         __VA_ARGS__;                                                               \
     } while (0)
 #define BKV_REV_ITER(j, CUR, NXT, ...)                                             \
@@ -888,6 +895,8 @@ void score_kernel(ScoreArgs a, int g) {
             }
         }
     }
+    lds_barrier();
+    p2_reduce(0, (ntiles - 1) & 1);  // the last tile walked is tile 0
 #undef BKV_REV_FAST
 #undef BKV_REV_LOOP
 #undef BKV_REV_ITER

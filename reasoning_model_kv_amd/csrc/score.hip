@@ -720,19 +720,23 @@ void score_kernel(ScoreArgs a, int g) {
     wait_vm<0>();
     lds_barrier();
     float* score_u = a.score + u * a.l_cap;
-    // The cross-wavefront step of a tile's reduction (wavefront 0), run
-    // after the next tile's barrier: the tiles alternate between the two
-    // halves of red, so pass 2 needs one barrier per tile.
+    // The cross-wavefront step of a tile's reduction (wavefront rw, lane =
+    // key), run after the next tile's barrier: the tiles alternate between
+    // the two halves of red, so pass 2 needs one barrier per tile.  With five
+    // to seven wavefronts, wavefront 3 is the one alone on its SIMD (waves
+    // are placed round-robin on the four), so it takes this extra work.
+    static_assert(KT == 64, "one lane per key of a tile");
+    const int rw = (nw >= 5 && nw <= 7) ? 3 : 0;
     auto p2_reduce = [&](int64_t kb, int b) {
-        if (tid < KT) {
-            const int64_t key = kb + tid;
+        if (h == rw) {
+            const int64_t key = kb + lane;
             if constexpr (MEAN) {
-                float tot = red[b][0][tid];
-                for (int w = 1; w < nw; ++w) tot += red[b][w][tid];
+                float tot = red[b][0][lane];
+                for (int w = 1; w < nw; ++w) tot += red[b][w][lane];
                 if (key < L) score_u[key] = tot * a.inv_rows;
             } else {
-                float best = red[b][0][tid];
-                for (int w = 1; w < nw; ++w) best = vmax(best, red[b][w][tid]);
+                float best = red[b][0][lane];
+                for (int w = 1; w < nw; ++w) best = vmax(best, red[b][w][lane]);
                 if (key < L) score_u[key] = exp2f(best);
             }
         }
@@ -809,14 +813,14 @@ void score_kernel(ScoreArgs a, int g) {
 // (6% faster than plain loads; pass 1's loads stay plain, as pass 2 reads
 // its last tiles from L2).  Iteration j scores tile T = ntiles - 1 - j from
 // CUR and loads tile T - 2 into NXT (the buffer tile T + 1 used, or an unused
-// one at j = 0); from j = 1 on, wavefront 0 then stores tile T + 1's scores,
+// one at j = 0); from j = 1 on, wavefront rw then stores tile T + 1's scores,
 // one store younger than those loads, which its wait allows for.
 #define BKV_REV_STEP(j, CUR, NXT, LOAD, ...)                                       \
     do {                                                                           \
         const int T = ntiles - 1 - (j);                                            \
         if (loader && T < t_res) {                                                 \
             if (T == 0) wait_vm<0>();                                              \
-            else if (h == 0) wait_vm<NPW + 1>();                                   \
+            else if (h == rw) wait_vm<NPW + 1>();                                  \
             else wait_vm<NPW>();                                                   \
         }                                                                          \
         lds_barrier();                                                           \

@@ -147,6 +147,11 @@ SCORE_CASES = [
     ("tiny", 256, 256, 240, "mean"),
     ("tiny_g7", 300, 320, 284, "max"),     # two workgroups per unit
     ("tiny_g5", 1000, 1000, 984, "max"),
+    ("tiny_g7", 256, 256, 0, "max"),       # group 7: every tile in the tail pass
+    ("tiny_g7", 256, 256, 256, "max"),     # group 7: no slot added
+    ("tiny_g7", 150, 192, 100, "max"),     # group 7: three tiles, pass 1 on two
+    ("tiny_g7", 40, 64, 24, "max"),        # group 7: one tile in all
+    ("tiny_g5", 517, 600, 501, "mean"),    # group 5: 5-key last tile, mean pooling
     ("tiny_g8", 300, 300, 284, "mean"),    # split group of eight, mean pooling
     ("tiny_g3", 129, 160, 113, "max"),     # three heads, a 1-key last tile
     ("qwen3_4b_layer", 2176, 2176, 2160, "max"),

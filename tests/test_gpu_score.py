@@ -61,7 +61,12 @@ CASES = [
     ("tiny", 700, 700, 37),           # eleven tiles, direct RoPE path
     ("tiny", 300, 300, "partial"),    # recent rows 0..7 moved, 8..15 from the table
     ("tiny_g7", 300, 320, 0),         # group 7
+    ("tiny_g7", 40, 64, 0),           # group 7, one tile
+    ("tiny_g7", 100, 128, 0),         # group 7, two tiles
+    ("tiny_g7", 150, 192, 37),        # group 7, three tiles, direct RoPE path
+    ("tiny_g7", 250, 256, 0),         # group 7, four tiles
     ("tiny_g5", 1000, 1000, 0),       # group 5
+    ("tiny_g5", 517, 600, 0),         # group 5, 5-key last tile
     ("qwen3_4b_layer", None, None, 0),
 ]
 
@@ -136,6 +141,8 @@ WINDOW_CASES = [
     ("tiny", 300, 300, 37),           # positions != t-32+i: direct RoPE path, all rows
     ("tiny", 300, 300, "partial"),    # rows 0..7 moved
     ("tiny_g7", 300, 320, 0),         # group 7 (two workgroups per unit)
+    ("tiny_g7", 40, 64, 0),           # group 7, one tile
+    ("tiny_g7", 150, 150, 0),         # group 7, three tiles
     ("tiny_g5", 1000, 1000, 0),       # group 5
     ("qwen3_4b_layer", None, None, 0),
 ]

@@ -221,6 +221,33 @@ def test_long_buffer_fps_duplicate_rows(d, n, m):
         assert np.array_equal(out[q, :m], host[q][np.sort(sel[q])]), f"head {q} rows"
 
 
+def test_long_buffer_fps_degenerate_rows():
+    """Zero rows, rows with a NaN or an infinity among ordinary ones: no
+    parity is defined for such rows, but the call finishes and keeps m
+    distinct rows of the buffer."""
+    d, n, nq, m = 128, 900, 3, 16
+    r = np.random.default_rng(21)
+    host = r.standard_normal((nq, n, d)).astype(np.float32)
+    host[0, 100:140] = 0.0
+    host[1, 5, 7] = np.nan
+    host[1, 300:310, 0] = np.inf
+    host[2, :] = host[2, :1]          # every row the same
+    shape = bkv.Shape(n_units=nq, group=1, d_head=d, l_cap=64, prefix=0, rope_theta=1e6,
+                      buf_cap=n)
+    buf = torch.from_numpy(host.copy()).to(DEV)
+    count = torch.full((nq,), n, dtype=torch.int32, device=DEV)
+    sel = torch.full((nq, m), -7, dtype=torch.int32, device=DEV)
+    bkv.fps_update(shape, buf, count, trigger=n, m=m, sel_order=sel)
+    torch.cuda.synchronize()
+    assert torch.all(count == m)
+    out, sel = buf.cpu().numpy(), sel.cpu().numpy()
+    for q in range(nq):
+        assert len(set(sel[q].tolist())) == m and sel[q].min() >= 0 and sel[q].max() < n
+        assert np.array_equal(out[q, :m], host[q][np.sort(sel[q])], equal_nan=True)
+    # Identical rows tie everywhere: the lowest slots win, seed first.
+    assert sel[2].tolist() == list(range(m))
+
+
 def test_long_buffer_append_only():
     d, cap, nq = 128, 600, 5
     r = np.random.default_rng(3)

@@ -248,6 +248,36 @@ def test_long_buffer_fps_degenerate_rows():
     assert sel[2].tolist() == list(range(m))
 
 
+@pytest.mark.parametrize("name,n", [("qwen3_4b_full_b2048", 2048), ("qwen3_4b_layer", 8192)])
+def test_long_buffer_fps_full_size_sampled(name, n):
+    """The prefill FPS at the benchmark's sizes (every query head of the
+    Qwen3-4B step with its 2048-row prompt: 18,432 heads; one layer with
+    8192-row prompts), in the launch bench.py --prefill-fps times; sampled
+    heads against the oracle."""
+    w = synth.shrink(synth.WORKLOADS[name], prefix=n)
+    log(f"fps long buffer full size {w.name}: {w.n_qheads} heads x {n} rows")
+    _, _, q = synth.StreamInputs(w, DEV).prompt()
+    q0 = q.contiguous()
+    del q
+    nq, d, m = w.n_qheads, w.d_head, 16
+    buf = q0.clone()
+    count = torch.full((nq,), n, dtype=torch.int32, device=DEV)
+    sel = torch.full((nq, m), -7, dtype=torch.int32, device=DEV)
+    shape = bkv.Shape(w.n_units, w.group, d, 64, 0, w.theta, buf_cap=n)
+    bkv.fps_update(shape, buf, count, trigger=n, m=m, sel_order=sel)
+    torch.cuda.synchronize()
+    assert torch.all(count == m)
+    sel = sel.cpu().numpy()
+    assert np.all((sel >= 0) & (sel < n))
+    exact = 0
+    heads = sorted({0, 1, nq // 3, nq // 2, nq - 1})
+    for h in heads:
+        rows = q0[h].cpu().numpy()
+        exact += check_fps(rows, sel[h], m, f"{w.name} head {h}")
+        assert np.array_equal(buf[h, :m].cpu().numpy(), rows[np.sort(sel[h])]), f"head {h} rows"
+    log(f"  {exact}/{len(heads)} sampled heads outside near-ties matched exactly")
+
+
 def test_long_buffer_append_only():
     d, cap, nq = 128, 600, 5
     r = np.random.default_rng(3)

@@ -42,6 +42,8 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
 
 constexpr int KT = 64;               // keys per tile
 // Key tiles in the scoring kernel's LDS ring: loads run two tiles ahead, so
@@ -53,6 +55,7 @@ constexpr float kNegBig = -1.0e30f;  // finite "no key seen yet" running max
 // Buffer-resource flags word (gfx9 family: raw 32-bit data, no swizzle).
 constexpr int kBufferFlags = 0x00020000;
 constexpr float kRescaleBig = 0x1p64f; // lazy rescale: largest tile term sum kept
+constexpr float kRescaleExp = 64.0f;    // the same bound on an exponent (log2 units)
 // Cache-policy word of a load whose data is not read again (non-temporal:
 // it does not displace lines that other loads will reuse).
 constexpr int kLoadStreaming = 2;
@@ -925,16 +928,16 @@ void score_kernel(ScoreArgs a, int g) {
 //
 // Mapping: one workgroup per unit, one wavefront per query head (g <= 4;
 // larger groups are split over two workgroups, see decode_kernel).
-// A fragments (rows of the 32 x 32 x 16 MFMA): rows 0..15 the beacons, row
-// 16 the new query, rows 17..31 zero; each lane rotates its own row's dims
-// (16 s + 8 (lane / 32) .. + 8 for step s pair with the same dims of step
-// s + D/32) in fp64 and rounds through fp32 to bf16.  Keys and values stream
-// through rings of three LDS tiles of 32 rows, two tiles ahead.  Per tile:
-// one 32 x 32 logit block; the beacon rows update a per-lane running (max,
-// sum of exp2) as the scoring's pass 1 does; the new query's 32 logits (row
-// 16: accumulator 8 of lanes 0..31) update a running max and sum, and the
-// lane owning dims 2 lane (D = 128) or lane (D = 64) of the output adds
-// p_j * V[j] for the tile's 32 rows (p_j read from lane j into a scalar).
+// A fragments (rows of the 32 x 32 x 16 MFMA): rows 0..15 the beacons, rows
+// 16 and 20 the new query, the other rows zero; each lane rotates its own
+// row's dims (16 s + 8 (lane / 32) .. + 8 for step s pair with the same dims
+// of step s + D/32) in fp64 and rounds through fp32 to bf16.  Keys and
+// values stream through rings of three LDS tiles of 32 rows.  Per tile: one
+// 32 x 32 logit block; the beacon rows update a per-lane running (max, sum
+// of exp2) as the scoring's pass 1 does; the new query's 32 logits
+// (accumulator 8: row 16 in lanes 0..31, its copy in row 20 in lanes
+// 32..63) update a lazily raised running max and a per-lane sum, and the
+// weights times the value tile run on the matrix cores (see vt_offset).
 // Keys and values are read once, with streaming (non-temporal) loads.
 constexpr int DT = 32;  // keys per tile of the decode kernel
 
@@ -956,31 +959,48 @@ struct DecodeArgs {
     int64_t n_units;
 };
 
+// Value products on the matrix cores: one 16 x 16 x 32 bf16 MFMA per 16
+// dims of the output.  B is the value tile (32 keys x 16 dims); A holds the
+// query's 32 weights, a bf16 high part (the top 16 bits of the fp32 weight)
+// in the even rows and the truncated remainder in the odd rows, so that
+// accumulators 0 and 1 of a lane (rows 4 (lane / 16) and 4 (lane / 16) + 1,
+// column lane % 16) add up to sum_j p_j V[j][dim] with each weight kept to
+// about 2^-14 relative.  Key slots 0..7 of lane group q (lanes 16 q ..
+// 16 q + 15) are keys 4 q + i and 16 + 4 q + i (i < 4): the two halves read
+// rows with the same XOR swizzle, 16 rows apart.  Each half is one LDS
+// transpose read (ds_read_b64_tr_b16): in a group of 16 lanes, lane 4 r + c
+// reads dims 4 c .. 4 c + 3 of the block from key row r of the half, and
+// lane n receives the four rows' values of dim n.  vt_offset is this lane's
+// byte offset for block 0 and the first half; block b is that offset XOR
+// 32 b (the swizzle permutes 16-byte chunks within a row), the second half
+// is 32 D bytes further.
 template <int D>
-__device__ __forceinline__ float2 v_pair(const uint16_t* vt, int j, int lane) {
+__device__ __forceinline__ uint32_t vt_offset(int lane) {
     constexpr int CPR = D / 8;
-    const char* b = reinterpret_cast<const char*>(vt);
-    if constexpr (D == 128) {
-        const int c = lane >> 2;
-        const uint32_t w = *reinterpret_cast<const uint32_t*>(
-            b + (j * CPR + (c ^ (j % CPR))) * 16 + (lane & 3) * 4);
-        return float2{__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u)};
-    } else {
-        const int c = lane >> 3;
-        const uint16_t x = *reinterpret_cast<const uint16_t*>(
-            b + (j * CPR + (c ^ (j % CPR))) * 16 + (lane & 7) * 2);
-        return float2{__uint_as_float((uint32_t)x << 16), 0.f};
-    }
+    const int q = (lane >> 4) & 3, t = lane & 15;
+    const int j = 4 * q + (t >> 2);
+    const int c = ((t & 3) >> 1) ^ (j % CPR);
+    return (uint32_t)(j * D * 2 + c * 16 + (t & 1) * 8);
 }
 
-// Groups of more than four heads (SPLIT) are shared by two workgroups of hs
-// wavefronts on one XCD (blocks b and b + 8; the second may have an idle
-// wavefront, which loads and keeps the barriers but writes nothing), so
-// that more than one group fits on a CU; each reads the unit's keys and
-// values, the second mostly from L2.  Their heads are disjoint, so nothing
-// is combined.
-template <int D, int NL, bool SPLIT>
-__global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a, int g, int hs) {
+__device__ __forceinline__ i16x4 lds_read_tr16(const char* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(p));
+}
+
+// The running max of the new query's logits (log2 units) is raised only
+// when a logit exceeds it by more than this, so that the value accumulators
+// are rescaled rarely; weights stay below 2^8.
+constexpr float kQueryLazy = 8.0f;
+
+// One workgroup per unit, one wavefront per query head.  Groups of more
+// than four heads (WIDE) are held to 128 VGPRs, four wavefronts per SIMD, so
+// that two groups of up to eight wavefronts share a CU (R1-Distill-Qwen-7B
+// shape, g = 7: 1.50 ms per call against 1.68 for two workgroups of four
+// wavefronts per unit, whose second workgroup re-read the keys and values
+// partly from HBM); smaller groups keep three per SIMD and more registers.
+template <int D, int NL, bool WIDE>
+__global__ __launch_bounds__(512, WIDE ? 4 : 1) void decode_kernel(DecodeArgs a, int g) {
     __shared__ __attribute__((aligned(16))) uint16_t k0[DT * D];
     __shared__ __attribute__((aligned(16))) uint16_t k1[DT * D];
     __shared__ __attribute__((aligned(16))) uint16_t k2[DT * D];
@@ -990,21 +1010,14 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a, int g, int hs
     __shared__ double2 tab[2][D / 2];  // cos/sin at t_obs (beacons), at t_q (new query)
     constexpr int NPW = TileLoad<D, NL, DT>::NPW;
     constexpr int NS = D / 16;
+    constexpr int NB = D / 16;  // 16-dim output blocks
 
     const int tid = threadIdx.x;
     const int h = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const bool loader = h < NL;
-    int64_t u = blockIdx.x;
-    int hg = h;  // query head of the group this wavefront attends for
-    if (SPLIT) {
-        const int64_t b = blockIdx.x;
-        u = (b / 16) * 8 + (b % 8);
-        hg = (int)((b / 8) & 1) * hs + h;
-        if (u >= a.n_units) return;  // whole workgroup, before any barrier
-    }
-    const bool active = !SPLIT || hg < g;
-    const int64_t qh = u * g + hg;
+    const int64_t u = blockIdx.x;
+    const int64_t qh = u * g + h;
     const int64_t L = a.L;
     const uint16_t* Ku = a.K + u * a.l_cap * D;
     const uint16_t* Vu = a.V + u * a.l_cap * D;
@@ -1027,8 +1040,8 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a, int g, int hs
     // ones without the beacon rows.
     const int r = lane & 31, hh = lane >> 5;
     const float* src = nullptr;
-    if (active && r < 16 && obs) src = a.beacons + (qh * a.buf_cap + r) * (int64_t)D;
-    else if (active && r == 16) src = a.q + qh * (int64_t)D;
+    if (r < 16 && obs) src = a.beacons + (qh * a.buf_cap + r) * (int64_t)D;
+    else if (r == 16 || r == 20) src = a.q + qh * (int64_t)D;
     float4 x1[NS / 2][2], x2[NS / 2][2];
 #pragma unroll
     for (int s = 0; s < NS / 2; ++s) {
@@ -1041,13 +1054,13 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a, int g, int hs
             x2[s][1] = *reinterpret_cast<const float4*>(src + k + D / 2 + 4);
         }
     }
+    auto load_tile = [&](int64_t base, uint16_t* kd, uint16_t* vd) {
+        ld.template issue<kLoadStreaming>(Ku, L, base, kd, h);
+        ld.template issue<kLoadStreaming>(Vu, L, base, vd, h);
+    };
     if (loader) {
-        ld.template issue<kLoadStreaming>(Ku, L, 0, k0, h);
-        ld.template issue<kLoadStreaming>(Vu, L, 0, v0, h);
-        if (1 < ntiles) {
-            ld.template issue<kLoadStreaming>(Ku, L, DT, k1, h);
-            ld.template issue<kLoadStreaming>(Vu, L, DT, v1, h);
-        }
+        load_tile(0, k0, v0);
+        if (1 < ntiles) load_tile(DT, k1, v1);
     }
     // A full barrier here and in the tile loop: with the LDS-only barrier the
     // decode kernel's beacon rows took 946 instead of 907 us (Qwen3-4B shape).
@@ -1057,7 +1070,7 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a, int g, int hs
     // rotate to zero).
     bf16x8 frag[NS];
     {
-        const double2* cs_tab = tab[r == 16 ? 1 : 0];
+        const double2* cs_tab = tab[(r == 16 || r == 20) ? 1 : 0];
 #pragma unroll
         for (int s = 0; s < NS / 2; ++s) {
             const int k = 16 * s + 8 * hh;
@@ -1070,7 +1083,11 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a, int g, int hs
             frag[s + NS / 2] = __builtin_bit_cast(bf16x8, (uint4{ra.z, ra.w, rb.z, rb.w}));
         }
     }
-    const TileRead<D> rd(lane);
+    // Byte offsets of this lane's key chunks for MFMA step s and of its value
+    // transpose reads for block b are koff ^ 32 s and vto ^ 32 b (the XOR
+    // swizzle permutes 16-byte chunks within a row).  The wide form forms
+    // them per tile from the two bases rather than holding sixteen registers.
+    const uint32_t koff = TileRead<D>(lane).off[0];
     const float c2 = a.c2;
 
     // Beacon rows (accumulators 0..7): running max and sum of exp2, lazily
@@ -1080,7 +1097,14 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a, int g, int hs
 #pragma unroll
     for (int v = 0; v < 8; ++v) { mc[v] = kNegBig; l[v] = 0.f; }
     float m = -__builtin_inff(), ls = 0.f;
-    float o0 = 0.f, o1 = 0.f;
+    f32x4 pv[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) pv[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const uint32_t vto = vt_offset<D>(lane);
+    // Source lane (times 4) of this lane's first weight pair: lane group q
+    // takes keys 4 q .. 4 q + 3 and 16 + 4 q .. 16 + 4 q + 3, even rows the
+    // high parts (lanes 0..31), odd rows the remainders (lanes 32..63).
+    const int wsrc = 4 * ((lane & 1) * 32 + 4 * ((lane >> 4) & 3));
 
 #define BKV_DEC_ITER(it, KC, VC, KN, VN)                                           \
     do {                                                                           \
@@ -1089,60 +1113,81 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a, int g, int hs
             else wait_vm<2 * NPW>();                                               \
         }                                                                          \
         __syncthreads();                                                           \
-        if (loader && (it) + 2 < ntiles) {                                         \
-            ld.template issue<kLoadStreaming>(Ku, L, (int64_t)((it) + 2) * DT, KN, h);                   \
-            ld.template issue<kLoadStreaming>(Vu, L, (int64_t)((it) + 2) * DT, VN, h);                   \
-        }                                                                          \
+        if (loader && (it) + 2 < ntiles) load_tile((int64_t)((it) + 2) * DT, KN, VN); \
+        uint32_t kb = koff, vb = vto;                                              \
+        if constexpr (WIDE) asm volatile("" : "+v"(kb), "+v"(vb));                 \
         f32x16 acc = f32x16{};                                                     \
         {                                                                          \
             const char* kt = reinterpret_cast<const char*>(KC);                    \
             _Pragma("unroll") for (int s = 0; s < NS; ++s) {                       \
-                const uint4 w = *reinterpret_cast<const uint4*>(kt + rd.off[s]);   \
+                const uint4 w = *reinterpret_cast<const uint4*>(kt + (kb ^ (uint32_t)(32 * s))); \
                 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                     \
                     frag[s], __builtin_bit_cast(bf16x8, w), acc, 0, 0, 0);         \
             }                                                                      \
         }                                                                          \
-        const int64_t key = (int64_t)(it) * DT + (lane & 31);                      \
-        if (key >= L) {                                                            \
-            _Pragma("unroll") for (int v = 0; v < 16; ++v) acc[v] = -__builtin_inff(); \
+        if ((int64_t)((it) + 1) * DT > L) {  /* only the last tile is partial */  \
+            if ((int64_t)(it) * DT + (lane & 31) >= L) {                           \
+                _Pragma("unroll") for (int v = 0; v < 16; ++v) acc[v] = -__builtin_inff(); \
+            }                                                                      \
         }                                                                          \
         if (obs) {                                                                 \
-            float tsum[8];                                                         \
-            float big = 0.f;                                                       \
+            /* exponents against the running maxima; raise those only when a  \
+               term would pass kRescaleBig (log2 64), then add the terms */    \
+            float e[8];                                                            \
+            float big = -__builtin_inff();                                         \
             _Pragma("unroll") for (int v = 0; v < 8; ++v) {                        \
-                tsum[v] = exp2_sum(fmaf(acc[v], c2, -mc[v]));                      \
-                big = vmax(big, tsum[v]);                                          \
+                e[v] = fmaf(acc[v], c2, -mc[v]);                                   \
+                big = vmax(big, e[v]);                                             \
             }                                                                      \
-            if (__builtin_amdgcn_ballot_w64(!(big <= kRescaleBig)) == 0) {         \
-                _Pragma("unroll") for (int v = 0; v < 8; ++v) l[v] += tsum[v];     \
-            } else {                                                               \
+            if (__builtin_amdgcn_ballot_w64(!(big <= kRescaleExp)) != 0) {         \
                 _Pragma("unroll") for (int v = 0; v < 8; ++v) {                    \
                     const float mn = vmax(mc[v], acc[v] * c2);                     \
-                    l[v] = l[v] * exp2_sum(mc[v] - mn) + exp2_sum(fmaf(acc[v], c2, -mn)); \
+                    l[v] *= exp2_sum(mc[v] - mn);                                  \
                     mc[v] = mn;                                                    \
+                    e[v] = fmaf(acc[v], c2, -mn);                                  \
                 }                                                                  \
             }                                                                      \
+            _Pragma("unroll") for (int v = 0; v < 8; ++v) l[v] += exp2_sum(e[v]);  \
         }                                                                          \
-        /* New query: logits in accumulator 8 of lanes 0..31. */                  \
-        const float x = lane < 32 ? acc[8] * c2 : -__builtin_inff();               \
-        float tm = x;                                                              \
-        _Pragma("unroll") for (int o = 1; o < 32; o <<= 1) tm = vmax(tm, __shfl_xor(tm, o)); \
-        const float mt = __builtin_bit_cast(float,                                 \
-            __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, tm)));          \
-        const float mn = vmax(m, mt);                                              \
-        const float alpha = exp2_sum(m - mn);                                      \
-        m = mn;                                                                    \
-        const float p = exp2_sum(x - mn);                                          \
-        ls = ls * alpha + p;                                                       \
-        o0 *= alpha;                                                               \
-        o1 *= alpha;                                                               \
-        _Pragma("unroll") for (int j = 0; j < DT; ++j) {                           \
-            if (j % 8 == 0) __builtin_amdgcn_sched_barrier(0);                     \
-            const float pj = __builtin_bit_cast(float,                             \
-                __builtin_amdgcn_readlane(__builtin_bit_cast(int, p), j));         \
-            const float2 vv = v_pair<D>(VC, j, lane);                              \
-            o0 = fmaf(pj, vv.x, o0);                                               \
-            o1 = fmaf(pj, vv.y, o1);                                               \
+        /* New query: logits in accumulator 8 (rows 16 and 20 of the block both \
+           hold the query, so lanes j and 32 + j both have key j's logit). */  \
+        const float x = acc[8] * c2;                                               \
+        if (__builtin_amdgcn_ballot_w64(x > m + kQueryLazy) != 0) {                \
+            float tm = x;                                                          \
+            _Pragma("unroll") for (int o = 1; o < 32; o <<= 1) tm = vmax(tm, __shfl_xor(tm, o)); \
+            const float mt = __builtin_bit_cast(float,                             \
+                __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, tm)));      \
+            const float alpha = exp2_sum(m - mt);                                  \
+            m = mt;                                                                \
+            ls *= alpha;                                                           \
+            _Pragma("unroll") for (int b = 0; b < NB; ++b) pv[b] *= alpha;         \
+        }                                                                          \
+        const float p = exp2_sum(x - m);                                           \
+        ls += p;  /* lanes 0..31 are summed at the end */                         \
+        bf16x8 wa;                                                                 \
+        {   /* lanes 0..31 hold the high parts, lanes 32..63 the remainders;      \
+               even lanes pack keys j, j + 1, then the A operand is gathered */   \
+            const uint32_t pb = __float_as_uint(p);                                \
+            const uint32_t wb = lane < 32 ? pb                                     \
+                : __float_as_uint(p - __uint_as_float(pb & 0xffff0000u));          \
+            const uint32_t nb = (uint32_t)__builtin_amdgcn_mov_dpp((int)wb, 0xB1, 0xF, 0xF, false); \
+            const int pk = (int)__builtin_amdgcn_perm(nb, wb, 0x07060302u);       \
+            const uint4 g4 = uint4{(uint32_t)__builtin_amdgcn_ds_bpermute(wsrc, pk),      \
+                                   (uint32_t)__builtin_amdgcn_ds_bpermute(wsrc + 8, pk),  \
+                                   (uint32_t)__builtin_amdgcn_ds_bpermute(wsrc + 64, pk), \
+                                   (uint32_t)__builtin_amdgcn_ds_bpermute(wsrc + 72, pk)};\
+            wa = __builtin_bit_cast(bf16x8, g4);                                   \
+        }                                                                          \
+        {                                                                          \
+            const char* vt = reinterpret_cast<const char*>(VC);                    \
+            _Pragma("unroll") for (int b = 0; b < NB; ++b) {                       \
+                const char* pa = vt + (vb ^ (uint32_t)(32 * b));                   \
+                const i16x4 lo4 = lds_read_tr16(pa);                               \
+                const i16x4 hi4 = lds_read_tr16(pa + 32 * D);                      \
+                const bf16x8 vb = __builtin_bit_cast(bf16x8,                       \
+                    __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));    \
+                pv[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, vb, pv[b], 0, 0, 0); \
+            }                                                                      \
         }                                                                          \
     } while (0)
 
@@ -1159,11 +1204,11 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a, int g, int hs
     for (int o = 1; o < 32; o <<= 1) lt += __shfl_xor(lt, o);
     lt = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, lt)));
     const float inv = 1.0f / lt;
-    if (!active) return;  // an idle wavefront of a split group (no barrier follows)
-    if constexpr (D == 128) {
-        *reinterpret_cast<float2*>(a.out + qh * (int64_t)D + 2 * lane) = float2{o0 * inv, o1 * inv};
-    } else {
-        a.out[qh * (int64_t)D + lane] = o0 * inv;
+    {
+        const int q = (lane >> 4) & 3;
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+            if (b % 4 == q) a.out[qh * (int64_t)D + 16 * b + (lane & 15)] = (pv[b][0] + pv[b][1]) * inv;
     }
     constexpr float kLn2 = 0.6931471805599453f;
     if (lane == 0) a.lse_q[qh] = (m + log2f(lt)) * kLn2;
@@ -1187,18 +1232,14 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a, int g, int hs
     }
 }
 
-template __global__ void decode_kernel<128, 4, false>(DecodeArgs, int, int);
-template __global__ void decode_kernel<128, 2, false>(DecodeArgs, int, int);
-template __global__ void decode_kernel<128, 1, false>(DecodeArgs, int, int);
-template __global__ void decode_kernel<64, 4, false>(DecodeArgs, int, int);
-template __global__ void decode_kernel<64, 2, false>(DecodeArgs, int, int);
-template __global__ void decode_kernel<64, 1, false>(DecodeArgs, int, int);
-template __global__ void decode_kernel<128, 4, true>(DecodeArgs, int, int);
-template __global__ void decode_kernel<128, 2, true>(DecodeArgs, int, int);
-template __global__ void decode_kernel<64, 4, true>(DecodeArgs, int, int);
-template __global__ void decode_kernel<64, 2, true>(DecodeArgs, int, int);
-template __global__ void decode_kernel<128, 1, true>(DecodeArgs, int, int);
-template __global__ void decode_kernel<64, 1, true>(DecodeArgs, int, int);
+template __global__ void decode_kernel<128, 4, false>(DecodeArgs, int);
+template __global__ void decode_kernel<128, 2, false>(DecodeArgs, int);
+template __global__ void decode_kernel<128, 1, false>(DecodeArgs, int);
+template __global__ void decode_kernel<64, 4, false>(DecodeArgs, int);
+template __global__ void decode_kernel<64, 2, false>(DecodeArgs, int);
+template __global__ void decode_kernel<64, 1, false>(DecodeArgs, int);
+template __global__ void decode_kernel<128, 4, true>(DecodeArgs, int);
+template __global__ void decode_kernel<64, 4, true>(DecodeArgs, int);
 
 // Every variant is instantiated explicitly, so each gets its host launch stub
 // even though it is launched from one branch of a conditional.
@@ -1313,25 +1354,22 @@ hipError_t launch_decode(const uint16_t* K, const uint16_t* V, int64_t n_units, 
     a.lse_q = lse_q;
     a.lse_obs = lse_obs;
     a.n_units = n_units;
-    // Groups of more than four heads: two workgroups per unit (see decode_kernel).
-    const bool split = g > 4;
-    const int hs = split ? (g + 1) / 2 : g;
-    const dim3 grid(split ? (unsigned)((n_units + 7) / 8 * 16) : (unsigned)n_units);
-    const dim3 block(64 * hs);
-    const int nl = hs >= 4 ? 4 : (hs >= 2 ? 2 : 1);
-#define BKV_LAUNCH_DEC(DD, NN)                                                     \
-    do {                                                                           \
-        if (split) decode_kernel<DD, NN, true><<<grid, block, 0, s>>>(a, g, hs);   \
-        else decode_kernel<DD, NN, false><<<grid, block, 0, s>>>(a, g, hs);        \
-    } while (0)
+    // Groups of more than four heads: the 128-VGPR form (see decode_kernel).
+    const bool wide = g > 4;
+    const dim3 grid((unsigned)n_units);
+    const dim3 block(64 * g);
+    const int nl = g >= 4 ? 4 : (g >= 2 ? 2 : 1);
+#define BKV_LAUNCH_DEC(DD, NN, WW) decode_kernel<DD, NN, WW><<<grid, block, 0, s>>>(a, g)
     if (d == 128) {
-        if (nl == 4) BKV_LAUNCH_DEC(128, 4);
-        else if (nl == 2) BKV_LAUNCH_DEC(128, 2);
-        else BKV_LAUNCH_DEC(128, 1);
+        if (wide) BKV_LAUNCH_DEC(128, 4, true);
+        else if (nl == 4) BKV_LAUNCH_DEC(128, 4, false);
+        else if (nl == 2) BKV_LAUNCH_DEC(128, 2, false);
+        else BKV_LAUNCH_DEC(128, 1, false);
     } else {
-        if (nl == 4) BKV_LAUNCH_DEC(64, 4);
-        else if (nl == 2) BKV_LAUNCH_DEC(64, 2);
-        else BKV_LAUNCH_DEC(64, 1);
+        if (wide) BKV_LAUNCH_DEC(64, 4, true);
+        else if (nl == 4) BKV_LAUNCH_DEC(64, 4, false);
+        else if (nl == 2) BKV_LAUNCH_DEC(64, 2, false);
+        else BKV_LAUNCH_DEC(64, 1, false);
     }
 #undef BKV_LAUNCH_DEC
     return hipGetLastError();

@@ -3,9 +3,9 @@ from known denominators (bkv_score_lse) against the float64 oracle.
 
 The decode kernel streams keys and values in tiles of 32 through rings of
 three LDS tiles; the cases cover one slot, a single partial tile, ragged
-tails with l_cap > L, several ring turns, groups of 2, 4, 5 and 7 and both
-head sizes, a long cache, and the two-workgroup split of groups larger than
-four.  The scoring cases place lse_from so that the tail pass covers one
+tails with l_cap > L, several ring turns, groups of 1, 2, 3, 4, 5, 7 and 8
+and both head sizes, a long cache, and the 128-register form that groups
+larger than four use.  The scoring cases place lse_from so that the tail pass covers one
 tile (the prologue then loads the first tile the backward walk needs beyond
 it, and the walk visits the buffers in the reflected order), two tiles,
 every tile (lse_from = 0) and no slot at all (lse_from = L); the 32-query

@@ -83,6 +83,29 @@ def test_decode_attend_matches_oracle(name, L, l_cap, with_beacons):
     w = _workload(name)
     log(f"decode {name} L={L} l_cap={l_cap} beacons={with_beacons}")
     inp, dev, shape = _setup(w, max(L, 16), l_cap)
+    _check_decode(w, inp, dev, shape, L, with_beacons)
+
+
+@pytest.mark.parametrize("name,L", [("tiny_g7", 300), ("tiny", 203), ("qwen3_4b_layer", 700)])
+def test_decode_late_logit_jump(name, L):
+    """Key j and its negation, both scaled by 64 (exact in bf16), in a late
+    tile: for most rows one of them has a logit far above all earlier ones
+    (measured in float64 on these inputs: the new query's jumps past its lazy
+    threshold of 8 log2 units for 86-100% of the heads, the beacon rows' past
+    64 for 46-82% of the rows), so after many tiles both rescale paths run;
+    the output and every log-sum-exp still match the oracle."""
+    w = _workload(name)
+    log(f"decode late jump {name} L={L}")
+    inp, dev, shape = _setup(w, L, L)
+    j = L - 40
+    inp["keys"][:, j] *= 64.0
+    inp["keys"][:, j + 1] = -inp["keys"][:, j]
+    dev["keys"][:, j] *= 64.0
+    dev["keys"][:, j + 1] = -dev["keys"][:, j]
+    _check_decode(w, inp, dev, shape, L, True)
+
+
+def _check_decode(w, inp, dev, shape, L, with_beacons):
     g, d = w.group, w.d_head
     # The step's query: buffer row 20 of each head, at the newest slot's position.
     q_host = inp["buf"][:, :, 20]                           # [U, g, d]

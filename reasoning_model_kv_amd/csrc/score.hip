@@ -926,8 +926,8 @@ void score_kernel(ScoreArgs a, int g) {
 // cache is the beacon rows' softmax denominator; the new query's own
 // log-sum-exp is a recent row's denominator at the next eviction.
 //
-// Mapping: one workgroup per unit, one wavefront per query head (g <= 4;
-// larger groups are split over two workgroups, see decode_kernel).
+// Mapping: one workgroup per unit, one wavefront per query head (groups of
+// more than four heads in a 128-VGPR form, see decode_kernel).
 // A fragments (rows of the 32 x 32 x 16 MFMA): rows 0..15 the beacons, rows
 // 16 and 20 the new query, the other rows zero; each lane rotates its own
 // row's dims (16 s + 8 (lane / 32) .. + 8 for step s pair with the same dims

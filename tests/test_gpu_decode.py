@@ -35,6 +35,8 @@ def _workload(name):
         return synth.shrink(synth.WORKLOADS["tiny"], group=3, d_head=128, theta=1e6)
     if name == "tiny_g8":
         return synth.shrink(synth.WORKLOADS["tiny"], group=8, d_head=64)
+    if name == "tiny_g8_128":
+        return synth.shrink(synth.WORKLOADS["tiny"], group=8, d_head=128, theta=1e6)
     if name == "long_g4":
         return synth.shrink(synth.WORKLOADS["tiny"], group=4, d_head=128, theta=1e6, h_kv=1)
     return synth.WORKLOADS[name]
@@ -70,6 +72,7 @@ DECODE_CASES = [
     ("tiny_g1", 150, 160),        # one head per group (one loader wavefront)
     ("tiny_g3", 97, 128),         # three wavefronts, two of them loaders
     ("tiny_g8", 129, 160),        # eight wavefronts (512 threads), d 64
+    ("tiny_g8_128", 257, 288),    # eight wavefronts, d 128: the 128-VGPR form
     ("tiny_g7", 300, 320),        # group 7, d 128
     ("tiny_g5", 1000, 1000),      # group 5
     ("qwen3_4b_layer", 2176, 2176),
@@ -168,14 +171,15 @@ SCORE_CASES = [
     ("tiny", 150, 192, 100, "max"),        # three tiles, pass 1 on two: the third at pass 2's start
     ("tiny", 517, 600, 501, "max"),        # 5-key last tile
     ("tiny", 256, 256, 240, "mean"),
-    ("tiny_g7", 300, 320, 284, "max"),     # two workgroups per unit
+    ("tiny_g7", 300, 320, 284, "max"),     # group 7 (the 128-VGPR form)
     ("tiny_g5", 1000, 1000, 984, "max"),
     ("tiny_g7", 256, 256, 0, "max"),       # group 7: every tile in the tail pass
     ("tiny_g7", 256, 256, 256, "max"),     # group 7: no slot added
     ("tiny_g7", 150, 192, 100, "max"),     # group 7: three tiles, pass 1 on two
     ("tiny_g7", 40, 64, 24, "max"),        # group 7: one tile in all
     ("tiny_g5", 517, 600, 501, "mean"),    # group 5: 5-key last tile, mean pooling
-    ("tiny_g8", 300, 300, 284, "mean"),    # split group of eight, mean pooling
+    ("tiny_g8", 300, 300, 284, "mean"),    # group of eight (d 64), mean pooling
+    ("tiny_g8_128", 300, 320, 284, "max"), # group of eight, d 128
     ("tiny_g3", 129, 160, 113, "max"),     # three heads, a 1-key last tile
     ("qwen3_4b_layer", 2176, 2176, 2160, "max"),
 ]

@@ -97,7 +97,7 @@ def test_evict_small_all_units(name):
 @pytest.mark.parametrize("name,samples", [
     ("tiny", None),
     ("qwen3_4b_layer", None),
-    ("r1_qwen_7b", [0, 1791, 3583]),   # group 7: two workgroups per unit add their sums
+    ("r1_qwen_7b", [0, 1791, 3583]),   # group 7: the score kernel's 128-VGPR form
 ])
 def test_evict_mean_pooling(name, samples):
     """The mean-aggregation ablation through the whole step."""

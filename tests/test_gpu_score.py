@@ -26,6 +26,8 @@ def _workload(name):
     if name == "tiny_g5":
         return synth.shrink(synth.WORKLOADS["tiny"], group=5, d_head=128, theta=1e6,
                             h_kv=3)
+    if name == "tiny_g8":
+        return synth.shrink(synth.WORKLOADS["tiny"], group=8, d_head=128, theta=1e6)
     return synth.WORKLOADS[name]
 
 
@@ -67,6 +69,7 @@ CASES = [
     ("tiny_g7", 250, 256, 0),         # group 7, four tiles
     ("tiny_g5", 1000, 1000, 0),       # group 5
     ("tiny_g5", 517, 600, 0),         # group 5, 5-key last tile
+    ("tiny_g8", 300, 320, 0),         # group 8: eight wavefronts (512 threads)
     ("qwen3_4b_layer", None, None, 0),
 ]
 
@@ -103,8 +106,9 @@ def test_score_matches_oracle(name, L, l_cap, t_shift):
 MEAN_CASES = [
     ("tiny", 203, 256),       # ragged tail, l_cap > L
     ("tiny", 40, 64),         # one tile, recent rows masked inside it
-    ("tiny_g7", 300, 320),    # group 7: two workgroups add their sums
+    ("tiny_g7", 300, 320),    # group 7: seven wavefronts, the 128-VGPR form
     ("tiny_g5", 1000, 1000),  # group 5
+    ("tiny_g8", 203, 256),    # group 8
     ("qwen3_4b_layer", None, None),
 ]
 
@@ -140,7 +144,7 @@ WINDOW_CASES = [
     ("tiny", 517, 600, 0),            # 5-key last tile
     ("tiny", 300, 300, 37),           # positions != t-32+i: direct RoPE path, all rows
     ("tiny", 300, 300, "partial"),    # rows 0..7 moved
-    ("tiny_g7", 300, 320, 0),         # group 7 (two workgroups per unit)
+    ("tiny_g7", 300, 320, 0),         # group 7 (the 128-VGPR form)
     ("tiny_g7", 40, 64, 0),           # group 7, one tile
     ("tiny_g7", 150, 150, 0),         # group 7, three tiles
     ("tiny_g5", 1000, 1000, 0),       # group 5

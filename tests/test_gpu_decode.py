@@ -272,6 +272,47 @@ def test_fused_path_full_size_sampled():
     log(f"  one-read vs two-pass max rel diff {rel:.3g}; sampled max rel err {worst:.3g}")
 
 
+@pytest.mark.parametrize("name", ["r1_qwen_7b", "qwen3_4b_full_b2048"])
+def test_decode_full_size_sampled(name):
+    """Decode attention with the beacon rows at the beacon fix (L - 16
+    slots) over every unit of the full workload, in the launch configuration
+    the bench times (R1-Distill-Qwen-7B: groups of seven, the 128-VGPR form);
+    sampled units against the oracle."""
+    w = synth.WORKLOADS[name]
+    U, g, d, L = w.n_units, w.group, w.d_head, w.L
+    Lf = L - 16
+    log(f"decode full size {name}: U={U} g={g} L={Lf}")
+    dev = synth.device_inputs(w, DEV)
+    shape = bkv.Shape(U, g, d, L, w.prefix, w.theta, recent_tok=w.recent_tok)
+    K, V, P = dev["keys"], dev["values"], dev["kpos"]
+    q = dev["buf"][:, 30].contiguous()
+    t_q = int(P[0, Lf - 1])
+    out = torch.empty((U * g, d), device=DEV)
+    lq = torch.empty((U * g,), device=DEV)
+    lo = torch.empty((U * g, 16), device=DEV)
+    bkv.decode_attend(shape, K, V, Lf, q, t_q, out, lq, dev["buf"], L, lo)
+    torch.cuda.synchronize()
+    worst_o, worst_l = 0.0, 0.0
+    for u in (0, U // 2 + 7, U - 1):
+        keys = K[u, :Lf].float().cpu().numpy()
+        vals = V[u, :Lf].float().cpu().numpy()
+        qu = q[u * g:(u + 1) * g].cpu().numpy()
+        ref_o, ref_l = oracle.decode.decode_attention(keys, vals, qu, t_q, w.theta)
+        qhat = oracle.decode.rotated_queries(qu, t_q, w.theta)
+        s = qhat @ np.asarray(keys, np.float64).T / np.sqrt(d)
+        bound = TOL * (np.exp(s - ref_l[:, None]) @ np.abs(np.asarray(vals, np.float64))) + 1e-6
+        err = np.abs(out[u * g:(u + 1) * g].cpu().numpy() - ref_o)
+        assert np.all(err <= bound), f"unit {u}: output error {err.max():.3g}"
+        worst_o = max(worst_o, float((err / bound).max()))
+        dl = np.abs(lq[u * g:(u + 1) * g].cpu().numpy() - ref_l)
+        ref_b = oracle.decode.beacon_lse(keys, dev["buf"][u * g:(u + 1) * g, :16].cpu().numpy(),
+                                         L, w.theta)
+        db = np.abs(lo[u * g:(u + 1) * g].cpu().numpy() - ref_b)
+        assert dl.max() <= TOL and db.max() <= TOL, f"unit {u}: lse errors {dl.max():.3g} {db.max():.3g}"
+        worst_l = max(worst_l, float(dl.max()), float(db.max()))
+    log(f"  output err / bound {worst_o:.3g}, max lse abs err {worst_l:.3g}")
+
+
 @pytest.mark.parametrize("L,l_cap", [(256, 256), (203, 256)])
 def test_score_lse_recent_window(L, l_cap):
     """The baselines' window of 32 recent queries (no beacons): every row's

@@ -225,6 +225,54 @@ class Stream:
         if L == self.b_max:
             self._evict()
 
+    def run(self, k, v, q):
+        """n decode steps at once: k, v bf16 [n, U, d]; q fp32 [n, U*g, d].
+
+        Leaves the same state at every policy event and at the end as n calls
+        of step().  Between events nothing reads the cache, the positions or
+        the query buffers (attention is the caller's), so a stretch of steps
+        that only append is issued together: one bkv_fps_update appending its
+        queries (the fill step with n_new rows) and one write each of the K,
+        V and position slots, instead of four launches per step.  Steps that
+        compress, fix the beacons, switch phase or evict, and the recent
+        phase's steps with fused decode (each attends), run through step(),
+        so an observer sees the same states."""
+        n = k.shape[0]
+        s = 0
+        while s < n:
+            m = min(self._append_run(), n - s)
+            if m <= 1:
+                self.step(k[s], v[s], q[s])
+                s += 1
+            else:
+                self._append_steps(k[s:s + m], v[s:s + m], q[s:s + m])
+                s += m
+
+    def _append_run(self):
+        """How many steps from here only append (and write the cache)."""
+        L, lim = self.L, self.b_max - self.n_recent_q
+        if self.phase == "recent":
+            return 0 if self.fused else self.b_max - 1 - L   # the step reaching b_max evicts
+        room = lim - 1 - L                                     # the step reaching lim switches phase
+        if self.policy == "initial":
+            return min(room, 15 - self.rows) if self.rows < 16 else room
+        return min(room, 31 - self.rows)                       # the step reaching 32 rows compresses
+
+    def _append_steps(self, k, v, q):
+        m, L, t = k.shape[0], self.L, self.t
+        self.last_q = q[-1]
+        self.K[:, L:L + m] = k.transpose(0, 1)
+        self.V[:, L:L + m] = v.transpose(0, 1)
+        self.kpos[:, L:L + m] = torch.arange(t, t + m, dtype=torch.int32, device=self.kpos.device)
+        if self.phase == "recent":
+            bkv.fps_update(self.rshape, self.recents, self.rcount,
+                           q.transpose(0, 1).contiguous(), trigger=self.rshape.buf_cap + 1, m=16)
+        elif self.policy == "fps" or self.rows < 16:
+            bkv.fps_update(self.shape, self.buf, self.count, q.transpose(0, 1).contiguous(),
+                           trigger=self.shape.buf_cap + 1, m=16)
+            self.rows += m
+        self.L, self.t = L + m, t + m
+
     def _step_initial(self, q, L):
         if self.phase == "collect":
             if self.rows < 16:  # one of the first 16 generated queries: append only

@@ -127,7 +127,7 @@ def _oracle_events(w, n_steps, policy="fps"):
 
 
 def _run(w, n_steps, units, chunk=128, policy="fps", unsorted=False, fused=False,
-         every_evict=1, every_fps=1):
+         every_evict=1, every_fps=1, batched=False):
     chk = Checker(w, units, policy, unsorted, every_evict, every_fps)
     st = bstream.Stream(w.n_units, w.group, w.d_head, w.L, w.b_kv, w.prefix, w.theta,
                         device=DEV, observer=chk, beacon_policy=policy, unsorted=unsorted,
@@ -139,9 +139,13 @@ def _run(w, n_steps, units, chunk=128, policy="fps", unsorted=False, fused=False
     while done < n_steps:
         k, v, q = gen.chunk(c, chunk)
         c += 1
-        for s in range(min(chunk, n_steps - done)):
-            st.step(k[s], v[s], q[s])
-        done += min(chunk, n_steps - done)
+        m = min(chunk, n_steps - done)
+        if batched:  # stretches of appends issued together (Stream.run)
+            st.run(k[:m], v[:m], q[:m])
+        else:
+            for s in range(m):
+                st.step(k[s], v[s], q[s])
+        done += m
     torch.cuda.synchronize()
     return st, chk
 
@@ -175,7 +179,8 @@ def test_stream_qwen3_14b_two_intervals_sampled():
 
 def test_stream_qwen3_14b_full_run_sampled():
     """All 32,768 decode steps of the Qwen3-14B shape (5120 units, 226
-    evictions per unit): the cadence equals the oracle's over the whole run,
+    evictions per unit), driven as the streaming bench drives them (chunks of
+    128 steps through Stream.run): the cadence equals the oracle's over the whole run,
     every 16th eviction and every 64th FPS event is checked in lockstep on
     three units spread over the cache, and at the end every unit's positions
     are strictly ascending and every head holds the rows the cadence says."""
@@ -183,7 +188,7 @@ def test_stream_qwen3_14b_full_run_sampled():
     n = w.stream_steps
     units = [0, 2047, w.n_units - 1]
     log(f"stream {w.name}: all {n} steps, units {units}, every 16th eviction checked")
-    st, chk = _run(w, n, units, every_evict=16, every_fps=64)
+    st, chk = _run(w, n, units, every_evict=16, every_fps=64, batched=True)
     assert st.events == _oracle_events(w, n)
     first = w.L - w.prefix
     assert st.n_evictions == 1 + (n - first) // 128 == 226
@@ -263,6 +268,50 @@ def test_stream_qwen3_14b_fused_decode_sampled():
     assert st.events == _oracle_events(w, n)
     assert st.n_evictions == 2 and chk.n["evict"] == 2
     log(f"  max score rel err {chk.worst:.3g}")
+
+
+@pytest.mark.parametrize("policy,unsorted,fused", [("fps", False, False), ("fps", True, False),
+                                                   ("initial", False, False), ("fps", False, True)])
+def test_stream_run_equals_step(policy, unsorted, fused):
+    """Stream.run (stretches of appends issued together) leaves every tensor
+    and host field bit for bit as step() does, over three evictions, with
+    chunks that start and end inside stretches."""
+    w = synth.WORKLOADS["stream_small"]
+    n = 700
+    log(f"stream run vs step ({policy}, unsorted={unsorted}, fused={fused}): {n} steps")
+    gen = synth.StreamInputs(w, DEV)
+    prompt = gen.prompt()
+    chunks = [gen.chunk(c, 128) for c in range((n + 127) // 128)]
+    k = torch.cat([c[0] for c in chunks])[:n]
+    v = torch.cat([c[1] for c in chunks])[:n]
+    q = torch.cat([c[2] for c in chunks])[:n]
+
+    def make():
+        st = bstream.Stream(w.n_units, w.group, w.d_head, w.L, w.b_kv, w.prefix, w.theta,
+                            device=DEV, beacon_policy=policy, unsorted=unsorted,
+                            fused_decode=fused)
+        st.prefill(*prompt)
+        return st
+
+    a, b = make(), make()
+    for i in range(n):
+        a.step(k[i], v[i], q[i])
+    s0 = 0
+    for m in (37, 128, 1, 200, 99, 235):  # 700 steps in uneven chunks
+        b.run(k[s0:s0 + m], v[s0:s0 + m], q[s0:s0 + m])
+        s0 += m
+    assert s0 == n
+    torch.cuda.synchronize()
+    assert a.n_evictions == b.n_evictions >= 3
+    assert a.events == b.events and (a.L, a.t, a.rows, a.phase) == (b.L, b.t, b.rows, b.phase)
+    for name in ("K", "V"):
+        assert torch.equal(getattr(a, name).view(torch.int16), getattr(b, name).view(torch.int16)), name
+    names = ["kpos", "buf", "count", "recents", "rcount", "kept", "score", "sel"]
+    if fused:
+        names += ["lse_in", "lse_obs"]
+    for name in names:
+        assert torch.equal(getattr(a, name), getattr(b, name)), name
+    log(f"  evictions {a.n_evictions}, events {len(a.events)}")
 
 
 @pytest.mark.parametrize("fused", [False, True])

@@ -109,3 +109,59 @@ def test_eviction_refuses_a_buffer_that_is_not_the_beacons(rec):
     st.rows = 20
     with pytest.raises(RuntimeError):
         st._evict()
+
+
+@pytest.mark.parametrize("policy", ["fps", "initial"])
+def test_run_batches_appends_with_the_same_cadence(rec, policy):
+    """Stream.run issues each stretch of append-only steps as one fill call
+    (n_new rows) and keeps every other call, and the event log, as step()
+    makes them; the oracle's log is the same."""
+    b_max, b_kv, prefix, n_steps = 200, 160, 8, 400
+    g, d, P = 1, 64, 20
+
+    def make():
+        st = smod.Stream(1, g, d, b_max=b_max, b_kv=b_kv, prefix=prefix, theta=1e4,
+                         device="cpu", beacon_policy=policy)
+        st.prefill(torch.zeros(1, P, d, dtype=torch.bfloat16),
+                   torch.zeros(1, P, d, dtype=torch.bfloat16), torch.zeros(g, P, d))
+        return st
+
+    a = make()
+    for _ in range(n_steps):
+        a.step(torch.zeros(1, d, dtype=torch.bfloat16), torch.zeros(1, d, dtype=torch.bfloat16),
+               torch.zeros(g, d))
+    calls_a = list(rec.calls)
+    rec.calls.clear()
+    b = make()
+    done = 0
+    for m in (7, 128, 1, 64, 200):
+        b.run(torch.zeros(m, 1, d, dtype=torch.bfloat16), torch.zeros(m, 1, d, dtype=torch.bfloat16),
+              torch.zeros(m, g, d))
+        done += m
+    assert done == n_steps
+    calls_b = list(rec.calls)
+    assert a.events == b.events and (a.L, a.t, a.rows, a.phase) == (b.L, b.t, b.rows, b.phase)
+    assert a.n_evictions == b.n_evictions >= 2
+
+    def split(calls):  # (appended rows per buffer, every other call in order)
+        rows = {}
+        other = []
+        for c in calls:
+            if c[0] == "fps" and c[2] == c[1] + 1:  # append only: trigger past the capacity
+                rows[c[1]] = rows.get(c[1], 0) + c[3]
+            else:
+                other.append(c)
+        return rows, other
+
+    rows_a, other_a = split(calls_a)
+    rows_b, other_b = split(calls_b)
+    assert rows_a == rows_b and other_a == other_b
+    assert len(calls_b) < len(calls_a) / 4
+    ora = oracle.stream.UnitStream(g, d, b_max=b_max, b_kv=b_kv, prefix=prefix, theta=1e4,
+                                   beacons=policy)
+    r = np.random.default_rng(0)
+    ora.prefill(r.standard_normal((P, d)), r.standard_normal((P, d)),
+                r.standard_normal((g, P, d)))
+    for _ in range(n_steps):
+        ora.step(r.standard_normal(d), r.standard_normal(d), r.standard_normal((g, d)))
+    assert b.events == ora.events

@@ -842,7 +842,7 @@ def stream_main(args, w):
 
     st = bstream.Stream(U, g, d, w.L, w.b_kv, w.prefix, w.theta, device=dev, observer=observer,
                         beacon_policy=args.beacon_policy,
-                        unsorted=args.compaction == "unsorted")
+                        unsorted=args.compaction == "unsorted", observe={"evict"})
     gen = synth.StreamInputs(w, dev)
     st.prefill(*gen.prompt())
     torch.cuda.synchronize()

@@ -35,7 +35,7 @@ Writing the new token's key, value and position into the cache is the
 decoder's own work and is done here with plain tensor writes; every step of
 the policy runs in the library.  An optional observer is called with
 (event, stage, stream) before ("pre") and after ("post") every FPS and
-eviction event, for verification.
+eviction event, for verification (or only the event kinds in `observe`).
 """
 from dataclasses import replace
 
@@ -47,7 +47,7 @@ from . import bkv
 class Stream:
     def __init__(self, n_units, group, d_head, b_max, b_kv, prefix, theta, recent_tok=16,
                  device="cuda", observer=None, beacon_policy="fps", unsorted=False,
-                 fused_decode=False):
+                 fused_decode=False, observe=None):
         # The recent phase starts when the cache reaches b_max - n_recent_q, so
         # that n_recent_q queries are collected before the eviction at b_max;
         # after an eviction the cache holds b_kv slots and must lie below that
@@ -82,6 +82,7 @@ class Stream:
         self.score = torch.zeros((U, b_max), dtype=torch.float32, device=dev)
         self.kept = torch.zeros((U, b_kv), dtype=torch.int32, device=dev)
         self.sel = torch.zeros((nq, 16), dtype=torch.int32, device=dev)
+        self._steps = torch.arange(b_max, dtype=torch.int32, device=dev)  # run(): position offsets
         self.ws = bkv.alloc_workspace(self.shape, b_max, b_kv, dev)
         self.L = 0        # live slots (all units)
         self.t = 0        # position of the next token
@@ -89,6 +90,7 @@ class Stream:
         self.phase = "collect"
         self.events = []  # (kind, cache length)
         self.observer = observer
+        self.observe = None if observe is None else frozenset(observe)
         self.n_evictions = 0
         if fused_decode:
             self.attn_out = torch.zeros((nq, d_head), dtype=torch.float32, device=dev)
@@ -134,8 +136,11 @@ class Stream:
         if sd.get("prompt_queries") is not None:
             self.prompt_queries = sd["prompt_queries"].to(self.K.device)
 
+    def _observed(self, kind):
+        return self.observer is not None and (self.observe is None or kind in self.observe)
+
     def _note(self, kind, stage):
-        if self.observer is not None:
+        if self._observed(kind):
             self.observer(kind, stage, self)
 
     def prefill(self, keys, values, queries):
@@ -234,9 +239,12 @@ class Stream:
         that only append is issued together: one bkv_fps_update appending its
         queries (the fill step with n_new rows) and one write each of the K,
         V and position slots, instead of four launches per step.  Steps that
-        compress, fix the beacons, switch phase or evict, and the recent
-        phase's steps with fused decode (each attends), run through step(),
-        so an observer sees the same states."""
+        fix the beacons, switch phase or evict, and the recent phase's steps
+        with fused decode (each attends), run through step().  A step that
+        compresses (or completes the initial references) ends its stretch
+        when nothing observes the stream (the fill call appends, then
+        compresses); when its event is observed it runs alone, so the observer
+        sees the states step() shows it."""
         n = k.shape[0]
         s = 0
         while s < n:
@@ -254,24 +262,35 @@ class Stream:
         if self.phase == "recent":
             return 0 if self.fused else self.b_max - 1 - L   # the step reaching b_max evicts
         room = lim - 1 - L                                     # the step reaching lim switches phase
+        fold = not self._observed("collect_fps")
         if self.policy == "initial":
-            return min(room, 15 - self.rows) if self.rows < 16 else room
-        return min(room, 31 - self.rows)                       # the step reaching 32 rows compresses
+            return min(room, (16 if fold else 15) - self.rows) if self.rows < 16 else room
+        return min(room, (32 if fold else 31) - self.rows)     # the step reaching 32 rows compresses
 
     def _append_steps(self, k, v, q):
         m, L, t = k.shape[0], self.L, self.t
         self.last_q = q[-1]
         self.K[:, L:L + m] = k.transpose(0, 1)
         self.V[:, L:L + m] = v.transpose(0, 1)
-        self.kpos[:, L:L + m] = torch.arange(t, t + m, dtype=torch.int32, device=self.kpos.device)
+        torch.add(self._steps[:m].expand(self.kpos.shape[0], m), t, out=self.kpos[:, L:L + m])
+        self.L, self.t = L + m, t + m
         if self.phase == "recent":
             bkv.fps_update(self.rshape, self.recents, self.rcount,
                            q.transpose(0, 1).contiguous(), trigger=self.rshape.buf_cap + 1, m=16)
-        elif self.policy == "fps" or self.rows < 16:
+        elif self.policy == "fps":
+            compress = self.rows + m >= 32
+            bkv.fps_update(self.shape, self.buf, self.count, q.transpose(0, 1).contiguous(),
+                           trigger=32 if compress else self.shape.buf_cap + 1, m=16,
+                           sel_order=self.sel if compress else None)
+            self.rows = 16 if compress else self.rows + m
+            if compress:
+                self.events.append(("collect_fps", L + m))
+        elif self.rows < 16:
             bkv.fps_update(self.shape, self.buf, self.count, q.transpose(0, 1).contiguous(),
                            trigger=self.shape.buf_cap + 1, m=16)
             self.rows += m
-        self.L, self.t = L + m, t + m
+            if self.rows == 16:
+                self.events.append(("initial_set", L + m))
 
     def _step_initial(self, q, L):
         if self.phase == "collect":

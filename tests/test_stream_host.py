@@ -113,9 +113,10 @@ def test_eviction_refuses_a_buffer_that_is_not_the_beacons(rec):
 
 @pytest.mark.parametrize("policy", ["fps", "initial"])
 def test_run_batches_appends_with_the_same_cadence(rec, policy):
-    """Stream.run issues each stretch of append-only steps as one fill call
-    (n_new rows) and keeps every other call, and the event log, as step()
-    makes them; the oracle's log is the same."""
+    """Stream.run issues each stretch of append-only steps (with no observer,
+    up to and including a compressing step) as one fill call of n_new rows
+    and keeps every other call, and the event log, as step() makes them; the
+    oracle's log is the same."""
     b_max, b_kv, prefix, n_steps = 200, 160, 8, 400
     g, d, P = 1, 64, 20
 
@@ -143,12 +144,14 @@ def test_run_batches_appends_with_the_same_cadence(rec, policy):
     assert a.events == b.events and (a.L, a.t, a.rows, a.phase) == (b.L, b.t, b.rows, b.phase)
     assert a.n_evictions == b.n_evictions >= 2
 
-    def split(calls):  # (appended rows per buffer, every other call in order)
+    def split(calls):  # (rows appended per buffer, every other call in order)
         rows = {}
         other = []
         for c in calls:
-            if c[0] == "fps" and c[2] == c[1] + 1:  # append only: trigger past the capacity
+            if c[0] == "fps":
                 rows[c[1]] = rows.get(c[1], 0) + c[3]
+                if c[2] != c[1] + 1:  # not append-only (trigger within the capacity): a
+                    other.append(c[:3])  # compression, whatever rows it appended first
             else:
                 other.append(c)
         return rows, other

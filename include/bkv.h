@@ -136,7 +136,7 @@ size_t bkv_workspace_bytes(const bkv_dims* dims, const bkv_policy* pol,
  * The cosine matrix of a buffer of up to 32 rows is formed on bf16 MFMA
  * from a high/low split of the fp32 rows (each cosine within about 2^-15 of
  * fp32); other arithmetic is fp32.  Requires
- * 0 <= n_new <= buf_cap, new_q NULL iff n_new == 0,
+ * 0 <= n_new <= buf_cap, new_q NULL iff n_new == 0 (and 16-byte aligned),
  * 1 <= m < trigger <= buf_cap + 1, buf_cap <= 8192 (and m <= 64 when
  * buf_cap > 256 and heads can compress), every count in
  * [0, buf_cap] on entry.  buf and count are updated in place; new_q must not
@@ -146,6 +146,28 @@ int bkv_fps_update(const bkv_dims* dims, const bkv_policy* pol, float* buf,
                    int32_t* count, const float* new_q, int32_t n_new,
                    int32_t trigger, int32_t m, int32_t* sel_order,
                    int32_t* n_overflow, void* stream);
+
+/*
+ * bkv_fps_update_strided -- bkv_fps_update with the new rows at strides.
+ *
+ * The same operation (paper text §4.2, "Continual FPS"; summary steps (2),
+ * (3) and (6)), with head q's new row i read at
+ * new_q + q * q_head_stride + i * q_row_stride (floats) instead of
+ * new_q + (q * n_new + i) * d_head; bkv_fps_update is this call with
+ * q_head_stride = n_new * d_head and q_row_stride = d_head.  It lets a
+ * decode loop append a block of steps' queries held step-major
+ * ([n_new, Uq, d_head]: q_head_stride = d_head, q_row_stride =
+ * Uq * d_head) without first copying them into head-major order.
+ * Requires, besides what bkv_fps_update requires: new_q 16-byte aligned,
+ * both strides multiples of 4, q_head_stride >= 0 and
+ * q_row_stride >= d_head; every row read must lie in the caller's
+ * allocation (the library cannot check it) and must not overlap buf.
+ */
+int bkv_fps_update_strided(const bkv_dims* dims, const bkv_policy* pol, float* buf,
+                           int32_t* count, const float* new_q, int32_t n_new,
+                           int64_t q_head_stride, int64_t q_row_stride,
+                           int32_t trigger, int32_t m, int32_t* sel_order,
+                           int32_t* n_overflow, void* stream);
 
 /*
  * bkv_score -- observation-set attention score of every live slot.

@@ -25,7 +25,7 @@ BKV_FLAG_UNSORTED = 2  # policy flag: bkv_evict fills holes instead of shifting
 EXPORTS = ("bkv_abi_version", "bkv_last_error", "bkv_workspace_bytes", "bkv_fps_update",
            "bkv_score", "bkv_select", "bkv_compact", "bkv_compact_unsorted", "bkv_evict",
            "bkv_score_lse", "bkv_decode_attend", "bkv_select_compact", "bkv_evict_lse",
-           "bkv_evict_noalloc")
+           "bkv_evict_noalloc", "bkv_fps_update_strided")
 
 
 class BkvError(RuntimeError):
@@ -106,6 +106,9 @@ def load_library(path=LIB_PATH):
     lib.bkv_workspace_bytes.argtypes = [_PD, _PP, _I64, _I64]
     lib.bkv_fps_update.restype = ctypes.c_int
     lib.bkv_fps_update.argtypes = [_PD, _PP, _VP, _VP, _VP, _I32, _I32, _I32, _VP, _VP, _VP]
+    lib.bkv_fps_update_strided.restype = ctypes.c_int
+    lib.bkv_fps_update_strided.argtypes = [_PD, _PP, _VP, _VP, _VP, _I32, _I64, _I64, _I32, _I32,
+                                           _VP, _VP, _VP]
     lib.bkv_score.restype = ctypes.c_int
     lib.bkv_score.argtypes = [_PD, _PP, _VP, _VP, _I64, _VP, _VP, _I64, _VP, _VP, _VP,
                               ctypes.c_size_t, _VP]
@@ -200,6 +203,21 @@ def fps_update(shape, buf, count, new_q=None, trigger=32, m=16, sel_order=None,
     _need(new_q, nq * n_new * d, "new_q")
     _need(sel_order, nq * m, "sel_order")
     _need(n_overflow, 1, "n_overflow")
+    if new_q is not None and not new_q.is_contiguous():
+        # A strided view [U*g, n_new, d] (unit stride along d), e.g. a block of
+        # steps' queries [n_new, U*g, d] transposed: bkv_fps_update_strided.
+        if tuple(new_q.shape) != (nq, n_new, d) or new_q.stride(2) != 1:
+            raise ValueError(f"new_q: a strided view must be [{nq}, n_new, {d}] with unit "
+                             f"stride along d, got {tuple(new_q.shape)} strides {new_q.stride()}")
+        if new_q.dtype != torch.float32 or not new_q.is_cuda:
+            raise TypeError("new_q: expected a float32 device tensor")
+        _check(lib.bkv_fps_update_strided(
+            ctypes.byref(shape.dims()), ctypes.byref(shape.policy()),
+            _ptr(buf, torch.float32, "buf"), _ptr(count, torch.int32, "count"),
+            ctypes.c_void_p(new_q.data_ptr()), n_new, new_q.stride(0), new_q.stride(1),
+            int(trigger), int(m), _ptr(sel_order, torch.int32, "sel_order", True),
+            _ptr(n_overflow, torch.int32, "n_overflow", True), _stream(stream)))
+        return
     _check(lib.bkv_fps_update(
         ctypes.byref(shape.dims()), ctypes.byref(shape.policy()),
         _ptr(buf, torch.float32, "buf"), _ptr(count, torch.int32, "count"),

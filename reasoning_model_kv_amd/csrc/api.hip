@@ -210,10 +210,10 @@ size_t bkv_workspace_bytes(const bkv_dims* dims, const bkv_policy* pol, int64_t 
     return ws_layout(dims, pol, b_kv).total;
 }
 
-int bkv_fps_update(const bkv_dims* dims, const bkv_policy* pol, float* buf, int32_t* count,
-                   const float* new_q, int32_t n_new, int32_t trigger, int32_t m,
-                   int32_t* sel_order, int32_t* n_overflow, void* stream) {
-    const char* fn = "bkv_fps_update";
+static int fps_update_impl(const char* fn, const bkv_dims* dims, const bkv_policy* pol,
+                           float* buf, int32_t* count, const float* new_q, int32_t n_new,
+                           int64_t q_head_stride, int64_t q_row_stride, int32_t trigger,
+                           int32_t m, int32_t* sel_order, int32_t* n_overflow, void* stream) {
     CHECK(check_dims(fn, dims));
     CHECK(check_policy(fn, pol));
     if (!buf || !count) return fail(BKV_EINVAL, "%s: NULL buf or count", fn);
@@ -221,6 +221,12 @@ int bkv_fps_update(const bkv_dims* dims, const bkv_policy* pol, float* buf, int3
         return fail(BKV_EINVAL, "%s: n_new %d not in [0, buf_cap=%d]", fn, n_new, pol->buf_cap);
     if ((new_q == nullptr) != (n_new == 0))
         return fail(BKV_EINVAL, "%s: new_q must be NULL exactly when n_new == 0", fn);
+    if (new_q && (q_head_stride < 0 || q_row_stride < dims->d_head || q_head_stride % 4 != 0 ||
+                  q_row_stride % 4 != 0 || (reinterpret_cast<uintptr_t>(new_q) & 15) != 0))
+        return fail(BKV_EINVAL,
+                    "%s: new_q strides (head %lld, row %lld floats) must be multiples of 4, the row "
+                    "stride at least d_head = %d, and new_q 16-byte aligned",
+                    fn, (long long)q_head_stride, (long long)q_row_stride, dims->d_head);
     if (!(1 <= m && m < trigger && trigger <= pol->buf_cap + 1))
         return fail(BKV_EINVAL, "%s: need 1 <= m (%d) < trigger (%d) <= buf_cap + 1 (%d)", fn, m,
                     trigger, pol->buf_cap + 1);
@@ -230,10 +236,26 @@ int bkv_fps_update(const bkv_dims* dims, const bkv_policy* pol, float* buf, int3
     if (dims->n_units == 0) return ok();
     if (fault_injected(fn)) return fail(BKV_EHIP, "%s: injected HIP failure", fn);
     const int64_t n_heads = dims->n_units * dims->group;
-    return hip_result(bkv::launch_fps(buf, count, new_q, n_new, n_heads, dims->d_head,
-                                      pol->buf_cap, trigger, m, sel_order, n_overflow,
-                                      (hipStream_t)stream),
+    return hip_result(bkv::launch_fps(buf, count, new_q, n_new, q_head_stride, q_row_stride,
+                                      n_heads, dims->d_head, pol->buf_cap, trigger, m, sel_order,
+                                      n_overflow, (hipStream_t)stream),
                       fn);
+}
+
+int bkv_fps_update(const bkv_dims* dims, const bkv_policy* pol, float* buf, int32_t* count,
+                   const float* new_q, int32_t n_new, int32_t trigger, int32_t m,
+                   int32_t* sel_order, int32_t* n_overflow, void* stream) {
+    const int64_t d = dims ? dims->d_head : 0;
+    return fps_update_impl("bkv_fps_update", dims, pol, buf, count, new_q, n_new,
+                           (int64_t)n_new * d, d, trigger, m, sel_order, n_overflow, stream);
+}
+
+int bkv_fps_update_strided(const bkv_dims* dims, const bkv_policy* pol, float* buf,
+                           int32_t* count, const float* new_q, int32_t n_new,
+                           int64_t q_head_stride, int64_t q_row_stride, int32_t trigger, int32_t m,
+                           int32_t* sel_order, int32_t* n_overflow, void* stream) {
+    return fps_update_impl("bkv_fps_update_strided", dims, pol, buf, count, new_q, n_new,
+                           q_head_stride, q_row_stride, trigger, m, sel_order, n_overflow, stream);
 }
 
 static int score_impl(const char* fn, const bkv_dims* dims, const bkv_policy* pol,
@@ -437,6 +459,7 @@ static hipError_t evict_launch(const bkv_dims* dims, const bkv_policy* pol, uint
                                 b_kv, nullptr, nullptr, nullptr, dims->l_cap, s);
     if (e == hipSuccess && buf)
         e = bkv::launch_fps(buf, count, recents, pol->n_recent_q,
+                            (int64_t)pol->n_recent_q * dims->d_head, dims->d_head,
                             dims->n_units * dims->group, dims->d_head, pol->buf_cap,
                             pol->n_beacon + pol->n_recent_q, pol->n_beacon, nullptr, nullptr, s);
     return e;

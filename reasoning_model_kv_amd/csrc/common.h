@@ -9,8 +9,9 @@
 namespace bkv {
 
 // Launchers: enqueue kernels, return hipSuccess or the launch error.
+// new_q: head h's new row r at new_q + h * qhs + r * qrs (floats).
 hipError_t launch_fps(float* buf, int32_t* count, const float* new_q,
-                      int32_t n_new, int64_t n_heads, int d, int buf_cap,
+                      int32_t n_new, int64_t qhs, int64_t qrs, int64_t n_heads, int d, int buf_cap,
                       int trigger, int m, int32_t* sel_order,
                       int32_t* n_overflow, hipStream_t s);
 

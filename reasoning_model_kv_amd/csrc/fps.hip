@@ -123,8 +123,8 @@ __device__ __forceinline__ int half_argmin_key(uint32_t k) {
 template <int D>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void fps_wave_kernel(
     float* __restrict__ buf, int32_t* __restrict__ count,
-    const float* __restrict__ new_q, int n_new, int cap, int trigger, int m,
-    int32_t* __restrict__ sel_order, int32_t* __restrict__ n_overflow) {
+    const float* __restrict__ new_q, int n_new, int64_t qhs, int64_t qrs, int cap, int trigger,
+    int m, int32_t* __restrict__ sel_order, int32_t* __restrict__ n_overflow) {
     constexpr int HD = D / 2;   // dims held by one lane of a pair
     constexpr int TS = 33;      // LDS stride (floats) of the transposed rows and of C
     constexpr int RS = D + 4;   // LDS stride (floats) of a staged output row
@@ -142,7 +142,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void fp
     const int row = lane >> 1;
     const int half = lane & 1;
     float* hb = buf + head * (int64_t)cap * D;
-    const float* nq = new_q ? new_q + head * (int64_t)n_new * D : nullptr;
+    const float* nq = new_q ? new_q + head * qhs : nullptr;  // row r at nq + r * qrs
 
     const int cnt = count[head];
     const int N = cnt + n_new;
@@ -156,7 +156,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void fp
         // Append only.
         for (int e = lane * 4; e < n_new * D; e += 64 * 4)
             *reinterpret_cast<float4*>(hb + (int64_t)cnt * D + e) =
-                *reinterpret_cast<const float4*>(nq + e);
+                *reinterpret_cast<const float4*>(nq + (int64_t)(e / D) * qrs + e % D);
         if (lane == 0) count[head] = N;
         return;
     }
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void fp
     float x[HD];
     const bool valid = row < N;
     if (valid) {
-        const float* src = row < cnt ? hb + (int64_t)row * D : nq + (int64_t)(row - cnt) * D;
+        const float* src = row < cnt ? hb + (int64_t)row * D : nq + (int64_t)(row - cnt) * qrs;
         src += half * HD;
 #pragma unroll
         for (int k = 0; k < HD; k += 4) {
@@ -274,8 +274,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void fp
 template <int D>
 __global__ __launch_bounds__(256) void fps_block_kernel(
     float* __restrict__ buf, int32_t* __restrict__ count,
-    const float* __restrict__ new_q, int n_new, int cap, int trigger, int m,
-    int32_t* __restrict__ sel_order, int32_t* __restrict__ n_overflow) {
+    const float* __restrict__ new_q, int n_new, int64_t qhs, int64_t qrs, int cap, int trigger,
+    int m, int32_t* __restrict__ sel_order, int32_t* __restrict__ n_overflow) {
     __shared__ float svec[D];
     __shared__ float bc[D];
     __shared__ float inv_s[256];
@@ -289,7 +289,7 @@ __global__ __launch_bounds__(256) void fps_block_kernel(
     const int lane = tid & 63;
     const int64_t head = blockIdx.x;
     float* hb = buf + head * (int64_t)cap * D;
-    const float* nq = new_q ? new_q + head * (int64_t)n_new * D : nullptr;
+    const float* nq = new_q ? new_q + head * qhs : nullptr;  // row r at nq + r * qrs
 
     const int cnt = count[head];
     const int N = cnt + n_new;
@@ -302,13 +302,13 @@ __global__ __launch_bounds__(256) void fps_block_kernel(
     if (!compress) {
         for (int e = tid * 4; e < n_new * D; e += 256 * 4)
             *reinterpret_cast<float4*>(hb + (int64_t)cnt * D + e) =
-                *reinterpret_cast<const float4*>(nq + e);
+                *reinterpret_cast<const float4*>(nq + (int64_t)(e / D) * qrs + e % D);
         if (tid == 0) count[head] = N;
         return;
     }
 
     auto row_ptr = [&](int j) -> const float* {
-        return j < cnt ? hb + (int64_t)j * D : nq + (int64_t)(j - cnt) * D;
+        return j < cnt ? hb + (int64_t)j * D : nq + (int64_t)(j - cnt) * qrs;
     };
 
     const int row = tid;
@@ -515,8 +515,8 @@ __device__ __forceinline__ float rows_sum_scatter(float (&v)[NI], int c4) {
 template <int D>
 __global__ __launch_bounds__(kLongThreads, 6) void fps_long_kernel(
     float* __restrict__ buf, int32_t* __restrict__ count, const float* __restrict__ new_q,
-    int n_new, int cap, int trigger, int m, int32_t* __restrict__ sel_order,
-    int32_t* __restrict__ n_overflow) {
+    int n_new, int64_t qhs, int64_t qrs, int cap, int trigger, int m,
+    int32_t* __restrict__ sel_order, int32_t* __restrict__ n_overflow) {
     extern __shared__ float dyn[];  // pick rows [m][D], then lb [cap], then ep [cap] bytes
     __shared__ float bc[D];
     __shared__ float part[kLongWaves][D];
@@ -538,7 +538,7 @@ __global__ __launch_bounds__(kLongThreads, 6) void fps_long_kernel(
     const int sub = lane / C4, c4 = lane % C4;
     const int64_t head = blockIdx.x;
     float* hb = buf + head * (int64_t)cap * D;
-    const float* nq = new_q ? new_q + head * (int64_t)n_new * D : nullptr;
+    const float* nq = new_q ? new_q + head * qhs : nullptr;  // row r at nq + r * qrs
 
     const int cnt = count[head];
     const int N = cnt + n_new;
@@ -552,7 +552,7 @@ __global__ __launch_bounds__(kLongThreads, 6) void fps_long_kernel(
     if (!compress) {
         for (int e = tid * 4; e < n_new * D; e += NT * 4)
             *reinterpret_cast<float4*>(hb + (int64_t)cnt * D + e) =
-                *reinterpret_cast<const float4*>(nq + e);
+                *reinterpret_cast<const float4*>(nq + (int64_t)(e / D) * qrs + e % D);
         if (tid == 0) count[head] = N;
         return;
     }
@@ -561,7 +561,7 @@ __global__ __launch_bounds__(kLongThreads, 6) void fps_long_kernel(
     uint8_t* ep = reinterpret_cast<uint8_t*>(lb + cap);
 
     auto row_ptr = [&](int j) -> const float* {
-        return j < cnt ? hb + (int64_t)j * D : nq + (int64_t)(j - cnt) * D;
+        return j < cnt ? hb + (int64_t)j * D : nq + (int64_t)(j - cnt) * qrs;
     };
     auto load4 = [&](int j) -> float4 {
         return (j >= 0 && j < N) ? *reinterpret_cast<const float4*>(row_ptr(j) + 4 * c4)
@@ -905,7 +905,7 @@ __global__ __launch_bounds__(kLongThreads, 6) void fps_long_kernel(
 template <int CPH>
 __global__ __launch_bounds__(256) void fps_append_kernel(
     float* __restrict__ buf, int32_t* __restrict__ count, const float* __restrict__ new_q,
-    int n_new, int d, int cap, int m, int32_t* __restrict__ sel_order,
+    int n_new, int64_t qhs, int64_t qrs, int d, int cap, int m, int32_t* __restrict__ sel_order,
     int32_t* __restrict__ n_overflow, int64_t n_heads) {
     const int64_t head = ((int64_t)blockIdx.x * 256 + threadIdx.x) / CPH;
     const int c = threadIdx.x % CPH;
@@ -920,14 +920,15 @@ __global__ __launch_bounds__(256) void fps_append_kernel(
     }
     if (c < nch)
         reinterpret_cast<float4*>(buf + (head * cap + cnt) * (int64_t)d)[c] =
-            reinterpret_cast<const float4*>(new_q + head * (int64_t)n_new * d)[c];
+            *reinterpret_cast<const float4*>(new_q + head * qhs + (int64_t)(c / (d / 4)) * qrs +
+                                             (c % (d / 4)) * 4);
     if (c == 0) count[head] = cnt + n_new;
 }
 
 }  // namespace
 
 hipError_t launch_fps(float* buf, int32_t* count, const float* new_q,
-                      int32_t n_new, int64_t n_heads, int d, int buf_cap,
+                      int32_t n_new, int64_t qhs, int64_t qrs, int64_t n_heads, int d, int buf_cap,
                       int trigger, int m, int32_t* sel_order,
                       int32_t* n_overflow, hipStream_t s) {
     if (n_heads <= 0) return hipSuccess;
@@ -937,27 +938,27 @@ hipError_t launch_fps(float* buf, int32_t* count, const float* new_q,
         const unsigned blocks32 = (unsigned)((n_heads * 32 + 255) / 256);
         const unsigned blocks64 = (unsigned)((n_heads * 64 + 255) / 256);
         if (nch <= 32)
-            fps_append_kernel<32><<<blocks32, 256, 0, s>>>(buf, count, new_q, n_new, d, buf_cap,
+            fps_append_kernel<32><<<blocks32, 256, 0, s>>>(buf, count, new_q, n_new, qhs, qrs, d, buf_cap,
                                                            m, sel_order, n_overflow, n_heads);
         else
-            fps_append_kernel<64><<<blocks64, 256, 0, s>>>(buf, count, new_q, n_new, d, buf_cap,
+            fps_append_kernel<64><<<blocks64, 256, 0, s>>>(buf, count, new_q, n_new, qhs, qrs, d, buf_cap,
                                                            m, sel_order, n_overflow, n_heads);
         return hipGetLastError();
     }
     const dim3 grid((unsigned)n_heads);
     if (buf_cap <= 32) {
         if (d == 128)
-            fps_wave_kernel<128><<<grid, 64, 0, s>>>(buf, count, new_q, n_new, buf_cap,
+            fps_wave_kernel<128><<<grid, 64, 0, s>>>(buf, count, new_q, n_new, qhs, qrs, buf_cap,
                                                      trigger, m, sel_order, n_overflow);
         else
-            fps_wave_kernel<64><<<grid, 64, 0, s>>>(buf, count, new_q, n_new, buf_cap,
+            fps_wave_kernel<64><<<grid, 64, 0, s>>>(buf, count, new_q, n_new, qhs, qrs, buf_cap,
                                                     trigger, m, sel_order, n_overflow);
     } else if (buf_cap <= 256) {
         if (d == 128)
-            fps_block_kernel<128><<<grid, 256, 0, s>>>(buf, count, new_q, n_new, buf_cap,
+            fps_block_kernel<128><<<grid, 256, 0, s>>>(buf, count, new_q, n_new, qhs, qrs, buf_cap,
                                                        trigger, m, sel_order, n_overflow);
         else
-            fps_block_kernel<64><<<grid, 256, 0, s>>>(buf, count, new_q, n_new, buf_cap,
+            fps_block_kernel<64><<<grid, 256, 0, s>>>(buf, count, new_q, n_new, qhs, qrs, buf_cap,
                                                       trigger, m, sel_order, n_overflow);
     } else {
         if (buf_cap > kLongCap || (m > kLongM && trigger <= buf_cap)) return hipErrorInvalidValue;
@@ -972,10 +973,10 @@ hipError_t launch_fps(float* buf, int32_t* count, const float* new_q,
                 if (e != hipSuccess) return e;
             }
             fps_long_kernel<128><<<grid, kLongThreads, lds, s>>>(
-                buf, count, new_q, n_new, buf_cap, trigger, m, sel_order, n_overflow);
+                buf, count, new_q, n_new, qhs, qrs, buf_cap, trigger, m, sel_order, n_overflow);
         } else {
             fps_long_kernel<64><<<grid, kLongThreads, lds, s>>>(
-                buf, count, new_q, n_new, buf_cap, trigger, m, sel_order, n_overflow);
+                buf, count, new_q, n_new, qhs, qrs, buf_cap, trigger, m, sel_order, n_overflow);
         }
     }
     return hipGetLastError();

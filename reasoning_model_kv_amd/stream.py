@@ -237,7 +237,8 @@ class Stream:
         of step().  Between events nothing reads the cache, the positions or
         the query buffers (attention is the caller's), so a stretch of steps
         that only append is issued together: one bkv_fps_update appending its
-        queries (the fill step with n_new rows) and one write each of the K,
+        queries (the fill step with n_new rows, read in place from the
+        step-major block through the strided entry point) and one write each of the K,
         V and position slots, instead of four launches per step.  Steps that
         fix the beacons, switch phase or evict, and the recent phase's steps
         with fused decode (each attends), run through step().  A step that
@@ -275,18 +276,18 @@ class Stream:
         torch.add(self._steps[:m].expand(self.kpos.shape[0], m), t, out=self.kpos[:, L:L + m])
         self.L, self.t = L + m, t + m
         if self.phase == "recent":
-            bkv.fps_update(self.rshape, self.recents, self.rcount,
-                           q.transpose(0, 1).contiguous(), trigger=self.rshape.buf_cap + 1, m=16)
+            bkv.fps_update(self.rshape, self.recents, self.rcount, q.transpose(0, 1),
+                           trigger=self.rshape.buf_cap + 1, m=16)
         elif self.policy == "fps":
             compress = self.rows + m >= 32
-            bkv.fps_update(self.shape, self.buf, self.count, q.transpose(0, 1).contiguous(),
+            bkv.fps_update(self.shape, self.buf, self.count, q.transpose(0, 1),
                            trigger=32 if compress else self.shape.buf_cap + 1, m=16,
                            sel_order=self.sel if compress else None)
             self.rows = 16 if compress else self.rows + m
             if compress:
                 self.events.append(("collect_fps", L + m))
         elif self.rows < 16:
-            bkv.fps_update(self.shape, self.buf, self.count, q.transpose(0, 1).contiguous(),
+            bkv.fps_update(self.shape, self.buf, self.count, q.transpose(0, 1),
                            trigger=self.shape.buf_cap + 1, m=16)
             self.rows += m
             if self.rows == 16:

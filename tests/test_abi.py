@@ -136,6 +136,29 @@ def test_fps_validation(lib):
         None, None, None)
     assert lcall(1000, 65) == bkv.BKV_ENOTSUP          # long buffers keep at most 64
     assert lcall(1001, 65) == bkv.BKV_OK               # append only: no limit on m
+    # new_q not 16-byte aligned (no units: the checks run before the early
+    # return, and nothing could be launched if they did not)
+    z = _shape(n_units=0)
+    assert lib.bkv_fps_update(ctypes.byref(z.dims()), ctypes.byref(z.policy()), FAKE, FAKE,
+                              ctypes.c_void_p(0x10004), 1, 32, 16, None, None,
+                              None) == bkv.BKV_EINVAL
+
+
+def test_fps_strided_validation(lib):
+    # No units: every check runs before the library's early return, so a
+    # check that failed to refuse would still launch nothing.
+    s = _shape(n_units=0)
+    scall = lambda nq, n_new, hs, rs: lib.bkv_fps_update_strided(
+        ctypes.byref(s.dims()), ctypes.byref(s.policy()), FAKE, FAKE, nq, n_new, hs, rs, 32, 16,
+        None, None, None)
+    d = s.d_head
+    assert scall(FAKE, 2, d, d - 4) == bkv.BKV_EINVAL             # row stride below d_head
+    assert scall(FAKE, 2, d + 2, 2 * d) == bkv.BKV_EINVAL         # head stride not a multiple of 4
+    assert scall(FAKE, 2, -4, d) == bkv.BKV_EINVAL                # negative head stride
+    assert scall(ctypes.c_void_p(0x10008), 2, d, 2 * d) == bkv.BKV_EINVAL  # misaligned new_q
+    assert scall(FAKE, 0, d, d) == bkv.BKV_EINVAL                 # new_q without rows
+    assert scall(FAKE, 33, d, d) == bkv.BKV_EINVAL                # n_new > buf_cap
+    assert scall(FAKE, 2, 4 * d, d) == bkv.BKV_OK                 # valid: accepted, no launch
 
 
 def test_evict_validation_and_workspace(lib):

@@ -294,3 +294,43 @@ def test_long_buffer_append_only():
     assert np.array_equal(got[:, 500:540], newq.cpu().numpy())
     assert np.array_equal(got[:, :500], host[:, :500])
     assert np.array_equal(got[:, 540:], host[:, 540:])
+
+
+@pytest.mark.parametrize("d,cap,cnt,n_new,trigger,m", [
+    (128, 32, 16, 16, 32, 16),     # fill and compress with 16 new rows (one wavefront per head)
+    (128, 32, 10, 7, 33, 16),      # append only, many heads per workgroup
+    (64, 16, 3, 9, 17, 16),        # append only into a recents-sized buffer
+    (128, 64, 40, 24, 64, 16),     # one workgroup per head (buffers of up to 256 rows)
+    (128, 400, 300, 100, 400, 16), # long buffers: passes over the rows, lazy shortlist
+])
+def test_strided_new_rows(d, cap, cnt, n_new, trigger, m):
+    """bkv_fps_update_strided reading a step-major block of new rows
+    ([n_new, heads, d], transposed as a view) leaves the buffers, counts and
+    pick orders bit for bit as bkv_fps_update does with the same rows copied
+    head-major; appended rows equal the inputs."""
+    nq = 6
+    log(f"strided new rows d={d} cap={cap} count={cnt} n_new={n_new} trigger={trigger}")
+    r = np.random.default_rng(cap + n_new)
+    host = r.standard_normal((nq, cap, d)).astype(np.float32)
+    block = torch.from_numpy(r.standard_normal((n_new, nq, d)).astype(np.float32)).to(DEV)
+    shape = bkv.Shape(n_units=nq, group=1, d_head=d, l_cap=64, prefix=0, rope_theta=1e6,
+                      buf_cap=cap)
+    out = []
+    for view in (block.transpose(0, 1).contiguous(), block.transpose(0, 1)):
+        buf = torch.from_numpy(host.copy()).to(DEV)
+        count = torch.full((nq,), cnt, dtype=torch.int32, device=DEV)
+        sel = torch.full((nq, m), -7, dtype=torch.int32, device=DEV)
+        bkv.fps_update(shape, buf, count, view, trigger=trigger, m=m, sel_order=sel)
+        torch.cuda.synchronize()
+        out.append((buf.cpu().numpy(), count.cpu().numpy(), sel.cpu().numpy()))
+    (b0, c0, s0), (b1, c1, s1) = out
+    assert np.array_equal(c0, c1) and np.array_equal(s0, s1)
+    live = int(c0[0])
+    assert np.all(c0 == live)
+    assert np.array_equal(b0[:, :live], b1[:, :live])
+    if trigger > cap:  # append only: the rows land after the old ones, unchanged
+        assert live == cnt + n_new
+        assert np.array_equal(b1[:, cnt:live], block.transpose(0, 1).cpu().numpy())
+        assert np.array_equal(b1[:, :cnt], host[:, :cnt])
+    else:
+        assert live == m and np.all(s1 >= 0)

@@ -162,6 +162,8 @@ int bkv_fps_update(const bkv_dims* dims, const bkv_policy* pol, float* buf,
  * both strides multiples of 4, q_head_stride >= 0 and
  * q_row_stride >= d_head; every row read must lie in the caller's
  * allocation (the library cannot check it) and must not overlap buf.
+ * Buffers of more than 256 rows take other strides only for appends of
+ * at most 64 16-byte chunks per head (BKV_ENOTSUP otherwise).
  */
 int bkv_fps_update_strided(const bkv_dims* dims, const bkv_policy* pol, float* buf,
                            int32_t* count, const float* new_q, int32_t n_new,

@@ -233,6 +233,12 @@ static int fps_update_impl(const char* fn, const bkv_dims* dims, const bkv_polic
     if (pol->buf_cap > 256 && m > 64 && trigger <= pol->buf_cap)
         return fail(BKV_ENOTSUP, "%s: buffers of more than 256 rows keep at most 64 (m = %d)", fn,
                     m);
+    const int64_t nch = (int64_t)n_new * dims->d_head / 4;
+    const bool append_kernel = trigger > pol->buf_cap && n_new > 0 && nch <= 64;
+    if (pol->buf_cap > 256 && new_q && !append_kernel &&
+        (q_row_stride != dims->d_head || q_head_stride != (int64_t)n_new * dims->d_head))
+        return fail(BKV_ENOTSUP, "%s: buffers of more than 256 rows take head-major contiguous "
+                    "new rows", fn);
     if (dims->n_units == 0) return ok();
     if (fault_injected(fn)) return fail(BKV_EHIP, "%s: injected HIP failure", fn);
     const int64_t n_heads = dims->n_units * dims->group;

@@ -515,8 +515,8 @@ __device__ __forceinline__ float rows_sum_scatter(float (&v)[NI], int c4) {
 template <int D>
 __global__ __launch_bounds__(kLongThreads, 6) void fps_long_kernel(
     float* __restrict__ buf, int32_t* __restrict__ count, const float* __restrict__ new_q,
-    int n_new, int64_t qhs, int64_t qrs, int cap, int trigger, int m,
-    int32_t* __restrict__ sel_order, int32_t* __restrict__ n_overflow) {
+    int n_new, int cap, int trigger, int m, int32_t* __restrict__ sel_order,
+    int32_t* __restrict__ n_overflow) {
     extern __shared__ float dyn[];  // pick rows [m][D], then lb [cap], then ep [cap] bytes
     __shared__ float bc[D];
     __shared__ float part[kLongWaves][D];
@@ -538,7 +538,7 @@ __global__ __launch_bounds__(kLongThreads, 6) void fps_long_kernel(
     const int sub = lane / C4, c4 = lane % C4;
     const int64_t head = blockIdx.x;
     float* hb = buf + head * (int64_t)cap * D;
-    const float* nq = new_q ? new_q + head * qhs : nullptr;  // row r at nq + r * qrs
+    const float* nq = new_q ? new_q + head * (int64_t)n_new * D : nullptr;
 
     const int cnt = count[head];
     const int N = cnt + n_new;
@@ -552,7 +552,7 @@ __global__ __launch_bounds__(kLongThreads, 6) void fps_long_kernel(
     if (!compress) {
         for (int e = tid * 4; e < n_new * D; e += NT * 4)
             *reinterpret_cast<float4*>(hb + (int64_t)cnt * D + e) =
-                *reinterpret_cast<const float4*>(nq + (int64_t)(e / D) * qrs + e % D);
+                *reinterpret_cast<const float4*>(nq + e);
         if (tid == 0) count[head] = N;
         return;
     }
@@ -561,7 +561,7 @@ __global__ __launch_bounds__(kLongThreads, 6) void fps_long_kernel(
     uint8_t* ep = reinterpret_cast<uint8_t*>(lb + cap);
 
     auto row_ptr = [&](int j) -> const float* {
-        return j < cnt ? hb + (int64_t)j * D : nq + (int64_t)(j - cnt) * qrs;
+        return j < cnt ? hb + (int64_t)j * D : nq + (int64_t)(j - cnt) * D;
     };
     auto load4 = [&](int j) -> float4 {
         return (j >= 0 && j < N) ? *reinterpret_cast<const float4*>(row_ptr(j) + 4 * c4)
@@ -962,6 +962,8 @@ hipError_t launch_fps(float* buf, int32_t* count, const float* new_q,
                                                       trigger, m, sel_order, n_overflow);
     } else {
         if (buf_cap > kLongCap || (m > kLongM && trigger <= buf_cap)) return hipErrorInvalidValue;
+        // Long buffers take their new rows head-major and contiguous.
+        if (n_new > 0 && (qrs != d || qhs != (int64_t)n_new * d)) return hipErrorInvalidValue;
         // Pick rows [min(m, kLongM)][d] floats, lb [buf_cap] floats, ep [buf_cap] bytes.
         const size_t lds = ((size_t)std::min(m, kLongM) * d * 4 + (size_t)buf_cap * 5 + 15) &
                            ~(size_t)15;
@@ -973,10 +975,10 @@ hipError_t launch_fps(float* buf, int32_t* count, const float* new_q,
                 if (e != hipSuccess) return e;
             }
             fps_long_kernel<128><<<grid, kLongThreads, lds, s>>>(
-                buf, count, new_q, n_new, qhs, qrs, buf_cap, trigger, m, sel_order, n_overflow);
+                buf, count, new_q, n_new, buf_cap, trigger, m, sel_order, n_overflow);
         } else {
             fps_long_kernel<64><<<grid, kLongThreads, lds, s>>>(
-                buf, count, new_q, n_new, qhs, qrs, buf_cap, trigger, m, sel_order, n_overflow);
+                buf, count, new_q, n_new, buf_cap, trigger, m, sel_order, n_overflow);
         }
     }
     return hipGetLastError();

@@ -159,6 +159,13 @@ def test_fps_strided_validation(lib):
     assert scall(FAKE, 0, d, d) == bkv.BKV_EINVAL                 # new_q without rows
     assert scall(FAKE, 33, d, d) == bkv.BKV_EINVAL                # n_new > buf_cap
     assert scall(FAKE, 2, 4 * d, d) == bkv.BKV_OK                 # valid: accepted, no launch
+    big = _shape(n_units=0, buf_cap=1000)
+    bcall = lambda n_new, hs, rs, trig: lib.bkv_fps_update_strided(
+        ctypes.byref(big.dims()), ctypes.byref(big.policy()), FAKE, FAKE, FAKE, n_new, hs, rs,
+        trig, 16, None, None, None)
+    assert bcall(100, d, 6 * d, 1000) == bkv.BKV_ENOTSUP          # long buffers: head-major only
+    assert bcall(100, 100 * d, d, 1000) == bkv.BKV_OK             # ... which they take
+    assert bcall(2, d, 6 * d, 1001) == bkv.BKV_OK                 # small appends: any strides
 
 
 def test_evict_validation_and_workspace(lib):

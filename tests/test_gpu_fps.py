@@ -301,13 +301,13 @@ def test_long_buffer_append_only():
     (128, 32, 10, 7, 33, 16),      # append only, many heads per workgroup
     (64, 16, 3, 9, 17, 16),        # append only into a recents-sized buffer
     (128, 64, 40, 24, 64, 16),     # one workgroup per head (buffers of up to 256 rows)
-    (128, 400, 300, 100, 400, 16), # long buffers: passes over the rows, lazy shortlist
 ])
 def test_strided_new_rows(d, cap, cnt, n_new, trigger, m):
     """bkv_fps_update_strided reading a step-major block of new rows
     ([n_new, heads, d], transposed as a view) leaves the buffers, counts and
     pick orders bit for bit as bkv_fps_update does with the same rows copied
-    head-major; appended rows equal the inputs."""
+    head-major; appended rows equal the inputs.  (Buffers of more than 256
+    rows take head-major rows only; test_abi checks the refusal.)"""
     nq = 6
     log(f"strided new rows d={d} cap={cap} count={cnt} n_new={n_new} trigger={trigger}")
     r = np.random.default_rng(cap + n_new)

@@ -238,14 +238,14 @@ class Stream:
         the query buffers (attention is the caller's), so a stretch of steps
         that only append is issued together: one bkv_fps_update appending its
         queries (the fill step with n_new rows, read in place from the
-        step-major block through the strided entry point) and one write each of the K,
-        V and position slots, instead of four launches per step.  Steps that
-        fix the beacons, switch phase or evict, and the recent phase's steps
-        with fused decode (each attends), run through step().  A step that
-        compresses (or completes the initial references) ends its stretch
-        when nothing observes the stream (the fill call appends, then
-        compresses); when its event is observed it runs alone, so the observer
-        sees the states step() shows it."""
+        step-major block through the strided entry point) and one write each
+        of the K, V and position slots, instead of four launches per step.
+        Steps that fix the beacons, switch phase or evict, and the recent
+        phase's steps with fused decode (each attends), run through step().
+        The step that completes the initial references ends its stretch, and
+        so does a step that compresses unless that event is observed (the
+        fill call appends, then compresses); an observed one runs alone, so
+        the observer sees the states step() shows it."""
         n = k.shape[0]
         s = 0
         while s < n:
@@ -263,9 +263,9 @@ class Stream:
         if self.phase == "recent":
             return 0 if self.fused else self.b_max - 1 - L   # the step reaching b_max evicts
         room = lim - 1 - L                                     # the step reaching lim switches phase
+        if self.policy == "initial":  # completing the references notifies no observer
+            return min(room, 16 - self.rows) if self.rows < 16 else room
         fold = not self._observed("collect_fps")
-        if self.policy == "initial":
-            return min(room, (16 if fold else 15) - self.rows) if self.rows < 16 else room
         return min(room, (32 if fold else 31) - self.rows)     # the step reaching 32 rows compresses
 
     def _append_steps(self, k, v, q):
